@@ -1,0 +1,323 @@
+"""Plain CPU oracle for the diagonal-batching forward of a layer-level recurrent
+memory transformer (ARMT).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or run this module.  It shares no code
+with the HIP library: it is NumPy on the host, float64 by default, slow and
+written to be read against the pages:
+
+  * paper page "Diagonal Batching Unlocks Parallelism in Recurrent Memory
+    Transformers for Long Contexts" (abstract);
+  * skill page "Diagonal Batching for Recurrent Memory Transformers" (Core
+    Concept, Implementation, Practical Guidance);
+  * Pith review of arXiv 2506.05229 ("What carries the argument", "Extended
+    reading notes", referee report, assumptions, Figures 1-6);
+  * Pith verdict record for arXiv 2506.05229 (skeptic_critique.concrete_test).
+
+The pages define the schedule exactly and name the model family (ARMT, an
+associative-memory PRMT) but print none of its layer or memory equations.  The
+node below follows the plainest reading the rest supports: a Llama-shaped block
+(RMSNorm, RoPE, grouped-query causal attention, SwiGLU, no biases) whose input
+first reads a per-layer associative memory (A_l, z_l) with phi = elu + 1 keys,
+and whose memory-token outputs then update that memory with a gated delta rule.
+Every such reading is listed with the design notes of this repository.
+
+Precision: arithmetic in float64.  For bf16 workloads the activations are
+rounded to bfloat16 (round to nearest even, directly from float64) at the
+storage points the GPU path stores in bf16 -- after the memory read, after each
+RMSNorm, Q/K/V after RoPE, the attention output, each residual add and the
+SwiGLU product.  The memory state (A, z) is stored in float32 after every
+update.  For fp32 workloads activations stay in float64.
+
+Pins (tests marked "not gpu"): schedule brute force and Lemma 3.1; the RMT
+counter-example of the Pith verdict; diagonal == sequential order bitwise and
+wave-shuffle invariance; split (resume) invariance; hand-derived closed forms of
+the memory read and write; the zero-memory node against torch's library
+routines (rms_norm, scaled_dot_product_attention, silu, linear); RoPE against
+complex rotation plus its norm and relative-position invariants; bf16 rounding
+against torch's conversion; phi against torch's elu.  No function here is
+"parity unpinned" with respect to the stated reading; the reading itself (the
+ARMT memory equations) cannot be pinned to the authors' model, which the pages
+do not print.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "waves", "round_bf16", "phi", "sigmoid", "silu", "rms_norm", "rope",
+    "causal_gqa_attention", "mem_read", "mem_write", "node",
+    "forward_sequential", "forward_diagonal", "Oracle",
+]
+
+
+# ---------------------------------------------------------------------------
+# Schedule
+# ---------------------------------------------------------------------------
+
+def waves(n_layers: int, n_segments: int):
+    """Diagonal enumeration of the (segment, layer) grid.
+
+    Wave i holds every node (s, l) with s + l = i, 0 <= s < S, 0 <= l < L; there
+    are S + L - 1 waves (Pith review, "What carries the argument" and "Core
+    claim", Lemma 3.1; skill page, Implementation: positions with constant
+    segment + layer can run in parallel).  Nodes inside a wave are listed by
+    increasing layer.
+    """
+    out = []
+    for i in range(n_segments + n_layers - 1):
+        wave = []
+        for l in range(n_layers):
+            s = i - l
+            if 0 <= s < n_segments:
+                wave.append((s, l))
+        out.append(wave)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Element-wise definitions
+# ---------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as
+    float64.  bfloat16 keeps 8 significant bits and float32's exponent range;
+    values beyond its largest finite value become +-inf."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    # quantum of the 8-bit significand, floored at the smallest subnormal 2**-133
+    q_exp = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(x, -q_exp)), q_exp)   # np.rint: half to even
+    big = np.abs(r) > 3.3895313892515355e38             # largest finite bf16
+    r = np.where(big, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def _identity(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _round_f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def phi(u):
+    """Feature map of the associative memory, elu(u) + 1: u + 1 for u > 0, else
+    exp(u).  Strictly positive, so memory denominators stay positive."""
+    u = np.asarray(u, dtype=np.float64)
+    return np.where(u > 0, u + 1.0, np.exp(np.minimum(u, 0.0)))
+
+
+def sigmoid(u):
+    u = np.asarray(u, dtype=np.float64)
+    e = np.exp(-np.abs(u))
+    return np.where(u >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def silu(u):
+    return np.asarray(u, dtype=np.float64) * sigmoid(u)
+
+
+def rms_norm(h, g, eps):
+    """h / sqrt(mean(h^2) + eps) * g over the last axis (Llama RMSNorm)."""
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rope(x, theta):
+    """Rotary position embedding on x [n, heads, hd], positions 0..n-1.
+
+    Half-split pairing: coordinate i is paired with i + hd/2 and the pair is
+    rotated by angle pos * theta**(-2i/hd) (Llama convention)."""
+    x = np.asarray(x, dtype=np.float64)
+    n, _, hd = x.shape
+    half = hd // 2
+    inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / hd)
+    ang = np.arange(n, dtype=np.float64)[:, None] * inv_freq[None, :]     # [n, half]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+def causal_gqa_attention(Q, K, V):
+    """softmax(Q K^T / sqrt(hd) + causal mask) V per query head.
+
+    Q [n, H, hd], K and V [n, G, hd]; query head j reads key/value head
+    j // (H/G) (contiguous groups).  Returns [n, H*hd].  Each node attends only
+    over its own n rows (segment tokens then memory tokens)."""
+    n, H, hd = Q.shape
+    G = K.shape[1]
+    rep = H // G
+    out = np.empty((n, H, hd), dtype=np.float64)
+    mask = np.triu(np.ones((n, n), dtype=bool), k=1)
+    for j in range(H):
+        kv = j // rep
+        s = (Q[:, j, :] @ K[:, kv, :].T) / math.sqrt(hd)
+        s = np.where(mask, -np.inf, s)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, j, :] = p @ V[:, kv, :]
+    return out.reshape(n, H * hd)
+
+
+# ---------------------------------------------------------------------------
+# Associative memory (read, gated delta-rule write)
+# ---------------------------------------------------------------------------
+
+def mem_read(h, w_mq, A, z, eps):
+    """Read of the layer's associative memory, added to the residual stream.
+
+    q = phi(h W_mq^T) [rows, d_k];  r = (q A^T) / (q . z + eps);  return h + r.
+    A is [d, d_k], z is [d_k].  From the zero state the read is exactly 0."""
+    h = np.asarray(h, dtype=np.float64)
+    q = phi(h @ np.asarray(w_mq, dtype=np.float64).T)
+    num = q @ np.asarray(A, dtype=np.float64).T
+    den = q @ np.asarray(z, dtype=np.float64) + eps
+    return h + num / den[:, None]
+
+
+def mem_write(y_mem, w_mk, w_mv, w_beta, A, z, eps):
+    """Gated delta-rule update of (A, z) from the memory-token outputs.
+
+    k_m = phi(y_m W_mk^T), v_m = y_m W_mv^T, beta_m = sigmoid(y_m . w_beta);
+    vbar_m = (k_m A^T) / (k_m . z + eps) is what the pre-update memory returns
+    for k_m; then A += sum_m beta_m (v_m - vbar_m) k_m^T and z += sum_m k_m.
+    All tokens of one write see the pre-update state.  Returns new (A, z)."""
+    y = np.asarray(y_mem, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    k = phi(y @ np.asarray(w_mk, dtype=np.float64).T)          # [M, d_k]
+    v = y @ np.asarray(w_mv, dtype=np.float64).T               # [M, d]
+    beta = sigmoid(y @ np.asarray(w_beta, dtype=np.float64))   # [M]
+    vbar = (k @ A.T) / (k @ z + eps)[:, None]                  # [M, d]
+    A_new = A + ((beta[:, None] * (v - vbar)).T @ k)           # [d, d_k]
+    z_new = z + k.sum(axis=0)
+    return A_new, z_new
+
+
+# ---------------------------------------------------------------------------
+# One node of the grid and the two schedules
+# ---------------------------------------------------------------------------
+
+class Oracle:
+    """Holds a workload's weights (float64 copies are made per layer on use)
+    and runs nodes.  ``inputs`` is an ``armt_inputs.ArmtInputs``-like object
+    with fields cfg, x, mem_emb, weights (name -> [L, ...]), g_attn, g_mlp."""
+
+    def __init__(self, inputs):
+        self.inp = inputs
+        self.cfg = inputs.cfg
+        self.dtype = np.float64
+        self.R = round_bf16 if self.cfg.dtype == "bf16" else _identity
+
+    def w(self, name, l):
+        return np.asarray(self.inp.weights[name][l], dtype=self.dtype)
+
+    def node_input(self, s, prev=None):
+        """Layer-0 input of segment s: its T token rows, then the M memory
+        token rows; deeper layers take the previous layer's node output."""
+        if prev is not None:
+            return prev
+        T = self.cfg.seg_len
+        x = np.asarray(self.inp.x[s * T:(s + 1) * T], dtype=self.dtype)
+        return np.concatenate([x, np.asarray(self.inp.mem_emb, dtype=self.dtype)], axis=0)
+
+    def node(self, l, h_in, A, z, rows=None):
+        """Node (s, l): memory read, attention block, MLP block, memory write.
+
+        Returns (h_out, A_new, z_new).  With ``rows`` = r < n only the first r
+        rows are computed (causal attention makes them independent of later
+        rows) and the memory write is skipped (A_new, z_new are None)."""
+        c, R = self.cfg, self.R
+        T, H, G, hd = c.seg_len, c.n_heads, c.n_kv_heads, c.head_dim
+        h = np.asarray(h_in, dtype=self.dtype)
+        if rows is not None:
+            h = h[:rows]
+        n = h.shape[0]
+        # 1. memory read
+        h = R(mem_read(h, self.w("w_mq", l), A, z, c.mem_eps))
+        # 2. attention block
+        a = R(rms_norm(h, self.inp.g_attn[l], c.rms_eps))
+        qkv = a @ self.w("w_qkv", l).T
+        Q = qkv[:, :H * hd].reshape(n, H, hd)
+        K = qkv[:, H * hd:(H + G) * hd].reshape(n, G, hd)
+        V = qkv[:, (H + G) * hd:].reshape(n, G, hd)
+        Q = R(rope(Q, c.rope_theta))
+        K = R(rope(K, c.rope_theta))
+        V = R(V)
+        O = R(causal_gqa_attention(Q, K, V))
+        h = R(h + O @ self.w("w_o", l).T)
+        # 3. MLP block
+        b = R(rms_norm(h, self.inp.g_mlp[l], c.rms_eps))
+        U = R(silu(b @ self.w("w_gate", l).T) * (b @ self.w("w_up", l).T))
+        h = R(h + U @ self.w("w_down", l).T)
+        if rows is not None:
+            return h, None, None
+        # 4. memory write from the memory-token rows
+        A_new, z_new = mem_write(h[T:], self.w("w_mk", l), self.w("w_mv", l),
+                                 self.w("w_beta", l), A, z, c.mem_eps)
+        return h, _round_f32(A_new), _round_f32(z_new)
+
+    def initial_state(self, A0=None, z0=None):
+        c = self.cfg
+        L = self.inp.weights["w_qkv"].shape[0]
+        A = [np.zeros((c.d_model, c.d_key)) if A0 is None else _round_f32(A0[l]) for l in range(L)]
+        z = [np.zeros(c.d_key) if z0 is None else _round_f32(z0[l]) for l in range(L)]
+        return A, z
+
+    def run(self, order, n_segments, A0=None, z0=None):
+        """Run the nodes in ``order`` (a list of (s, l)); every node's inputs
+        must already have been produced.  Returns (Y, A, z) with Y [S*T, d] the
+        last layer's segment-token rows and A [L, d, d_k], z [L, d_k]."""
+        c = self.cfg
+        L = self.inp.weights["w_qkv"].shape[0]
+        T = c.seg_len
+        A, z = self.initial_state(A0, z0)
+        out = {}
+        Y = np.zeros((n_segments * T, c.d_model))
+        for (s, l) in order:
+            prev = None if l == 0 else out.pop((s, l - 1))
+            h, A[l], z[l] = self.node(l, self.node_input(s, prev), A[l], z[l])
+            if l == L - 1:
+                Y[s * T:(s + 1) * T] = h[:T]
+            else:
+                out[(s, l)] = h
+        return Y, np.stack(A), np.stack(z)
+
+
+def forward_sequential(inputs, A0=None, z0=None, n_segments=None):
+    """Segment-major order: for s: for l: node(s, l) -- the L*S sequential
+    steps of the baseline schedule (Pith review, Figure 3)."""
+    o = Oracle(inputs)
+    L = inputs.weights["w_qkv"].shape[0]
+    S = n_segments or inputs.x.shape[0] // inputs.cfg.seg_len
+    order = [(s, l) for s in range(S) for l in range(L)]
+    return o.run(order, S, A0, z0)
+
+
+def forward_diagonal(inputs, A0=None, z0=None, n_segments=None, shuffle_seed=None):
+    """Wave order: for each diagonal s + l = i, all its nodes (Pith review,
+    "What carries the argument").  ``shuffle_seed`` permutes the nodes inside
+    every wave, which must not change any result."""
+    o = Oracle(inputs)
+    L = inputs.weights["w_qkv"].shape[0]
+    S = n_segments or inputs.x.shape[0] // inputs.cfg.seg_len
+    rng = None if shuffle_seed is None else np.random.default_rng(shuffle_seed)
+    order = []
+    for wave in waves(L, S):
+        wave = list(wave)
+        if rng is not None:
+            rng.shuffle(wave)
+        order.extend(wave)
+    return o.run(order, S, A0, z0)
+
+
+def node(inputs, l, h_in, A, z, rows=None):
+    """Convenience wrapper: one node of layer l."""
+    return Oracle(inputs).node(l, h_in, A, z, rows)
