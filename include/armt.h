@@ -1,0 +1,205 @@
+/*
+ * armt.h -- C ABI of libarmt.so: the forward pass of a layer-level recurrent
+ * memory transformer (ARMT) on one AMD Instinct MI355X (gfx950), run either
+ * segment-major ("sequential") or by diagonal waves ("diagonal batching").
+ *
+ * What is computed.  A sequence of S segments of T tokens passes through L
+ * layers.  Node (s, l) -- segment s at layer l -- reads layer l's associative
+ * memory (A_l, z_l), runs a Llama-shaped block over its n = T + M rows (the T
+ * segment tokens followed by M memory tokens) and then updates (A_l, z_l) from
+ * its M memory-token rows.  Node (s, l) needs only node (s, l-1)'s hidden
+ * states and node (s-1, l)'s memory state, so all nodes with s + l = i are
+ * independent and the grid runs as S + L - 1 waves, each launched as one
+ * grouped layer over stacked per-layer weights (Pith review of arXiv
+ * 2506.05229, "What carries the argument", Lemma 3.1 and Section 3.3 on
+ * uniform layer geometry; skill page "Diagonal Batching for Recurrent Memory
+ * Transformers", Implementation and Practical Guidance).  Per node:
+ *
+ *   read : h  = R(h_in + (q A^T) / (q . z + mem_eps)),  q = phi(h_in W_mq^T)
+ *   attn : a  = R(rms(h) * g_attn);  Q|K|V = a W_qkv^T;  Q, K = RoPE;  R(Q,K,V)
+ *          O  = R(causal softmax(Q K^T / sqrt(hd)) V), q-head j reads kv-head
+ *               j / (H/G);  h = R(h + O W_o^T)
+ *   mlp  : b  = R(rms(h) * g_mlp);  U = R(silu(b W_gate^T) * (b W_up^T))
+ *          h  = R(h + U W_down^T)            -> node output; rows 0..T-1 of the
+ *                                               last layer are y[sT:(s+1)T]
+ *   write: Y = h[T:n]; k_m = phi(Y_m W_mk^T); v_m = Y_m W_mv^T;
+ *          beta_m = sigmoid(Y_m . w_beta); vbar_m = (k_m A^T) / (k_m . z + mem_eps)
+ *          A += sum_m beta_m (v_m - vbar_m) k_m^T;  z += sum_m k_m
+ *
+ * phi(u) = elu(u) + 1; rms(u) = u / sqrt(mean(u^2) + rms_eps); RoPE pairs
+ * coordinate i with i + hd/2 at angle pos * rope_theta^(-2i/hd), positions
+ * 0..n-1 in every segment.  R() stores in the activation dtype (identity for
+ * ARMT_F32, round-to-nearest-even bfloat16 for ARMT_BF16); products
+ * accumulate in fp32; the memory state (A, z) is always fp32.  The pages name
+ * the model family but print none of these equations: this is the reading the
+ * library implements.
+ *
+ * Conventions.  Every pointer argument that is not documented as host memory
+ * is a device pointer on the HIP device that was current at armt_create.
+ * Matrices are row-major [out_features, in_features], stacked over a leading
+ * layer axis.  All calls return an armt_status; a non-OK return enqueues no
+ * GPU work and armt_last_error() gives a message.  No C++ exception crosses
+ * this boundary.
+ */
+#ifndef ARMT_H
+#define ARMT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ARMT_OK = 0,
+  ARMT_E_INVALID = -1,      /* NULL pointer, non-positive or inconsistent size */
+  ARMT_E_UNSUPPORTED = -2,  /* valid but outside what the kernels implement   */
+  ARMT_E_WORKSPACE = -3,    /* workspace missing, too small or misaligned      */
+  ARMT_E_HIP = -4           /* a HIP runtime call failed                       */
+} armt_status;
+
+typedef enum { ARMT_F32 = 0, ARMT_BF16 = 1 } armt_dtype;
+
+/* Model geometry.  All layers share it (uniform layer geometry, Pith review
+ * assumptions / Section 3.3).  Constraints checked by armt_create:
+ * every size > 0; d_model == n_heads * head_dim; n_heads % n_kv_heads == 0;
+ * head_dim in {32, 64, 128}; d_key == 64; d_model % 64 == 0;
+ * ffn_hidden % 64 == 0; seg_len + n_mem <= 4096; n_mem <= 64;
+ * dtype ARMT_BF16 or ARMT_F32.  Defaults used by the workloads:
+ * rms_eps 1e-5, rope_theta 10000, mem_eps 1e-6. */
+typedef struct {
+  int32_t n_layers;    /* L */
+  int32_t d_model;     /* d */
+  int32_t n_heads;     /* H query heads */
+  int32_t n_kv_heads;  /* G key/value heads */
+  int32_t head_dim;    /* hd */
+  int32_t ffn_hidden;  /* F (SwiGLU hidden size) */
+  int32_t seg_len;     /* T tokens per segment */
+  int32_t n_mem;       /* M memory tokens per segment */
+  int32_t d_key;       /* d_k, phi-key width of the associative memory */
+  int32_t dtype;       /* armt_dtype of activations and weights */
+  float rms_eps;
+  float rope_theta;
+  float mem_eps;
+} armt_config;
+
+/* Stacked weights, all in the config's dtype, device memory.  Borrowed: they
+ * must stay alive and unchanged until armt_destroy. */
+typedef struct {
+  const void *w_qkv;   /* [L, (H + 2G) * hd, d]  rows: Q heads, K heads, V heads */
+  const void *w_o;     /* [L, d, H * hd] */
+  const void *w_gate;  /* [L, F, d] */
+  const void *w_up;    /* [L, F, d] */
+  const void *w_down;  /* [L, d, F] */
+  const void *g_attn;  /* [L, d]  RMSNorm gain before attention */
+  const void *g_mlp;   /* [L, d]  RMSNorm gain before the MLP */
+  const void *w_mq;    /* [L, d_k, d]  memory-read query projection */
+  const void *w_mk;    /* [L, d_k, d]  memory-write key projection */
+  const void *w_mv;    /* [L, d, d]    memory-write value projection */
+  const void *w_beta;  /* [L, d]       memory-write gate */
+  const void *mem_emb; /* [M, d]       memory-token embeddings */
+} armt_weights;
+
+typedef struct armt_handle armt_handle;
+
+/* Bytes of device workspace armt_create needs for this config (host call,
+ * no GPU work).  Returns ARMT_E_INVALID / ARMT_E_UNSUPPORTED for a config
+ * armt_create would reject. */
+int armt_workspace_size(const armt_config *cfg, size_t *bytes);
+
+/* Validate the config, borrow the weights and carve the caller's workspace
+ * (device memory of at least armt_workspace_size bytes, 256-byte aligned,
+ * owned by the caller and not touched by anyone else until armt_destroy).
+ * hip_stream is the hipStream_t every forward is enqueued on (NULL = the
+ * device's null stream).  Uploads the RoPE table (synchronous, once).
+ * On success *out receives a handle to release with armt_destroy. */
+int armt_create(const armt_config *cfg, const armt_weights *w, void *workspace,
+                size_t ws_bytes, void *hip_stream, armt_handle **out);
+
+/* Forward over n_segments segments in segment-major order: for s, for l,
+ * node(s, l) -- the S*L-step baseline schedule (Pith review, Figure 3).
+ *   x     [n_segments * T, d]  input token embeddings (config dtype)
+ *   A0    [L, d, d_k] fp32 initial memory, or NULL for zeros
+ *   z0    [L, d_k]    fp32 initial normaliser, or NULL for zeros
+ *   y     [n_segments * T, d]  last layer's segment-token rows (config dtype)
+ *   A_out [L, d, d_k], z_out [L, d_k]  fp32 memory after the last segment;
+ *         may alias A0 / z0 (streaming a long input chunk by chunk).
+ * Asynchronous on the handle's stream, no host synchronisation; results are
+ * valid once the stream is synchronised.  Calls on one handle must not
+ * overlap (they share the workspace). */
+int armt_forward_sequential(armt_handle *h, const void *x, int32_t n_segments,
+                            const float *A0, const float *z0, void *y,
+                            float *A_out, float *z_out);
+
+/* Same arguments and results; runs the S + L - 1 diagonal waves, each wave's
+ * nodes as one grouped launch per step (Pith review, "What carries the
+ * argument"; abstract on the paper page).  Bitwise identical to
+ * armt_forward_sequential: the kernels never depend on the wave width. */
+int armt_forward_diagonal(armt_handle *h, const void *x, int32_t n_segments,
+                          const float *A0, const float *z0, void *y,
+                          float *A_out, float *z_out);
+
+void armt_destroy(armt_handle *h);
+
+/* Message of the last non-OK status on this thread ("" if none).  Host
+ * memory owned by the library, valid until the next call on this thread. */
+const char *armt_last_error(void);
+
+/* Host-only: the diagonal schedule.  Wave i runs layers l_lo[i]..l_hi[i]
+ * with segment s = i - l (Lemma 3.1: S + L - 1 waves).  l_lo, l_hi are host
+ * arrays of capacity `cap`; *n_waves receives S + L - 1.  ARMT_E_INVALID if
+ * a size is non-positive or cap is too small. */
+int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t *l_lo,
+                       int32_t *l_hi, int32_t cap, int32_t *n_waves);
+
+/* Execution options (host call).  ARMT_OPT_GRAPHS: 1 = replay one captured
+ * hipGraph per wave shape (default), 0 = launch kernels directly.
+ * ARMT_OPT_TIME_KERNEL: k >= 0 brackets every launch of kernel k (an
+ * armt_kernel_id) with HIP events on the handle's stream (forces direct
+ * launches); -1 turns it off. */
+enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1 };
+int armt_set_option(armt_handle *h, int32_t option, int32_t value);
+
+/* Kernels of one wave, in launch order. */
+typedef enum {
+  ARMT_K_MEM_READ = 0,   /* memory read + RMSNorm (attention input) */
+  ARMT_K_QKV = 1,        /* grouped GEMM, RoPE epilogue */
+  ARMT_K_ATTN = 2,       /* batched causal segment attention */
+  ARMT_K_OPROJ = 3,      /* grouped GEMM, residual epilogue */
+  ARMT_K_MLP_NORM = 4,   /* RMSNorm (MLP input) */
+  ARMT_K_GATE_UP = 5,    /* grouped dual GEMM, SiLU * up epilogue */
+  ARMT_K_DOWN = 6,       /* grouped GEMM, residual (+ y rows) epilogue */
+  ARMT_K_MEM_KEYS = 7,   /* memory-write keys, gate, normaliser update */
+  ARMT_K_MEM_UPDATE = 8, /* memory-write delta-rule update of A */
+  ARMT_K_COUNT = 9
+} armt_kernel_id;
+
+/* Accumulated timing of the kernel selected with ARMT_OPT_TIME_KERNEL since it
+ * was selected: total milliseconds, number of launches and the algorithmic
+ * FLOPs and minimum HBM bytes those launches process.  Synchronises the
+ * handle's stream.  All outputs are host pointers. */
+int armt_kernel_stats(armt_handle *h, double *ms, int64_t *launches,
+                      double *flops, double *bytes);
+
+/* Read-only view of an internal workspace buffer, for white-box tests of the
+ * individual steps (host call, no GPU work).  After a forward the buffers hold
+ * the last wave's values, slabbed by layer:
+ *   ARMT_VIEW_ACT0 / ACT1  [L][n][d] node outputs of even / odd waves
+ *   ARMT_VIEW_NORMED       [L][n][d] last RMSNorm output (MLP input)
+ *   ARMT_VIEW_QKV          [L][n][(H+2G)hd] (bf16: V columns unused)
+ *   ARMT_VIEW_VT           [L][G*hd][roundup(n, 64)] (bf16 only)
+ *   ARMT_VIEW_ATTN         [L][n][H*hd]
+ *   ARMT_VIEW_SWIGLU       [L][n][F]
+ *   ARMT_VIEW_A / Z        fp32 state [L][d][d_k] / [L][d_k]
+ * *ptr receives a device pointer into the workspace, *bytes its size. */
+enum { ARMT_VIEW_ACT0 = 0, ARMT_VIEW_ACT1 = 1, ARMT_VIEW_NORMED = 2, ARMT_VIEW_QKV = 3,
+       ARMT_VIEW_VT = 4, ARMT_VIEW_ATTN = 5, ARMT_VIEW_SWIGLU = 6, ARMT_VIEW_A = 7,
+       ARMT_VIEW_Z = 8 };
+int armt_debug_view(armt_handle *h, int32_t which, void **ptr, size_t *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARMT_H */

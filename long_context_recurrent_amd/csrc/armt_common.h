@@ -1,0 +1,53 @@
+// Shared device helpers and the launch-parameter structs of the ARMT kernels.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace armt {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---- element conversions (round to nearest even on the way to bf16) ----
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// phi(u) = elu(u) + 1
+__device__ __forceinline__ float phi_f(float u) { return u > 0.f ? u + 1.f : __expf(u); }
+__device__ __forceinline__ float sigmoid_f(float u) { return 1.f / (1.f + __expf(-u)); }
+
+// Per-call descriptor shared by the kernels of one forward: the caller's
+// input/output pointers and the running wave counter c.  In wave c the node
+// of layer l works on segment s = c - l.  Kept in device memory so captured
+// graphs can be replayed for any call and any wave of the same shape.
+struct CallDesc {
+  const void* x;   // [S*T, d]
+  void* y;         // [S*T, d]
+  int32_t c;       // current wave (diagonal) or s + l (sequential)
+  int32_t n_segments;
+};
+
+// ---- wave reductions -------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+}  // namespace armt

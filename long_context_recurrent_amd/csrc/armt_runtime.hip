@@ -1,0 +1,584 @@
+// Runtime and C ABI of libarmt.so (declared in include/armt.h).
+//
+// Scheduling follows the pages: node (s, l) needs (s, l-1) and (s-1, l), so
+// wave i = {(s, l) : s + l = i} and the S x L grid runs as S + L - 1 waves
+// (Pith review of arXiv 2506.05229, "What carries the argument", Lemma 3.1);
+// each wave is one grouped launch per step over the active layers' stacked
+// weights (skill page "Diagonal Batching for Recurrent Memory Transformers",
+// Architecture Overview: one grouped kernel launch per diagonal), and the
+// per-layer memory state stays on the GPU between waves with no host
+// synchronisation (same page, Practical Guidance).  The sequential baseline
+// (Pith review, Figure 3) runs the same kernels one node at a time.
+//
+// Buffers.  Node outputs live in two slots act[c & 1][L][n][d] (c = wave
+// index; node (s, l) of wave c reads layer l-1's row of slot (c-1) & 1 and
+// writes layer l's row of slot c & 1, so the nodes of one wave never touch a
+// buffer another node of that wave writes).  Per-layer scratch (normalised
+// activations, QKV, V^T, attention output, SwiGLU product, memory-write keys)
+// is indexed by layer, so a node computes at the same addresses in either
+// schedule.  The caller's x and y pointers and the running wave counter sit in
+// a small device descriptor, which lets one captured hipGraph per wave shape
+// (first layer, last layer, slot parity) be replayed for every call and every
+// wave of that shape.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/armt.h"
+#include "armt_kernels.h"
+
+using namespace armt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ARMT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, kbuf, pden, beta, total;
+};
+
+int validate_config(const armt_config* c) {
+  if (!c) return fail(ARMT_E_INVALID, "config is NULL");
+  if (c->n_layers <= 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->ffn_hidden <= 0 || c->seg_len <= 0 || c->n_mem <= 0 || c->d_key <= 0)
+    return fail(ARMT_E_INVALID, "every size in the config must be positive");
+  if (c->dtype != ARMT_F32 && c->dtype != ARMT_BF16) return fail(ARMT_E_INVALID, "dtype must be ARMT_F32 or ARMT_BF16");
+  if (c->d_model != c->n_heads * c->head_dim)
+    return fail(ARMT_E_INVALID, "d_model (%d) must equal n_heads * head_dim (%d)", c->d_model, c->n_heads * c->head_dim);
+  if (c->n_heads % c->n_kv_heads) return fail(ARMT_E_INVALID, "n_heads must be a multiple of n_kv_heads");
+  if (!(c->rms_eps > 0.f) || !(c->mem_eps > 0.f) || !(c->rope_theta > 0.f))
+    return fail(ARMT_E_INVALID, "rms_eps, mem_eps and rope_theta must be positive");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(ARMT_E_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (c->d_key != 64) return fail(ARMT_E_UNSUPPORTED, "d_key must be 64");
+  if (c->d_model % 64 || c->ffn_hidden % 64) return fail(ARMT_E_UNSUPPORTED, "d_model and ffn_hidden must be multiples of 64");
+  if (c->n_mem > 64) return fail(ARMT_E_UNSUPPORTED, "n_mem must be <= 64");
+  const int n = c->seg_len + c->n_mem;
+  if (c->dtype == ARMT_BF16) {
+    if (n > 4096) return fail(ARMT_E_UNSUPPORTED, "seg_len + n_mem must be <= 4096");
+    if (c->d_model > 4096) return fail(ARMT_E_UNSUPPORTED, "d_model must be <= 4096");
+  } else {
+    if (n > 2048) return fail(ARMT_E_UNSUPPORTED, "fp32: seg_len + n_mem must be <= 2048");
+    if (c->d_model > 1024) return fail(ARMT_E_UNSUPPORTED, "fp32: d_model must be <= 1024");
+  }
+  return ARMT_OK;
+}
+
+Layout make_layout(const armt_config* c) {
+  const size_t L = c->n_layers, d = c->d_model, n = c->seg_len + c->n_mem;
+  const size_t n_pad = (n + 63) / 64 * 64;
+  const size_t es = c->dtype == ARMT_BF16 ? 2 : 4;
+  const size_t qkv_dim = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  const size_t hhd = (size_t)c->n_heads * c->head_dim;
+  const size_t M = c->n_mem, dk = c->d_key, F = c->ffn_hidden;
+  Layout lo{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+  lo.desc = take(sizeof(CallDesc));
+  lo.rope = take(n * (c->head_dim / 2) * 2 * sizeof(float));
+  lo.A = take(L * d * dk * 4);
+  lo.z = take(L * dk * 4);
+  lo.act0 = take(L * n * d * es);
+  lo.act1 = take(L * n * d * es);
+  lo.abuf = take(L * n * d * es);
+  lo.qkv = take(L * n * qkv_dim * es);
+  lo.vt = take(c->dtype == ARMT_BF16 ? L * c->n_kv_heads * c->head_dim * n_pad * 2 : 0);
+  lo.attn = take(L * n * hhd * es);
+  lo.ubuf = take(L * n * F * es);
+  lo.kbuf = take(L * M * dk * 4);
+  lo.pden = take(L * M * 16 * 4);
+  lo.beta = take(L * M * 4);
+  lo.total = off;
+  return lo;
+}
+
+enum Sched { SCHED_DIAG = 0, SCHED_SEQ = 1 };
+
+}  // namespace
+
+struct armt_handle {
+  armt_config cfg;
+  armt_weights w;
+  hipStream_t stream = nullptr;
+  hipStream_t cap_stream = nullptr;
+  int device = 0;
+  bool bf16 = true;
+  int n = 0, n_pad = 0, qkv_dim = 0, mb = 13;
+  size_t es = 2;
+  char* ws = nullptr;
+  Layout lo{};
+  CallDesc* desc = nullptr;
+  float* rope = nullptr;
+  float* A = nullptr;
+  float* z = nullptr;
+  void* act[2] = {nullptr, nullptr};
+  void *abuf = nullptr, *qkv = nullptr, *vt = nullptr, *attn = nullptr, *ubuf = nullptr;
+  float *kbuf = nullptr, *pden = nullptr, *beta = nullptr;
+  std::map<std::tuple<int, int, int, int, int>, hipGraphExec_t> graphs;
+  bool use_graphs = true;
+  int time_kernel = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t events_used = 0;
+  int64_t t_launches = 0;
+  double t_flops = 0, t_bytes = 0;
+};
+
+namespace {
+
+// Algorithmic FLOPs and minimum HBM bytes of kernel k for one node.
+void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
+  const armt_config& c = h->cfg;
+  const double n = h->n, d = c.d_model, F = c.ffn_hidden, dk = c.d_key, M = c.n_mem;
+  const double H = c.n_heads, hd = c.head_dim, q = h->qkv_dim, es = (double)h->es;
+  const double tri = n * (n + 1) / 2;
+  double f = 0, b = 0;
+  switch (k) {
+    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 3 * n * d * es + dk * d * es + d * dk * 4; break;
+    case ARMT_K_QKV: f = 2 * n * d * q; b = (n * d + q * d + n * q) * es; break;
+    case ARMT_K_ATTN: f = 4 * tri * hd * H; b = (n * q + n * H * hd) * es; break;
+    case ARMT_K_OPROJ: f = 2 * n * H * hd * d; b = (n * H * hd + d * H * hd + 2 * n * d) * es; break;
+    case ARMT_K_MLP_NORM: f = 0; b = (2 * n * d + d) * es; break;
+    case ARMT_K_GATE_UP: f = 4 * n * d * F; b = (n * d + 2 * F * d + n * F) * es; break;
+    case ARMT_K_DOWN: f = 2 * n * F * d; b = (n * F + d * F + 2 * n * d) * es; break;
+    case ARMT_K_MEM_KEYS: f = 2 * M * d * (dk + 1); b = (M * d + dk * d + d) * es; break;
+    case ARMT_K_MEM_UPDATE: f = 2 * M * d * d + 4 * M * dk * d; b = (M * d + d * d) * es + 2 * d * dk * 4; break;
+  }
+  *flops = f;
+  *bytes = b;
+}
+
+struct StepCtx {
+  armt_handle* h;
+  hipStream_t st;
+  bool timing;
+};
+
+hipError_t timed(StepCtx& cx, int kid, int P, hipError_t (*fn)(const void*, hipStream_t), const void* arg) {
+  armt_handle* h = cx.h;
+  const bool t = cx.timing && h->time_kernel == kid;
+  if (t) {
+    if (h->events_used == h->events.size()) {
+      hipEvent_t a, b;
+      hipError_t e = hipEventCreate(&a);
+      if (e != hipSuccess) return e;
+      e = hipEventCreate(&b);
+      if (e != hipSuccess) return e;
+      h->events.push_back({a, b});
+    }
+    hipError_t e = hipEventRecord(h->events[h->events_used].first, cx.st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = fn(arg, cx.st);
+  if (e != hipSuccess) return e;
+  if (t) {
+    e = hipEventRecord(h->events[h->events_used].second, cx.st);
+    if (e != hipSuccess) return e;
+    h->events_used++;
+    double f, b;
+    node_cost(h, kid, &f, &b);
+    h->t_launches++;
+    h->t_flops += f * P;
+    h->t_bytes += b * P;
+  }
+  return hipSuccess;
+}
+
+struct GemmCall { const armt_handle* h; GemmArgs g; int epi; };
+struct AttnCall { const armt_handle* h; AttnArgs a; };
+struct MemCall { const armt_handle* h; MemArgs m; int which; };
+
+hipError_t run_gemm(const void* p, hipStream_t st) {
+  const GemmCall* c = (const GemmCall*)p;
+  return c->h->bf16 ? launch_gemm_bf16(c->g, c->epi, c->h->mb, st) : launch_gemm_f32(c->g, c->epi, st);
+}
+hipError_t run_attn(const void* p, hipStream_t st) {
+  const AttnCall* c = (const AttnCall*)p;
+  return launch_attention(c->a, c->h->bf16, st);
+}
+hipError_t run_mem(const void* p, hipStream_t st) {
+  const MemCall* c = (const MemCall*)p;
+  switch (c->which) {
+    case ARMT_K_MEM_READ: return launch_mem_read(c->m, c->h->bf16, st);
+    case ARMT_K_MLP_NORM: return launch_rmsnorm(c->m, c->h->bf16, st);
+    case ARMT_K_MEM_KEYS: return launch_mem_keys(c->m, c->h->bf16, st);
+    default: return launch_mem_update(c->m, c->h->bf16, st);
+  }
+}
+
+// Enqueue the kernels of one step: layers l_lo..l_hi of slot parity par.
+hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
+  armt_handle* h = cx.h;
+  const armt_config& c = h->cfg;
+  const int P = l_hi - l_lo + 1;
+  const int d = c.d_model, n = h->n, F = c.ffn_hidden, hhd = c.n_heads * c.head_dim;
+  const int64_t nd = (int64_t)n * d;
+  const size_t es = h->es;
+
+  MemArgs m{};
+  m.P = P; m.l0 = l_lo; m.n = n; m.d = d; m.T = c.seg_len; m.M = c.n_mem; m.dk = c.d_key; m.L = c.n_layers;
+  m.act_prev = h->act[par ^ 1]; m.act_cur = h->act[par]; m.abuf = h->abuf; m.act_stride = nd;
+  m.mem_emb = h->w.mem_emb; m.w_mq = h->w.w_mq; m.w_mk = h->w.w_mk; m.w_mv = h->w.w_mv; m.w_beta = h->w.w_beta;
+  m.A = h->A; m.z = h->z; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
+  m.mem_eps = c.mem_eps; m.rms_eps = c.rms_eps; m.advance = 0;
+
+  GemmArgs g0{};
+  g0.P = P; g0.l0 = l_lo; g0.M = n; g0.T = c.seg_len; g0.last_layer = c.n_layers - 1;
+  g0.head_dim = c.head_dim;
+
+  hipError_t e;
+  // 1. memory read + attention norm
+  {
+    MemCall mc{h, m, ARMT_K_MEM_READ};
+    mc.m.gain = h->w.g_attn;
+    if ((e = timed(cx, ARMT_K_MEM_READ, P, run_mem, &mc)) != hipSuccess) return e;
+  }
+  // 2. QKV projection with RoPE
+  {
+    GemmCall gc{h, g0, EPI_QKV};
+    GemmArgs& g = gc.g;
+    g.A = h->abuf; g.a_stride = nd; g.lda = d;
+    g.B = h->w.w_qkv; g.b_stride = (int64_t)h->qkv_dim * d; g.N = h->qkv_dim; g.K = d;
+    g.C = h->qkv; g.c_stride = (int64_t)n * h->qkv_dim; g.ldc = h->qkv_dim;
+    g.rope_cs = h->rope; g.rope_cols = (c.n_heads + c.n_kv_heads) * c.head_dim;
+    g.v_col0 = g.rope_cols; g.vt = h->vt; g.vt_ld = h->n_pad;
+    g.vt_stride = (int64_t)c.n_kv_heads * c.head_dim * h->n_pad;
+    if ((e = timed(cx, ARMT_K_QKV, P, run_gemm, &gc)) != hipSuccess) return e;
+  }
+  // 3. attention
+  {
+    AttnCall ac{h, {}};
+    AttnArgs& a = ac.a;
+    a.P = P; a.l0 = l_lo; a.qkv = h->qkv; a.qkv_stride = (int64_t)n * h->qkv_dim; a.ld_qkv = h->qkv_dim;
+    a.vt = h->vt; a.vt_stride = (int64_t)c.n_kv_heads * c.head_dim * h->n_pad; a.vt_ld = h->n_pad;
+    a.out = h->attn; a.out_stride = (int64_t)n * hhd; a.ld_out = hhd;
+    a.n = n; a.H = c.n_heads; a.G = c.n_kv_heads; a.hd = c.head_dim;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    if ((e = timed(cx, ARMT_K_ATTN, P, run_attn, &ac)) != hipSuccess) return e;
+  }
+  // 4. output projection + residual
+  {
+    GemmCall gc{h, g0, EPI_RESID};
+    GemmArgs& g = gc.g;
+    g.A = h->attn; g.a_stride = (int64_t)n * hhd; g.lda = hhd;
+    g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
+    g.C = h->act[par]; g.c_stride = nd; g.ldc = d; g.desc = nullptr;
+    if ((e = timed(cx, ARMT_K_OPROJ, P, run_gemm, &gc)) != hipSuccess) return e;
+  }
+  // 5. MLP norm
+  {
+    MemCall mc{h, m, ARMT_K_MLP_NORM};
+    mc.m.gain = h->w.g_mlp;
+    if ((e = timed(cx, ARMT_K_MLP_NORM, P, run_mem, &mc)) != hipSuccess) return e;
+  }
+  // 6. gate/up + SiLU product
+  {
+    GemmCall gc{h, g0, EPI_SWIGLU};
+    GemmArgs& g = gc.g;
+    g.A = h->abuf; g.a_stride = nd; g.lda = d;
+    g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
+    g.C = h->ubuf; g.c_stride = (int64_t)n * F; g.ldc = F;
+    if ((e = timed(cx, ARMT_K_GATE_UP, P, run_gemm, &gc)) != hipSuccess) return e;
+  }
+  // 7. down projection + residual (+ y rows of the last layer)
+  {
+    GemmCall gc{h, g0, EPI_RESID};
+    GemmArgs& g = gc.g;
+    g.A = h->ubuf; g.a_stride = (int64_t)n * F; g.lda = F;
+    g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
+    g.C = h->act[par]; g.c_stride = nd; g.ldc = d; g.desc = h->desc;
+    if ((e = timed(cx, ARMT_K_DOWN, P, run_gemm, &gc)) != hipSuccess) return e;
+  }
+  // 8-9. memory write
+  {
+    MemCall mc{h, m, ARMT_K_MEM_KEYS};
+    if ((e = timed(cx, ARMT_K_MEM_KEYS, P, run_mem, &mc)) != hipSuccess) return e;
+    MemCall mu{h, m, ARMT_K_MEM_UPDATE};
+    mu.m.advance = advance;
+    if ((e = timed(cx, ARMT_K_MEM_UPDATE, P, run_mem, &mu)) != hipSuccess) return e;
+  }
+  (void)es;
+  return hipSuccess;
+}
+
+int run_step(armt_handle* h, int sched, int l_lo, int l_hi, int par, int advance) {
+  const bool timing = h->time_kernel >= 0;
+  if (!h->use_graphs || timing) {
+    StepCtx cx{h, h->stream, timing};
+    hipError_t e = enqueue_step(cx, l_lo, l_hi, par, advance);
+    return e == hipSuccess ? ARMT_OK : hip_fail(e, "kernel launch");
+  }
+  auto key = std::make_tuple(sched, l_lo, l_hi, par, advance);
+  auto it = h->graphs.find(key);
+  if (it == h->graphs.end()) {
+    hipError_t e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+    StepCtx cx{h, h->cap_stream, false};
+    hipError_t le = enqueue_step(cx, l_lo, l_hi, par, advance);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(h->cap_stream, &graph);
+    if (le != hipSuccess) {
+      if (graph) hipGraphDestroy(graph);
+      return hip_fail(le, "kernel launch during capture");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+    it = h->graphs.emplace(key, exec).first;
+  }
+  hipError_t e = hipGraphLaunch(it->second, h->stream);
+  return e == hipSuccess ? ARMT_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+int forward(armt_handle* h, int sched, const void* x, int32_t S, const float* A0, const float* z0,
+            void* y, float* A_out, float* z_out) {
+  if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  if (!x || !y || !A_out || !z_out) return fail(ARMT_E_INVALID, "x, y, A_out and z_out must not be NULL");
+  if (S < 1) return fail(ARMT_E_INVALID, "n_segments must be >= 1 (got %d)", S);
+  const armt_config& c = h->cfg;
+  const int L = c.n_layers;
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  const int64_t a_count = (int64_t)L * c.d_model * c.d_key, z_count = (int64_t)L * c.d_key;
+  if ((e = launch_set_desc(h->desc, x, y, 0, S, h->stream)) != hipSuccess) return hip_fail(e, "set_desc");
+  if ((e = launch_fill_f32(h->A, A0, a_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
+  if ((e = launch_fill_f32(h->z, z0, z_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
+  int rc;
+  if (sched == SCHED_DIAG) {
+    for (int w = 0; w < S + L - 1; ++w) {
+      const int l_lo = w - S + 1 > 0 ? w - S + 1 : 0;
+      const int l_hi = w < L - 1 ? w : L - 1;
+      if ((rc = run_step(h, SCHED_DIAG, l_lo, l_hi, w & 1, 1)) != ARMT_OK) return rc;
+    }
+  } else {
+    for (int s = 0; s < S; ++s)
+      for (int l = 0; l < L; ++l) {
+        // counter = s + l; after the last layer move to (s + 1) + 0
+        const int adv = (l == L - 1) ? 2 - L : 1;
+        if ((rc = run_step(h, SCHED_SEQ, l, l, (s + l) & 1, adv)) != ARMT_OK) return rc;
+      }
+  }
+  if ((e = hipMemcpyAsync(A_out, h->A, a_count * 4, hipMemcpyDeviceToDevice, h->stream)) != hipSuccess)
+    return hip_fail(e, "copy A_out");
+  if ((e = hipMemcpyAsync(z_out, h->z, z_count * 4, hipMemcpyDeviceToDevice, h->stream)) != hipSuccess)
+    return hip_fail(e, "copy z_out");
+  return ARMT_OK;
+}
+
+int pick_row_blocks(int n) {
+  int best = kGemmRowBlocks[0];
+  long best_pad = -1;
+  for (int i = 0; i < kGemmRowBlocksCount; ++i) {
+    const int mb = kGemmRowBlocks[i], bm = 16 * mb;
+    const long padded = (long)((n + bm - 1) / bm) * bm;
+    if (best_pad < 0 || padded < best_pad || (padded == best_pad && mb > best)) {
+      best = mb;
+      best_pad = padded;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int armt_workspace_size(const armt_config* cfg, size_t* bytes) {
+  int rc = validate_config(cfg);
+  if (rc != ARMT_OK) return rc;
+  if (!bytes) return fail(ARMT_E_INVALID, "bytes is NULL");
+  *bytes = make_layout(cfg).total;
+  return ARMT_OK;
+}
+
+int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, size_t ws_bytes,
+                void* hip_stream, armt_handle** out) {
+  int rc = validate_config(cfg);
+  if (rc != ARMT_OK) return rc;
+  if (!w || !out) return fail(ARMT_E_INVALID, "weights and out must not be NULL");
+  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn,
+                        w->g_mlp, w->w_mq, w->w_mk, w->w_mv, w->w_beta, w->mem_emb};
+  for (const void* p : ptrs)
+    if (!p) return fail(ARMT_E_INVALID, "every weight pointer must be non-NULL");
+  const Layout lo = make_layout(cfg);
+  if (!workspace) return fail(ARMT_E_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(ARMT_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < lo.total)
+    return fail(ARMT_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, lo.total);
+
+  armt_handle* h = new (std::nothrow) armt_handle();
+  if (!h) return fail(ARMT_E_INVALID, "out of host memory");
+  h->cfg = *cfg;
+  h->w = *w;
+  h->stream = (hipStream_t)hip_stream;
+  h->bf16 = cfg->dtype == ARMT_BF16;
+  h->es = h->bf16 ? 2 : 4;
+  h->n = cfg->seg_len + cfg->n_mem;
+  h->n_pad = (h->n + 63) / 64 * 64;
+  h->qkv_dim = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+  h->mb = pick_row_blocks(h->n);
+  h->lo = lo;
+  char* base = (char*)workspace;
+  h->ws = base;
+  h->desc = (CallDesc*)(base + lo.desc);
+  h->rope = (float*)(base + lo.rope);
+  h->A = (float*)(base + lo.A);
+  h->z = (float*)(base + lo.z);
+  h->act[0] = base + lo.act0;
+  h->act[1] = base + lo.act1;
+  h->abuf = base + lo.abuf;
+  h->qkv = base + lo.qkv;
+  h->vt = base + lo.vt;
+  h->attn = base + lo.attn;
+  h->ubuf = base + lo.ubuf;
+  h->kbuf = (float*)(base + lo.kbuf);
+  h->pden = (float*)(base + lo.pden);
+  h->beta = (float*)(base + lo.beta);
+
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { delete h; return hip_fail(e, "hipGetDevice"); }
+  e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) { delete h; return hip_fail(e, "hipStreamCreateWithFlags"); }
+
+  // RoPE table: angle = pos * theta^(-2i/hd), computed in double on the host
+  const int half = cfg->head_dim / 2;
+  std::vector<float> tab((size_t)h->n * half * 2);
+  for (int p = 0; p < h->n; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = p * std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      tab[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+      tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  e = hipMemcpy(h->rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
+  // V^T padding columns (keys n .. n_pad-1) must read as zeros; nothing else
+  // ever writes them
+  if (e == hipSuccess && h->bf16) e = hipMemset(h->vt, 0, lo.attn - lo.vt);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    hipStreamDestroy(h->cap_stream);
+    delete h;
+    return hip_fail(e, "workspace initialisation");
+  }
+  *out = h;
+  return ARMT_OK;
+}
+
+int armt_forward_sequential(armt_handle* h, const void* x, int32_t n_segments, const float* A0,
+                            const float* z0, void* y, float* A_out, float* z_out) {
+  return forward(h, SCHED_SEQ, x, n_segments, A0, z0, y, A_out, z_out);
+}
+
+int armt_forward_diagonal(armt_handle* h, const void* x, int32_t n_segments, const float* A0,
+                          const float* z0, void* y, float* A_out, float* z_out) {
+  return forward(h, SCHED_DIAG, x, n_segments, A0, z0, y, A_out, z_out);
+}
+
+void armt_destroy(armt_handle* h) {
+  if (!h) return;
+  hipSetDevice(h->device);
+  for (auto& kv : h->graphs) hipGraphExecDestroy(kv.second);
+  for (auto& ev : h->events) {
+    hipEventDestroy(ev.first);
+    hipEventDestroy(ev.second);
+  }
+  if (h->cap_stream) hipStreamDestroy(h->cap_stream);
+  delete h;
+}
+
+const char* armt_last_error(void) { return g_last_error.c_str(); }
+
+int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t* l_lo, int32_t* l_hi, int32_t cap,
+                       int32_t* n_waves) {
+  if (n_layers <= 0 || n_segments <= 0) return fail(ARMT_E_INVALID, "n_layers and n_segments must be positive");
+  if (!l_lo || !l_hi || !n_waves) return fail(ARMT_E_INVALID, "output arrays must not be NULL");
+  const int nw = n_layers + n_segments - 1;
+  if (cap < nw) return fail(ARMT_E_INVALID, "capacity %d < %d waves", cap, nw);
+  for (int w = 0; w < nw; ++w) {
+    l_lo[w] = w - n_segments + 1 > 0 ? w - n_segments + 1 : 0;
+    l_hi[w] = w < n_layers - 1 ? w : n_layers - 1;
+  }
+  *n_waves = nw;
+  return ARMT_OK;
+}
+
+int armt_set_option(armt_handle* h, int32_t option, int32_t value) {
+  if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  switch (option) {
+    case ARMT_OPT_GRAPHS: h->use_graphs = value != 0; return ARMT_OK;
+    case ARMT_OPT_TIME_KERNEL:
+      if (value < -1 || value >= ARMT_K_COUNT) return fail(ARMT_E_INVALID, "kernel id %d out of range", value);
+      h->time_kernel = value;
+      h->events_used = 0;
+      h->t_launches = 0;
+      h->t_flops = h->t_bytes = 0;
+      return ARMT_OK;
+    default: return fail(ARMT_E_INVALID, "unknown option %d", option);
+  }
+}
+
+int armt_kernel_stats(armt_handle* h, double* ms, int64_t* launches, double* flops, double* bytes) {
+  if (!h || !ms || !launches || !flops || !bytes) return fail(ARMT_E_INVALID, "NULL argument");
+  hipError_t e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  double total = 0;
+  for (size_t i = 0; i < h->events_used; ++i) {
+    float t = 0;
+    e = hipEventElapsedTime(&t, h->events[i].first, h->events[i].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    total += t;
+  }
+  *ms = total;
+  *launches = h->t_launches;
+  *flops = h->t_flops;
+  *bytes = h->t_bytes;
+  return ARMT_OK;
+}
+
+int armt_debug_view(armt_handle* h, int32_t which, void** ptr, size_t* bytes) {
+  if (!h || !ptr || !bytes) return fail(ARMT_E_INVALID, "NULL argument");
+  const Layout& lo = h->lo;
+  size_t at, end;
+  switch (which) {
+    case ARMT_VIEW_ACT0: at = lo.act0; end = lo.act1; break;
+    case ARMT_VIEW_ACT1: at = lo.act1; end = lo.abuf; break;
+    case ARMT_VIEW_NORMED: at = lo.abuf; end = lo.qkv; break;
+    case ARMT_VIEW_QKV: at = lo.qkv; end = lo.vt; break;
+    case ARMT_VIEW_VT: at = lo.vt; end = lo.attn; break;
+    case ARMT_VIEW_ATTN: at = lo.attn; end = lo.ubuf; break;
+    case ARMT_VIEW_SWIGLU: at = lo.ubuf; end = lo.kbuf; break;
+    case ARMT_VIEW_A: at = lo.A; end = lo.z; break;
+    case ARMT_VIEW_Z: at = lo.z; end = lo.act0; break;
+    default: return fail(ARMT_E_INVALID, "unknown view %d", which);
+  }
+  *ptr = h->ws + at;
+  *bytes = end - at;
+  return ARMT_OK;
+}
+
+}  // extern "C"

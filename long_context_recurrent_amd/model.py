@@ -1,0 +1,109 @@
+"""Torch-facing wrapper around the C ABI: owns the workspace and output
+buffers of one libarmt handle.  torch provides device memory and streams only;
+the forward runs entirely in libarmt.so."""
+
+from __future__ import annotations
+
+import torch
+
+from . import armt as _c
+
+WEIGHT_FIELDS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_mlp",
+                 "w_mq", "w_mk", "w_mv", "w_beta", "mem_emb")
+
+
+def make_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden, seg_len, n_mem,
+                d_key=64, dtype="bf16", rms_eps=1e-5, rope_theta=10000.0, mem_eps=1e-6):
+    return _c.armt_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden, seg_len,
+                          n_mem, d_key, _c.ARMT_BF16 if dtype == "bf16" else _c.ARMT_F32,
+                          rms_eps, rope_theta, mem_eps)
+
+
+class ArmtModel:
+    """One handle: ``weights`` maps the armt_weights field names to contiguous
+    device tensors of the config dtype (kept referenced here: the library
+    borrows them)."""
+
+    def __init__(self, cfg: _c.armt_config, weights: dict, stream: torch.cuda.Stream | None = None):
+        self.cfg = cfg
+        self.dtype = torch.bfloat16 if cfg.dtype == _c.ARMT_BF16 else torch.float32
+        self.weights = {}
+        for k in WEIGHT_FIELDS:
+            t = weights[k]
+            if not (t.is_cuda and t.is_contiguous() and t.dtype == self.dtype):
+                raise ValueError(f"weight {k} must be a contiguous {self.dtype} CUDA tensor")
+            self.weights[k] = t
+        self.device = self.weights["w_qkv"].device
+        self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
+        self.ws_bytes = _c.armt_workspace_size(cfg)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = (base + 255) // 256 * 256
+        w = _c.armt_weights(*[self.weights[k].data_ptr() for k in WEIGHT_FIELDS])
+        with torch.cuda.device(self.device):
+            self.handle = _c.armt_create(cfg, w, self.ws_ptr, self.ws_bytes, self.stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _c.armt_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_option(self, option: int, value: int):
+        _c.armt_set_option(self.handle, option, value)
+
+    def kernel_stats(self):
+        return _c.armt_kernel_stats(self.handle)
+
+    def alloc_outputs(self, n_segments: int):
+        c = self.cfg
+        y = torch.empty(n_segments * c.seg_len, c.d_model, dtype=self.dtype, device=self.device)
+        A = torch.empty(c.n_layers, c.d_model, c.d_key, dtype=torch.float32, device=self.device)
+        z = torch.empty(c.n_layers, c.d_key, dtype=torch.float32, device=self.device)
+        return y, A, z
+
+    def forward(self, x: torch.Tensor, schedule: str = "diagonal", A0=None, z0=None, out=None,
+                sync: bool = True):
+        """x [S*T, d] device tensor of the config dtype.  Returns (y, A, z)."""
+        c = self.cfg
+        if x.dim() != 2 or x.shape[1] != c.d_model or x.shape[0] % c.seg_len:
+            raise ValueError("x must be [n_segments * seg_len, d_model]")
+        if x.dtype != self.dtype or not x.is_contiguous() or x.device != self.device:
+            raise ValueError("x must be a contiguous device tensor of the config dtype")
+        S = x.shape[0] // c.seg_len
+        y, A, z = out if out is not None else self.alloc_outputs(S)
+        for t in (A0, z0):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+                raise ValueError("A0 / z0 must be contiguous float32 device tensors")
+        if schedule not in ("diagonal", "sequential"):
+            raise ValueError("schedule must be 'diagonal' or 'sequential'")
+        fn = _c.armt_forward_diagonal if schedule == "diagonal" else _c.armt_forward_sequential
+        # the library's stream must see the inputs the caller's stream produced
+        self.stream.wait_stream(torch.cuda.current_stream(self.device))
+        fn(self.handle, x, S, A0, z0, y, A, z)
+        if sync:
+            self.stream.synchronize()
+        else:
+            torch.cuda.current_stream(self.device).wait_stream(self.stream)
+        return y, A, z
+
+    def view(self, which: str, dtype=None, shape=None):
+        """Device tensor aliasing an internal workspace buffer (tests only)."""
+        ptr, nbytes = _c.armt_debug_view(self.handle, which)
+        off = ptr - self.workspace.data_ptr()
+        raw = self.workspace[off:off + nbytes]
+        dt = dtype or (torch.float32 if which in ("A", "z") else self.dtype)
+        t = raw.view(dt)
+        return t if shape is None else t[: _numel(shape)].view(*shape)
+
+
+def _numel(shape):
+    n = 1
+    for s in shape:
+        n *= s
+    return n

@@ -228,12 +228,13 @@ class Oracle:
         x = np.asarray(self.inp.x[s * T:(s + 1) * T], dtype=self.dtype)
         return np.concatenate([x, np.asarray(self.inp.mem_emb, dtype=self.dtype)], axis=0)
 
-    def node(self, l, h_in, A, z, rows=None):
+    def node(self, l, h_in, A, z, rows=None, trace=None):
         """Node (s, l): memory read, attention block, MLP block, memory write.
 
         Returns (h_out, A_new, z_new).  With ``rows`` = r < n only the first r
         rows are computed (causal attention makes them independent of later
-        rows) and the memory write is skipped (A_new, z_new are None)."""
+        rows) and the memory write is skipped (A_new, z_new are None).  A dict
+        passed as ``trace`` receives the intermediate values by name."""
         c, R = self.cfg, self.R
         T, H, G, hd = c.seg_len, c.n_heads, c.n_kv_heads, c.head_dim
         h = np.asarray(h_in, dtype=self.dtype)
@@ -242,6 +243,7 @@ class Oracle:
         n = h.shape[0]
         # 1. memory read
         h = R(mem_read(h, self.w("w_mq", l), A, z, c.mem_eps))
+        h_read = h
         # 2. attention block
         a = R(rms_norm(h, self.inp.g_attn[l], c.rms_eps))
         qkv = a @ self.w("w_qkv", l).T
@@ -253,10 +255,14 @@ class Oracle:
         V = R(V)
         O = R(causal_gqa_attention(Q, K, V))
         h = R(h + O @ self.w("w_o", l).T)
+        h_attn = h
         # 3. MLP block
         b = R(rms_norm(h, self.inp.g_mlp[l], c.rms_eps))
         U = R(silu(b @ self.w("w_gate", l).T) * (b @ self.w("w_up", l).T))
         h = R(h + U @ self.w("w_down", l).T)
+        if trace is not None:
+            trace.update(h_read=h_read, a_attn=a, Q=Q, K=K, V=V, O=O, h_attn=h_attn,
+                         a_mlp=b, U=U, h_out=h)
         if rows is not None:
             return h, None, None
         # 4. memory write from the memory-token rows

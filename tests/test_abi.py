@@ -1,0 +1,91 @@
+"""Host-side checks of the C ABI (no GPU compute): the library loads, exports
+every function include/armt.h declares, its wave scheduler matches the
+oracle's enumeration, and invalid arguments return status codes instead of
+crashing."""
+
+import ctypes
+import os
+
+import pytest
+
+import oracle
+from long_context_recurrent_amd import armt as A
+
+LIB = A.library_path()
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libarmt.so not built")
+
+
+def test_exports_every_declared_symbol():
+    lib = A.load_library()
+    declared = A.declared_functions()
+    assert {"armt_create", "armt_forward_sequential", "armt_forward_diagonal",
+            "armt_workspace_size", "armt_destroy", "armt_last_error"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in armt.h but not exported"
+
+
+@pytest.mark.parametrize("L,S", [(L, S) for L in range(1, 13) for S in range(1, 13)]
+                         + [(16, 32), (16, 128), (28, 128), (28, 64), (28, 32)])
+def test_native_schedule_matches_oracle(L, S):
+    waves = A.armt_wave_schedule(L, S)
+    ref = oracle.waves(L, S)
+    assert len(waves) == len(ref) == S + L - 1
+    for (lo, hi), wave in zip(waves, ref):
+        assert [l for (_, l) in wave] == list(range(lo, hi + 1))
+
+
+def test_schedule_errors():
+    with pytest.raises(A.ArmtError) as e:
+        A.armt_wave_schedule(0, 4)
+    assert e.value.code == -1
+    with pytest.raises(A.ArmtError):
+        A.armt_wave_schedule(4, 4, cap=3)
+
+
+def _cfg(**kw):
+    base = dict(n_layers=2, d_model=64, n_heads=2, n_kv_heads=2, head_dim=32, ffn_hidden=128,
+                seg_len=16, n_mem=4, d_key=64, dtype=A.ARMT_F32, rms_eps=1e-5, rope_theta=1e4, mem_eps=1e-6)
+    base.update(kw)
+    return A.armt_config(**base)
+
+
+def test_workspace_size_and_config_validation():
+    assert A.armt_workspace_size(_cfg()) > 0
+    small = A.armt_workspace_size(_cfg(seg_len=16))
+    big = A.armt_workspace_size(_cfg(seg_len=64))
+    assert big > small
+    cases = [
+        (dict(n_layers=0), -1), (dict(d_model=96), -1), (dict(n_kv_heads=3, n_heads=2), -1),
+        (dict(head_dim=16, n_heads=4), -2), (dict(d_key=32), -2), (dict(n_mem=65), -2),
+        (dict(dtype=7), -1), (dict(rms_eps=0.0), -1), (dict(ffn_hidden=100), -2),
+        (dict(dtype=A.ARMT_BF16, seg_len=4090, n_mem=16), -2),
+    ]
+    for kw, code in cases:
+        with pytest.raises(A.ArmtError) as e:
+            A.armt_workspace_size(_cfg(**kw))
+        assert e.value.code == code, (kw, e.value)
+        assert A.armt_last_error()
+
+
+def test_create_rejects_bad_arguments_before_any_gpu_work():
+    lib = A.load_library()
+    cfg = _cfg()
+    w = A.armt_weights(*([1024] * 12))
+    out = ctypes.c_void_p(0)
+    # NULL workspace
+    rc = lib.armt_create(ctypes.byref(cfg), ctypes.byref(w), None, 1 << 20, None, ctypes.byref(out))
+    assert rc == -3 and out.value is None
+    # misaligned and too small
+    rc = lib.armt_create(ctypes.byref(cfg), ctypes.byref(w), 4096 + 8, 1 << 30, None, ctypes.byref(out))
+    assert rc == -3
+    rc = lib.armt_create(ctypes.byref(cfg), ctypes.byref(w), 4096, 16, None, ctypes.byref(out))
+    assert rc == -3 and "too small" in A.armt_last_error()
+    # a NULL weight pointer
+    w2 = A.armt_weights(*([1024] * 11 + [0]))
+    rc = lib.armt_create(ctypes.byref(cfg), ctypes.byref(w2), 4096, 1 << 30, None, ctypes.byref(out))
+    assert rc == -1
+    # NULL handle on the forward entry points and options
+    assert lib.armt_forward_diagonal(None, 1, 1, None, None, 1, 1, 1) == -1
+    assert lib.armt_forward_sequential(None, 1, 1, None, None, 1, 1, 1) == -1
+    assert lib.armt_set_option(None, 0, 1) == -1
+    lib.armt_destroy(None)

@@ -1,0 +1,177 @@
+"""GPU parity of libarmt.so (through the C ABI) against the CPU oracle.
+
+Bars: relative L2 <= 1e-4 for fp32 workloads, <= 2e-2 for bf16 workloads, on
+y and on every layer's (A, z); bitwise equality between the diagonal and the
+sequential schedule, between graph replay and direct launches, and across a
+split/resume of the sequence (the schedule is a pure reordering of the same
+recurrence: Pith review of arXiv 2506.05229, "What carries the argument";
+skill page "Diagonal Batching for Recurrent Memory Transformers", Practical
+Guidance).
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from armt_inputs import get_config, make_inputs, make_state
+from long_context_recurrent_amd import armt as C
+
+from gpu_util import build_model, rel_l2, state_to_device, to_device, to_np, tol
+
+pytestmark = pytest.mark.gpu
+
+# Shapes that span several GEMM tiles, a ragged last row tile, GQA and both
+# bf16 head sizes, small enough for the oracle to finish in seconds.
+MID64 = get_config("small_bf16").with_(name="mid_hd64", n_layers=3, d_model=512, n_heads=8, n_kv_heads=2,
+                                       head_dim=64, ffn_hidden=1536, seg_len=200, n_mem=16, n_segments=5)
+MID128 = get_config("small_bf16").with_(name="mid_hd128", n_layers=3, d_model=768, n_heads=6, n_kv_heads=2,
+                                        head_dim=128, ffn_hidden=1280, seg_len=120, n_mem=8, n_segments=4)
+TINY = get_config("tiny_fp32")
+SMALL = get_config("small_bf16")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
+# one node, every step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [MID64.with_(n_layers=1, n_segments=1), MID128.with_(n_layers=1, n_segments=1),
+                                 TINY.with_(n_layers=1, n_segments=1)], ids=lambda c: c.name)
+def test_single_node_steps(cfg):
+    say(f"[single node] {cfg.name} n={cfg.n}")
+    inp = make_inputs(cfg)
+    A0, z0 = make_state(cfg)
+    o = oracle.Oracle(inp)
+    tr = {}
+    h_ref, A_ref, z_ref = o.node(0, o.node_input(0), A0[0], z0[0], trace=tr)
+    model = build_model(inp)
+    dA0, dz0 = state_to_device(A0, z0)
+    x = to_device(inp.x, cfg)
+    y, A, z = model.forward(x, "diagonal", dA0, dz0)
+    n, d, H, G, hd = cfg.n, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    t = tol(cfg)
+    errs = {}
+    qkv = to_np(model.view("qkv", shape=(n, cfg.qkv_dim)))
+    errs["Q"] = rel_l2(qkv[:, :H * hd], tr["Q"].reshape(n, -1))
+    errs["K"] = rel_l2(qkv[:, H * hd:(H + G) * hd], tr["K"].reshape(n, -1))
+    if cfg.dtype == "bf16":
+        n_pad = (n + 63) // 64 * 64
+        vt = to_np(model.view("vt", shape=(G * hd, n_pad)))
+        errs["V"] = rel_l2(vt[:, :n].T, tr["V"].reshape(n, -1))
+        assert np.all(vt[:, n:] == 0), "V^T padding must stay zero"
+    else:
+        errs["V"] = rel_l2(qkv[:, (H + G) * hd:], tr["V"].reshape(n, -1))
+    errs["O"] = rel_l2(to_np(model.view("attn", shape=(n, H * hd))), tr["O"])
+    errs["a_mlp"] = rel_l2(to_np(model.view("normed", shape=(n, d))), tr["a_mlp"])
+    errs["U"] = rel_l2(to_np(model.view("swiglu", shape=(n, cfg.ffn_hidden))), tr["U"])
+    errs["h_out"] = rel_l2(to_np(model.view("act0", shape=(n, d))), tr["h_out"])
+    errs["y"] = rel_l2(to_np(y), tr["h_out"][:cfg.seg_len])
+    errs["A"] = rel_l2(to_np(A)[0], A_ref)
+    errs["z"] = rel_l2(to_np(z)[0], z_ref)
+    say("  rel L2:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= t, f"{k}: rel L2 {v:.3e} > {t}"
+
+
+# ---------------------------------------------------------------------------
+# whole forward
+# ---------------------------------------------------------------------------
+
+def _compare(cfg, inp, A0=None, z0=None, check_seq=True):
+    y_ref, A_ref, z_ref = oracle.forward_sequential(inp, A0, z0)
+    model = build_model(inp)
+    x = to_device(inp.x, cfg)
+    dA0, dz0 = state_to_device(A0, z0)
+    yd, Ad, zd = model.forward(x, "diagonal", dA0, dz0)
+    e = (rel_l2(to_np(yd), y_ref), rel_l2(to_np(Ad), A_ref), rel_l2(to_np(zd), z_ref))
+    say(f"  {cfg.name} diag rel L2 y={e[0]:.2e} A={e[1]:.2e} z={e[2]:.2e}")
+    for v in e:
+        assert v <= tol(cfg)
+    # per-layer state too
+    for l in range(cfg.n_layers):
+        assert rel_l2(to_np(Ad)[l], A_ref[l]) <= tol(cfg)
+        assert rel_l2(to_np(zd)[l], z_ref[l]) <= tol(cfg)
+    if check_seq:
+        ys, As, zs = model.forward(x, "sequential", dA0, dz0)
+        assert torch.equal(ys, yd), "sequential and diagonal y differ"
+        assert torch.equal(As, Ad) and torch.equal(zs, zd), "sequential and diagonal state differ"
+    return model, x, (yd, Ad, zd)
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL, MID64, MID128], ids=lambda c: c.name)
+@pytest.mark.parametrize("state", ["zero", "given"])
+def test_forward_parity(cfg, state):
+    say(f"[forward] {cfg.name} state={state}")
+    inp = make_inputs(cfg)
+    A0, z0 = make_state(cfg) if state == "given" else (None, None)
+    _compare(cfg, inp, A0, z0)
+
+
+def test_graphs_replay_and_direct_launch_agree():
+    cfg = SMALL
+    inp = make_inputs(cfg)
+    model = build_model(inp)
+    x = to_device(inp.x, cfg)
+    y1, A1, z1 = [t.clone() for t in model.forward(x, "diagonal")]
+    y2, A2, z2 = model.forward(x, "diagonal")           # replay of cached graphs
+    assert torch.equal(y1, y2) and torch.equal(A1, A2) and torch.equal(z1, z2)
+    model.set_option(C.ARMT_OPT_GRAPHS, 0)
+    y3, A3, z3 = model.forward(x, "diagonal")
+    assert torch.equal(y1, y3) and torch.equal(A1, A3) and torch.equal(z1, z3)
+    # a second input through the same graphs (pointers come from the descriptor)
+    x2 = torch.flip(x, dims=[0]).contiguous()
+    model.set_option(C.ARMT_OPT_GRAPHS, 1)
+    y4, _, _ = model.forward(x2, "diagonal")
+    model.set_option(C.ARMT_OPT_GRAPHS, 0)
+    y5, _, _ = model.forward(x2, "diagonal")
+    assert torch.equal(y4, y5)
+    assert not torch.equal(y4, y1)
+
+
+@pytest.mark.parametrize("cfg", [TINY, MID64], ids=lambda c: c.name)
+def test_split_resume_bitwise(cfg):
+    inp = make_inputs(cfg)
+    model = build_model(inp)
+    T, S = cfg.seg_len, cfg.n_segments
+    x = to_device(inp.x, cfg)
+    y, A, z = [t.clone() for t in model.forward(x, "diagonal")]
+    S1 = S // 2 + 1
+    y1, A1, z1 = [t.clone() for t in model.forward(x[:S1 * T].contiguous(), "sequential")]
+    y2, A2, z2 = model.forward(x[S1 * T:].contiguous(), "diagonal", A1, z1)
+    assert torch.equal(torch.cat([y1, y2]), y)
+    assert torch.equal(A2, A) and torch.equal(z2, z)
+    # in-place streaming: A_out aliases A0
+    Ab, zb = A1.clone(), z1.clone()
+    y3 = torch.empty_like(y2)
+    model.forward(x[S1 * T:].contiguous(), "diagonal", Ab, zb, out=(y3, Ab, zb))
+    assert torch.equal(y3, y2) and torch.equal(Ab, A) and torch.equal(zb, z)
+
+
+def test_single_segment_and_single_layer_edges():
+    for cfg in [SMALL.with_(n_segments=1), SMALL.with_(n_layers=1), MID64.with_(n_segments=1, n_layers=2)]:
+        say(f"[edge] L={cfg.n_layers} S={cfg.n_segments}")
+        _compare(cfg, make_inputs(cfg))
+
+
+def test_forward_argument_errors():
+    cfg = SMALL.with_(n_segments=2)
+    inp = make_inputs(cfg)
+    model = build_model(inp)
+    x = to_device(inp.x, cfg)
+    y, A, z = model.alloc_outputs(2)
+    lib = C.load_library()
+    h = model.handle
+    assert lib.armt_forward_diagonal(h, x.data_ptr(), 0, None, None, y.data_ptr(), A.data_ptr(), z.data_ptr()) == -1
+    assert lib.armt_forward_sequential(h, None, 2, None, None, y.data_ptr(), A.data_ptr(), z.data_ptr()) == -1
+    assert lib.armt_forward_diagonal(h, x.data_ptr(), 2, None, None, y.data_ptr(), None, z.data_ptr()) == -1
+    assert "n_segments" in C.armt_last_error() or "NULL" in C.armt_last_error()
+    # the handle still works after rejected calls
+    model.forward(x, "diagonal")
