@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-seq", action="store_true", help="skip the sequential-schedule timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--gemm-rows", type=int, default=0,
+                    help="rows per GEMM tile / 16 (0: the library's choice)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the diagonal forward (for profiler runs)")
     return ap.parse_args()
@@ -82,6 +84,8 @@ def main():
     ccfg = make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                        cfg.ffn_hidden, cfg.seg_len, cfg.n_mem, cfg.d_key, cfg.dtype)
     model = ArmtModel(ccfg, w)
+    if args.gemm_rows:
+        model.set_option(C.ARMT_OPT_GEMM_ROWS, args.gemm_rows)
     S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
     tokens = S * T
     out = model.alloc_outputs(S)
@@ -114,7 +118,7 @@ def main():
 
     # per-kernel durations from HIP events on the library's stream
     kstats = {}
-    for kname in ("gate_up", "qkv", "o_proj", "down", "attn", "mem_read", "mem_update", "mem_keys", "mlp_norm"):
+    for kname in C.KERNELS:
         kid = C.KERNELS.index(kname)
         model.set_option(C.ARMT_OPT_TIME_KERNEL, kid)
         run("diagonal", max(1, min(args.steps, 3)))

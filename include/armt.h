@@ -157,22 +157,25 @@ int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t *l_lo,
  * hipGraph per wave shape (default), 0 = launch kernels directly.
  * ARMT_OPT_TIME_KERNEL: k >= 0 brackets every launch of kernel k (an
  * armt_kernel_id) with HIP events on the handle's stream (forces direct
- * launches); -1 turns it off. */
-enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1 };
+ * launches); -1 turns it off.  ARMT_OPT_GEMM_ROWS: rows per grouped-GEMM
+ * tile as a multiple of 32 (2 .. 7; 0 = pick for the workload); results do
+ * not depend on it.  Changing it drops the captured graphs. */
+enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1, ARMT_OPT_GEMM_ROWS = 2 };
 int armt_set_option(armt_handle *h, int32_t option, int32_t value);
 
 /* Kernels of one wave, in launch order. */
 typedef enum {
-  ARMT_K_MEM_READ = 0,   /* memory read + RMSNorm (attention input) */
-  ARMT_K_QKV = 1,        /* grouped GEMM, RoPE epilogue */
-  ARMT_K_ATTN = 2,       /* batched causal segment attention */
-  ARMT_K_OPROJ = 3,      /* grouped GEMM, residual epilogue */
-  ARMT_K_MLP_NORM = 4,   /* RMSNorm (MLP input) */
-  ARMT_K_GATE_UP = 5,    /* grouped dual GEMM, SiLU * up epilogue */
-  ARMT_K_DOWN = 6,       /* grouped GEMM, residual (+ y rows) epilogue */
-  ARMT_K_MEM_KEYS = 7,   /* memory-write keys, gate, normaliser update */
-  ARMT_K_MEM_UPDATE = 8, /* memory-write delta-rule update of A */
-  ARMT_K_COUNT = 9
+  ARMT_K_MEM_READ = 0,   /* memory read: q projection and h += (q A^T)/(q.z+eps) */
+  ARMT_K_ATTN_NORM = 1,  /* RMSNorm (attention input) */
+  ARMT_K_QKV = 2,        /* grouped GEMM, RoPE epilogue */
+  ARMT_K_ATTN = 3,       /* batched causal segment attention */
+  ARMT_K_OPROJ = 4,      /* grouped GEMM, residual epilogue */
+  ARMT_K_MLP_NORM = 5,   /* RMSNorm (MLP input) */
+  ARMT_K_GATE_UP = 6,    /* grouped dual GEMM, SiLU * up epilogue */
+  ARMT_K_DOWN = 7,       /* grouped GEMM, residual (+ y rows) epilogue */
+  ARMT_K_MEM_KEYS = 8,   /* memory-write keys, gate, normaliser update */
+  ARMT_K_MEM_UPDATE = 9, /* memory-write delta-rule update of A */
+  ARMT_K_COUNT = 10
 } armt_kernel_id;
 
 /* Accumulated timing of the kernel selected with ARMT_OPT_TIME_KERNEL since it

@@ -18,13 +18,13 @@ __all__ = [
     "armt_forward_diagonal", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
-    "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "KERNELS", "VIEWS",
+    "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "KERNELS", "VIEWS",
 ]
 
 ARMT_OK, ARMT_E_INVALID, ARMT_E_UNSUPPORTED, ARMT_E_WORKSPACE, ARMT_E_HIP = 0, -1, -2, -3, -4
 ARMT_F32, ARMT_BF16 = 0, 1
-ARMT_OPT_GRAPHS, ARMT_OPT_TIME_KERNEL = 0, 1
-KERNELS = ["mem_read", "qkv", "attn", "o_proj", "mlp_norm", "gate_up", "down", "mem_keys", "mem_update"]
+ARMT_OPT_GRAPHS, ARMT_OPT_TIME_KERNEL, ARMT_OPT_GEMM_ROWS = 0, 1, 2
+KERNELS = ["mem_read", "attn_norm", "qkv", "attn", "o_proj", "mlp_norm", "gate_up", "down", "mem_keys", "mem_update"]
 VIEWS = {"act0": 0, "act1": 1, "normed": 2, "qkv": 3, "vt": 4, "attn": 5, "swiglu": 6, "A": 7, "z": 8}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))

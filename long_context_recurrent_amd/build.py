@@ -39,9 +39,15 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source device flags.  The GEMM keeps its MFMA accumulators in VGPRs:
+# with the accumulator-register form this compiler rotates loop-carried
+# accumulators through extra AGPR copies every iteration.
+EXTRA = {"gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         msg = "\n".join(l for l in proc.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -73,8 +73,9 @@ struct MemArgs {
   const void* gain;          // [L][d] (g_attn or g_mlp)
   float* A;                  // [L][d][dk] fp32 state
   float* z;                  // [L][dk]
+  float* qbuf;               // [L][n][dk] read keys phi(h W_mq^T) (bf16 path)
   float* kbuf;               // [L][M][dk] write keys phi(Y W_mk^T)
-  float* pden;               // [L][M][16] partial k . z (pre-update z)
+  float* pden;               // [L][M][4] partial k . z (pre-update z), 16 keys each
   float* beta;               // [L][M]
   CallDesc* desc;
   int advance;               // mem_update: wave-counter increment (0: none)
@@ -92,6 +93,9 @@ hipError_t launch_mem_read(const MemArgs& m, bool use_bf16, hipStream_t st);
 hipError_t launch_rmsnorm(const MemArgs& m, bool use_bf16, hipStream_t st);
 hipError_t launch_mem_keys(const MemArgs& m, bool use_bf16, hipStream_t st);
 hipError_t launch_mem_update(const MemArgs& m, bool use_bf16, hipStream_t st);
+hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st);
+hipError_t launch_mem_keys_bf16(const MemArgs& m, hipStream_t st);
+hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
 

@@ -59,7 +59,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, kbuf, pden, beta, total;
+  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, qbuf, kbuf, pden, beta, total;
 };
 
 int validate_config(const armt_config* c) {
@@ -110,8 +110,9 @@ Layout make_layout(const armt_config* c) {
   lo.vt = take(c->dtype == ARMT_BF16 ? L * c->n_kv_heads * c->head_dim * n_pad * 2 : 0);
   lo.attn = take(L * n * hhd * es);
   lo.ubuf = take(L * n * F * es);
+  lo.qbuf = take(c->dtype == ARMT_BF16 ? L * n * dk * 4 : 0);
   lo.kbuf = take(L * M * dk * 4);
-  lo.pden = take(L * M * 16 * 4);
+  lo.pden = take(L * M * 4 * 4);
   lo.beta = take(L * M * 4);
   lo.total = off;
   return lo;
@@ -128,7 +129,7 @@ struct armt_handle {
   hipStream_t cap_stream = nullptr;
   int device = 0;
   bool bf16 = true;
-  int n = 0, n_pad = 0, qkv_dim = 0, mb = 13;
+  int n = 0, n_pad = 0, qkv_dim = 0, mb = 0, cus = 256;   // mb 0: per-launch choice
   size_t es = 2;
   char* ws = nullptr;
   Layout lo{};
@@ -138,7 +139,7 @@ struct armt_handle {
   float* z = nullptr;
   void* act[2] = {nullptr, nullptr};
   void *abuf = nullptr, *qkv = nullptr, *vt = nullptr, *attn = nullptr, *ubuf = nullptr;
-  float *kbuf = nullptr, *pden = nullptr, *beta = nullptr;
+  float *qbuf = nullptr, *kbuf = nullptr, *pden = nullptr, *beta = nullptr;
   std::map<std::tuple<int, int, int, int, int>, hipGraphExec_t> graphs;
   bool use_graphs = true;
   int time_kernel = -1;
@@ -158,7 +159,8 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
   const double tri = n * (n + 1) / 2;
   double f = 0, b = 0;
   switch (k) {
-    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 3 * n * d * es + dk * d * es + d * dk * 4; break;
+    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 2 * n * d * es + dk * d * es + d * dk * 4; break;
+    case ARMT_K_ATTN_NORM: f = 0; b = (2 * n * d + d) * es; break;
     case ARMT_K_QKV: f = 2 * n * d * q; b = (n * d + q * d + n * q) * es; break;
     case ARMT_K_ATTN: f = 4 * tri * hd * H; b = (n * q + n * H * hd) * es; break;
     case ARMT_K_OPROJ: f = 2 * n * H * hd * d; b = (n * H * hd + d * H * hd + 2 * n * d) * es; break;
@@ -170,6 +172,12 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
   }
   *flops = f;
   *bytes = b;
+}
+
+int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus);
+
+int gemm_rows(const armt_handle* h, int n_cols, int cols_per_tile, int P) {
+  return h->mb ? h->mb : pick_row_blocks(h->n, n_cols, cols_per_tile, P, h->cus);
 }
 
 struct StepCtx {
@@ -208,13 +216,13 @@ hipError_t timed(StepCtx& cx, int kid, int P, hipError_t (*fn)(const void*, hipS
   return hipSuccess;
 }
 
-struct GemmCall { const armt_handle* h; GemmArgs g; int epi; };
+struct GemmCall { const armt_handle* h; GemmArgs g; int epi; int mb; };
 struct AttnCall { const armt_handle* h; AttnArgs a; };
 struct MemCall { const armt_handle* h; MemArgs m; int which; };
 
 hipError_t run_gemm(const void* p, hipStream_t st) {
   const GemmCall* c = (const GemmCall*)p;
-  return c->h->bf16 ? launch_gemm_bf16(c->g, c->epi, c->h->mb, st) : launch_gemm_f32(c->g, c->epi, st);
+  return c->h->bf16 ? launch_gemm_bf16(c->g, c->epi, c->mb, st) : launch_gemm_f32(c->g, c->epi, st);
 }
 hipError_t run_attn(const void* p, hipStream_t st) {
   const AttnCall* c = (const AttnCall*)p;
@@ -224,6 +232,7 @@ hipError_t run_mem(const void* p, hipStream_t st) {
   const MemCall* c = (const MemCall*)p;
   switch (c->which) {
     case ARMT_K_MEM_READ: return launch_mem_read(c->m, c->h->bf16, st);
+    case ARMT_K_ATTN_NORM:
     case ARMT_K_MLP_NORM: return launch_rmsnorm(c->m, c->h->bf16, st);
     case ARMT_K_MEM_KEYS: return launch_mem_keys(c->m, c->h->bf16, st);
     default: return launch_mem_update(c->m, c->h->bf16, st);
@@ -243,7 +252,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   m.P = P; m.l0 = l_lo; m.n = n; m.d = d; m.T = c.seg_len; m.M = c.n_mem; m.dk = c.d_key; m.L = c.n_layers;
   m.act_prev = h->act[par ^ 1]; m.act_cur = h->act[par]; m.abuf = h->abuf; m.act_stride = nd;
   m.mem_emb = h->w.mem_emb; m.w_mq = h->w.w_mq; m.w_mk = h->w.w_mk; m.w_mv = h->w.w_mv; m.w_beta = h->w.w_beta;
-  m.A = h->A; m.z = h->z; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
+  m.A = h->A; m.z = h->z; m.qbuf = h->qbuf; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
   m.mem_eps = c.mem_eps; m.rms_eps = c.rms_eps; m.advance = 0;
 
   GemmArgs g0{};
@@ -251,15 +260,17 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   g0.head_dim = c.head_dim;
 
   hipError_t e;
-  // 1. memory read + attention norm
+  // 1. memory read, then the attention norm
   {
     MemCall mc{h, m, ARMT_K_MEM_READ};
-    mc.m.gain = h->w.g_attn;
     if ((e = timed(cx, ARMT_K_MEM_READ, P, run_mem, &mc)) != hipSuccess) return e;
+    MemCall nc{h, m, ARMT_K_ATTN_NORM};
+    nc.m.gain = h->w.g_attn;
+    if ((e = timed(cx, ARMT_K_ATTN_NORM, P, run_mem, &nc)) != hipSuccess) return e;
   }
   // 2. QKV projection with RoPE
   {
-    GemmCall gc{h, g0, EPI_QKV};
+    GemmCall gc{h, g0, EPI_QKV, gemm_rows(h, h->qkv_dim, 256, P)};
     GemmArgs& g = gc.g;
     g.A = h->abuf; g.a_stride = nd; g.lda = d;
     g.B = h->w.w_qkv; g.b_stride = (int64_t)h->qkv_dim * d; g.N = h->qkv_dim; g.K = d;
@@ -282,7 +293,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 4. output projection + residual
   {
-    GemmCall gc{h, g0, EPI_RESID};
+    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, P)};
     GemmArgs& g = gc.g;
     g.A = h->attn; g.a_stride = (int64_t)n * hhd; g.lda = hhd;
     g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
@@ -297,7 +308,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 6. gate/up + SiLU product
   {
-    GemmCall gc{h, g0, EPI_SWIGLU};
+    GemmCall gc{h, g0, EPI_SWIGLU, gemm_rows(h, F, 128, P)};
     GemmArgs& g = gc.g;
     g.A = h->abuf; g.a_stride = nd; g.lda = d;
     g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
@@ -306,7 +317,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 7. down projection + residual (+ y rows of the last layer)
   {
-    GemmCall gc{h, g0, EPI_RESID};
+    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, P)};
     GemmArgs& g = gc.g;
     g.A = h->ubuf; g.a_stride = (int64_t)n * F; g.lda = F;
     g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
@@ -391,15 +402,26 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, const float* A0
   return ARMT_OK;
 }
 
-int pick_row_blocks(int n) {
-  int best = kGemmRowBlocks[0];
-  long best_pad = -1;
+// 32-row blocks per GEMM tile for one grouped launch of P problems with
+// n_cols output columns per problem (cols_per_tile per workgroup).  Every
+// tile height gives bitwise identical results, so the choice is free: it
+// minimises rounds x (tile rows + a fixed per-tile cost), where a round is
+// one workgroup on every compute unit (the tiles hold one workgroup per CU).
+// Tiles shorter than 128 rows are not considered: their operand traffic per
+// FLOP is too high.
+int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus) {
+  constexpr int kTileOverheadRows = 48;
+  int best = 6;
+  long best_cost = -1;
   for (int i = 0; i < kGemmRowBlocksCount; ++i) {
-    const int mb = kGemmRowBlocks[i], bm = 16 * mb;
-    const long padded = (long)((n + bm - 1) / bm) * bm;
-    if (best_pad < 0 || padded < best_pad || (padded == best_pad && mb > best)) {
+    const int mb = kGemmRowBlocks[i], bm = 32 * mb;
+    if (bm < 128) continue;
+    const long tiles = (long)((n + bm - 1) / bm) * ((n_cols + cols_per_tile - 1) / cols_per_tile) * P;
+    const long rounds = (tiles + cus - 1) / cus;
+    const long cost = rounds * (bm + kTileOverheadRows);
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && mb > best)) {
       best = mb;
-      best_pad = padded;
+      best_cost = cost;
     }
   }
   return best;
@@ -442,7 +464,7 @@ int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, 
   h->n = cfg->seg_len + cfg->n_mem;
   h->n_pad = (h->n + 63) / 64 * 64;
   h->qkv_dim = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
-  h->mb = pick_row_blocks(h->n);
+  h->mb = 0;
   h->lo = lo;
   char* base = (char*)workspace;
   h->ws = base;
@@ -457,12 +479,15 @@ int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, 
   h->vt = base + lo.vt;
   h->attn = base + lo.attn;
   h->ubuf = base + lo.ubuf;
+  h->qbuf = (float*)(base + lo.qbuf);
   h->kbuf = (float*)(base + lo.kbuf);
   h->pden = (float*)(base + lo.pden);
   h->beta = (float*)(base + lo.beta);
 
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device);
+  if (e != hipSuccess || h->cus <= 0) { delete h; return hip_fail(e, "hipDeviceGetAttribute"); }
   e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) { delete h; return hip_fail(e, "hipStreamCreateWithFlags"); }
 
@@ -538,6 +563,15 @@ int armt_set_option(armt_handle* h, int32_t option, int32_t value) {
       h->t_launches = 0;
       h->t_flops = h->t_bytes = 0;
       return ARMT_OK;
+    case ARMT_OPT_GEMM_ROWS: {
+      bool ok = value == 0;
+      for (int i = 0; i < kGemmRowBlocksCount; ++i) ok = ok || kGemmRowBlocks[i] == value;
+      if (!ok || !h->bf16) return fail(ARMT_E_INVALID, "unsupported GEMM row blocks %d", value);
+      h->mb = value;
+      for (auto& kv : h->graphs) hipGraphExecDestroy(kv.second);
+      h->graphs.clear();
+      return ARMT_OK;
+    }
     default: return fail(ARMT_E_INVALID, "unknown option %d", option);
   }
 }
@@ -571,7 +605,7 @@ int armt_debug_view(armt_handle* h, int32_t which, void** ptr, size_t* bytes) {
     case ARMT_VIEW_QKV: at = lo.qkv; end = lo.vt; break;
     case ARMT_VIEW_VT: at = lo.vt; end = lo.attn; break;
     case ARMT_VIEW_ATTN: at = lo.attn; end = lo.ubuf; break;
-    case ARMT_VIEW_SWIGLU: at = lo.ubuf; end = lo.kbuf; break;
+    case ARMT_VIEW_SWIGLU: at = lo.ubuf; end = lo.qbuf; break;
     case ARMT_VIEW_A: at = lo.A; end = lo.z; break;
     case ARMT_VIEW_Z: at = lo.z; end = lo.act0; break;
     default: return fail(ARMT_E_INVALID, "unknown view %d", which);

@@ -6,24 +6,34 @@
 // carries the argument"; Figure 4 caption on grouped GEMM scaling; skill page
 // "Diagonal Batching for Recurrent Memory Transformers", Implementation).
 //
-// CDNA4 mapping.  A workgroup of 4 waves owns a BM x 256 tile (BM = 16*MB
-// rows, chosen per workload so that the n = T + M node rows split with little
-// padding: 1040 = 5 * 208).  Each wave owns all BM rows and 64 of the 256
-// columns and issues v_mfma_f32_16x16x32_bf16 on 16x16 blocks (fp32
-// accumulators, MB*16 registers per lane).  K advances 64 at a time through a
-// double-buffered LDS tile with padded rows (144 B pitch: conflict-free 16-byte
-// fragment reads); the next K slice is loaded into registers while the current
-// one is multiplied.  Tiles are ordered so that each of the 8 XCDs gets a
-// contiguous range (same weights, neighbouring rows), keeping shared operands
-// in that XCD's L2.  The epilogue stages fp32 results through LDS, so every
-// global store is a coalesced 16-byte write and every bf16 rounding happens
-// once, on the fp32 value:
-//   EPI_QKV   : RoPE on the Q and K heads (pairs i, i + hd/2 are kept in the
-//               same lane by the column map), bf16 store; V heads are stored
-//               transposed ([G][hd][n_pad]) for the attention kernel.
-//   EPI_RESID : C = R(C + acc) in place (residual add); for the last layer the
-//               segment-token rows are also written to the caller's y.
-//   EPI_SWIGLU: B holds gate rows then up rows; U = R(silu(gate) * up).
+// CDNA4 mapping.
+//  * Matrix core: v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  On MI355X it
+//    sustains the full dense bf16 rate, twice that of the 16x16x32 form.
+//  * Tile: a workgroup of 4 waves owns BM x 256 outputs, BM = 32 * MB rows,
+//    chosen per workload to pad the n = T + M node rows little.  Each wave owns
+//    all BM rows and 64 columns: MB x 2 accumulator blocks of 32 x 32
+//    (32 * MB accumulator registers per lane).
+//  * Operands: K advances 32 per pipeline stage.  Stages are filled straight
+//    from global memory into LDS by global_load_lds_dwordx4 (no staging
+//    registers), issued NS - 1 stages ahead; each 64-byte tile row keeps its
+//    four 16-byte chunks XOR-swizzled so the fragment reads of 8 consecutive
+//    rows hit 8 different bank groups.  The fragments of the next stage are
+//    read while the MFMAs of the current one run.
+//  * Schedule: tiles are numbered so that each of the 8 XCDs works through a
+//    contiguous range (same layer, same weight columns, neighbouring rows),
+//    keeping the shared operand tiles in that XCD's L2.
+//  * Epilogue: fp32 results are staged through LDS, so every global store is a
+//    coalesced 16-byte write and every bf16 rounding happens once, on the fp32
+//    value:
+//      EPI_QKV   : RoPE on the Q and K heads (partner column i + hd/2 read from
+//                  the staged tile), bf16 store; V heads are stored transposed
+//                  ([G * hd][n_pad]) for the attention kernel.
+//      EPI_RESID : C = R(C + acc) in place (residual add); for the last layer
+//                  the segment-token rows are also written to the caller's y.
+//      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
+//                  rows; U = R(silu(gate) * up).
+//  Every output element accumulates over K in the same order whatever MB or
+//  the number of problems, so results do not depend on the wave width.
 #include "armt_common.h"
 #include "armt_kernels.h"
 
@@ -31,74 +41,77 @@ namespace armt {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int PITCH = BK + 8;   // bf16 elements per LDS row (144 bytes)
-constexpr int BNB = 256;        // B-tile rows held in LDS
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 32;          // k per pipeline stage
+constexpr int ROWB = BK * 2;    // bytes per tile row in a stage (64)
+constexpr int BNB = 256;        // B-tile rows per stage
 constexpr int RC = 64;          // epilogue rows staged per pass
-constexpr int CPITCH_PAD = 4;
+constexpr int CPITCH = 256 + 4; // staged tile pitch (floats)
+constexpr int LDS_BYTES = 160 * 1024;
 
-// Column-block map: block j (0..3) of wave w -> first B-tile row it uses.
-// MAP_LINEAR (also hd 32 and 64): 64w + 16j.  MAP_HD128: a 128-wide head split
-// so that block j and j + 2 are hd/2 = 64 apart.  MAP_DUAL: j < 2 gate rows
-// 32w + 16j, j >= 2 the matching up rows 128 + 32w + 16(j - 2).
-enum { MAP_LINEAR = 0, MAP_HD32 = 1, MAP_HD64 = 2, MAP_HD128 = 3, MAP_DUAL = 4 };
+// Stages that fit in LDS (at most 4); each holds BM + 256 rows of 64 bytes.
+template <int MB>
+constexpr int n_stages() {
+  return (LDS_BYTES / ((32 * MB + BNB) * ROWB)) > 4 ? 4 : (LDS_BYTES / ((32 * MB + BNB) * ROWB));
+}
 
-template <int MAP>
+// 16-byte chunk c (0..3) of tile row r sits at physical chunk c ^ ((r >> 1) & 3).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+// s_waitcnt immediate (gfx9 layout): vmcnt <= n, lgkmcnt = 0, expcnt free.
+__host__ __device__ constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier without the release fence of __syncthreads(), which would
+// also wait for every outstanding global->LDS load.  Callers wait for exactly
+// what they need with s_waitcnt first; the empty asm statements keep the
+// compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// First B-tile row (output column) of wave w's column block j (0, 1).
+template <int EPI>
 __device__ __forceinline__ int col_block(int w, int j) {
-  if (MAP == MAP_HD128) return 128 * (w >> 1) + 32 * (w & 1) + (j & 1) * 16 + (j >> 1) * 64;
-  if (MAP == MAP_DUAL) return (j < 2) ? (32 * w + 16 * j) : (128 + 32 * w + 16 * (j - 2));
-  return 64 * w + 16 * j;
+  if (EPI == EPI_SWIGLU) return j == 0 ? 32 * w : 128 + 32 * w;   // gate, matching up
+  return 64 * w + 32 * j;
 }
 
-// Output column (relative to the tile's first output column) of block j's
-// lane column 0.
-template <int MAP>
-__device__ __forceinline__ int out_col_block(int w, int j) {
-  if (MAP == MAP_DUAL) return 32 * w + 16 * (j & 1);
-  return col_block<MAP>(w, j);
-}
-
-// RoPE partner of block j (hd/2 columns to the right) under each head map.
-template <int MAP>
-constexpr int rope_pmask() { return MAP == MAP_HD32 ? 1 : 2; }
-template <int MAP>
-constexpr int rope_hd() { return MAP == MAP_HD32 ? 32 : (MAP == MAP_HD64 ? 64 : 128); }
-
-__device__ __forceinline__ void xcd_tile(int id, int total, int& logical) {
+__device__ __forceinline__ int xcd_tile(int id, int total) {
   // Hardware dispatches workgroup id to XCD id % 8.  Give XCD x the
   // contiguous logical range [start(x), start(x) + count(x)).
   const int q = total >> 3, r = total & 7;
   const int x = id & 7, j = id >> 3;
-  logical = x * q + (x < r ? x : r) + j;
+  return x * q + (x < r ? x : r) + j;
 }
 
 }  // namespace
 
-template <int MB, int EPI, int MAP>
+template <int MB, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int BM = 16 * MB;
+  constexpr int BM = 32 * MB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
-  constexpr int A_CHUNKS = BM * (BK / 8);              // 16-byte chunks per A tile
-  constexpr int A_ITERS = (A_CHUNKS + 255) / 256;
-  constexpr int B_ITERS = BNB * (BK / 8) / 256;        // = 8
-  constexpr int LDS_TILE = (BM + BNB) * PITCH;         // bf16 elements per stage
-  constexpr int CPITCH = BN_OUT + CPITCH_PAD;
-  static_assert(2 * LDS_TILE * 2 <= 160 * 1024, "LDS budget");
-  static_assert(RC * CPITCH * 4 <= 2 * LDS_TILE * 2, "epilogue staging fits");
+  constexpr int NS = n_stages<MB>();
+  constexpr int STAGE = (BM + BNB) * ROWB;             // bytes per stage
+  constexpr int A_INSTR = BM / 16;                     // 1 KB wave loads per stage
+  constexpr int INSTR = A_INSTR + BNB / 16;
+  constexpr int MAXQ = (INSTR + 3) / 4;                // loads per wave per stage
+  static_assert(NS >= 3, "pipeline depth");
+  static_assert(RC * CPITCH * 4 <= NS * STAGE, "epilogue staging fits");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * LDS_TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + BN_OUT - 1) / BN_OUT;
-  const int total = tiles_m * tiles_n * g.P;
-  int logical;
-  xcd_tile(blockIdx.x, total, logical);
+  const int logical = xcd_tile(blockIdx.x, tiles_m * tiles_n * g.P);
   const int tm = logical % tiles_m;
   const int tn = (logical / tiles_m) % tiles_n;
-  const int p = logical / (tiles_m * tiles_n);
-  const int layer = g.l0 + p;
+  const int layer = g.l0 + logical / (tiles_m * tiles_n);
   const int m0 = tm * BM;
   const int n0 = tn * BN_OUT;
 
@@ -107,141 +120,131 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   const bf16* __restrict__ B2 =
       (EPI == EPI_SWIGLU) ? (const bf16*)g.B2 + (int64_t)layer * g.b_stride : B;
 
-  // ---- global -> register staging (element offsets; chunk c = tid + 256 i
-  // covers tile row c / 8, 16-byte column chunk c % 8) ----
-  int a_off[A_ITERS];
-  int b_off[B_ITERS];
+  // ---- direct global -> LDS loads.  A stage holds INSTR blocks of 16 tile
+  // rows (A rows, then B rows), each filled by one 1 KB wave load in which
+  // lane L brings tile row 16q + L/4, physical chunk L%4 (= logical chunk
+  // swz(row, L%4)).  Wave w issues blocks q = w, w + 4, ...; every wave issues
+  // exactly MAXQ loads per stage (a wave with fewer blocks repeats its first
+  // one, rewriting identical bytes), so the vmcnt waits are constants.
+  const bf16* src[MAXQ];
+  int dst[MAXQ];
 #pragma unroll
-  for (int i = 0; i < A_ITERS; ++i) {
-    const int c = tid + 256 * i;
-    int row = m0 + c / 8;
-    row = row < g.M ? row : g.M - 1;
-    a_off[i] = row * g.lda + (c % 8) * 8;
+  for (int t = 0; t < MAXQ; ++t) {
+    int q = w + 4 * t;
+    q = q < INSTR ? q : w;
+    const int rl = lane >> 2, pc = lane & 3;
+    if (q < A_INSTR) {
+      const int r = 16 * q + rl;
+      int row = m0 + r;
+      row = row < g.M ? row : g.M - 1;
+      src[t] = A + (int64_t)row * g.lda + swz(r, pc) * 8;
+      dst[t] = 16 * q * ROWB;
+    } else {
+      const int r = 16 * (q - A_INSTR) + rl;          // B-tile row 0..255
+      int nrow = n0 + ((EPI == EPI_SWIGLU) ? (r & 127) : r);
+      nrow = nrow < g.N ? nrow : g.N - 1;
+      const bf16* base = (EPI == EPI_SWIGLU && r >= 128) ? B2 : B;
+      src[t] = base + (int64_t)nrow * g.K + swz(r, pc) * 8;
+      dst[t] = (BM + 16 * (q - A_INSTR)) * ROWB;
+    }
   }
+  const int KT = g.K / BK;
+  // Stage kt of the K loop; tiles past the end re-fetch the last tile into a
+  // stage nobody reads any more.
+  auto issue = [&](int kt) {
+    const int kc = kt < KT ? kt : KT - 1;
+    unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-  for (int i = 0; i < B_ITERS; ++i) {
-    const int c = tid + 256 * i;
-    // dual: tile rows 0..127 (i < 4) are gate rows, 128..255 the up rows
-    int nrow = n0 + ((EPI == EPI_SWIGLU) ? ((c / 8) & 127) : (c / 8));
-    nrow = nrow < g.N ? nrow : g.N - 1;
-    b_off[i] = nrow * g.K + (c % 8) * 8;
-  }
-
-  u32x4 ra[A_ITERS], rb[B_ITERS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_ITERS; ++i)
-      if (A_CHUNKS % 256 == 0 || tid + 256 * i < A_CHUNKS)
-        ra[i] = *(const u32x4*)(A + a_off[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      const bf16* base = (EPI == EPI_SWIGLU && i >= B_ITERS / 2) ? B2 : B;
-      rb[i] = *(const u32x4*)(base + b_off[i] + kt * BK);
-    }
-  };
-  auto lstore = [&](int buf) {
-    bf16* As = smem + buf * LDS_TILE;
-    bf16* Bs = As + BM * PITCH;
-#pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-      const int c = tid + 256 * i;
-      if (A_CHUNKS % 256 == 0 || c < A_CHUNKS)
-        *(u32x4*)(As + (c / 8) * PITCH + (c % 8) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4*)(Bs + (c / 8) * PITCH + (c % 8) * 8) = rb[i];
-    }
+    for (int t = 0; t < MAXQ; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(src[t] + kc * BK),
+                                       (__attribute__((address_space(3))) void*)(st + dst[t]), 16, 0, 0);
   };
 
-  f32x4 acc[MB][4];
+  f32x16 acc[MB][2];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int KT = g.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const bf16* As = smem + buf * LDS_TILE;
-    const bf16* Bs = As + BM * PITCH;
+  // Fragments of one stage: two 16-wide k-steps; lane (r32 = lane % 32,
+  // h = lane / 32) holds k = 8h..8h+7 of its row, i.e. logical chunk 2ks + h.
+  const int r32 = lane & 31, h = lane >> 5;
+  bf16x8 fa0[2][MB], fb0[2][2], fa1[2][MB], fb1[2][2];
+  auto read_frags = [&](int kt, bf16x8 (*fa)[MB], bf16x8 (*fb)[2]) {
+    const unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 bfr[4];
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *(const bf16x8*)(Bs + (col_block<MAP>(w, j) + frag_row) * PITCH + kk + frag_k);
+      for (int j = 0; j < 2; ++j) {
+        const int r = col_block<EPI>(w, j) + r32;
+        fb[ks][j] = *(const bf16x8*)(st + (BM + r) * ROWB + swz(r, 2 * ks + h) * 16);
+      }
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        const bf16x8 afr = *(const bf16x8*)(As + (16 * i + frag_row) * PITCH + kk + frag_k);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+        const int r = 32 * i + r32;
+        fa[ks][i] = *(const bf16x8*)(st + r * ROWB + swz(r, 2 * ks + h) * 16);
       }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  auto mfma_all = [&](bf16x8 (*fa)[MB], bf16x8 (*fb)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+  };
 
-  // ---- register epilogue: RoPE (QKV) or SiLU * up (SWIGLU) ----
-  const int lrow = (lane >> 4) * 4;    // first of the lane's 4 accumulator rows
-  const int lcol = lane & 15;
-  if (EPI == EPI_QKV) {
-    constexpr int hd = rope_hd<MAP>(), half = hd / 2, pmask = rope_pmask<MAP>();
+  // prologue: stages 0 .. NS-2 in flight; stage 0 landed; its fragments read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((j & pmask) != 0) continue;
-      const int pj = j ^ pmask;
-      const int c = n0 + col_block<MAP>(w, j) + lcol;      // global output column
-      if (c < g.rope_cols) {
-        const int e = c % hd;                                // < half
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            int m = m0 + 16 * i + lrow + r;
-            m = m < g.M ? m : g.M - 1;
-            const float2 cs = *(const float2*)(g.rope_cs + ((int64_t)m * half + e) * 2);
-            const float x1 = acc[i][j][r], x2 = acc[i][pj][r];
-            acc[i][j][r] = x1 * cs.x - x2 * cs.y;
-            acc[i][pj][r] = x2 * cs.x + x1 * cs.y;
-          }
-        }
-      }
-    }
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * MAXQ));
+  lds_barrier();
+  read_frags(0, fa0, fb0);
+  // One pipeline step: refill the stage freed two steps ago, wait until this
+  // wave's loads of stage kt+1 landed (the wait also drains this wave's LDS
+  // reads, so nobody refills a stage another wave still reads), barrier, read
+  // stage kt+1's fragments into the other register set, and multiply the
+  // fragments of stage kt already in registers.  After the last step the
+  // fragments read belong to a re-fetched stage and are never used; KT is even
+  // because K is a multiple of 64.
+  auto step = [&](int kt, bf16x8 (*fa_cur)[MB], bf16x8 (*fb_cur)[2], bf16x8 (*fa_nxt)[MB],
+                  bf16x8 (*fb_nxt)[2]) {
+    issue(kt + NS - 1);
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * MAXQ));
+    lds_barrier();
+    read_frags(kt + 1, fa_nxt, fb_nxt);
+    mfma_all(fa_cur, fb_cur);
+    // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
+    // each read next to the MFMA of the following step that uses it)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MB + 2), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB, 0);
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, fa0, fb0, fa1, fb1);
+    step(kt + 1, fa1, fb1, fa0, fb0);
   }
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+  __syncthreads();
 
-  // ---- staged store ----
+  // ---- epilogue: stage RC rows at a time as fp32 in LDS, then store.
+  // Accumulator element e of block (i, j) in lane (r32, h) is output row
+  // 32i + 8(e/4) + 4h + e%4, column col_block(w, j) + r32.
   float* Cs = (float*)smem;
   for (int rc0 = 0; rc0 < BM; rc0 += RC) {
-    // waves write their fp32 results for rows [rc0, rc0 + RC) of the tile
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      if (16 * i < rc0 || 16 * i >= rc0 + RC) continue;
-      if (EPI == EPI_SWIGLU) {
+      if (32 * i < rc0 || 32 * i >= rc0 + RC) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int oc = out_col_block<MAP>(w, j) + lcol;
+      for (int e = 0; e < 16; ++e) {
+        const int rl = 32 * i - rc0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (EPI == EPI_SWIGLU) {
+          const float gt = acc[i][0][e], up = acc[i][1][e];
+          Cs[rl * CPITCH + 32 * w + r32] = gt * sigmoid_f(gt) * up;
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gt = acc[i][j][r], up = acc[i][j + 2][r];
-            Cs[(16 * i - rc0 + lrow + r) * CPITCH + oc] = gt * sigmoid_f(gt) * up;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int oc = out_col_block<MAP>(w, j) + lcol;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Cs[(16 * i - rc0 + lrow + r) * CPITCH + oc] = acc[i][j][r];
+          for (int j = 0; j < 2; ++j) Cs[rl * CPITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
         }
       }
     }
@@ -250,18 +253,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     constexpr int PIECES_ROW = BN_OUT / 8;
     bf16* C = (bf16*)g.C + (int64_t)layer * g.c_stride;
     if (EPI == EPI_QKV) {
-      // row-major pieces for Q and K columns
+      // Q and K columns: RoPE with the partner column i +- hd/2 of the same
+      // head (heads never straddle the 256-column tile: hd divides 256)
+      const int hd = g.head_dim, half = hd >> 1;
       for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.v_col0) continue;
-        const float* src = Cs + r * CPITCH + c8;
+        const float* src_row = Cs + r * CPITCH;
         bf16x8 o;
+        if (n < g.rope_cols) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)src[e];
+          for (int e = 0; e < 8; ++e) {
+            const int c = c8 + e, hi = (n + e) % hd;
+            const bool first = hi < half;
+            const int fi = first ? hi : hi - half;
+            const float2 cs = *(const float2*)(g.rope_cs + ((int64_t)m * half + fi) * 2);
+            const float x = src_row[c], xp = src_row[first ? c + half : c - half];
+            o[e] = (bf16)(first ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)src_row[c8 + e];
+        }
         *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
       }
-      // transposed pieces for V columns: 8 consecutive rows of one column
+      // V columns, transposed: 8 consecutive rows of one column per piece
       bf16* Vt = (bf16*)g.vt + (int64_t)layer * g.vt_stride;
       const int rgroups = (rows_here + 7) / 8;
       for (int pc = tid; pc < rgroups * BN_OUT; pc += 256) {
@@ -270,16 +287,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         if (n < g.v_col0 || n >= g.N) continue;
         const int m = m0 + rc0 + rg * 8;
         if (m >= g.M) continue;
-        const int vc = n - g.v_col0;                       // kv_head * hd + e
-        bf16* dst = Vt + (int64_t)vc * g.vt_ld + m;
-        const float* src = Cs + (rg * 8) * CPITCH + col;
+        bf16* dstp = Vt + (int64_t)(n - g.v_col0) * g.vt_ld + m;
+        const float* s = Cs + (rg * 8) * CPITCH + col;
         if (m + 8 <= g.M) {
           bf16x8 o;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)src[e * CPITCH];
-          *(bf16x8*)dst = o;
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e * CPITCH];
+          *(bf16x8*)dstp = o;
         } else {
-          for (int e = 0; m + e < g.M; ++e) dst[e] = (bf16)src[e * CPITCH];
+          for (int e = 0; m + e < g.M; ++e) dstp[e] = (bf16)s[e * CPITCH];
         }
       }
     } else {
@@ -294,18 +310,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.N) continue;
-        const float* src = Cs + r * CPITCH + c8;
-        bf16* dst = C + (int64_t)m * g.ldc + n;
+        const float* s = Cs + r * CPITCH + c8;
+        bf16* dstp = C + (int64_t)m * g.ldc + n;
         bf16x8 o;
         if (EPI == EPI_RESID) {
-          const bf16x8 res = *(const bf16x8*)dst;
+          const bf16x8 res = *(const bf16x8*)dstp;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)res[e] + src[e]);
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)res[e] + s[e]);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)src[e];
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e];
         }
-        *(bf16x8*)dst = o;
+        *(bf16x8*)dstp = o;
         if (m < y_rows) *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
       }
     }
@@ -317,41 +333,40 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
 // host launchers
 // ---------------------------------------------------------------------------
 
-template <int MB, int EPI, int MAP>
+template <int MB, int EPI>
 static hipError_t launch_mb(const GemmArgs& g, hipStream_t st) {
-  constexpr int BM = 16 * MB;
+  constexpr int BM = 32 * MB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN_OUT - 1) / BN_OUT) * g.P;
-  hipLaunchKernelGGL((gemm_bf16_kernel<MB, EPI, MAP>), dim3(tiles), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MB, EPI>), dim3(tiles), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
-template <int EPI, int MAP>
-static hipError_t launch_map(const GemmArgs& g, int mb, hipStream_t st) {
+template <int EPI>
+static hipError_t launch_epi(const GemmArgs& g, int mb, hipStream_t st) {
   switch (mb) {
-    case 4: return launch_mb<4, EPI, MAP>(g, st);
-    case 8: return launch_mb<8, EPI, MAP>(g, st);
-    case 9: return launch_mb<9, EPI, MAP>(g, st);
-    case 11: return launch_mb<11, EPI, MAP>(g, st);
-    case 12: return launch_mb<12, EPI, MAP>(g, st);
-    case 13: return launch_mb<13, EPI, MAP>(g, st);
+    case 2: return launch_mb<2, EPI>(g, st);
+    case 3: return launch_mb<3, EPI>(g, st);
+    case 4: return launch_mb<4, EPI>(g, st);
+    case 5: return launch_mb<5, EPI>(g, st);
+    case 6: return launch_mb<6, EPI>(g, st);
+    case 7: return launch_mb<7, EPI>(g, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-const int kGemmRowBlocks[] = {4, 8, 9, 11, 12, 13};
+const int kGemmRowBlocks[] = {2, 3, 4, 5, 6, 7};
 const int kGemmRowBlocksCount = 6;
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int mb, hipStream_t st) {
-  if (g.P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK) return hipErrorInvalidValue;
+  // K must be a multiple of 64 (two pipeline stages per loop trip)
+  if (g.P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % (2 * BK)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV:
-      if (g.head_dim == 128) return launch_map<EPI_QKV, MAP_HD128>(g, mb, st);
-      if (g.head_dim == 64) return launch_map<EPI_QKV, MAP_HD64>(g, mb, st);
-      if (g.head_dim == 32) return launch_map<EPI_QKV, MAP_HD32>(g, mb, st);
-      return hipErrorInvalidValue;
-    case EPI_RESID: return launch_map<EPI_RESID, MAP_LINEAR>(g, mb, st);
-    case EPI_SWIGLU: return launch_map<EPI_SWIGLU, MAP_DUAL>(g, mb, st);
+      if (g.head_dim <= 0 || 256 % g.head_dim) return hipErrorInvalidValue;
+      return launch_epi<EPI_QKV>(g, mb, st);
+    case EPI_RESID: return launch_epi<EPI_RESID>(g, mb, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, mb, st);
     default: return hipErrorInvalidValue;
   }
 }

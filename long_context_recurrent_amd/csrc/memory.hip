@@ -57,11 +57,10 @@ constexpr int RB = 8;    // rows per memory-read workgroup
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Memory read + attention RMSNorm.  Workgroup = (8 rows, node).  Builds the
+// Memory read (fp32 workloads).  Workgroup = (8 rows, node).  Builds the
 // node's input (layer 0: the segment's token rows from x, then the memory
 // embeddings; deeper layers: the previous layer's output slot), reads the
-// memory, writes h to this wave's slot and a = R(rms(h) g_attn) for the QKV
-// GEMM.
+// memory and writes h to this wave's slot.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
@@ -70,13 +69,11 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
   T* hs = (T*)smem_raw;                                   // [RB][d]
   float* qs = (float*)(smem_raw + (size_t)RB * d * sizeof(T));   // [RB][64]
   float* dens = qs + RB * 64;                             // [RB]
-  float* part = dens + RB;                                // [4][RB]
-  float* rstd = part + 4 * RB;                            // [RB]
 
   const int layer = a.l0 + blockIdx.y;
   const int r0 = blockIdx.x * RB;
   const int nr = min(RB, a.n - r0);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int64_t slab = (int64_t)layer * a.act_stride;
 
   // (a) stage the input rows
@@ -147,9 +144,6 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
   // (d) h <- R(h + (q A^T) / den); one model coordinate i per lane
   const float* A = a.A + (int64_t)layer * d * dk;
   T* out = (T*)a.act_cur + slab;
-  float ss[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) ss[r] = 0.f;
   for (int i = tid; i < d; i += 256) {
     float num[RB];
 #pragma unroll
@@ -169,34 +163,9 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if (r < nr) {
-        const T hv = from_f32<T>(to_f32(hs[r * d + i]) + num[r] / dens[r]);
-        hs[r * d + i] = hv;
-        out[(int64_t)(r0 + r) * d + i] = hv;
-        const float f = to_f32(hv);
-        ss[r] = fmaf(f, f, ss[r]);
+        out[(int64_t)(r0 + r) * d + i] = from_f32<T>(to_f32(hs[r * d + i]) + num[r] / dens[r]);
       }
     }
-  }
-  // (e) row RMS
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const float s = wave_sum(ss[r]);
-    if (lane == 0) part[w * RB + r] = s;
-  }
-  __syncthreads();
-  if (tid < RB) {
-    const float s = part[tid] + part[RB + tid] + part[2 * RB + tid] + part[3 * RB + tid];
-    rstd[tid] = rsqrtf(s / (float)d + a.rms_eps);
-  }
-  __syncthreads();
-  // (f) a = R(h * rstd * g)
-  const T* gain = (const T*)a.gain + (int64_t)layer * d;
-  T* ab = (T*)a.abuf + slab;
-  for (int i = tid; i < d; i += 256) {
-    const float gi = to_f32(gain[i]);
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-      if (r < nr) ab[(int64_t)(r0 + r) * d + i] = from_f32<T>(to_f32(hs[r * d + i]) * rstd[r] * gi);
   }
 }
 
@@ -242,47 +211,49 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Memory write, part 1.  Workgroup (jg < 16, node): keys k[:, 4jg .. 4jg+3]
-// (one wave per key column, lanes over d), the partial denominators
-// sum_{j in group} k_mj z_j with the pre-update z, then z_j += sum_m k_mj for
-// the group's own columns.  Workgroup jg = 16: the gates beta_m.
+// Memory write, part 1 (fp32 workloads).  Workgroup (jg < 4, node): keys
+// k[:, 16jg .. 16jg+15] (wave w computes columns 16jg + 4w .. +3, lanes over
+// d), the partial denominators sum_{j in group} k_mj z_j with the pre-update
+// z, then z_j += sum_m k_mj for the group's own columns.  Workgroup jg = 4:
+// the gates beta_m.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void mem_keys_kernel(MemArgs a) {
-  __shared__ float ks[64][4];
+  __shared__ float ks[64][16];
   const int layer = a.l0 + blockIdx.y;
   const int jg = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int d = a.d, M = a.M, dk = a.dk;
   const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
-  if (jg < 16) {
-    const int j = jg * 4 + w;
-    const T* wk = (const T*)a.w_mk + ((int64_t)layer * dk + j) * d;
-    for (int m = 0; m < M; ++m) {
-      float s = 0.f;
-      for (int k = lane * 8; k < d; k += 512) {
-        float yv[8], wv[8];
-        load8(Y + (int64_t)m * d + k, yv);
-        load8(wk + k, wv);
+  if (jg < 4) {
+    for (int jj = 0; jj < 4; ++jj) {
+      const int jl = 4 * w + jj, j = 16 * jg + jl;
+      const T* wk = (const T*)a.w_mk + ((int64_t)layer * dk + j) * d;
+      for (int m = 0; m < M; ++m) {
+        float s = 0.f;
+        for (int k = lane * 8; k < d; k += 512) {
+          float yv[8], wv[8];
+          load8(Y + (int64_t)m * d + k, yv);
+          load8(wk + k, wv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(yv[e], wv[e], s);
+          for (int e = 0; e < 8; ++e) s = fmaf(yv[e], wv[e], s);
+        }
+        s = wave_sum(s);
+        if (lane == 0) ks[m][jl] = phi_f(s);
       }
-      s = wave_sum(s);
-      if (lane == 0) ks[m][w] = phi_f(s);
     }
     __syncthreads();
-    float* z = a.z + (int64_t)layer * dk + jg * 4;
+    float* z = a.z + (int64_t)layer * dk + jg * 16;
     if (tid < M) {
       float pd = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < 16; ++jj) {
         pd = fmaf(ks[tid][jj], z[jj], pd);
-        a.kbuf[((int64_t)layer * M + tid) * dk + jg * 4 + jj] = ks[tid][jj];
+        a.kbuf[((int64_t)layer * M + tid) * dk + jg * 16 + jj] = ks[tid][jj];
       }
-      a.pden[((int64_t)layer * M + tid) * 16 + jg] = pd;
+      a.pden[((int64_t)layer * M + tid) * 4 + jg] = pd;
     }
     __syncthreads();   // every read of the old z of this group is done
-    if (tid < 4) {
+    if (tid < 16) {
       float s = 0.f;
       for (int m = 0; m < M; ++m) s += ks[m][tid];
       z[tid] = z[tid] + s;
@@ -305,7 +276,7 @@ __global__ __launch_bounds__(256) void mem_keys_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Memory write, part 2.  Workgroup = (16 rows i of A, node): values
+// Memory write, part 2 (fp32 workloads).  Workgroup = (16 rows i of A, node): values
 // v_m[i] = Y_m . W_mv[i] (one wave per 4 rows, lanes over d), retrieved values
 // vbar_m[i] = (k_m . A[i]) / (sum of the partial denominators + eps), then
 // A[i][j] += sum_m beta_m (v_m[i] - vbar_m[i]) k_mj.  Each A row is owned by
@@ -328,10 +299,8 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
     ks[idx / dk][idx % dk] = a.kbuf[(int64_t)layer * M * dk + idx];
   if (tid < M) {
     betas[tid] = a.beta[(int64_t)layer * M + tid];
-    const float* pd = a.pden + ((int64_t)layer * M + tid) * 16;
-    float s = 0.f;
-    for (int jg = 0; jg < 16; ++jg) s += pd[jg];
-    dens[tid] = s + a.mem_eps;
+    const float* pd = a.pden + ((int64_t)layer * M + tid) * 4;
+    dens[tid] = ((pd[0] + pd[1]) + (pd[2] + pd[3])) + a.mem_eps;
   }
 
   // v_m[i] for the wave's 4 rows, memory tokens in chunks of 16
@@ -403,11 +372,11 @@ __global__ void fill_f32_kernel(float* dst, const float* src, int64_t count) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_mem_read(const MemArgs& m, bool use_bf16, hipStream_t st) {
-  const size_t lds = (size_t)RB * m.d * (use_bf16 ? 2 : 4) + (RB * 64 + RB + 4 * RB + RB) * sizeof(float);
+  if (use_bf16) return launch_mem_read_bf16(m, st);
+  const size_t lds = (size_t)RB * m.d * sizeof(float) + (RB * 64 + RB) * sizeof(float);
   if (lds > 64 * 1024 || m.dk != 64 || m.d % 8) return hipErrorInvalidValue;
   dim3 grid((m.n + RB - 1) / RB, m.P);
-  if (use_bf16) hipLaunchKernelGGL(mem_read_kernel<bf16>, grid, dim3(256), lds, st, m);
-  else hipLaunchKernelGGL(mem_read_kernel<float>, grid, dim3(256), lds, st, m);
+  hipLaunchKernelGGL(mem_read_kernel<float>, grid, dim3(256), lds, st, m);
   return hipGetLastError();
 }
 
@@ -420,18 +389,16 @@ hipError_t launch_rmsnorm(const MemArgs& m, bool use_bf16, hipStream_t st) {
 }
 
 hipError_t launch_mem_keys(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (use_bf16) return launch_mem_keys_bf16(m, st);
   if (m.dk != 64 || m.M > 64 || m.d % 8) return hipErrorInvalidValue;
-  dim3 grid(17, m.P);
-  if (use_bf16) hipLaunchKernelGGL(mem_keys_kernel<bf16>, grid, dim3(256), 0, st, m);
-  else hipLaunchKernelGGL(mem_keys_kernel<float>, grid, dim3(256), 0, st, m);
+  hipLaunchKernelGGL(mem_keys_kernel<float>, dim3(5, m.P), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
 hipError_t launch_mem_update(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (use_bf16) return launch_mem_update_bf16(m, st);
   if (m.dk != 64 || m.M > 64 || m.d % 16) return hipErrorInvalidValue;
-  dim3 grid(m.d / 16, m.P);
-  if (use_bf16) hipLaunchKernelGGL(mem_update_kernel<bf16>, grid, dim3(256), 0, st, m);
-  else hipLaunchKernelGGL(mem_update_kernel<float>, grid, dim3(256), 0, st, m);
+  hipLaunchKernelGGL(mem_update_kernel<float>, dim3(m.d / 16, m.P), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 

@@ -175,3 +175,19 @@ def test_forward_argument_errors():
     assert "n_segments" in C.armt_last_error() or "NULL" in C.armt_last_error()
     # the handle still works after rejected calls
     model.forward(x, "diagonal")
+
+
+def test_gemm_tile_rows_do_not_change_results():
+    """Every output element accumulates over K in the same order whatever the
+    GEMM tile height, so all tile heights give bitwise equal results."""
+    cfg = MID64
+    inp = make_inputs(cfg)
+    model = build_model(inp)
+    x = to_device(inp.x, cfg)
+    ref = [t.clone() for t in model.forward(x, "diagonal")]
+    for mb in (2, 3, 4, 5, 6, 7):
+        model.set_option(C.ARMT_OPT_GEMM_ROWS, mb)
+        got = model.forward(x, "diagonal")
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"GEMM rows {32 * mb} changed the result"
+    model.set_option(C.ARMT_OPT_GEMM_ROWS, 0)
