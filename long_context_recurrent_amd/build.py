@@ -39,10 +39,8 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-source device flags.  The GEMM keeps its MFMA accumulators in VGPRs:
-# with the accumulator-register form this compiler rotates loop-carried
-# accumulators through extra AGPR copies every iteration.
-EXTRA = {"gemm_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra device flags (none needed at present).
+EXTRA: dict = {}
 
 
 def _compile(src: str) -> str:

@@ -16,8 +16,8 @@
 //  * Operands: K advances 32 per pipeline stage.  Stages are filled straight
 //    from global memory into LDS by global_load_lds_dwordx4 (no staging
 //    registers), issued NS - 1 stages ahead; each 64-byte tile row keeps its
-//    four 16-byte chunks XOR-swizzled so the fragment reads of 8 consecutive
-//    rows hit 8 different bank groups.  The fragments of the next stage are
+//    four 16-byte chunks XOR-swizzled so the fragment reads of 16 consecutive
+//    rows hit 16 different bank groups.  The fragments of the next stage are
 //    read while the MFMAs of the current one run.
 //  * Schedule: tiles are numbered so that each of the 8 XCDs works through a
 //    contiguous range (same layer, same weight columns, neighbouring rows),
@@ -56,8 +56,11 @@ constexpr int n_stages() {
   return (LDS_BYTES / ((32 * MB + BNB) * ROWB)) > 4 ? 4 : (LDS_BYTES / ((32 * MB + BNB) * ROWB));
 }
 
-// 16-byte chunk c (0..3) of tile row r sits at physical chunk c ^ ((r >> 1) & 3).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3); }
+// 16-byte chunk c (0..3) of tile row r sits at physical chunk
+// c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the same logical chunk of any 8 (or 16)
+// consecutive rows lands in 8 (16) different 16-byte bank groups, so fragment
+// reads are conflict-free whether the LDS serves 128 or 256 bytes per cycle.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 // s_waitcnt immediate (gfx9 layout): vmcnt <= n, lgkmcnt = 0, expcnt free.
 __host__ __device__ constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
@@ -216,10 +219,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     lds_barrier();
     read_frags(kt + 1, fa_nxt, fb_nxt);
     mfma_all(fa_cur, fb_cur);
-    // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
-    // each read next to the MFMA of the following step that uses it)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MB + 2), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB, 0);
+    // Interleave the reads with the MFMAs (one read, then one MFMA) so the
+    // LDS and the matrix core work side by side; left alone, the scheduler
+    // sinks each read next to the MFMA of the following step that uses it.
+    constexpr int NREAD = 2 * (MB + 2), NMFMA = 4 * MB;
+#pragma unroll
+    for (int i = 0; i < NREAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
   };
   for (int kt = 0; kt < KT; kt += 2) {
     step(kt, fa0, fb0, fa1, fb1);
