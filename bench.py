@@ -49,6 +49,9 @@ def parse():
                     help="rows per GEMM tile / 16 (0: the library's choice)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the diagonal forward (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only a plain 256 MiB device-to-device copy, three times (to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     return ap.parse_args()
 
 
@@ -64,6 +67,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {a.numel() * 4} bytes x3")
+        return
 
     from armt_inputs import get_config, make_inputs
     from long_context_recurrent_amd import armt as C
@@ -126,6 +139,7 @@ def main():
         model.set_option(C.ARMT_OPT_TIME_KERNEL, -1)
     rk = kstats[args.roofline_kernel]
     achieved = rk["flops"] / (rk["ms"] * 1e-3) / 1e12
+    traffic = measured_traffic(args.roofline_kernel, args.workload)
     gemm = [kstats[k] for k in ("qkv", "o_proj", "gate_up", "down")]
     g_flops = sum(k["flops"] for k in gemm)
     g_ms = sum(k["ms"] for k in gemm)
@@ -139,7 +153,7 @@ def main():
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
     res = {
-        "metric": "tokens/s, 131K-token 1B-shape ARMT forward (diagonal schedule)",
+        "metric": "tokens/s, 131K-token 1B-shape ARMT forward (diag vs seq); GEMM MFMA util %",
         "value": tokens / diag_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -160,15 +174,51 @@ def main():
             "diag_speedup": seq_s / diag_s},
         "roofline": {"kernel": args.roofline_kernel, "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "launches": rk["launches"],
+                     "traffic": traffic, "launches": rk["launches"],
                      "avg_launch_us": rk["ms"] / max(rk["launches"], 1) * 1e3},
         "gemm_util": {"achieved": g_flops / (g_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
                       "frac": g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "kernels_us_per_forward": {k: v["ms"] * 1e3 / max(1, min(args.steps, 3)) for k, v in kstats.items()},
+        "kernels": {k: kernel_summary(v, max(1, min(args.steps, 3))) for k, v in kstats.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     model.close()
+
+
+def kernel_summary(v, forwards):
+    """Per-kernel figures from HIP-event timing: time per forward, algorithmic
+    FLOP/s against the bf16 MFMA peak and algorithmic bytes/s against HBM."""
+    sec = v["ms"] * 1e-3
+    tf = v["flops"] / sec / 1e12 if sec else 0.0
+    gbs = v["bytes"] / sec / 1e9 if sec else 0.0
+    return {"us_per_forward": v["ms"] * 1e3 / forwards, "launches_per_forward": v["launches"] // forwards,
+            "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS, "gb_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+
+
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"gate_up": "gemm_bf16.hip", "down": "gemm_bf16.hip", "qkv": "gemm_bf16.hip",
+                  "o_proj": "gemm_bf16.hip", "attn": "attention.hip"}
+
+
+def measured_traffic(kernel, workload):
+    """Average HBM bytes per launch of ``kernel`` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record of this workload, scaled by the copy-kernel
+    calibration factors stored with it; None when there is no record or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
+    src = KERNEL_SOURCES.get(kernel)
+    if not (src and os.path.exists(path)):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, "long_context_recurrent_amd", "csrc", src), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        log(f"traffic record for {kernel} is stale (kernel source changed); reporting null")
+        return None
+    return (rec["fetch_kib_per_dispatch"] * rec["fetch_factor"]
+            + rec["write_kib_per_dispatch"] * rec["write_factor"]) * 1024.0
 
 
 def cpu_baseline(inp, seconds):

@@ -15,24 +15,25 @@
  * uniform layer geometry; skill page "Diagonal Batching for Recurrent Memory
  * Transformers", Implementation and Practical Guidance).  Per node:
  *
- *   read : h  = R(h_in + (q A^T) / (q . z + mem_eps)),  q = phi(h_in W_mq^T)
+ *   read : h  = h_in + (q A^T) / (q . z + mem_eps),  q = phi(h_in W_mq^T)
  *   attn : a  = R(rms(h) * g_attn);  Q|K|V = a W_qkv^T;  Q, K = RoPE;  R(Q,K,V)
  *          O  = R(causal softmax(Q K^T / sqrt(hd)) V), q-head j reads kv-head
- *               j / (H/G);  h = R(h + O W_o^T)
+ *               j / (H/G);  h = h + O W_o^T
  *   mlp  : b  = R(rms(h) * g_mlp);  U = R(silu(b W_gate^T) * (b W_up^T))
- *          h  = R(h + U W_down^T)            -> node output; rows 0..T-1 of the
- *                                               last layer are y[sT:(s+1)T]
+ *          h  = h + U W_down^T               -> node output; rows 0..T-1 of the
+ *                                               last layer give y[sT:(s+1)T] = R(h)
  *   write: Y = h[T:n]; k_m = phi(Y_m W_mk^T); v_m = Y_m W_mv^T;
  *          beta_m = sigmoid(Y_m . w_beta); vbar_m = (k_m A^T) / (k_m . z + mem_eps)
  *          A += sum_m beta_m (v_m - vbar_m) k_m^T;  z += sum_m k_m
  *
  * phi(u) = elu(u) + 1; rms(u) = u / sqrt(mean(u^2) + rms_eps); RoPE pairs
  * coordinate i with i + hd/2 at angle pos * rope_theta^(-2i/hd), positions
- * 0..n-1 in every segment.  R() stores in the activation dtype (identity for
- * ARMT_F32, round-to-nearest-even bfloat16 for ARMT_BF16); products
- * accumulate in fp32; the memory state (A, z) is always fp32.  The pages name
- * the model family but print none of these equations: this is the reading the
- * library implements.
+ * 0..n-1 in every segment.  R() stores a branch activation in the config
+ * dtype (identity for ARMT_F32, round-to-nearest-even bfloat16 for ARMT_BF16);
+ * the residual stream h -- the running sum of the memory read and the branch
+ * outputs across layers -- is fp32 in both dtypes, and so is the memory state
+ * (A, z); products accumulate in fp32.  The pages name the model family but
+ * print none of these equations: this is the reading the library implements.
  *
  * Conventions.  Every pointer argument that is not documented as host memory
  * is a device pointer on the HIP device that was current at armt_create.
@@ -65,8 +66,9 @@ typedef enum { ARMT_F32 = 0, ARMT_BF16 = 1 } armt_dtype;
  * assumptions / Section 3.3).  Constraints checked by armt_create:
  * every size > 0; d_model == n_heads * head_dim; n_heads % n_kv_heads == 0;
  * head_dim in {32, 64, 128}; d_key == 64; d_model % 64 == 0;
- * ffn_hidden % 64 == 0; seg_len + n_mem <= 4096; n_mem <= 64;
- * dtype ARMT_BF16 or ARMT_F32.  Defaults used by the workloads:
+ * ffn_hidden % 64 == 0; n_mem <= 64; dtype ARMT_BF16 or ARMT_F32;
+ * ARMT_BF16: seg_len + n_mem <= 4096 and d_model <= 4096;
+ * ARMT_F32: seg_len + n_mem <= 2048 and d_model <= 1024.  Defaults used by the workloads:
  * rms_eps 1e-5, rope_theta 10000, mem_eps 1e-6. */
 typedef struct {
   int32_t n_layers;    /* L */
@@ -188,7 +190,7 @@ int armt_kernel_stats(armt_handle *h, double *ms, int64_t *launches,
 /* Read-only view of an internal workspace buffer, for white-box tests of the
  * individual steps (host call, no GPU work).  After a forward the buffers hold
  * the last wave's values, slabbed by layer:
- *   ARMT_VIEW_ACT0 / ACT1  [L][n][d] node outputs of even / odd waves
+ *   ARMT_VIEW_ACT0 / ACT1  [L][n][d] fp32 node outputs of even / odd waves
  *   ARMT_VIEW_NORMED       [L][n][d] last RMSNorm output (MLP input)
  *   ARMT_VIEW_QKV          [L][n][(H+2G)hd] (bf16: V columns unused)
  *   ARMT_VIEW_VT           [L][G*hd][roundup(n, 64)] (bf16 only)

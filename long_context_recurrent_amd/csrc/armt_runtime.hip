@@ -10,7 +10,9 @@
 // synchronisation (same page, Practical Guidance).  The sequential baseline
 // (Pith review, Figure 3) runs the same kernels one node at a time.
 //
-// Buffers.  Node outputs live in two slots act[c & 1][L][n][d] (c = wave
+// Buffers.  Node outputs (the residual stream, fp32 in every workload; bf16
+// workloads store only branch activations in bf16) live in two slots
+// act[c & 1][L][n][d] (c = wave
 // index; node (s, l) of wave c reads layer l-1's row of slot (c-1) & 1 and
 // writes layer l's row of slot c & 1, so the nodes of one wave never touch a
 // buffer another node of that wave writes).  Per-layer scratch (normalised
@@ -103,8 +105,8 @@ Layout make_layout(const armt_config* c) {
   lo.rope = take(n * (c->head_dim / 2) * 2 * sizeof(float));
   lo.A = take(L * d * dk * 4);
   lo.z = take(L * dk * 4);
-  lo.act0 = take(L * n * d * es);
-  lo.act1 = take(L * n * d * es);
+  lo.act0 = take(L * n * d * 4);   // residual stream: fp32 in every workload
+  lo.act1 = take(L * n * d * 4);
   lo.abuf = take(L * n * d * es);
   lo.qkv = take(L * n * qkv_dim * es);
   lo.vt = take(c->dtype == ARMT_BF16 ? L * c->n_kv_heads * c->head_dim * n_pad * 2 : 0);
@@ -159,16 +161,18 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
   const double tri = n * (n + 1) / 2;
   double f = 0, b = 0;
   switch (k) {
-    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 2 * n * d * es + dk * d * es + d * dk * 4; break;
-    case ARMT_K_ATTN_NORM: f = 0; b = (2 * n * d + d) * es; break;
+    // the residual stream h (read and written by the memory read, read by the
+    // norms, updated by the residual epilogues, read by the memory write) is fp32
+    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 2 * n * d * 4 + dk * d * es + d * dk * 4; break;
+    case ARMT_K_ATTN_NORM: f = 0; b = n * d * 4 + (n * d + d) * es; break;
     case ARMT_K_QKV: f = 2 * n * d * q; b = (n * d + q * d + n * q) * es; break;
     case ARMT_K_ATTN: f = 4 * tri * hd * H; b = (n * q + n * H * hd) * es; break;
-    case ARMT_K_OPROJ: f = 2 * n * H * hd * d; b = (n * H * hd + d * H * hd + 2 * n * d) * es; break;
-    case ARMT_K_MLP_NORM: f = 0; b = (2 * n * d + d) * es; break;
+    case ARMT_K_OPROJ: f = 2 * n * H * hd * d; b = (n * H * hd + d * H * hd) * es + 2 * n * d * 4; break;
+    case ARMT_K_MLP_NORM: f = 0; b = n * d * 4 + (n * d + d) * es; break;
     case ARMT_K_GATE_UP: f = 4 * n * d * F; b = (n * d + 2 * F * d + n * F) * es; break;
-    case ARMT_K_DOWN: f = 2 * n * F * d; b = (n * F + d * F + 2 * n * d) * es; break;
-    case ARMT_K_MEM_KEYS: f = 2 * M * d * (dk + 1); b = (M * d + dk * d + d) * es; break;
-    case ARMT_K_MEM_UPDATE: f = 2 * M * d * d + 4 * M * dk * d; b = (M * d + d * d) * es + 2 * d * dk * 4; break;
+    case ARMT_K_DOWN: f = 2 * n * F * d; b = (n * F + d * F) * es + 2 * n * d * 4; break;
+    case ARMT_K_MEM_KEYS: f = 2 * M * d * (dk + 1); b = M * d * 4 + (dk * d + d) * es; break;
+    case ARMT_K_MEM_UPDATE: f = 2 * M * d * d + 4 * M * dk * d; b = M * d * 4 + d * d * es + 2 * d * dk * 4; break;
   }
   *flops = f;
   *bytes = b;

@@ -14,8 +14,9 @@
 // O^T = V^T P^T needs them (the two MFMA operands agree on which key each of a
 // lane's 8 k-slots means), and the online-softmax rescale is one scalar per
 // lane.  Row max and row sum over a tile need only two cross-lane exchanges
-// (lanes 16 and 32 apart).  Softmax statistics are fp32; P is rounded to bf16
-// for the second product.  Query blocks are launched heaviest first.
+// (lanes 16 and 32 apart).  Softmax statistics are fp32; P enters the second
+// product as a bf16 pair (hi + lo), so only the output O is rounded to bf16,
+// as in the layer definition.  Query blocks are launched heaviest first.
 #include "armt_common.h"
 #include "armt_kernels.h"
 
@@ -98,7 +99,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     lsum *= alpha;
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) o[eb] *= alpha;
-    bf16x8 pf[2];
+    // P = P_hi + P_lo with both parts bf16: the two products together carry
+    // P to about 16 significant bits, so P itself is never rounded to bf16.
+    bf16x8 ph[2], pl[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -106,8 +109,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         const float p0 = exp2f(s[2 * c][r] - mnew);
         const float p1 = exp2f(s[2 * c + 1][r] - mnew);
         lsum += p0 + p1;
-        pf[c][r] = (bf16)p0;
-        pf[c][4 + r] = (bf16)p1;
+        ph[c][r] = (bf16)p0;
+        ph[c][4 + r] = (bf16)p1;
+        pl[c][r] = (bf16)(p0 - (float)ph[c][r]);
+        pl[c][4 + r] = (bf16)(p1 - (float)ph[c][4 + r]);
       }
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb)
@@ -117,7 +122,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         const bf16x4 lo = *(const bf16x4*)vrow;
         const bf16x4 hi = *(const bf16x4*)(vrow + 16);
         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c], o[eb], 0, 0, 0);
+        o[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[c], o[eb], 0, 0, 0);
+        o[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[c], o[eb], 0, 0, 0);
       }
   }
   lsum += __shfl_xor(lsum, 16, kWave);

@@ -28,8 +28,9 @@
 //      EPI_QKV   : RoPE on the Q and K heads (partner column i + hd/2 read from
 //                  the staged tile), bf16 store; V heads are stored transposed
 //                  ([G * hd][n_pad]) for the attention kernel.
-//      EPI_RESID : C = R(C + acc) in place (residual add); for the last layer
-//                  the segment-token rows are also written to the caller's y.
+//      EPI_RESID : C += acc in place on the fp32 residual stream; for the
+//                  last layer the segment-token rows are also written to the
+//                  caller's y, rounded to bf16.
 //      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
 //                  rows; U = R(silu(gate) * up).
 //  Every output element accumulates over K in the same order whatever MB or
@@ -307,10 +308,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
           for (int e = 0; m + e < g.M; ++e) dstp[e] = (bf16)s[e * CPITCH];
         }
       }
-    } else {
+    } else if (EPI == EPI_RESID) {
+      // residual stream (fp32) += acc; the last layer's segment-token rows
+      // also go to the caller's y, rounded once to bf16
+      float* Cf = (float*)g.C + (int64_t)layer * g.c_stride;
       bf16* Y = nullptr;
       int y_rows = 0;
-      if (EPI == EPI_RESID && g.desc != nullptr && layer == g.last_layer) {
+      if (g.desc != nullptr && layer == g.last_layer) {
         const int s = g.desc->c - layer;
         Y = (bf16*)g.desc->y + (int64_t)s * g.T * g.ldc;
         y_rows = g.T;
@@ -320,18 +324,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.N) continue;
         const float* s = Cs + r * CPITCH + c8;
-        bf16* dstp = C + (int64_t)m * g.ldc + n;
-        bf16x8 o;
-        if (EPI == EPI_RESID) {
-          const bf16x8 res = *(const bf16x8*)dstp;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)res[e] + s[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e];
+        float* dstp = Cf + (int64_t)m * g.ldc + n;
+        const f32x4 r0 = *(const f32x4*)dstp, r1 = *(const f32x4*)(dstp + 4);
+        const f32x4 o0 = f32x4{r0[0] + s[0], r0[1] + s[1], r0[2] + s[2], r0[3] + s[3]};
+        const f32x4 o1 = f32x4{r1[0] + s[4], r1[1] + s[5], r1[2] + s[6], r1[3] + s[7]};
+        *(f32x4*)dstp = o0;
+        *(f32x4*)(dstp + 4) = o1;
+        if (m < y_rows) {
+          const bf16x8 o = {(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3],
+                            (bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
+          *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
         }
-        *(bf16x8*)dstp = o;
-        if (m < y_rows) *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
+      }
+    } else {
+      for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
+        const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
+        const int m = m0 + rc0 + r, n = n0 + c8;
+        if (m >= g.M || n >= g.N) continue;
+        const float* s = Cs + r * CPITCH + c8;
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e];
+        *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
       }
     }
     __syncthreads();

@@ -5,7 +5,7 @@
 // 2506.05229, "What carries the argument" and its reference list) but print no
 // equations.  The reading implemented here, per layer l with state
 // A_l [d, d_k], z_l [d_k] (fp32) and phi(u) = elu(u) + 1:
-//   read : q = phi(h W_mq^T);  h <- R(h + (q A^T) / (q . z + eps))
+//   read : q = phi(h W_mq^T);  h <- h + (q A^T) / (q . z + eps)
 //   write: from the node's M memory-token output rows Y,
 //          k = phi(Y W_mk^T), v = Y W_mv^T, beta = sigmoid(Y w_beta),
 //          vbar = (k A^T) / (k . z + eps) against the pre-update state,
@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm of this wave's slot into abuf: a = R(rms(h) g_mlp).  One wave per row.
+// RMSNorm of this wave's slot (the fp32 residual stream) into abuf:
+// a = R(rms(h) g), R the storage rounding of the workload dtype T.  One wave
+// per row.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(MemArgs a) {
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(MemArgs a) {
   if (row >= a.n) return;
   const int d = a.d;
   const int64_t off = (int64_t)layer * a.act_stride + (int64_t)row * d;
-  const T* h = (const T*)a.act_cur + off;
+  const float* h = (const float*)a.act_cur + off;     // residual stream: fp32
   float v[MAXC][8];
   float ss = 0.f;
 #pragma unroll

@@ -1,7 +1,7 @@
 // Associative-memory kernels for bf16 workloads, on CDNA4 matrix cores.
 //
 // Same reading of the ARMT memory as the fp32 kernels (see memory.hip):
-//   read : q = phi(h W_mq^T);  h <- R(h + (q A^T) / (q . z + eps))
+//   read : q = phi(h W_mq^T);  h <- h + (q A^T) / (q . z + eps)
 //   write: k = phi(Y W_mk^T), v = Y W_mv^T, beta = sigmoid(Y w_beta),
 //          vbar = (k A^T) / (k . z + eps) against the pre-update state,
 //          A += sum_m beta_m (v_m - vbar_m) k_m^T,  z += sum_m k_m
@@ -9,10 +9,12 @@
 // review of arXiv 2506.05229 and its reference list -- but print no
 // equations).
 //
-// Products against bf16 weights (h W_mq^T, Y W_mk^T, Y W_mv^T) use
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation: the operands are exactly
-// the stored bf16 values, so this is the fp32-accumulated product the reading
-// asks for.  The product with the fp32 state (q A^T) uses the fp32 matrix
+// h and Y belong to the residual stream, which is fp32 (bf16 only for the
+// layer-0 inputs x and the memory embeddings).  Their products with the bf16
+// weights (h W_mq^T, Y W_mk^T, Y W_mv^T) run on v_mfma_f32_16x16x32_bf16 with
+// each fp32 operand split into a bf16 pair, v = hi + lo (hi = R(v),
+// lo = R(v - hi), |v - hi - lo| <= 2^-17 |v|), so the stream enters the
+// products without being rounded to bf16; accumulation is fp32.  The product with the fp32 state (q A^T) uses the fp32 matrix
 // instruction v_mfma_f32_16x16x4_f32, so the state is never rounded.  The
 // small state updates stay on the vector ALU.  All sums have a fixed order.
 #include "armt_common.h"
@@ -22,14 +24,34 @@ namespace armt {
 
 namespace {
 
-// Row pointer of the node input h_in (layer 0: token rows of the segment from
-// the caller's x, then the memory embeddings; deeper layers: previous slot).
-__device__ __forceinline__ const bf16* input_row(const MemArgs& a, int layer, int row) {
+__device__ __forceinline__ void load8f(const float* p, float* v) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+}
+
+// Elements col..col+7 of row `row` of the node input h_in as fp32.  Layer 0:
+// the segment's token rows of the caller's x, then the memory embeddings
+// (bf16); deeper layers: the previous layer's fp32 output in the other slot.
+__device__ __forceinline__ void input8(const MemArgs& a, int layer, int row, int col, float* v) {
   if (layer == 0) {
-    if (row < a.T) return (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + row) * a.d;
-    return (const bf16*)a.mem_emb + (int64_t)(row - a.T) * a.d;
+    const bf16* p = row < a.T ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + row) * a.d
+                              : (const bf16*)a.mem_emb + (int64_t)(row - a.T) * a.d;
+    const bf16x8 x = *(const bf16x8*)(p + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  } else {
+    load8f((const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)row * a.d + col, v);
   }
-  return (const bf16*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)row * a.d;
+}
+
+// v = hi + lo with both parts bf16 (hi = R(v), lo = R(v - hi)).
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (bf16)v[e];
+    lo[e] = (bf16)(v[e] - (float)hi[e]);
+  }
 }
 
 }  // namespace
@@ -44,19 +66,22 @@ __global__ __launch_bounds__(256) void memq_bf16_kernel(MemArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int row = blockIdx.x * 64 + 16 * w + c16;
   const int rowc = row < a.n ? row : a.n - 1;
-  const bf16* src = input_row(a, layer, rowc) + 8 * g;
   const bf16* wq = (const bf16*)a.w_mq + ((int64_t)layer * 64 + c16) * a.d + 8 * g;
   const int64_t jstride = (int64_t)16 * a.d;
   f32x4 acc[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 2
   for (int k0 = 0; k0 < a.d; k0 += 32) {
-    const bf16x8 av = *(const bf16x8*)(src + k0);
+    float v[8];
+    input8(a, layer, rowc, k0 + 8 * g, v);
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       const bf16x8 bv = *(const bf16x8*)(wq + jb * jstride + k0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[jb], 0, 0, 0);
     }
   }
   // lane holds rows 4g + r of the wave's 16, column c16 of each block
@@ -72,7 +97,7 @@ __global__ __launch_bounds__(256) void memq_bf16_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// h = R(h_in + (q A^T) / (q . z + eps)) for a 64-row x 256-column tile.
+// h = h_in + (q A^T) / (q . z + eps) (fp32) for a 64-row x 256-column tile.
 // q and the A rows of the tile are staged in LDS; wave w computes rows
 // 16w..16w+15 x 256 columns with v_mfma_f32_16x16x4_f32.  Lane (c16, g) feeds
 // key indices 16g + ks at step ks, so its 16 values per row are one
@@ -146,16 +171,18 @@ __global__ __launch_bounds__(256) void memapply_bf16_kernel(MemArgs a) {
       st[rl * SP + 16 * cb + c16] = acc[cb][r] / dens[rl];
     }
   __syncthreads();
-  bf16* out = (bf16*)a.act_cur + (int64_t)layer * a.act_stride;
+  float* out = (float*)a.act_cur + (int64_t)layer * a.act_stride;
   for (int idx = tid; idx < 64 * 32; idx += 256) {
     const int r = idx >> 5, c8 = (idx & 31) * 8;
     const int row = r0 + r, col = c0 + c8;
     if (row >= a.n || col >= d) continue;
-    const bf16x8 hin = *(const bf16x8*)(input_row(a, layer, row) + col);
-    bf16x8 o;
+    float o[8];
+    input8(a, layer, row, col, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)hin[e] + st[r * SP + c8 + e]);
-    *(bf16x8*)(out + (int64_t)row * d + col) = o;
+    for (int e = 0; e < 8; ++e) o[e] += st[r * SP + c8 + e];
+    float* dst = out + (int64_t)row * d + col;
+    *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
   }
 }
 
@@ -174,7 +201,7 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int d = a.d, M = a.M;
-  const bf16* Y = (const bf16*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
   if (jb < 4) {
     const int mblocks = (M + 15) / 16;
     const bf16* wk = (const bf16*)a.w_mk + ((int64_t)layer * 64 + 16 * jb + c16) * d + 8 * g;
@@ -188,8 +215,12 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
         if (mb < mblocks) {
           int m = 16 * mb + c16;
           m = m < M ? m : M - 1;
-          const bf16x8 av = *(const bf16x8*)(Y + (int64_t)m * d + k0 + 8 * g);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mb], 0, 0, 0);
+          float v[8];
+          load8f(Y + (int64_t)m * d + k0 + 8 * g, v);
+          bf16x8 hi, lo;
+          split8(v, hi, lo);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[mb], 0, 0, 0);
         }
       }
     }
@@ -226,10 +257,11 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
     for (int m = w; m < M; m += 4) {
       float s = 0.f;
       for (int k = lane * 8; k < d; k += 512) {
-        const bf16x8 yv = *(const bf16x8*)(Y + (int64_t)m * d + k);
+        float yv[8];
+        load8f(Y + (int64_t)m * d + k, yv);
         const bf16x8 wv = *(const bf16x8*)(wb + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf((float)yv[e], (float)wv[e], s);
+        for (int e = 0; e < 8; ++e) s = fmaf(yv[e], (float)wv[e], s);
       }
       s = wave_sum(s);
       if (lane == 0) a.beta[(int64_t)layer * M + m] = sigmoid_f(s);
@@ -257,7 +289,7 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int d = a.d, M = a.M;
-  const bf16* Y = (const bf16*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
   float* A = a.A + (int64_t)layer * d * 64;
 
   for (int idx = tid; idx < M * 64; idx += 256) ks[idx >> 6][idx & 63] = a.kbuf[(int64_t)layer * M * 64 + idx];
@@ -286,8 +318,12 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
       if (mb < mblocks) {
         int m = 16 * mb + c16;
         m = m < M ? m : M - 1;
-        const bf16x8 av = *(const bf16x8*)(Y + (int64_t)m * d + k0 + 8 * g);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mb], 0, 0, 0);
+        float v[8];
+        load8f(Y + (int64_t)m * d + k0 + 8 * g, v);
+        bf16x8 hi, lo;
+        split8(v, hi, lo);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[mb], 0, 0, 0);
       }
     }
   }

@@ -97,7 +97,7 @@ class ArmtModel:
         ptr, nbytes = _c.armt_debug_view(self.handle, which)
         off = ptr - self.workspace.data_ptr()
         raw = self.workspace[off:off + nbytes]
-        dt = dtype or (torch.float32 if which in ("A", "z") else self.dtype)
+        dt = dtype or (torch.float32 if which in ("A", "z", "act0", "act1") else self.dtype)
         t = raw.view(dt)
         return t if shape is None else t[: _numel(shape)].view(*shape)
 

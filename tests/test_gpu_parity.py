@@ -76,6 +76,8 @@ def test_single_node_steps(cfg):
     errs["y"] = rel_l2(to_np(y), tr["h_out"][:cfg.seg_len])
     errs["A"] = rel_l2(to_np(A)[0], A_ref)
     errs["z"] = rel_l2(to_np(z)[0], z_ref)
+    errs["dA"] = rel_l2(to_np(A)[0] - A0[0], A_ref - A0[0])
+    errs["dz"] = rel_l2(to_np(z)[0] - z0[0], z_ref - z0[0])
     say("  rel L2:", {k: f"{v:.2e}" for k, v in errs.items()})
     for k, v in errs.items():
         assert v <= t, f"{k}: rel L2 {v:.3e} > {t}"
@@ -95,10 +97,16 @@ def _compare(cfg, inp, A0=None, z0=None, check_seq=True):
     say(f"  {cfg.name} diag rel L2 y={e[0]:.2e} A={e[1]:.2e} z={e[2]:.2e}")
     for v in e:
         assert v <= tol(cfg)
-    # per-layer state too
+    # per-layer state too, and (from a given state) its increment, which a
+    # large initial state would otherwise hide
+    An, zn = to_np(Ad), to_np(zd)
     for l in range(cfg.n_layers):
-        assert rel_l2(to_np(Ad)[l], A_ref[l]) <= tol(cfg)
-        assert rel_l2(to_np(zd)[l], z_ref[l]) <= tol(cfg)
+        assert rel_l2(An[l], A_ref[l]) <= tol(cfg)
+        assert rel_l2(zn[l], z_ref[l]) <= tol(cfg)
+        if A0 is not None:
+            eA = rel_l2(An[l] - A0[l], A_ref[l] - A0[l])
+            ez = rel_l2(zn[l] - z0[l], z_ref[l] - z0[l])
+            assert eA <= tol(cfg) and ez <= tol(cfg), f"layer {l} state increment: A {eA:.2e} z {ez:.2e}"
     if check_seq:
         ys, As, zs = model.forward(x, "sequential", dA0, dz0)
         assert torch.equal(ys, yd), "sequential and diagonal y differ"

@@ -306,3 +306,35 @@ def test_memory_carries_information_across_segments():
     ya, _, _ = oracle.forward_sequential(dataclasses.replace(inp, weights=w))
     yb, _, _ = oracle.forward_sequential(dataclasses.replace(inp, weights=w, x=x2))
     np.testing.assert_array_equal(ya[T:], yb[T:])
+
+
+def test_storage_precision_of_bf16_workloads():
+    """Stored values of a bf16 workload: branch activations are bf16 values,
+    the residual stream and the state are float32 values, y is the stream
+    rounded to bf16 (the reading of "bf16 activations with fp32 accumulate")."""
+    cfg = get_config("small_bf16").with_(n_layers=2, n_segments=2)
+    inp = make_inputs(cfg)
+    o = oracle.Oracle(inp)
+    A0, z0 = make_state(cfg)
+    tr = {}
+    h, A, z = o.node(0, o.node_input(0), A0[0], z0[0], trace=tr)
+
+    def is_bf16(a):
+        return np.array_equal(oracle.round_bf16(a), a)
+
+    def is_f32(a):
+        return np.array_equal(np.asarray(a, np.float32).astype(np.float64), a)
+
+    for k in ("a_attn", "Q", "K", "V", "O", "a_mlp", "U"):
+        assert is_bf16(tr[k]), k
+    for k in ("h_read", "h_attn", "h_out"):
+        assert is_f32(tr[k]), k
+        assert not is_bf16(tr[k]), f"{k} should carry more than bf16 precision"
+    assert is_f32(A) and is_f32(z)
+    y, _, _ = oracle.forward_sequential(inp, A0, z0)
+    assert is_bf16(y)
+    # y is the last layer's stream rounded once: recompute segment 0 by hand
+    h0 = o.node_input(0)
+    for l in range(cfg.n_layers):
+        h0, _, _ = o.node(l, h0, A0[l], z0[l])
+    np.testing.assert_array_equal(y[:cfg.seg_len], oracle.round_bf16(h0[:cfg.seg_len]))
