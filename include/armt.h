@@ -67,7 +67,7 @@ typedef enum { ARMT_F32 = 0, ARMT_BF16 = 1 } armt_dtype;
  * every size > 0; d_model == n_heads * head_dim; n_heads % n_kv_heads == 0;
  * head_dim in {32, 64, 128}; d_key == 64; d_model % 64 == 0;
  * ffn_hidden % 64 == 0; n_mem <= 64; dtype ARMT_BF16 or ARMT_F32;
- * ARMT_BF16: seg_len + n_mem <= 4096 and d_model <= 4096;
+ * ARMT_BF16: seg_len + n_mem <= 4096, d_model % 128 == 0 and d_model <= 3072;
  * ARMT_F32: seg_len + n_mem <= 2048 and d_model <= 1024.  Defaults used by the workloads:
  * rms_eps 1e-5, rope_theta 10000, mem_eps 1e-6. */
 typedef struct {

@@ -83,7 +83,8 @@ int validate_config(const armt_config* c) {
   const int n = c->seg_len + c->n_mem;
   if (c->dtype == ARMT_BF16) {
     if (n > 4096) return fail(ARMT_E_UNSUPPORTED, "seg_len + n_mem must be <= 4096");
-    if (c->d_model > 4096) return fail(ARMT_E_UNSUPPORTED, "d_model must be <= 4096");
+    if (c->d_model > 3072 || c->d_model % 128)
+      return fail(ARMT_E_UNSUPPORTED, "bf16: d_model must be a multiple of 128 and <= 3072");
   } else {
     if (n > 2048) return fail(ARMT_E_UNSUPPORTED, "fp32: seg_len + n_mem must be <= 2048");
     if (c->d_model > 1024) return fail(ARMT_E_UNSUPPORTED, "fp32: d_model must be <= 1024");
@@ -163,8 +164,12 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
   switch (k) {
     // the residual stream h (read and written by the memory read, read by the
     // norms, updated by the residual epilogues, read by the memory write) is fp32
-    case ARMT_K_MEM_READ: f = 4 * n * d * dk; b = 2 * n * d * 4 + dk * d * es + d * dk * 4; break;
-    case ARMT_K_ATTN_NORM: f = 0; b = n * d * 4 + (n * d + d) * es; break;
+    // bf16: the attention norm is fused into the memory read
+    case ARMT_K_MEM_READ:
+      f = 4 * n * d * dk;
+      b = 2 * n * d * 4 + dk * d * es + d * dk * 4 + (h->bf16 ? (n * d + d) * es : 0);
+      break;
+    case ARMT_K_ATTN_NORM: f = 0; b = h->bf16 ? 0 : n * d * 4 + (n * d + d) * es; break;
     case ARMT_K_QKV: f = 2 * n * d * q; b = (n * d + q * d + n * q) * es; break;
     case ARMT_K_ATTN: f = 4 * tri * hd * H; b = (n * q + n * H * hd) * es; break;
     case ARMT_K_OPROJ: f = 2 * n * H * hd * d; b = (n * H * hd + d * H * hd) * es + 2 * n * d * 4; break;
@@ -264,13 +269,16 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   g0.head_dim = c.head_dim;
 
   hipError_t e;
-  // 1. memory read, then the attention norm
+  // 1. memory read, then the attention norm (one fused kernel for bf16)
   {
     MemCall mc{h, m, ARMT_K_MEM_READ};
+    mc.m.gain = h->w.g_attn;
     if ((e = timed(cx, ARMT_K_MEM_READ, P, run_mem, &mc)) != hipSuccess) return e;
-    MemCall nc{h, m, ARMT_K_ATTN_NORM};
-    nc.m.gain = h->w.g_attn;
-    if ((e = timed(cx, ARMT_K_ATTN_NORM, P, run_mem, &nc)) != hipSuccess) return e;
+    if (!h->bf16) {
+      MemCall nc{h, m, ARMT_K_ATTN_NORM};
+      nc.m.gain = h->w.g_attn;
+      if ((e = timed(cx, ARMT_K_ATTN_NORM, P, run_mem, &nc)) != hipSuccess) return e;
+    }
   }
   // 2. QKV projection with RoPE
   {

@@ -30,21 +30,6 @@ __device__ __forceinline__ void load8f(const float* p, float* v) {
   for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
 }
 
-// Elements col..col+7 of row `row` of the node input h_in as fp32.  Layer 0:
-// the segment's token rows of the caller's x, then the memory embeddings
-// (bf16); deeper layers: the previous layer's fp32 output in the other slot.
-__device__ __forceinline__ void input8(const MemArgs& a, int layer, int row, int col, float* v) {
-  if (layer == 0) {
-    const bf16* p = row < a.T ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + row) * a.d
-                              : (const bf16*)a.mem_emb + (int64_t)(row - a.T) * a.d;
-    const bf16x8 x = *(const bf16x8*)(p + col);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-  } else {
-    load8f((const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)row * a.d + col, v);
-  }
-}
-
 // v = hi + lo with both parts bf16 (hi = R(v), lo = R(v - hi)).
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -57,132 +42,161 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// q = phi(h_in W_mq^T) -> qbuf [L][n][64] fp32.  Workgroup = (64 rows, node);
-// wave w owns rows 16w..16w+15 and all 64 key columns (4 MFMA blocks).
+// Memory read fused with the attention RMSNorm, for 16 rows of one node:
+//   q  = phi(h_in W_mq^T),  h = h_in + (q A^T) / (q . z + eps)   (fp32 stream)
+//   a  = R(rms(h) * g_attn)                                       (bf16)
+// Workgroup = (16 rows, node); wave w owns the column quarter
+// [w d/4, (w+1) d/4) as 32-column blocks, and keeps its h values in registers
+// from the first load to the last store.  Lane (c16, g) holds row c16 and, in
+// block b, the columns 32b + 4g + {0..3} and 32b + 16 + 4g + {0..3} (slots
+// 0..3 and 4..7): the MFMA output layout of a 16x16 block of r^T = A q^T, so
+// r lands in the lane that holds h.  The same slot order is the k order of
+// the first product (its weight operand is loaded in the same order).
+//   * q A^T: both fp32 operands as bf16 pairs, three products
+//     (A_hi q_hi + A_hi q_lo + A_lo q_hi), relative error ~2^-16.
+//   * The four waves' partial h W_mq^T, and their partial sums of squares,
+//     are added in LDS in a fixed order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void memq_bf16_kernel(MemArgs a) {
+template <int NBM>   // 32-column blocks per wave this instantiation can hold
+__global__ __launch_bounds__(256) void memread_norm_bf16_kernel(MemArgs a) {
+  __shared__ float ured[4][16][65];
+  __shared__ float qs[16][68];
+  __shared__ float dens[16];
+  __shared__ float ssq[4][16];
   const int layer = a.l0 + blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int row = blockIdx.x * 64 + 16 * w + c16;
+  const int d = a.d, nb = d >> 7;
+  const int row = blockIdx.x * 16 + c16;
   const int rowc = row < a.n ? row : a.n - 1;
-  const bf16* wq = (const bf16*)a.w_mq + ((int64_t)layer * 64 + c16) * a.d + 8 * g;
-  const int64_t jstride = (int64_t)16 * a.d;
-  f32x4 acc[4];
+  const int colw = w * (d >> 2) + 4 * g;     // + 32 b (+ 16 for slots 4..7)
+
+  // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0)
+  float hv[NBM][8];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    float v[8];
-    input8(a, layer, rowc, k0 + 8 * g, v);
-    bf16x8 hi, lo;
-    split8(v, hi, lo);
+  for (int b = 0; b < NBM; ++b) {
+    if (b < nb) {
+      const int c = colw + 32 * b;
+      if (layer == 0) {
+        const bf16* p = rowc < a.T ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + rowc) * d
+                                   : (const bf16*)a.mem_emb + (int64_t)(rowc - a.T) * d;
+        const bf16x4 x0 = *(const bf16x4*)(p + c), x1 = *(const bf16x4*)(p + c + 16);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const bf16x8 bv = *(const bf16x8*)(wq + jb * jstride + k0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[jb], 0, 0, 0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[jb], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) { hv[b][e] = (float)x0[e]; hv[b][4 + e] = (float)x1[e]; }
+      } else {
+        const float* p = (const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)rowc * d;
+        const f32x4 x0 = *(const f32x4*)(p + c), x1 = *(const f32x4*)(p + c + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { hv[b][e] = x0[e]; hv[b][4 + e] = x1[e]; }
+      }
     }
   }
-  // lane holds rows 4g + r of the wave's 16, column c16 of each block
-  float* q = a.qbuf + (int64_t)layer * a.n * 64;
+
+  // u = h W_mq^T over this wave's columns: key block jb, lane key c16
+  f32x4 u[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rr = blockIdx.x * 64 + 16 * w + 4 * g + r;
-    if (rr < a.n) {
+  for (int jb = 0; jb < 4; ++jb) u[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16* wq = (const bf16*)a.w_mq + (int64_t)layer * 64 * d;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) q[(int64_t)rr * 64 + jb * 16 + c16] = phi_f(acc[jb][r]);
+  for (int b = 0; b < NBM; ++b) {
+    if (b < nb) {
+      bf16x8 hi, lo;
+      split8(hv[b], hi, lo);
+      const int c = colw + 32 * b;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const bf16* wr = wq + (int64_t)(16 * jb + c16) * d;
+        const bf16x4 w0 = *(const bf16x4*)(wr + c), w1 = *(const bf16x4*)(wr + c + 16);
+        const bf16x8 bv = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, u[jb], 0, 0, 0);
+        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, u[jb], 0, 0, 0);
+      }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// h = h_in + (q A^T) / (q . z + eps) (fp32) for a 64-row x 256-column tile.
-// q and the A rows of the tile are staged in LDS; wave w computes rows
-// 16w..16w+15 x 256 columns with v_mfma_f32_16x16x4_f32.  Lane (c16, g) feeds
-// key indices 16g + ks at step ks, so its 16 values per row are one
-// contiguous 64-byte run (four 16-byte LDS reads; a 68-float pitch makes them
-// conflict-free).  The result is staged in LDS and written with coalesced
-// 16-byte stores.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void memapply_bf16_kernel(MemArgs a) {
-  constexpr int QP = 68;            // q / A tile pitch (floats)
-  constexpr int SP = 256 + 4;       // staging pitch
-  __shared__ __attribute__((aligned(16))) float qs[64 * QP];
-  __shared__ __attribute__((aligned(16))) float big[256 * QP];   // A tile, then staging
-  __shared__ float dens[64];
-  static_assert(64 * SP <= 256 * QP, "staging fits");
-
-  const int layer = a.l0 + blockIdx.z;
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 256;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int d = a.d;
-
-  const float* qsrc = a.qbuf + (int64_t)layer * a.n * 64;
-  for (int idx = tid; idx < 64 * 16; idx += 256) {
-    const int r = idx >> 4, c4 = (idx & 15) * 4;
-    const int rr = r0 + r < a.n ? r0 + r : a.n - 1;
-    *(f32x4*)(qs + r * QP + c4) = *(const f32x4*)(qsrc + (int64_t)rr * 64 + c4);
-  }
-  const float* A = a.A + (int64_t)layer * d * 64;
-  for (int idx = tid; idx < 256 * 16; idx += 256) {
-    const int i = idx >> 4, c4 = (idx & 15) * 4;
-    const int ii = c0 + i < d ? c0 + i : d - 1;
-    *(f32x4*)(big + i * QP + c4) = *(const f32x4*)(A + (int64_t)ii * 64 + c4);
+  // lane (c16, g) of block jb holds u[row 4g + i][key 16 jb + c16]
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ured[w][4 * g + i][16 * jb + c16] = u[jb][i];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * 64; idx += 256) {
+    const int r = idx >> 6, k = idx & 63;
+    qs[r][k] = phi_f(((ured[0][r][k] + ured[1][r][k]) + ured[2][r][k]) + ured[3][r][k]);
   }
   __syncthreads();
-  if (tid < 64) {
+  if (tid < 16) {
     const float* z = a.z + (int64_t)layer * 64;
-    float s = 0.f;
-    for (int j = 0; j < 64; ++j) s = fmaf(qs[tid * QP + j], z[j], s);
-    dens[tid] = s + a.mem_eps;
+    float sd = 0.f;
+    for (int k = 0; k < 64; ++k) sd = fmaf(qs[tid][k], z[k], sd);
+    dens[tid] = sd + a.mem_eps;
   }
+  // q^T as the second operand of r^T = A q^T: lane (c16, g) brings
+  // q[row c16][32 ks + 8 g .. + 7] as a bf16 pair
+  bf16x8 qh[2], ql[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = qs[c16][32 * ks + 8 * g + e];
+    split8(v, qh[ks], ql[ks]);
+  }
+  __syncthreads();   // dens visible
+  const float den = dens[c16];
 
-  float qa[16];
+  // h += r^T / den, block by block; partial sum of squares of the new h
+  const float* Ast = a.A + (int64_t)layer * d * 64;
+  float ss = 0.f;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const f32x4 t = *(const f32x4*)(qs + (16 * w + c16) * QP + 16 * g + 4 * v);
+  for (int b = 0; b < NBM; ++b) {
+    if (b < nb) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qa[4 * v + e] = t[e];
-  }
-  f32x4 acc[16];
+      for (int sb = 0; sb < 2; ++sb) {
+        const float* ar = Ast + (int64_t)(w * (d >> 2) + 32 * b + 16 * sb + c16) * 64 + 8 * g;
+        f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) {
-    float bb[16];
+        for (int ks = 0; ks < 2; ++ks) {
+          float av[8];
+          load8f(ar + 32 * ks, av);
+          bf16x8 ah, al;
+          split8(av, ah, al);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh[ks], r, 0, 0, 0);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql[ks], r, 0, 0, 0);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh[ks], r, 0, 0, 0);
+        }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const f32x4 t = *(const f32x4*)(big + (16 * cb + c16) * QP + 16 * g + 4 * v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bb[4 * v + e] = t[e];
+        for (int i = 0; i < 4; ++i) {
+          const float hn = hv[b][4 * sb + i] + r[i] / den;
+          hv[b][4 * sb + i] = hn;
+          ss = fmaf(hn, hn, ss);
+        }
+      }
     }
-    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[ks], bb[ks], c, 0, 0, 0);
-    acc[cb] = c;
   }
-  __syncthreads();   // A tile no longer needed; dens visible
-  float* st = big;
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = 16 * w + 4 * g + r;
-      st[rl * SP + 16 * cb + c16] = acc[cb][r] / dens[rl];
-    }
+  ss += __shfl_xor(ss, 16, kWave);
+  ss += __shfl_xor(ss, 32, kWave);
+  if (g == 0) ssq[w][c16] = ss;
   __syncthreads();
-  float* out = (float*)a.act_cur + (int64_t)layer * a.act_stride;
-  for (int idx = tid; idx < 64 * 32; idx += 256) {
-    const int r = idx >> 5, c8 = (idx & 31) * 8;
-    const int row = r0 + r, col = c0 + c8;
-    if (row >= a.n || col >= d) continue;
-    float o[8];
-    input8(a, layer, row, col, o);
+  const float rs = rsqrtf((((ssq[0][c16] + ssq[1][c16]) + ssq[2][c16]) + ssq[3][c16]) / (float)d + a.rms_eps);
+  if (row < a.n) {
+    float* ho = (float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)row * d;
+    bf16* ao = (bf16*)a.abuf + (int64_t)layer * a.act_stride + (int64_t)row * d;
+    const bf16* gn = (const bf16*)a.gain + (int64_t)layer * d;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] += st[r * SP + c8 + e];
-    float* dst = out + (int64_t)row * d + col;
-    *(f32x4*)dst = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4*)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    for (int b = 0; b < NBM; ++b) {
+      if (b < nb) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int c = colw + 32 * b + 16 * sb;
+          const float* v = &hv[b][4 * sb];
+          *(f32x4*)(ho + c) = f32x4{v[0], v[1], v[2], v[3]};
+          const bf16x4 gv = *(const bf16x4*)(gn + c);
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * rs * (float)gv[e]);
+          *(bf16x4*)(ao + c) = o;
+        }
+      }
+    }
   }
 }
 
@@ -355,11 +369,14 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st) {
-  if (m.dk != 64 || m.d % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(memq_bf16_kernel, dim3((m.n + 63) / 64, m.P), dim3(256), 0, st, m);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(memapply_bf16_kernel, dim3((m.n + 63) / 64, (m.d + 255) / 256, m.P), dim3(256), 0, st, m);
+  // d / 4 columns per wave in 32-column blocks; up to 24 blocks held per wave
+  if (m.dk != 64 || m.d % 128 || m.d > 3072) return hipErrorInvalidValue;
+  const dim3 grid((m.n + 15) / 16, m.P);
+  const int nb = m.d / 128;
+  if (nb <= 4) hipLaunchKernelGGL(memread_norm_bf16_kernel<4>, grid, dim3(256), 0, st, m);
+  else if (nb <= 8) hipLaunchKernelGGL(memread_norm_bf16_kernel<8>, grid, dim3(256), 0, st, m);
+  else if (nb <= 16) hipLaunchKernelGGL(memread_norm_bf16_kernel<16>, grid, dim3(256), 0, st, m);
+  else hipLaunchKernelGGL(memread_norm_bf16_kernel<24>, grid, dim3(256), 0, st, m);
   return hipGetLastError();
 }
 

@@ -59,7 +59,10 @@ def test_workspace_size_and_config_validation():
         (dict(head_dim=16, n_heads=4), -2), (dict(d_key=32), -2), (dict(n_mem=65), -2),
         (dict(dtype=7), -1), (dict(rms_eps=0.0), -1), (dict(ffn_hidden=100), -2),
         (dict(dtype=A.ARMT_BF16, seg_len=4090, n_mem=16), -2),
+        (dict(dtype=A.ARMT_BF16), -2),                                   # bf16: d_model % 128
+        (dict(dtype=A.ARMT_BF16, d_model=4096, n_heads=64, head_dim=64), -2),   # bf16: d_model <= 3072
     ]
+    assert A.armt_workspace_size(_cfg(dtype=A.ARMT_BF16, d_model=3072, n_heads=24, head_dim=128)) > 0
     for kw, code in cases:
         with pytest.raises(A.ArmtError) as e:
             A.armt_workspace_size(_cfg(**kw))
