@@ -193,7 +193,9 @@ int armt_kernel_stats(armt_handle *h, double *ms, int64_t *launches,
  *   ARMT_VIEW_ACT0 / ACT1  [L][n][d] fp32 node outputs of even / odd waves
  *   ARMT_VIEW_NORMED       [L][n][d] last RMSNorm output (MLP input)
  *   ARMT_VIEW_QKV          [L][n][(H+2G)hd] (bf16: V columns unused)
- *   ARMT_VIEW_VT           [L][G*hd][roundup(n, 64)] (bf16 only)
+ *   ARMT_VIEW_VT           [L][G*hd][roundup(n, 64)] (bf16 only); within every
+ *                          aligned group of 16 keys the stored order is
+ *                          0-3, 8-11, 4-7, 12-15
  *   ARMT_VIEW_ATTN         [L][n][H*hd]
  *   ARMT_VIEW_SWIGLU       [L][n][F]
  *   ARMT_VIEW_A / Z        fp32 state [L][d][d_k] / [L][d_k]

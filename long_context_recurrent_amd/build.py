@@ -39,8 +39,10 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-source extra device flags (none needed at present).
-EXTRA: dict = {}
+# Per-source extra device flags.  Attention keeps its MFMA results in
+# ordinary VGPRs: the softmax works on every score and accumulator element
+# between products, which would otherwise cost a register move each way.
+EXTRA: dict = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -5,139 +5,227 @@
 // batched attention inside the grouped layer; Figure 5 caption: groups are
 // treated as batches).
 //
-// bf16 path (flash-style, CDNA4 MFMA).  Workgroup = (64-query block, query
-// head, node); each of its 4 waves owns 16 queries.  Key tiles of 64 rows and
-// the matching V^T tile (V is stored transposed by the QKV GEMM) are staged in
-// LDS and shared by the 4 waves.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16, so each lane holds 4 keys of one
-// query: the probabilities then sit in registers exactly as the B operand of
-// O^T = V^T P^T needs them (the two MFMA operands agree on which key each of a
-// lane's 8 k-slots means), and the online-softmax rescale is one scalar per
-// lane.  Row max and row sum over a tile need only two cross-lane exchanges
-// (lanes 16 and 32 apart).  Softmax statistics are fp32; P enters the second
-// product as a bf16 pair (hi + lo), so only the output O is rounded to bf16,
-// as in the layer definition.  Query blocks are launched heaviest first.
+// bf16 path (flash-style, CDNA4 MFMA).  Workgroup = (128-query block, query
+// head, node); each of its 4 waves owns 32 queries.  Key tiles of 64 rows
+// and the matching V^T tiles (V is stored transposed by the QKV GEMM) stream
+// into LDS through global->LDS DMA loads, several tiles ahead, and are shared
+// by the 4 waves.  Both products run on v_mfma_f32_32x32x16_bf16:
+//  * S^T = K Q^T, so lane (r32, h) holds 16 keys of query r32 per 32-key
+//    block and the online-softmax statistics are per lane (one exchange with
+//    the lane 32 apart);
+//  * O^T = V^T P^T, with P taken straight from the S^T registers as the
+//    second operand.  A lane's 8 k-slots then name keys 4h..4h+3 and
+//    8+4h..8+4h+3 of a 16-key group, so V^T keeps the keys of every aligned
+//    group of 16 in the order 0-3, 8-11, 4-7, 12-15: each lane's V^T operand
+//    is one 16-byte read.
+// Softmax statistics are fp32; P enters the second product as a bf16 pair
+// (hi + lo), so only the output O is rounded to bf16, as in the layer
+// definition.  Tile rows keep their 16-byte chunks XOR-swizzled so the
+// fragment reads are free of bank conflicts.  Query blocks are launched
+// heaviest first.
 #include "armt_common.h"
 #include "armt_kernels.h"
 
 namespace armt {
 
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Physical 16-byte chunk of logical chunk c in row r of a tile whose rows
+// hold CH chunks: the same logical chunk of 8 (and of 16) consecutive rows
+// falls in distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int swzc(int r, int c) {
+  if (CH == 4) return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
+  if (CH == 8) return c ^ ((r ^ (r >> 3)) & 7);
+  return c ^ (r & 15);
+}
+
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt = 0, expcnt free
+__host__ __device__ constexpr int att_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+__device__ __forceinline__ void att_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace
+
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KP = HD + 8;    // K tile pitch (elements)
-  constexpr int VP = 64 + 8;    // V^T tile pitch
-  constexpr int ES = HD / 32;   // MFMA k-steps over the head dim
-  constexpr int EB = HD / 16;   // 16-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16 Ks[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[HD * VP];
+  constexpr int CH = HD / 8;                  // 16-byte chunks per K row
+  constexpr int K_BYTES = 64 * HD * 2;        // K tile: 64 keys x HD
+  constexpr int V_BYTES = HD * 64 * 2;        // V^T tile: HD rows x 64 keys
+  constexpr int TILE = K_BYTES + V_BYTES;
+  constexpr int NBUF = HD >= 128 ? 2 : 3;
+  constexpr int K_BLOCKS = K_BYTES / 1024;    // 1 KB wave loads per tile
+  constexpr int LOADS = (TILE / 1024) / 4;    // per wave per tile
+  constexpr int KROWS = 1024 / (HD * 2);      // K rows per 1 KB load
+  constexpr int ES = HD / 16, DB = HD / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TILE];
 
   const int n = a.n;
-  const int nqb = (n + 63) / 64;
+  const int nqb = (n + 127) / 128;
   const int qb = nqb - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
+  const int head = blockIdx.y;
   const int layer = a.l0 + blockIdx.z;
-  const int kvh = h / (a.H / a.G);
+  const int kvh = head / (a.H / a.G);
   const bf16* qkv = (const bf16*)a.qkv + (int64_t)layer * a.qkv_stride;
   const bf16* vt = (const bf16*)a.vt + (int64_t)layer * a.vt_stride + (int64_t)kvh * HD * a.vt_ld;
   const int kcol = (a.H + kvh) * HD;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int q = qb * 64 + 16 * w + c16;
-  const int qrow = q < n ? q : n - 1;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hh = lane >> 5;
+  const int q0w = qb * 128 + 32 * w;
+  const int q = q0w + r32;
+  const int qc = q < n ? q : n - 1;
+  const int q_end = (qb + 1) * 128 < n ? (qb + 1) * 128 : n;
+  const int ntile = (q_end + 63) / 64;
+  const int wq_end = q0w + 32 < n ? q0w + 32 : n;
+  const int wtiles = wq_end > q0w ? (wq_end + 63) / 64 : 0;
+
+  // DMA slots: 1 KB block b = w + 4t of a tile; K blocks first, then V^T
+  int roff[LOADS], coff[LOADS], dst[LOADS];
+#pragma unroll
+  for (int t = 0; t < LOADS; ++t) {
+    const int b = w + 4 * t;
+    dst[t] = b * 1024;
+    if (b < K_BLOCKS) {
+      const int r = b * KROWS + lane / CH;           // key row in the tile
+      roff[t] = r;
+      coff[t] = kcol + swzc<CH>(r, lane % CH) * 8;
+    } else {
+      const int dim = (b - K_BLOCKS) * 8 + lane / 8;   // V^T row
+      roff[t] = dim;
+      coff[t] = swzc<8>(dim, lane % 8) * 8;
+    }
+  }
+  auto issue = [&](int t) {
+    const int tt = t < ntile ? t : ntile - 1;
+    unsigned char* st = smem + (t % NBUF) * TILE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int b = w + 4 * i;
+      const bf16* src;
+      if (b < K_BLOCKS) {
+        int row = tt * 64 + roff[i];
+        row = row < n ? row : n - 1;
+        src = qkv + (int64_t)row * a.ld_qkv + coff[i];
+      } else {
+        src = vt + (int64_t)roff[i] * a.vt_ld + tt * 64 + coff[i];
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(st + dst[i]),
+                                       16, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NBUF - 1; ++s) issue(s);
 
   bf16x8 qf[ES];
 #pragma unroll
-  for (int es = 0; es < ES; ++es)
-    qf[es] = *(const bf16x8*)(qkv + (int64_t)qrow * a.ld_qkv + h * HD + 32 * es + g * 8);
+  for (int ks = 0; ks < ES; ++ks)
+    qf[ks] = *(const bf16x8*)(qkv + (int64_t)qc * a.ld_qkv + head * HD + 16 * ks + 8 * hh);
 
-  f32x4 o[EB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int eb = 0; eb < EB; ++eb) o[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float mrun = -INFINITY, lsum = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;   // scores in log2 units
 
-  for (int t = 0; t <= qb; ++t) {
-    __syncthreads();
-    for (int c = tid; c < 64 * (HD / 8); c += 256) {
-      const int key = c / (HD / 8), ch = c % (HD / 8);
-      int krow = t * 64 + key;
-      krow = krow < n ? krow : n - 1;
-      *(u32x4*)(Ks + key * KP + ch * 8) = *(const u32x4*)(qkv + (int64_t)krow * a.ld_qkv + kcol + ch * 8);
-    }
-    for (int c = tid; c < HD * 8; c += 256) {
-      const int e = c >> 3, ch = c & 7;
-      *(u32x4*)(Vs + e * VP + ch * 8) = *(const u32x4*)(vt + (int64_t)e * a.vt_ld + t * 64 + ch * 8);
-    }
-    __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    // tile t landed (this wave's loads; the barrier covers the others'),
+    // and every wave is done with tile t - 1, whose buffer is refilled next
+    __builtin_amdgcn_s_waitcnt(att_wait((NBUF - 2) * LOADS));
+    att_barrier();
+    issue(t + NBUF - 1);
+    if (t >= wtiles) continue;
+    const unsigned char* kt = smem + (t % NBUF) * TILE;
+    const unsigned char* vtile = kt + K_BYTES;
 
-    f32x4 s[4];
+    f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-      for (int es = 0; es < ES; ++es) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + (kb * 16 + c16) * KP + 32 * es + g * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[es], s[kb], 0, 0, 0);
+      for (int ks = 0; ks < ES; ++ks) {
+        const int r = kb * 32 + r32;
+        const bf16x8 kf = *(const bf16x8*)(kt + r * (HD * 2) + swzc<CH>(r, 2 * ks + hh) * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
       }
     }
+    // element e of block kb: key t*64 + 32kb + 8(e/4) + 4hh + e%4, query q.
+    // Only tiles that reach past the wave's first query need the causal mask.
     float mloc = -INFINITY;
+    if (t * 64 + 63 > q0w) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = t * 64 + kb * 16 + 4 * g + r;
-        const float v = (key <= q) ? s[kb][r] * sl2 : -INFINITY;
-        s[kb][r] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * 64 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (key > q) s[kb][e] = -INFINITY;
+          mloc = fmaxf(mloc, s[kb][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
+    }
+    // running max in raw score units; p = 2^(s * sl2 - m * sl2) (sl2 > 0)
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     const float mnew = fmaxf(mrun, mloc);
-    const float alpha = exp2f(mrun - mnew);
+    // rescale the running sums only when some lane's maximum grew
+    if (__any(mnew > mrun)) {
+      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float mb = mnew * sl2;
     mrun = mnew;
-    lsum *= alpha;
+    // P as the second operand of O^T = V^T P^T: 16-key group G = 2kb + ks,
+    // slot j = element 8ks + j of block kb
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) o[eb] *= alpha;
-    // P = P_hi + P_lo with both parts bf16: the two products together carry
-    // P to about 16 significant bits, so P itself is never rounded to bf16.
-    bf16x8 ph[2], pl[2];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int ks = 0; ks < 2; ++ks) {
+        f32x8 pv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p0 = exp2f(s[2 * c][r] - mnew);
-        const float p1 = exp2f(s[2 * c + 1][r] - mnew);
-        lsum += p0 + p1;
-        ph[c][r] = (bf16)p0;
-        ph[c][4 + r] = (bf16)p1;
-        pl[c][r] = (bf16)(p0 - (float)ph[c][r]);
-        pl[c][4 + r] = (bf16)(p1 - (float)ph[c][4 + r]);
-      }
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + j], sl2, -mb));
+          lsum += pv[j];
+        }
+        const bf16x8 ph = __builtin_convertvector(pv, bf16x8);
+        const bf16x8 pl = __builtin_convertvector(pv - __builtin_convertvector(ph, f32x8), bf16x8);
+        const int c = 2 * (2 * kb + ks) + hh;    // logical chunk of the V^T row
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16* vrow = Vs + (eb * 16 + c16) * VP + c * 32 + 4 * g;
-        const bf16x4 lo = *(const bf16x4*)vrow;
-        const bf16x4 hi = *(const bf16x4*)(vrow + 16);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[c], o[eb], 0, 0, 0);
-        o[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[c], o[eb], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          const int r = db * 32 + r32;
+          const bf16x8 vf = *(const bf16x8*)(vtile + r * 128 + swzc<8>(r, c) * 16);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, o[db], 0, 0, 0);
+        }
       }
   }
-  lsum += __shfl_xor(lsum, 16, kWave);
+  __builtin_amdgcn_s_waitcnt(att_wait(0));
   lsum += __shfl_xor(lsum, 32, kWave);
   if (q < n) {
     const float inv = 1.f / lsum;
-    bf16* out = (bf16*)a.out + (int64_t)layer * a.out_stride + (int64_t)q * a.ld_out + h * HD;
+    bf16* out = (bf16*)a.out + (int64_t)layer * a.out_stride + (int64_t)q * a.ld_out + head * HD;
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) {
-      bf16x4 v;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16)(o[eb][r] * inv);
-      *(bf16x4*)(out + eb * 16 + 4 * g) = v;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[db][4 * g4 + e] * inv);
+        *(bf16x4*)(out + db * 32 + 8 * g4 + 4 * hh) = v;
+      }
   }
 }
 
@@ -192,7 +280,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, bool use_bf16, hipStream_t st) {
   if (a.P <= 0 || a.n <= 0) return hipErrorInvalidValue;
   if (use_bf16) {
-    dim3 grid((a.n + 63) / 64, a.H, a.P);
+    dim3 grid((a.n + 127) / 128, a.H, a.P);
     switch (a.hd) {
       case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a); break;
       case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a); break;

@@ -27,7 +27,8 @@
 //    value:
 //      EPI_QKV   : RoPE on the Q and K heads (partner column i + hd/2 read from
 //                  the staged tile), bf16 store; V heads are stored transposed
-//                  ([G * hd][n_pad]) for the attention kernel.
+//                  ([G * hd][n_pad], keys reordered within groups of 16) for
+//                  the attention kernel.
 //      EPI_RESID : C += acc in place on the fp32 residual stream; for the
 //                  last layer the segment-token rows are also written to the
 //                  caller's y, rounded to bf16.
@@ -81,6 +82,13 @@ template <int EPI>
 __device__ __forceinline__ int col_block(int w, int j) {
   if (EPI == EPI_SWIGLU) return j == 0 ? 32 * w : 128 + 32 * w;   // gate, matching up
   return 64 * w + 32 * j;
+}
+
+// Stored position of key k in a V^T row: keys 4..7 and 8..11 of every
+// aligned group of 16 trade places.
+__device__ __forceinline__ int vt_pos(int k) {
+  const int a = (k >> 2) & 3;
+  return (k & ~15) + 4 * (a == 1 ? 2 : a == 2 ? 1 : a) + (k & 3);
 }
 
 __device__ __forceinline__ int xcd_tile(int id, int total) {
@@ -288,7 +296,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         }
         *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
       }
-      // V columns, transposed: 8 consecutive rows of one column per piece
+      // V columns, transposed: 8 consecutive rows (keys) of one column per
+      // piece.  Within every aligned group of 16 keys the stored order is
+      // 0-3, 8-11, 4-7, 12-15 (the k-slot order of the attention kernel's
+      // P V product), so keys m..m+3 and m+4..m+7 go to two 8-byte runs.
       bf16* Vt = (bf16*)g.vt + (int64_t)layer * g.vt_stride;
       const int rgroups = (rows_here + 7) / 8;
       for (int pc = tid; pc < rgroups * BN_OUT; pc += 256) {
@@ -297,15 +308,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         if (n < g.v_col0 || n >= g.N) continue;
         const int m = m0 + rc0 + rg * 8;
         if (m >= g.M) continue;
-        bf16* dstp = Vt + (int64_t)(n - g.v_col0) * g.vt_ld + m;
+        bf16* dstp = Vt + (int64_t)(n - g.v_col0) * g.vt_ld;
         const float* s = Cs + (rg * 8) * CPITCH + col;
         if (m + 8 <= g.M) {
-          bf16x8 o;
+          bf16x4 lo, hi;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e * CPITCH];
-          *(bf16x8*)dstp = o;
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = (bf16)s[e * CPITCH];
+            hi[e] = (bf16)s[(4 + e) * CPITCH];
+          }
+          *(bf16x4*)(dstp + vt_pos(m)) = lo;
+          *(bf16x4*)(dstp + vt_pos(m + 4)) = hi;
         } else {
-          for (int e = 0; m + e < g.M; ++e) dstp[e] = (bf16)s[e * CPITCH];
+          for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)s[e * CPITCH];
         }
       }
     } else if (EPI == EPI_RESID) {
