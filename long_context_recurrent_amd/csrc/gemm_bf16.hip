@@ -36,12 +36,26 @@
 //                  rows; U = R(silu(gate) * up).
 //  Every output element accumulates over K in the same order whatever MB or
 //  the number of problems, so results do not depend on the wave width.
+#include <type_traits>
+#include <utility>
+
 #include "armt_common.h"
 #include "armt_kernels.h"
 
 namespace armt {
 
 namespace {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time
+// (array indices stay static where a loop body holds barriers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -250,6 +264,74 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // Accumulator element e of block (i, j) in lane (r32, h) is output row
   // 32i + 8(e/4) + 4h + e%4, column col_block(w, j) + r32.
   float* Cs = (float*)smem;
+  if (EPI == EPI_RESID) {
+    // Residual stream (fp32) += acc.  Each pass's residual rows are loaded
+    // into registers while the previous pass is stored, and the barriers
+    // wait only for LDS traffic, so the loads overlap the staging and the
+    // stores.  The last layer's segment-token rows also go to the caller's y,
+    // rounded once to bf16.
+    constexpr int NPASS = (BM + RC - 1) / RC;
+    constexpr int PPT = RC * (BN_OUT / 8) / 256;     // pieces per thread per pass
+    float* Cf = (float*)g.C + (int64_t)layer * g.c_stride;
+    bf16* Y = nullptr;
+    int y_rows = 0;
+    if (g.desc != nullptr && layer == g.last_layer) {
+      Y = (bf16*)g.desc->y + (int64_t)(g.desc->c - layer) * g.T * g.ldc;
+      y_rows = g.T;
+    }
+    f32x4 rb[2][PPT][2];
+    auto load_pass = [&](int rc0, f32x4 (&dstv)[PPT][2]) {
+#pragma unroll
+      for (int k = 0; k < PPT; ++k) {
+        const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
+        const int m = m0 + rc0 + r, n = n0 + c8;
+        if (r < BM - rc0 && m < g.M && n < g.N) {
+          dstv[k][0] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n);
+          dstv[k][1] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n + 4);
+        }
+      }
+    };
+    load_pass(0, rb[0]);
+    static_for<NPASS>([&](auto PI) {
+      constexpr int p = decltype(PI)::value, rc0 = RC * p;
+      if (p + 1 < NPASS) load_pass(rc0 + RC, rb[(p + 1) & 1]);
+      static_for<MB>([&](auto II) {
+        constexpr int i = decltype(II)::value;
+        if (32 * i >= rc0 && 32 * i < rc0 + RC) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = 32 * i - rc0 + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) Cs[rl * CPITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
+          }
+        }
+      });
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
+      lds_barrier();
+#pragma unroll
+      for (int k = 0; k < PPT; ++k) {
+        const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
+        const int m = m0 + rc0 + r, n = n0 + c8;
+        if (r < BM - rc0 && m < g.M && n < g.N) {
+          const float* sv = Cs + r * CPITCH + c8;
+          const f32x4 x0 = rb[p & 1][k][0], x1 = rb[p & 1][k][1];
+          const f32x4 o0 = f32x4{x0[0] + sv[0], x0[1] + sv[1], x0[2] + sv[2], x0[3] + sv[3]};
+          const f32x4 o1 = f32x4{x1[0] + sv[4], x1[1] + sv[5], x1[2] + sv[6], x1[3] + sv[7]};
+          float* dstp = Cf + (int64_t)m * g.ldc + n;
+          *(f32x4*)dstp = o0;
+          *(f32x4*)(dstp + 4) = o1;
+          if (m < y_rows) {
+            const bf16x8 o = {(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3],
+                              (bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
+            *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
+      lds_barrier();
+    });
+    return;
+  }
   for (int rc0 = 0; rc0 < BM; rc0 += RC) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
