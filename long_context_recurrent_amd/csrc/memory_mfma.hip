@@ -218,23 +218,29 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
   if (jb < 4) {
     const int mblocks = (M + 15) / 16;
-    const bf16* wk = (const bf16*)a.w_mk + ((int64_t)layer * 64 + 16 * jb + c16) * d + 8 * g;
+    // waves take interleaved 64-wide k chunks; lane group g brings
+    // k0 + 16g .. +15 (same slot order for both operands, as in memupdate)
+    const bf16* wk = (const bf16*)a.w_mk + ((int64_t)layer * 64 + 16 * jb + c16) * d + 16 * g;
     f32x4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 32 * w; k0 < d; k0 += 128) {
-      const bf16x8 bv = *(const bf16x8*)(wk + k0);
+    for (int k0 = 64 * w; k0 < d; k0 += 256) {
+      const bf16x8 bv0 = *(const bf16x8*)(wk + k0), bv1 = *(const bf16x8*)(wk + k0 + 8);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (mb < mblocks) {
           int m = 16 * mb + c16;
           m = m < M ? m : M - 1;
-          float v[8];
-          load8f(Y + (int64_t)m * d + k0 + 8 * g, v);
-          bf16x8 hi, lo;
-          split8(v, hi, lo);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[mb], 0, 0, 0);
+          float v[16];
+          load8f(Y + (int64_t)m * d + k0 + 16 * g, v);
+          load8f(Y + (int64_t)m * d + k0 + 16 * g + 8, v + 8);
+          bf16x8 hi0, lo0, hi1, lo1;
+          split8(v, hi0, lo0);
+          split8(v + 8, hi1, lo1);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, bv0, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, bv0, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, bv1, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, bv1, acc[mb], 0, 0, 0);
         }
       }
     }
@@ -319,25 +325,32 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
     for (int e = 0; e < 4; ++e) At[i][c4 + e] = t[e];
   }
 
+  // k moves 64 per step: lane group g brings k0 + 16g .. +15 of its row (32
+  // bytes of W_mv, a whole 128-byte line per row across the four groups) and
+  // feeds them to two MFMAs (slots k0 + 16g + j, then k0 + 16g + 8 + j); the
+  // Y operand uses the same slot order.
   const int mblocks = (M + 15) / 16;
-  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)layer * d + i0 + 16 * w + c16) * d + 8 * g;
+  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)layer * d + i0 + 16 * w + c16) * d + 16 * g;
   f32x4 acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const bf16x8 bv = *(const bf16x8*)(wv + k0);
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    const bf16x8 bv0 = *(const bf16x8*)(wv + k0), bv1 = *(const bf16x8*)(wv + k0 + 8);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb < mblocks) {
         int m = 16 * mb + c16;
         m = m < M ? m : M - 1;
-        float v[8];
-        load8f(Y + (int64_t)m * d + k0 + 8 * g, v);
-        bf16x8 hi, lo;
-        split8(v, hi, lo);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc[mb], 0, 0, 0);
+        float v[16];
+        load8f(Y + (int64_t)m * d + k0 + 16 * g, v);
+        load8f(Y + (int64_t)m * d + k0 + 16 * g + 8, v + 8);
+        bf16x8 hi0, lo0, hi1, lo1;
+        split8(v, hi0, lo0);
+        split8(v + 8, hi1, lo1);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, bv0, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, bv0, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, bv1, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, bv1, acc[mb], 0, 0, 0);
       }
     }
   }
@@ -381,7 +394,7 @@ hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st) {
 }
 
 hipError_t launch_mem_keys_bf16(const MemArgs& m, hipStream_t st) {
-  if (m.dk != 64 || m.M > 64 || m.d % 32) return hipErrorInvalidValue;
+  if (m.dk != 64 || m.M > 64 || m.d % 64) return hipErrorInvalidValue;
   hipLaunchKernelGGL(memkeys_bf16_kernel, dim3(5, m.P), dim3(256), 0, st, m);
   return hipGetLastError();
 }
