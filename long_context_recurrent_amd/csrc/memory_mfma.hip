@@ -30,6 +30,18 @@ __device__ __forceinline__ void load8f(const float* p, float* v) {
   for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
 }
 
+// s_waitcnt immediates (gfx9 layout): vmcnt <= n with lgkmcnt = 0; lgkmcnt = 0 only
+__host__ __device__ constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int kLgkmOnly = 0xc07f;
+
+// Workgroup barrier that does not wait for outstanding global->LDS loads
+// (callers wait for exactly what they need with s_waitcnt first).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // v = hi + lo with both parts bf16 (hi = R(v), lo = R(v - hi)).
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -42,159 +54,219 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Memory read fused with the attention RMSNorm, for 16 rows of one node:
+// Memory read fused with the attention RMSNorm, for 32 rows of one node:
 //   q  = phi(h_in W_mq^T),  h = h_in + (q A^T) / (q . z + eps)   (fp32 stream)
 //   a  = R(rms(h) * g_attn)                                       (bf16)
-// Workgroup = (16 rows, node); wave w owns the column quarter
-// [w d/4, (w+1) d/4) as 32-column blocks, and keeps its h values in registers
-// from the first load to the last store.  Lane (c16, g) holds row c16 and, in
-// block b, the columns 32b + 4g + {0..3} and 32b + 16 + 4g + {0..3} (slots
-// 0..3 and 4..7): the MFMA output layout of a 16x16 block of r^T = A q^T, so
-// r lands in the lane that holds h.  The same slot order is the k order of
-// the first product (its weight operand is loaded in the same order).
-//   * q A^T: both fp32 operands as bf16 pairs, three products
-//     (A_hi q_hi + A_hi q_lo + A_lo q_hi), relative error ~2^-16.
-//   * The four waves' partial h W_mq^T, and their partial sums of squares,
-//     are added in LDS in a fixed order.
+// Workgroup = 8 waves: row group rg = w / 4 (16 rows) x column set cq = w % 4.
+// Columns come in 128-wide chunks s = 0 .. d/128 - 1; wave (rg, cq) owns
+// columns 128 s + 32 cq .. + 31 of every chunk and keeps its 16 rows of them
+// in registers from the first load to the last store: lane (c16, g) holds row
+// c16, columns 128 s + 32 cq + 8 g .. + 7.  The operands of a chunk -- the
+// W_mq columns [64 keys x 128] bf16 for the first product, then the A rows
+// [128 x 64] fp32 for the second -- stream into LDS by global->LDS DMA in
+// whole 256-byte rows, one chunk ahead, and are shared by both row groups.
+//  * u = h W_mq^T on v_mfma_f32_16x16x32_bf16 with h as a bf16 pair
+//    (hi = R(h), lo = R(h - hi)); the four column sets' partial u are added
+//    in LDS in a fixed order.
+//  * r^T = A q^T on the same instruction as three hi/lo products
+//    (A_hi q_hi + A_hi q_lo + A_lo q_hi, relative error ~2^-16).  The A rows
+//    feeding 16x16 output block sb are the columns 8(i/4) + 4 sb + i%4 of the
+//    wave's 32, so lane (c16, g) receives r for exactly the columns it holds.
+// Tile rows keep their 16-byte chunks XOR-swizzled (W_mq rows by key & 15, A
+// rows by (r & 3) | ((r >> 3) & 3) << 2) so the fragment reads are free of
+// bank conflicts.
 // ---------------------------------------------------------------------------
-template <int NBM>   // 32-column blocks per wave this instantiation can hold
-__global__ __launch_bounds__(256) void memread_norm_bf16_kernel(MemArgs a) {
-  __shared__ float ured[4][16][65];
-  __shared__ float qs[16][68];
-  __shared__ float dens[16];
-  __shared__ float ssq[4][16];
+template <int NBM>   // 128-column chunks this instantiation can hold (d / 128 <= NBM)
+__global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
+  constexpr int BUF = 128 * 64 * 4;           // one chunk buffer: A chunk 32 KB (W_mq chunk: 16 KB)
+  constexpr int LW = 64 * 128 * 2 / 1024 / 8;  // 1 KB DMA loads per wave per W_mq chunk (2)
+  constexpr int LA = BUF / 1024 / 8;            // ... per A chunk (4)
+  __shared__ __attribute__((aligned(1024))) unsigned char ops[2 * BUF];
+  __shared__ float ured[2][4][16][65];
+  __shared__ float qs[32][68];
+  __shared__ float dens[32];
+  __shared__ float ssq[2][4][16];
+
   const int layer = a.l0 + blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int rg = w >> 2, cq = w & 3;
   const int d = a.d, nb = d >> 7;
-  const int row = blockIdx.x * 16 + c16;
+  const int rl = 16 * rg + c16;                  // row within the workgroup's 32
+  const int row = blockIdx.x * 32 + rl;
   const int rowc = row < a.n ? row : a.n - 1;
-  const int colw = w * (d >> 2) + 4 * g;     // + 32 b (+ 16 for slots 4..7)
+  const int colw = 32 * cq + 8 * g;              // + 128 s
 
   // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0)
   float hv[NBM][8];
 #pragma unroll
-  for (int b = 0; b < NBM; ++b) {
-    if (b < nb) {
-      const int c = colw + 32 * b;
+  for (int s = 0; s < NBM; ++s) {
+    if (s < nb) {
+      const int c = 128 * s + colw;
       if (layer == 0) {
         const bf16* p = rowc < a.T ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + rowc) * d
                                    : (const bf16*)a.mem_emb + (int64_t)(rowc - a.T) * d;
-        const bf16x4 x0 = *(const bf16x4*)(p + c), x1 = *(const bf16x4*)(p + c + 16);
+        const bf16x8 x = *(const bf16x8*)(p + c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { hv[b][e] = (float)x0[e]; hv[b][4 + e] = (float)x1[e]; }
+        for (int e = 0; e < 8; ++e) hv[s][e] = (float)x[e];
       } else {
-        const float* p = (const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)rowc * d;
-        const f32x4 x0 = *(const f32x4*)(p + c), x1 = *(const f32x4*)(p + c + 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { hv[b][e] = x0[e]; hv[b][4 + e] = x1[e]; }
+        load8f((const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)rowc * d + c, hv[s]);
       }
     }
   }
 
-  // u = h W_mq^T over this wave's columns: key block jb, lane key c16
+  // chunk DMA: 1 KB block q = w + 8t covers 4 rows of 256 bytes; lane L
+  // brings row 4q + L/16, physical chunk L%16
+  const bf16* wq = (const bf16*)a.w_mq + (int64_t)layer * 64 * d;
+  const float* Ast = a.A + (int64_t)layer * d * 64;
+  auto issue_wq = [&](int s) {
+    unsigned char* buf = ops + (s & 1) * BUF;
+#pragma unroll
+    for (int t = 0; t < LW; ++t) {
+      const int q = w + 8 * t, key = 4 * q + (lane >> 4), pc = lane & 15;
+      const bf16* src = wq + (int64_t)key * d + 128 * s + 8 * (pc ^ (key & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(buf + q * 1024),
+                                       16, 0, 0);
+    }
+  };
+  auto aswz = [](int r) { return (r & 3) | (((r >> 3) & 3) << 2); };
+  auto issue_a = [&](int s) {
+    unsigned char* buf = ops + (s & 1) * BUF;
+#pragma unroll
+    for (int t = 0; t < LA; ++t) {
+      const int q = w + 8 * t, r = 4 * q + (lane >> 4), pc = lane & 15;
+      const float* src = Ast + (int64_t)(128 * s + r) * 64 + 4 * (pc ^ aswz(r));
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(buf + q * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- u = h W_mq^T: chunk s from buffer s & 1, chunk s + 1 in flight
+  issue_wq(0);
+  if (nb > 1) issue_wq(1);
   f32x4 u[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) u[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16* wq = (const bf16*)a.w_mq + (int64_t)layer * 64 * d;
 #pragma unroll
-  for (int b = 0; b < NBM; ++b) {
-    if (b < nb) {
+  for (int s = 0; s < NBM; ++s) {
+    if (s < nb) {
+      if (s + 1 < nb) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LW));
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+      lds_barrier();
+      const unsigned char* buf = ops + (s & 1) * BUF;
       bf16x8 hi, lo;
-      split8(hv[b], hi, lo);
-      const int c = colw + 32 * b;
+      split8(hv[s], hi, lo);
+      const int lc = 4 * cq + g;
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
-        const bf16* wr = wq + (int64_t)(16 * jb + c16) * d;
-        const bf16x4 w0 = *(const bf16x4*)(wr + c), w1 = *(const bf16x4*)(wr + c + 16);
-        const bf16x8 bv = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        const int key = 16 * jb + c16;
+        const bf16x8 bv = *(const bf16x8*)(buf + key * 256 + ((lc ^ (key & 15)) << 4));
         u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, u[jb], 0, 0, 0);
         u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, u[jb], 0, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+      lds_barrier();
+      if (s + 2 < nb) issue_wq(s + 2);
     }
   }
-  // lane (c16, g) of block jb holds u[row 4g + i][key 16 jb + c16]
+  // both buffers are free: start the A chunks while q is formed
+  issue_a(0);
+  if (nb > 1) issue_a(1);
+  // lane (c16, g) of block jb holds u[row 4g + i of its group][key 16 jb + c16]
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ured[w][4 * g + i][16 * jb + c16] = u[jb][i];
-  __syncthreads();
-  for (int idx = tid; idx < 16 * 64; idx += 256) {
-    const int r = idx >> 6, k = idx & 63;
-    qs[r][k] = phi_f(((ured[0][r][k] + ured[1][r][k]) + ured[2][r][k]) + ured[3][r][k]);
+    for (int i = 0; i < 4; ++i) ured[rg][cq][4 * g + i][16 * jb + c16] = u[jb][i];
+  __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+  lds_barrier();
+  for (int idx = tid; idx < 32 * 64; idx += 512) {
+    const int r = idx >> 6, k = idx & 63, gr = r >> 4, rr = r & 15;
+    qs[r][k] = phi_f(((ured[gr][0][rr][k] + ured[gr][1][rr][k]) + ured[gr][2][rr][k]) + ured[gr][3][rr][k]);
   }
-  __syncthreads();
-  if (tid < 16) {
+  __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+  lds_barrier();
+  if (tid < 32) {
     const float* z = a.z + (int64_t)layer * 64;
     float sd = 0.f;
     for (int k = 0; k < 64; ++k) sd = fmaf(qs[tid][k], z[k], sd);
     dens[tid] = sd + a.mem_eps;
   }
   // q^T as the second operand of r^T = A q^T: lane (c16, g) brings
-  // q[row c16][32 ks + 8 g .. + 7] as a bf16 pair
+  // q[row c16 of its group][32 ks + 8 g .. + 7] as a bf16 pair
   bf16x8 qh[2], ql[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = qs[c16][32 * ks + 8 * g + e];
+    for (int e = 0; e < 8; ++e) v[e] = qs[rl][32 * ks + 8 * g + e];
     split8(v, qh[ks], ql[ks]);
   }
-  __syncthreads();   // dens visible
-  const float den = dens[c16];
+  __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+  lds_barrier();   // dens visible
+  const float den = dens[rl];
 
-  // h += r^T / den, block by block; partial sum of squares of the new h
-  const float* Ast = a.A + (int64_t)layer * d * 64;
+  // ---- h += r^T / den, chunk by chunk; partial sum of squares of the new h
   float ss = 0.f;
 #pragma unroll
-  for (int b = 0; b < NBM; ++b) {
-    if (b < nb) {
+  for (int s = 0; s < NBM; ++s) {
+    if (s < nb) {
+      if (s + 1 < nb) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LA));
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+      lds_barrier();
+      const unsigned char* buf = ops + (s & 1) * BUF;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const float* ar = Ast + (int64_t)(w * (d >> 2) + 32 * b + 16 * sb + c16) * 64 + 8 * g;
+        const int ar = 32 * cq + 8 * (c16 >> 2) + 4 * sb + (c16 & 3);   // A row within the chunk
         f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          float av[8];
-          load8f(ar + 32 * ks, av);
+          const int lc = 8 * ks + 2 * g;
+          const f32x4 a0 = *(const f32x4*)(buf + ar * 256 + ((lc ^ aswz(ar)) << 4));
+          const f32x4 a1 = *(const f32x4*)(buf + ar * 256 + (((lc + 1) ^ aswz(ar)) << 4));
+          const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           bf16x8 ah, al;
           split8(av, ah, al);
           r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh[ks], r, 0, 0, 0);
           r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql[ks], r, 0, 0, 0);
           r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh[ks], r, 0, 0, 0);
         }
+        // lane (c16, g) holds r^T[block row 4g + i][row c16] = column 8g + 4sb + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float hn = hv[b][4 * sb + i] + r[i] / den;
-          hv[b][4 * sb + i] = hn;
+          const float hn = hv[s][4 * sb + i] + r[i] / den;
+          hv[s][4 * sb + i] = hn;
           ss = fmaf(hn, hn, ss);
         }
       }
+      __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+      lds_barrier();
+      if (s + 2 < nb) issue_a(s + 2);
     }
   }
   ss += __shfl_xor(ss, 16, kWave);
   ss += __shfl_xor(ss, 32, kWave);
-  if (g == 0) ssq[w][c16] = ss;
-  __syncthreads();
-  const float rs = rsqrtf((((ssq[0][c16] + ssq[1][c16]) + ssq[2][c16]) + ssq[3][c16]) / (float)d + a.rms_eps);
+  if (g == 0) ssq[rg][cq][c16] = ss;
+  __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+  lds_barrier();
+  const float rs = rsqrtf((((ssq[rg][0][c16] + ssq[rg][1][c16]) + ssq[rg][2][c16]) + ssq[rg][3][c16]) / (float)d +
+                          a.rms_eps);
   if (row < a.n) {
     float* ho = (float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)row * d;
     bf16* ao = (bf16*)a.abuf + (int64_t)layer * a.act_stride + (int64_t)row * d;
     const bf16* gn = (const bf16*)a.gain + (int64_t)layer * d;
 #pragma unroll
-    for (int b = 0; b < NBM; ++b) {
-      if (b < nb) {
+    for (int s = 0; s < NBM; ++s) {
+      if (s < nb) {
+        const int c = 128 * s + colw;
+        const float* v = hv[s];
+        *(f32x4*)(ho + c) = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4*)(ho + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        const bf16x8 gv = *(const bf16x8*)(gn + c);
+        bf16x8 o;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int c = colw + 32 * b + 16 * sb;
-          const float* v = &hv[b][4 * sb];
-          *(f32x4*)(ho + c) = f32x4{v[0], v[1], v[2], v[3]};
-          const bf16x4 gv = *(const bf16x4*)(gn + c);
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * rs * (float)gv[e]);
-          *(bf16x4*)(ao + c) = o;
-        }
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * rs * (float)gv[e]);
+        *(bf16x8*)(ao + c) = o;
       }
     }
   }
@@ -382,14 +454,14 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st) {
-  // d / 4 columns per wave in 32-column blocks; up to 24 blocks held per wave
+  // 128-column chunks; up to 24 held per wave
   if (m.dk != 64 || m.d % 128 || m.d > 3072) return hipErrorInvalidValue;
-  const dim3 grid((m.n + 15) / 16, m.P);
+  const dim3 grid((m.n + 31) / 32, m.P);
   const int nb = m.d / 128;
-  if (nb <= 4) hipLaunchKernelGGL(memread_norm_bf16_kernel<4>, grid, dim3(256), 0, st, m);
-  else if (nb <= 8) hipLaunchKernelGGL(memread_norm_bf16_kernel<8>, grid, dim3(256), 0, st, m);
-  else if (nb <= 16) hipLaunchKernelGGL(memread_norm_bf16_kernel<16>, grid, dim3(256), 0, st, m);
-  else hipLaunchKernelGGL(memread_norm_bf16_kernel<24>, grid, dim3(256), 0, st, m);
+  if (nb <= 4) hipLaunchKernelGGL(memread_norm_bf16_kernel<4>, grid, dim3(512), 0, st, m);
+  else if (nb <= 8) hipLaunchKernelGGL(memread_norm_bf16_kernel<8>, grid, dim3(512), 0, st, m);
+  else if (nb <= 16) hipLaunchKernelGGL(memread_norm_bf16_kernel<16>, grid, dim3(512), 0, st, m);
+  else hipLaunchKernelGGL(memread_norm_bf16_kernel<24>, grid, dim3(512), 0, st, m);
   return hipGetLastError();
 }
 
