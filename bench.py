@@ -1,29 +1,39 @@
 """Benchmark: 131,072-token 1B-shape ARMT forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1b_s128]
+    python bench.py --all-workloads      # diag + seq on every benchmark workload
+    python bench.py --group-sweep        # grouped kernels vs wave width k
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
 timing starts.  The headline value is tokens/s of the diagonal schedule
-(input tokens S*T per forward).  The same number of sequential-schedule
-forwards is timed next for the diagonal-vs-sequential ratio the pages quote
-(abstract on the paper page: 1.8x at 131,072 tokens, another GPU).
+(input tokens S*T per forward), over K forwards bracketed by synchronisations.
+The same number of sequential-schedule forwards is timed next for the
+diagonal-vs-sequential ratio the pages quote (abstract on the paper page: 1.8x
+at 131,072 tokens, another GPU).  Each forward is also timed alone with HIP
+events on the library's stream, for the median and the minimum.
 
 Extra fields:
   roofline      the grouped gate/up GEMM (the largest kernel, about half of all
                 FLOPs): algorithmic FLOPs of its launches divided by their
                 summed durations, from HIP events recorded around every launch
                 on the library's stream during a timed pass, against the bf16
-                dense MFMA peak of 2.5 PFLOP/s;
+                dense MFMA peak of 2.5 PFLOP/s; traffic = HBM bytes per launch
+                from the committed FETCH_SIZE / WRITE_SIZE record;
   gemm_util     the same for all four grouped GEMMs together;
+  kernels       every kernel: time per forward, FLOP/s and algorithmic GB/s,
+                each against its peak;
+  launches      kernel and graph launches per forward, diagonal vs sequential;
   cpu_baseline  the CPU oracle timed on a bounded sample (first nodes of
                 segment 0) on this host.
-Weights and inputs are random (seeded) of the 1B ARMT shape; no checkpoint.
+Weights and inputs are random (seeded) of the ARMT shapes; no checkpoint.
 """
 
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -33,6 +43,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+METRIC = "tokens/s, 131K-token 1B-shape ARMT forward (diag vs seq); GEMM MFMA util %"
 
 
 def parse():
@@ -46,12 +57,17 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--gemm-rows", type=int, default=0,
-                    help="rows per GEMM tile / 16 (0: the library's choice)")
+                    help="rows per GEMM tile / 32 (0: the library's choice)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the diagonal forward (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only a plain 256 MiB device-to-device copy, three times (to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="time diagonal and sequential forwards of every benchmark workload, one JSON "
+                         "line each")
+    ap.add_argument("--group-sweep", action="store_true",
+                    help="grouped GEMM and attention throughput against the wave width k (1B shapes)")
     return ap.parse_args()
 
 
@@ -59,130 +75,94 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
-                          "n_gpus_requested": args.gpus}))
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# shared helpers
+# ---------------------------------------------------------------------------
+
+def to_dev(a, dev):
     import numpy as np
     import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev, torch.bfloat16).contiguous()
 
-    if args.copy_calibration:
-        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"copied {a.numel() * 4} bytes x3")
-        return
 
-    from armt_inputs import get_config, make_inputs
+def build(inp, cfg, dev, layers=None, gemm_rows=0):
+    """Device weights and a model of the first `layers` layers of `inp`."""
     from long_context_recurrent_amd import armt as C
     from long_context_recurrent_amd.model import ArmtModel, make_config
-
-    cfg = get_config(args.workload)
-    dev = torch.device("cuda:0")
-    t0 = time.time()
-    inp = make_inputs(cfg)
-    log(f"inputs drawn in {time.time() - t0:.1f}s")
-
-    def t(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev, torch.bfloat16).contiguous()
-
-    w = {k: t(v) for k, v in inp.weights.items()}
-    w.update(g_attn=t(inp.g_attn), g_mlp=t(inp.g_mlp), mem_emb=t(inp.mem_emb))
-    x = t(inp.x)
-    ccfg = make_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+    L = layers or cfg.n_layers
+    w = {k: to_dev(v[:L], dev) for k, v in inp.weights.items()}
+    w.update(g_attn=to_dev(inp.g_attn[:L], dev), g_mlp=to_dev(inp.g_mlp[:L], dev),
+             mem_emb=to_dev(inp.mem_emb, dev))
+    ccfg = make_config(L, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                        cfg.ffn_hidden, cfg.seg_len, cfg.n_mem, cfg.d_key, cfg.dtype)
     model = ArmtModel(ccfg, w)
-    if args.gemm_rows:
-        model.set_option(C.ARMT_OPT_GEMM_ROWS, args.gemm_rows)
-    S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
-    tokens = S * T
-    out = model.alloc_outputs(S)
-    st = model.stream
+    if gemm_rows:
+        model.set_option(C.ARMT_OPT_GEMM_ROWS, gemm_rows)
+    return model
 
-    def run(schedule, k):
-        fn = C.armt_forward_diagonal if schedule == "diagonal" else C.armt_forward_sequential
+
+def node_gflop(cfg):
+    return sum(cfg.node_flops().values()) / 1e9
+
+
+class Runner:
+    """Times forwards of one model on its stream."""
+
+    def __init__(self, model, x, n_segments):
+        import torch
+        from long_context_recurrent_amd import armt as C
+        self.C, self.torch = C, torch
+        self.model, self.x, self.S = model, x, n_segments
+        self.out = model.alloc_outputs(n_segments)
+
+    def run(self, schedule, k):
+        fn = self.C.armt_forward_diagonal if schedule == "diagonal" else self.C.armt_forward_sequential
         for _ in range(k):
-            fn(model.handle, x, S, None, None, out[0], out[1], out[2])
+            fn(self.model.handle, self.x, self.S, None, None, self.out[0], self.out[1], self.out[2])
 
-    def timed(schedule, steps, warmup):
-        run(schedule, warmup)
+    def timed(self, schedule, steps, warmup):
+        """(mean seconds per forward over `steps` forwards bracketed by
+        synchronisations, [per-forward seconds from HIP events])."""
+        torch, st = self.torch, self.model.stream
+        self.run(schedule, warmup)
         torch.cuda.synchronize()
         st.synchronize()
         a = time.perf_counter()
-        run(schedule, steps)
+        self.run(schedule, steps)
         st.synchronize()
         torch.cuda.synchronize()
-        return (time.perf_counter() - a) / steps
+        mean = (time.perf_counter() - a) / steps
+        each = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            self.run(schedule, 1)
+            e1.record(st)
+            e1.synchronize()
+            each.append(e0.elapsed_time(e1) * 1e-3)
+        return mean, each
 
-    log(f"warmup {args.warmup}, timing {args.steps} diagonal forwards of {args.workload}")
-    diag_s = timed("diagonal", args.steps, args.warmup)
-    log(f"diagonal: {diag_s * 1e3:.1f} ms/forward, {tokens / diag_s:.0f} tokens/s")
-    if args.profile_only:
-        return
-    seq_s = None
-    if not args.no_seq:
-        seq_s = timed("sequential", args.steps, 1)
-        log(f"sequential: {seq_s * 1e3:.1f} ms/forward, {tokens / seq_s:.0f} tokens/s")
+    def kernel_stats(self, forwards):
+        C, stats = self.C, {}
+        for kname in C.KERNELS:
+            self.model.set_option(C.ARMT_OPT_TIME_KERNEL, C.KERNELS.index(kname))
+            self.run("diagonal", forwards)
+            stats[kname] = self.model.kernel_stats()
+            self.model.set_option(C.ARMT_OPT_TIME_KERNEL, -1)
+        return stats
 
-    # per-kernel durations from HIP events on the library's stream
-    kstats = {}
-    for kname in C.KERNELS:
-        kid = C.KERNELS.index(kname)
-        model.set_option(C.ARMT_OPT_TIME_KERNEL, kid)
-        run("diagonal", max(1, min(args.steps, 3)))
-        kstats[kname] = model.kernel_stats()
-        model.set_option(C.ARMT_OPT_TIME_KERNEL, -1)
-    rk = kstats[args.roofline_kernel]
-    achieved = rk["flops"] / (rk["ms"] * 1e-3) / 1e12
-    traffic = measured_traffic(args.roofline_kernel, args.workload)
-    gemm = [kstats[k] for k in ("qkv", "o_proj", "gate_up", "down")]
-    g_flops = sum(k["flops"] for k in gemm)
-    g_ms = sum(k["ms"] for k in gemm)
-    for k, v in kstats.items():
-        tf = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] else 0.0
-        gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9 if v["ms"] else 0.0
-        log(f"  {k:10s} {v['ms'] / max(v['launches'], 1) * 1e3:9.1f} us/launch  {tf:7.1f} TFLOP/s  {gbs:7.0f} GB/s")
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+def launches(cfg, S, L):
+    """Kernel and graph launches per forward of both schedules."""
+    per_node = 9 if cfg.dtype == "bf16" else 10
+    return {"diagonal": {"graph_launches": S + L - 1, "kernels": per_node * (S + L - 1)},
+            "sequential": {"graph_launches": S * L, "kernels": per_node * S * L},
+            "kernels_per_wave": per_node}
 
-    res = {
-        "metric": "tokens/s, 131K-token 1B-shape ARMT forward (diag vs seq); GEMM MFMA util %",
-        "value": tokens / diag_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": diag_s * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights of the 1B ARMT shape)",
-        "config": {"workload": args.workload, "n_layers": L, "d_model": cfg.d_model,
-                   "heads": f"{cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}", "ffn": cfg.ffn_hidden,
-                   "seg_len": T, "n_mem": cfg.n_mem, "n_segments": S, "tokens": tokens, "batch": 1,
-                   "waves": S + L - 1},
-        "sequential": None if seq_s is None else {
-            "value": tokens / seq_s, "unit": "tokens/s", "ms_per_step": seq_s * 1e3,
-            "diag_speedup": seq_s / diag_s},
-        "roofline": {"kernel": args.roofline_kernel, "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "launches": rk["launches"],
-                     "avg_launch_us": rk["ms"] / max(rk["launches"], 1) * 1e3},
-        "gemm_util": {"achieved": g_flops / (g_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-                      "frac": g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "kernels": {k: kernel_summary(v, max(1, min(args.steps, 3))) for k, v in kstats.items()},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(res), flush=True)
-    model.close()
+
+def timing_summary(mean, each, tokens):
+    return {"ms_mean": mean * 1e3, "ms_median": statistics.median(each) * 1e3, "ms_min": min(each) * 1e3,
+            "tokens_per_s_median": tokens / statistics.median(each)}
 
 
 def kernel_summary(v, forwards):
@@ -221,6 +201,19 @@ def measured_traffic(kernel, workload):
             + rec["write_kib_per_dispatch"] * rec["write_factor"]) * 1024.0
 
 
+def host_cpu():
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "model": model,
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline(inp, seconds):
     """The oracle as it stands, on this host: nodes of segment 0, layer by
     layer, until about `seconds` of CPU work; tokens/s = T / (L * mean node
@@ -247,9 +240,175 @@ def cpu_baseline(inp, seconds):
     per_node = el / done
     value = cfg.seg_len / (per_node * cfg.n_layers)
     log(f"cpu oracle: {done} nodes in {el:.1f}s -> {value:.1f} tokens/s")
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_cpu(),
             "sample": f"{done} node(s) of segment 0 (layers 0..{done - 1}, {cfg.seg_len + cfg.n_mem} rows each, "
-                      f"float64 NumPy) in {el:.1f}s; tokens/s = T / (L * mean node time)"}
+                      f"float64 NumPy, BLAS threads = {cores}) in {el:.1f}s; "
+                      f"tokens/s = T / (L * mean node time)"}
+
+
+# ---------------------------------------------------------------------------
+# modes
+# ---------------------------------------------------------------------------
+
+def headline(args, dev):
+    from armt_inputs import get_config, make_inputs
+    cfg = get_config(args.workload)
+    t0 = time.time()
+    inp = make_inputs(cfg)
+    log(f"inputs drawn in {time.time() - t0:.1f}s")
+    model = build(inp, cfg, dev, gemm_rows=args.gemm_rows)
+    x = to_dev(inp.x, dev)
+    S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
+    tokens = S * T
+    r = Runner(model, x, S)
+
+    log(f"warmup {args.warmup}, timing {args.steps} diagonal forwards of {args.workload}")
+    diag_s, diag_each = r.timed("diagonal", args.steps, args.warmup)
+    log(f"diagonal: {diag_s * 1e3:.1f} ms/forward, {tokens / diag_s:.0f} tokens/s "
+        f"(median {statistics.median(diag_each) * 1e3:.1f}, min {min(diag_each) * 1e3:.1f} ms)")
+    if args.profile_only:
+        return
+    seq_s = seq_each = None
+    if not args.no_seq:
+        seq_s, seq_each = r.timed("sequential", args.steps, 1)
+        log(f"sequential: {seq_s * 1e3:.1f} ms/forward, {tokens / seq_s:.0f} tokens/s")
+
+    nfwd = max(1, min(args.steps, 3))
+    kstats = r.kernel_stats(nfwd)
+    rk = kstats[args.roofline_kernel]
+    achieved = rk["flops"] / (rk["ms"] * 1e-3) / 1e12
+    traffic = measured_traffic(args.roofline_kernel, args.workload)
+    gemm = [kstats[k] for k in ("qkv", "o_proj", "gate_up", "down")]
+    g_flops = sum(k["flops"] for k in gemm)
+    g_ms = sum(k["ms"] for k in gemm)
+    for k, v in kstats.items():
+        tf = v["flops"] / (v["ms"] * 1e-3) / 1e12 if v["ms"] else 0.0
+        gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9 if v["ms"] else 0.0
+        log(f"  {k:10s} {v['ms'] / max(v['launches'], 1) * 1e3:9.1f} us/launch  {tf:7.1f} TFLOP/s  {gbs:7.0f} GB/s")
+
+    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds)
+    res = {
+        "metric": METRIC,
+        "value": tokens / diag_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": diag_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights of the 1B ARMT shape)",
+        "config": {"workload": args.workload, "n_layers": L, "d_model": cfg.d_model,
+                   "heads": f"{cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}", "ffn": cfg.ffn_hidden,
+                   "seg_len": T, "n_mem": cfg.n_mem, "n_segments": S, "tokens": tokens, "batch": 1,
+                   "waves": S + L - 1},
+        "diagonal": timing_summary(diag_s, diag_each, tokens),
+        "sequential": None if seq_s is None else dict(
+            timing_summary(seq_s, seq_each, tokens), value=tokens / seq_s, unit="tokens/s",
+            ms_per_step=seq_s * 1e3, diag_speedup=seq_s / diag_s),
+        "launches": launches(cfg, S, L),
+        "roofline": {"kernel": args.roofline_kernel, "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "launches": rk["launches"],
+                     "avg_launch_us": rk["ms"] / max(rk["launches"], 1) * 1e3},
+        "gemm_util": {"achieved": g_flops / (g_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                      "frac": g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "kernels": {k: kernel_summary(v, nfwd) for k, v in kstats.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    model.close()
+
+
+def all_workloads(args, dev):
+    """Diagonal and sequential forwards of every benchmark workload (the
+    oracle-sized ones excluded), one JSON line each."""
+    import gc
+    import torch
+    from armt_inputs import get_config, make_inputs
+    for names in (["1b_s32", "1b_s128"], ["3b_t512", "3b_t1024", "3b_t2048"]):
+        inp = make_inputs(get_config(names[-1]))    # the longest X of the group; row prefixes serve the rest
+        for name in names:
+            cfg = get_config(name)
+            S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
+            model = build(inp, cfg, dev)
+            x = to_dev(inp.x[:S * T], dev)
+            r = Runner(model, x, S)
+            d_mean, d_each = r.timed("diagonal", args.steps, args.warmup)
+            s_mean, s_each = r.timed("sequential", args.steps, 1)
+            line = {"workload": name, "tokens": S * T, "waves": S + L - 1,
+                    "node_gflop": node_gflop(cfg),
+                    "diagonal": timing_summary(d_mean, d_each, S * T),
+                    "sequential": timing_summary(s_mean, s_each, S * T),
+                    "diag_speedup": s_mean / d_mean,
+                    "tflops_diagonal": node_gflop(cfg) * S * L / d_mean / 1e3,
+                    "launches": launches(cfg, S, L)}
+            log(f"{name}: diag {d_mean * 1e3:.1f} ms, seq {s_mean * 1e3:.1f} ms, x{s_mean / d_mean:.2f}")
+            print(json.dumps(line), flush=True)
+            model.close()
+            del model, x, r
+            gc.collect()
+            torch.cuda.empty_cache()
+        del inp
+        gc.collect()
+
+
+def group_sweep(args, dev):
+    """Grouped GEMM and attention throughput against the wave width k: a
+    model of the first k layers of the 1B shape, run diagonally over 32 k
+    segments, so all but 2(k - 1) of its 33k - 1 waves have exactly k nodes."""
+    import numpy as np
+    from armt_inputs import get_config, make_inputs
+    base = get_config("1b_s128")
+    inp = make_inputs(base)
+    T = base.seg_len
+    for k in (1, 2, 4, 8, 16):
+        S = 32 * k
+        reps = -(-S * T // inp.x.shape[0])
+        xs = np.concatenate([inp.x] * reps)[:S * T] if reps > 1 else inp.x[:S * T]
+        model = build(inp, base, dev, layers=k)
+        r = Runner(model, to_dev(xs, dev), S)
+        r.run("diagonal", 1)
+        stats = r.kernel_stats(1)
+        gemm = [stats[n] for n in ("qkv", "o_proj", "gate_up", "down")]
+        gf, gms = sum(v["flops"] for v in gemm), sum(v["ms"] for v in gemm)
+        at = stats["attn"]
+        line = {"k": k, "n_segments": S, "waves": S + k - 1, "full_width_waves": S - k + 1,
+                "gemm_tflops": gf / (gms * 1e-3) / 1e12,
+                "attn_tflops": at["flops"] / (at["ms"] * 1e-3) / 1e12,
+                "per_kernel_tflops": {n: stats[n]["flops"] / (stats[n]["ms"] * 1e-3) / 1e12
+                                      for n in ("qkv", "o_proj", "gate_up", "down", "attn")}}
+        log(f"k={k:2d}: GEMM {line['gemm_tflops']:.0f} TFLOP/s, attention {line['attn_tflops']:.0f} TFLOP/s")
+        print(json.dumps(line), flush=True)
+        model.close()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    if args.copy_calibration:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {a.numel() * 4} bytes x3")
+        return
+    dev = torch.device("cuda:0")
+    if args.all_workloads:
+        all_workloads(args, dev)
+    elif args.group_sweep:
+        group_sweep(args, dev)
+    else:
+        headline(args, dev)
 
 
 if __name__ == "__main__":

@@ -35,7 +35,9 @@ differ by ~2e-2 relative L2 after 28 layers of the 3B shape.)  The memory state
 (A, z) is stored in float32 after every update.  For fp32 workloads every value
 stays in float64.
 
-Pins (tests marked "not gpu"): schedule brute force and Lemma 3.1; the RMT
+Pins (tests marked "not gpu"): the oracle rerun in float32 arithmetic
+(``working_precision``) stays far inside the parity bars of the float64 run;
+schedule brute force and Lemma 3.1; the RMT
 counter-example of the Pith verdict; diagonal == sequential order bitwise and
 wave-shuffle invariance; split (resume) invariance; hand-derived closed forms of
 the memory read and write; the zero-memory node against torch's library
@@ -49,14 +51,31 @@ do not print.
 
 from __future__ import annotations
 
+import contextlib
 import math
 
 import numpy as np
 
+# Working precision of every arithmetic step.  float64 always, except inside
+# ``working_precision`` (used by the tests to bound the oracle's own rounding
+# error by rerunning it in float32).
+_WP = np.float64
+
+
+@contextlib.contextmanager
+def working_precision(dtype):
+    """Run the oracle's arithmetic in ``dtype`` inside this block."""
+    global _WP
+    old, _WP = _WP, np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _WP = old
+
 __all__ = [
     "waves", "round_bf16", "phi", "sigmoid", "silu", "rms_norm", "rope",
     "causal_gqa_attention", "mem_read", "mem_write", "node",
-    "forward_sequential", "forward_diagonal", "Oracle",
+    "forward_sequential", "forward_diagonal", "Oracle", "working_precision",
 ]
 
 
@@ -99,39 +118,39 @@ def round_bf16(x) -> np.ndarray:
     r = np.ldexp(np.rint(np.ldexp(x, -q_exp)), q_exp)   # np.rint: half to even
     big = np.abs(r) > 3.3895313892515355e38             # largest finite bf16
     r = np.where(big, np.copysign(np.inf, x), r)
-    return np.where(np.isfinite(x), r, x)
+    return np.where(np.isfinite(x), r, x).astype(_WP)
 
 
 def _identity(x):
-    return np.asarray(x, dtype=np.float64)
+    return np.asarray(x, dtype=_WP)
 
 
 def _round_f32(x) -> np.ndarray:
-    return np.asarray(x, dtype=np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(_WP)
 
 
 def phi(u):
     """Feature map of the associative memory, elu(u) + 1: u + 1 for u > 0, else
     exp(u).  Strictly positive, so memory denominators stay positive."""
-    u = np.asarray(u, dtype=np.float64)
-    return np.where(u > 0, u + 1.0, np.exp(np.minimum(u, 0.0)))
+    u = np.asarray(u, dtype=_WP)
+    return np.where(u > 0, u + 1.0, np.exp(np.minimum(u, 0.0))).astype(_WP)
 
 
 def sigmoid(u):
-    u = np.asarray(u, dtype=np.float64)
+    u = np.asarray(u, dtype=_WP)
     e = np.exp(-np.abs(u))
-    return np.where(u >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return np.where(u >= 0, 1.0 / (1.0 + e), e / (1.0 + e)).astype(_WP)
 
 
 def silu(u):
-    return np.asarray(u, dtype=np.float64) * sigmoid(u)
+    return np.asarray(u, dtype=_WP) * sigmoid(u)
 
 
 def rms_norm(h, g, eps):
     """h / sqrt(mean(h^2) + eps) * g over the last axis (Llama RMSNorm)."""
-    h = np.asarray(h, dtype=np.float64)
+    h = np.asarray(h, dtype=_WP)
     ms = np.mean(h * h, axis=-1, keepdims=True)
-    return h / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+    return (h / np.sqrt(ms + _WP(eps)) * np.asarray(g, dtype=_WP)).astype(_WP)
 
 
 def rope(x, theta):
@@ -139,13 +158,13 @@ def rope(x, theta):
 
     Half-split pairing: coordinate i is paired with i + hd/2 and the pair is
     rotated by angle pos * theta**(-2i/hd) (Llama convention)."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=_WP)
     n, _, hd = x.shape
     half = hd // 2
     inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / hd)
     ang = np.arange(n, dtype=np.float64)[:, None] * inv_freq[None, :]     # [n, half]
-    cos = np.cos(ang)[:, None, :]
-    sin = np.sin(ang)[:, None, :]
+    cos = np.cos(ang).astype(_WP)[:, None, :]
+    sin = np.sin(ang).astype(_WP)[:, None, :]
     a, b = x[..., :half], x[..., half:]
     return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
 
@@ -159,11 +178,11 @@ def causal_gqa_attention(Q, K, V):
     n, H, hd = Q.shape
     G = K.shape[1]
     rep = H // G
-    out = np.empty((n, H, hd), dtype=np.float64)
+    out = np.empty((n, H, hd), dtype=_WP)
     mask = np.triu(np.ones((n, n), dtype=bool), k=1)
     for j in range(H):
         kv = j // rep
-        s = (Q[:, j, :] @ K[:, kv, :].T) / math.sqrt(hd)
+        s = (Q[:, j, :] @ K[:, kv, :].T) / _WP(math.sqrt(hd))
         s = np.where(mask, -np.inf, s)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
@@ -181,10 +200,10 @@ def mem_read(h, w_mq, A, z, eps):
 
     q = phi(h W_mq^T) [rows, d_k];  r = (q A^T) / (q . z + eps);  return h + r.
     A is [d, d_k], z is [d_k].  From the zero state the read is exactly 0."""
-    h = np.asarray(h, dtype=np.float64)
-    q = phi(h @ np.asarray(w_mq, dtype=np.float64).T)
-    num = q @ np.asarray(A, dtype=np.float64).T
-    den = q @ np.asarray(z, dtype=np.float64) + eps
+    h = np.asarray(h, dtype=_WP)
+    q = phi(h @ np.asarray(w_mq, dtype=_WP).T)
+    num = q @ np.asarray(A, dtype=_WP).T
+    den = q @ np.asarray(z, dtype=_WP) + _WP(eps)
     return h + num / den[:, None]
 
 
@@ -195,13 +214,13 @@ def mem_write(y_mem, w_mk, w_mv, w_beta, A, z, eps):
     vbar_m = (k_m A^T) / (k_m . z + eps) is what the pre-update memory returns
     for k_m; then A += sum_m beta_m (v_m - vbar_m) k_m^T and z += sum_m k_m.
     All tokens of one write see the pre-update state.  Returns new (A, z)."""
-    y = np.asarray(y_mem, dtype=np.float64)
-    A = np.asarray(A, dtype=np.float64)
-    z = np.asarray(z, dtype=np.float64)
-    k = phi(y @ np.asarray(w_mk, dtype=np.float64).T)          # [M, d_k]
-    v = y @ np.asarray(w_mv, dtype=np.float64).T               # [M, d]
-    beta = sigmoid(y @ np.asarray(w_beta, dtype=np.float64))   # [M]
-    vbar = (k @ A.T) / (k @ z + eps)[:, None]                  # [M, d]
+    y = np.asarray(y_mem, dtype=_WP)
+    A = np.asarray(A, dtype=_WP)
+    z = np.asarray(z, dtype=_WP)
+    k = phi(y @ np.asarray(w_mk, dtype=_WP).T)                 # [M, d_k]
+    v = y @ np.asarray(w_mv, dtype=_WP).T                      # [M, d]
+    beta = sigmoid(y @ np.asarray(w_beta, dtype=_WP))          # [M]
+    vbar = (k @ A.T) / (k @ z + _WP(eps))[:, None]             # [M, d]
     A_new = A + ((beta[:, None] * (v - vbar)).T @ k)           # [d, d_k]
     z_new = z + k.sum(axis=0)
     return A_new, z_new
@@ -219,7 +238,7 @@ class Oracle:
     def __init__(self, inputs):
         self.inp = inputs
         self.cfg = inputs.cfg
-        self.dtype = np.float64
+        self.dtype = _WP
         bf = self.cfg.dtype == "bf16"
         self.R = round_bf16 if bf else _identity         # branch activations
         self.Rs = _round_f32 if bf else _identity        # residual stream
@@ -281,8 +300,8 @@ class Oracle:
     def initial_state(self, A0=None, z0=None):
         c = self.cfg
         L = self.inp.weights["w_qkv"].shape[0]
-        A = [np.zeros((c.d_model, c.d_key)) if A0 is None else _round_f32(A0[l]) for l in range(L)]
-        z = [np.zeros(c.d_key) if z0 is None else _round_f32(z0[l]) for l in range(L)]
+        A = [np.zeros((c.d_model, c.d_key), dtype=_WP) if A0 is None else _round_f32(A0[l]) for l in range(L)]
+        z = [np.zeros(c.d_key, dtype=_WP) if z0 is None else _round_f32(z0[l]) for l in range(L)]
         return A, z
 
     def run(self, order, n_segments, A0=None, z0=None):
@@ -294,7 +313,7 @@ class Oracle:
         T = c.seg_len
         A, z = self.initial_state(A0, z0)
         out = {}
-        Y = np.zeros((n_segments * T, c.d_model))
+        Y = np.zeros((n_segments * T, c.d_model), dtype=_WP)
         for (s, l) in order:
             prev = None if l == 0 else out.pop((s, l - 1))
             h, A[l], z[l] = self.node(l, self.node_input(s, prev), A[l], z[l])

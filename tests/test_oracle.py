@@ -338,3 +338,28 @@ def test_storage_precision_of_bf16_workloads():
     for l in range(cfg.n_layers):
         h0, _, _ = o.node(l, h0, A0[l], z0[l])
     np.testing.assert_array_equal(y[:cfg.seg_len], oracle.round_bf16(h0[:cfg.seg_len]))
+
+
+@pytest.mark.parametrize("name,bar_y,bar_state", [("tiny_fp32", 1e-6, 1e-6), ("small_bf16", 2e-3, 1e-4)])
+def test_oracle_own_rounding_error_is_far_below_the_parity_bars(name, bar_y, bar_state):
+    """The same oracle run with float32 arithmetic stays within 1/100 (fp32
+    workload, bar 1e-4) and 1/10 (bf16 workload, bar 2e-2; its gap comes from
+    bf16 rounding decisions flipping) of the parity bars of the float64
+    oracle, so the oracle's own rounding cannot decide a parity test."""
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    A0, z0 = make_state(cfg)
+    ref = oracle.forward_sequential(inp, A0, z0)
+    with oracle.working_precision(np.float32):
+        low = oracle.forward_sequential(inp, A0, z0)
+    assert all(a.dtype == np.float32 for a in low)
+    again = oracle.forward_sequential(inp, A0, z0)      # back in float64, unchanged
+    for a, b in zip(ref, again):
+        assert a.dtype == np.float64
+        np.testing.assert_array_equal(a, b)
+
+    def rel(a, b):
+        return np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b)
+    assert rel(low[0], ref[0]) < bar_y
+    assert rel(low[1], ref[1]) < bar_state
+    assert rel(low[2], ref[2]) < bar_state
