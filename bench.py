@@ -68,6 +68,10 @@ def parse():
                          "line each")
     ap.add_argument("--group-sweep", action="store_true",
                     help="grouped GEMM and attention throughput against the wave width k (1B shapes)")
+    ap.add_argument("--traffic-record", metavar="DIR",
+                    help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
+                         "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
+                         "pmc_WRITE_SIZE, calib_FETCH_SIZE, calib_WRITE_SIZE); no GPU needed")
     return ap.parse_args()
 
 
@@ -199,6 +203,61 @@ def measured_traffic(kernel, workload):
         return None
     return (rec["fetch_kib_per_dispatch"] * rec["fetch_factor"]
             + rec["write_kib_per_dispatch"] * rec["write_factor"]) * 1024.0
+
+
+TRAFFIC_KERNEL_NAMES = {"gate_up": ("gate_up (gemm_bf16_kernel<MB, EPI_SWIGLU>)", "gemm_bf16_kernel<", ", 3>")}
+
+
+def _pmc_rows(path, counter):
+    import csv
+    with open(path, newline="") as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def write_traffic_record(args):
+    """Average FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the roofline
+    kernel over one profiled forward, with the factors that make the same
+    counters read the true byte count of a plain 256 MiB copy."""
+    import hashlib
+    label, prefix, suffix = TRAFFIC_KERNEL_NAMES[args.roofline_kernel]
+    d = args.traffic_record
+    rec = {"kernel": label, "workload": args.workload}
+    copy_bytes = 64 * 1024 * 1024 * 4
+    calib = {"copy_bytes": copy_bytes}
+    for ctr, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = [r for r in _pmc_rows(os.path.join(d, f"pmc_{ctr}", "run_counter_collection.csv"), ctr)
+                if prefix in r["Kernel_Name"] and r["Kernel_Name"].split("(")[0].endswith(suffix)]
+        if not rows:
+            sys.exit(f"no {ctr} rows for {label} under {d}")
+        rec["dispatches"] = len(rows)
+        rec[f"{key}_kib_per_dispatch"] = sum(float(r["Counter_Value"]) for r in rows) / len(rows)
+        crows = [r for r in _pmc_rows(os.path.join(d, f"calib_{ctr}", "run_counter_collection.csv"), ctr)
+                 if "copyBuffer" in r["Kernel_Name"]]
+        if not crows:
+            sys.exit(f"no copy-kernel {ctr} rows under {d}")
+        kib = sum(float(r["Counter_Value"]) for r in crows) / len(crows)
+        calib[f"{key}_kib"] = kib
+        rec[f"{key}_factor"] = round(copy_bytes / 1024.0 / kib, 4)
+    rec["calibration"] = calib
+    src = os.path.join(ROOT, "long_context_recurrent_amd", "csrc", KERNEL_SOURCES[args.roofline_kernel])
+    with open(src, "rb") as f:
+        rec["source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    rec["commands"] = [
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE "
+        "--kernel-include-regex \"gemm_bf16_kernel<[0-9], 3>\" --output-format csv -d DIR/pmc_FETCH_SIZE "
+        "-o run -- python3 /root/repo/bench.py --steps 1 --warmup 0 --profile-only",
+        "same with --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE",
+        "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/calib_FETCH_SIZE -o run "
+        "-- python3 /root/repo/bench.py --copy-calibration (and WRITE_SIZE into DIR/calib_WRITE_SIZE)",
+        "python3 bench.py --traffic-record DIR: per-dispatch Counter_Value averaged over the gate_up "
+        "dispatches of one forward; calibration = the __amd_rocclr_copyBuffer dispatches of 256 MiB",
+    ]
+    out = os.path.join(TRAFFIC_DIR, f"traffic_{args.roofline_kernel}_{args.workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(f"wrote {out}: {rec['dispatches']} dispatches, "
+        f"{(rec['fetch_kib_per_dispatch'] * rec['fetch_factor'] + rec['write_kib_per_dispatch'] * rec['write_factor']) / 1024:.1f} MiB/launch")
 
 
 def host_cpu():
@@ -391,6 +450,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
+    if args.traffic_record:
+        write_traffic_record(args)
+        return
     import torch
 
     if args.copy_calibration:
