@@ -41,6 +41,11 @@ Optional non-zero initial memory state (for resume tests), index 2 + 9*L:
     (scaled so that a memory read from it is of the order of the residual
     stream: q.z is about 64*24 and q A^T about 8*128)
 
+LM head (final RMSNorm + vocabulary projection after the last layer; the
+pages give no vocabulary size, so V is synthetic, ``HEAD_VOCAB``):
+    index 3 + 9*L: W_lm [V, d] N(0, 0.02);  index 4 + 9*L: g_final [d] =
+    1 + gain_std * N(0, 1) (gain_std 0 by default: gains of 1, like the layers').
+
 Matrices are stored row-major as [out_features, in_features].  Values are
 drawn in float32 and, for bf16 workloads, rounded once to bfloat16 so that the
 GPU path and the oracle consume the same numbers.
@@ -55,7 +60,7 @@ import os
 import numpy as np
 
 __all__ = ["ArmtConfig", "CONFIGS", "get_config", "ArmtInputs", "make_inputs",
-           "make_state", "WEIGHT_NAMES"]
+           "make_state", "make_head", "HEAD_VOCAB", "WEIGHT_NAMES"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -209,3 +214,21 @@ def make_state(cfg: ArmtConfig, seed: int = 0, layers: int | None = None):
     A0 = (128.0 * rng.standard_normal((L, cfg.d_model, cfg.d_key))).astype(np.float32)
     z0 = (16.0 * rng.uniform(1.0, 2.0, (L, cfg.d_key))).astype(np.float32)
     return A0, z0
+
+
+# Synthetic vocabulary sizes of the LM head per workload (multiples of 8; the
+# small ones leave ragged output tiles).
+HEAD_VOCAB = {"tiny_fp32": 100, "small_bf16": 1000, "1b_s32": 32000, "1b_s128": 32000,
+              "3b_t512": 32000, "3b_t1024": 32000, "3b_t2048": 32000}
+
+
+def make_head(cfg: ArmtConfig, vocab: int | None = None, seed: int = 0, gain_std: float = 0.0):
+    """LM-head weights (W_lm [V, d], g_final [d]) in the storage dtype."""
+    V = HEAD_VOCAB.get(cfg.name, 1000) if vocab is None else vocab
+    L = cfg.n_layers
+    w_lm = _to_storage(_draw(seed, 3 + 9 * L, (V, cfg.d_model), 0.02), cfg.dtype)
+    g = np.ones(cfg.d_model, dtype=np.float32)
+    if gain_std:
+        g = g + np.float32(gain_std) * _draw(seed, 4 + 9 * L, (cfg.d_model,), 1.0)
+    return w_lm, _to_storage(g.astype(np.float32), cfg.dtype)
+

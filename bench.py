@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1b_s128]
     python bench.py --all-workloads      # diag + seq on every benchmark workload
     python bench.py --group-sweep        # grouped kernels vs wave width k
+    python bench.py --logit-drift        # LM-head logits: diag vs seq vs oracle per segment count
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
@@ -68,6 +69,12 @@ def parse():
                          "line each")
     ap.add_argument("--group-sweep", action="store_true",
                     help="grouped GEMM and attention throughput against the wave width k (1B shapes)")
+    ap.add_argument("--logit-drift", action="store_true",
+                    help="LM-head logits of the last segment against the segment count: diagonal vs "
+                         "sequential vs the CPU oracle, one JSON line per count, plus the LM head's "
+                         "throughput over the whole sequence")
+    ap.add_argument("--drift-segments", type=int, default=8,
+                    help="largest segment count of --logit-drift (the oracle runs this many segments)")
     ap.add_argument("--traffic-record", metavar="DIR",
                     help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
                          "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
@@ -414,6 +421,77 @@ def all_workloads(args, dev):
         gc.collect()
 
 
+def logit_drift(args, dev):
+    """Relative logit drift against the number of segments processed, in the
+    manner of the pages' Table 2 (Pith review: falsifier and referee report):
+    for S = 1 .. S_max the logits of segment S - 1 from a diagonal and a
+    sequential forward of S segments, and from the float64 oracle run over the
+    same S segments (random weights of the workload's shape, synthetic V)."""
+    import numpy as np
+    import torch
+    import oracle
+    from armt_inputs import get_config, make_head, make_inputs
+    cfg = get_config(args.workload)
+    S_max, T, L = args.drift_segments, cfg.seg_len, cfg.n_layers
+    inp = make_inputs(cfg, n_segments=max(S_max, cfg.n_segments))
+    w_lm, g = make_head(cfg)
+    V = w_lm.shape[0]
+    model = build(inp, cfg, dev)
+    dw, dg = to_dev(w_lm, dev), to_dev(g, dev)
+    x = to_dev(inp.x, dev)
+
+    # LM head throughput over the workload's whole output (S * T rows)
+    S = cfg.n_segments
+    y, _, _ = model.forward(x[:S * T].contiguous(), "diagonal")
+    lg = torch.empty(S * T, V, dtype=torch.float32, device=dev)
+    st = model.stream
+    model.logits(y, dg, dw, out=lg)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(3):
+        model.logits(y, dg, dw, out=lg, sync=False)
+    e1.record(st)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    flops = 2.0 * S * T * V * cfg.d_model
+    head = {"rows": S * T, "vocab": V, "ms": ms, "tflops": flops / ms / 1e9,
+            "frac_mfma_bf16": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    log(f"LM head over {S * T} rows, V={V}: {ms:.2f} ms, {head['tflops']:.0f} TFLOP/s")
+    print(json.dumps({"workload": args.workload, "lm_head": head}), flush=True)
+    del lg, y
+
+    o = oracle.Oracle(inp)
+    A, z = o.initial_state()
+    for s in range(S_max):
+        xs = x[:(s + 1) * T].contiguous()
+        out = {}
+        for sched in ("diagonal", "sequential"):
+            y, _, _ = model.forward(xs, sched)
+            out[sched] = model.logits(y[s * T:].contiguous(), dg, dw).clone()
+        t0 = time.time()
+        h = o.node_input(s)
+        for l in range(L):
+            h, A[l], z[l] = o.node(l, h, A[l], z[l])
+        ref = oracle.logits(o.R(h[:T]), g, w_lm, cfg.dtype, cfg.rms_eps)
+        got = out["diagonal"].to(torch.float64).cpu().numpy()
+        diff = out["diagonal"] - out["sequential"]
+        line = {"workload": args.workload, "segments": s + 1, "tokens": (s + 1) * T, "vocab": V,
+                "rows_compared": T,
+                "diag_vs_seq": {"rel_l2": float(torch.linalg.vector_norm(diff) /
+                                                torch.linalg.vector_norm(out["sequential"])),
+                                "max_abs": float(diff.abs().max()),
+                                "bitwise_equal": bool(torch.equal(out["diagonal"], out["sequential"]))},
+                "gpu_vs_oracle": {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                                  "max_abs": float(np.abs(got - ref).max()),
+                                  "max_abs_ref": float(np.abs(ref).max()),
+                                  "argmax_agree": float(np.mean(got.argmax(1) == ref.argmax(1)))},
+                "oracle_s": time.time() - t0}
+        log(f"S={s + 1}: diag vs seq {line['diag_vs_seq']['rel_l2']:.1e}, "
+            f"vs oracle {line['gpu_vs_oracle']['rel_l2']:.2e} (oracle {line['oracle_s']:.0f}s)")
+        print(json.dumps(line), flush=True)
+    model.close()
+
+
 def group_sweep(args, dev):
     """Grouped GEMM and attention throughput against the wave width k: a
     model of the first k layers of the 1B shape, run diagonally over 32 k
@@ -467,6 +545,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.all_workloads:
         all_workloads(args, dev)
+    elif args.logit_drift:
+        logit_drift(args, dev)
     elif args.group_sweep:
         group_sweep(args, dev)
     else:

@@ -142,6 +142,27 @@ int armt_forward_diagonal(armt_handle *h, const void *x, int32_t n_segments,
                           const float *A0, const float *z0, void *y,
                           float *A_out, float *z_out);
 
+/* Final RMSNorm and LM head over rows of a forward's output: the logits the
+ * pages compare between the sequential and the diagonal schedule (Pith review
+ * of arXiv 2506.05229: falsifier, and the referee report on the relative
+ * logit drift of Table 2; skill page "Diagonal Batching for Recurrent Memory
+ * Transformers", the results listed after Practical Guidance: error
+ * accumulation under 2% at 32K tokens).
+ *   logits[r, v] = sum_k R(rms(y_r) * g_final)[k] * w_lm[v, k]
+ * accumulated and stored in fp32 (rms and R as above, eps = rms_eps).
+ *   y       [rows, d]     config dtype, e.g. the y of a forward
+ *   g_final [d]           config dtype, final RMSNorm gain
+ *   w_lm    [vocab, d]    config dtype, row-major [out, in]
+ *   logits  [rows, vocab] fp32, row-major; must not overlap y
+ * rows >= 1 and vocab >= 1 (ARMT_E_INVALID otherwise); ARMT_BF16 needs
+ * vocab % 8 == 0 (ARMT_E_UNSUPPORTED).  The normalised rows pass through the
+ * handle's workspace, L * (T + M) rows at a time, so the call is ordered with
+ * the forwards on the handle's stream and must not overlap them from another
+ * thread.  Asynchronous; logits are valid once the stream is synchronised.
+ * The weights are read only during the call (not borrowed). */
+int armt_logits(armt_handle *h, const void *y, int64_t rows, const void *g_final,
+                const void *w_lm, int32_t vocab, float *logits);
+
 void armt_destroy(armt_handle *h);
 
 /* Message of the last non-OK status on this thread ("" if none).  Host

@@ -15,7 +15,7 @@ import re
 __all__ = [
     "ArmtError", "armt_config", "armt_weights", "load_library", "library_path",
     "armt_workspace_size", "armt_create", "armt_forward_sequential",
-    "armt_forward_diagonal", "armt_destroy", "armt_last_error",
+    "armt_forward_diagonal", "armt_logits", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
     "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "KERNELS", "VIEWS",
@@ -74,6 +74,7 @@ def load_library():
                               ctypes.POINTER(P)]),
         "armt_forward_sequential": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_diagonal": (I32, [P, P, I32, P, P, P, P, P]),
+        "armt_logits": (I32, [P, P, ctypes.c_int64, P, P, I32, P]),
         "armt_destroy": (None, [P]),
         "armt_last_error": (ctypes.c_char_p, []),
         "armt_wave_schedule": (I32, [I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), I32,
@@ -145,6 +146,10 @@ def armt_forward_sequential(h, x, n_segments: int, A0, z0, y, A_out, z_out):
 def armt_forward_diagonal(h, x, n_segments: int, A0, z0, y, A_out, z_out):
     _check(load_library().armt_forward_diagonal(h, _ptr(x), n_segments, _ptr(A0), _ptr(z0), _ptr(y),
                                                 _ptr(A_out), _ptr(z_out)))
+
+
+def armt_logits(h, y, rows: int, g_final, w_lm, vocab: int, logits):
+    _check(load_library().armt_logits(h, _ptr(y), rows, _ptr(g_final), _ptr(w_lm), vocab, _ptr(logits)))
 
 
 def armt_destroy(h):

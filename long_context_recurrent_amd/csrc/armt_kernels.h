@@ -15,6 +15,7 @@
 
 namespace armt {
 
+// EPI_STORE: plain fp32 store of the product (LM-head logits)
 enum { EPI_STORE = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
@@ -82,6 +83,15 @@ struct MemArgs {
   float mem_eps, rms_eps;
 };
 
+// Final RMSNorm: out[r] = R(x[r] / sqrt(mean(x[r]^2) + eps) * gain), rows of d.
+struct NormArgs {
+  const void* x;             // [rows][d] config dtype
+  const void* gain;          // [d]
+  void* out;                 // [rows][d]
+  int rows, d;
+  float eps;
+};
+
 // number of 16-row MFMA blocks per GEMM tile that have instantiations
 extern const int kGemmRowBlocks[];
 extern const int kGemmRowBlocksCount;
@@ -96,6 +106,7 @@ hipError_t launch_mem_update(const MemArgs& m, bool use_bf16, hipStream_t st);
 hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_mem_keys_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st);
+hipError_t launch_final_norm(const NormArgs& a, bool use_bf16, hipStream_t st);
 hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
 

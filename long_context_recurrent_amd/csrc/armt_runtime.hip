@@ -536,6 +536,42 @@ int armt_forward_diagonal(armt_handle* h, const void* x, int32_t n_segments, con
   return forward(h, SCHED_DIAG, x, n_segments, A0, z0, y, A_out, z_out);
 }
 
+int armt_logits(armt_handle* h, const void* y, int64_t rows, const void* g_final, const void* w_lm,
+                int32_t vocab, float* logits) {
+  if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  if (!y || !g_final || !w_lm || !logits) return fail(ARMT_E_INVALID, "y, g_final, w_lm and logits must not be NULL");
+  if (rows < 1 || vocab < 1) return fail(ARMT_E_INVALID, "rows and vocab must be positive");
+  if (h->bf16 && vocab % 8) return fail(ARMT_E_UNSUPPORTED, "bf16: vocab must be a multiple of 8 (got %d)", vocab);
+  const armt_config& c = h->cfg;
+  const int d = c.d_model;
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  // normalised rows go through the workspace's normalised-activation buffer
+  // ([L][n][d]), a chunk of L * n rows at a time
+  const int64_t chunk = (int64_t)c.n_layers * h->n;
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int m = (int)(rows - r0 < chunk ? rows - r0 : chunk);
+    NormArgs na{};
+    na.x = (const char*)y + r0 * d * (int64_t)h->es;
+    na.gain = g_final;
+    na.out = h->abuf;
+    na.rows = m;
+    na.d = d;
+    na.eps = c.rms_eps;
+    if ((e = launch_final_norm(na, h->bf16, h->stream)) != hipSuccess) return hip_fail(e, "final norm launch");
+    GemmArgs g{};
+    g.P = 1; g.l0 = 0;
+    g.A = h->abuf; g.a_stride = 0; g.lda = d;
+    g.B = w_lm; g.b_stride = 0;
+    g.M = m; g.N = vocab; g.K = d;
+    g.C = logits + r0 * vocab; g.c_stride = 0; g.ldc = vocab;
+    e = h->bf16 ? launch_gemm_bf16(g, EPI_STORE, h->mb ? h->mb : pick_row_blocks(m, vocab, 256, 1, h->cus), h->stream)
+                : launch_gemm_f32(g, EPI_STORE, h->stream);
+    if (e != hipSuccess) return hip_fail(e, "LM-head GEMM launch");
+  }
+  return ARMT_OK;
+}
+
 void armt_destroy(armt_handle* h) {
   if (!h) return;
   hipSetDevice(h->device);

@@ -34,6 +34,7 @@
 //                  caller's y, rounded to bf16.
 //      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
 //                  rows; U = R(silu(gate) * up).
+//      EPI_STORE : fp32 store (LM-head logits; N a multiple of 8).
 //  Every output element accumulates over K in the same order whatever MB or
 //  the number of problems, so results do not depend on the wave width.
 #include <type_traits>
@@ -405,33 +406,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
           for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)s[e * CPITCH];
         }
       }
-    } else if (EPI == EPI_RESID) {
-      // residual stream (fp32) += acc; the last layer's segment-token rows
-      // also go to the caller's y, rounded once to bf16
+    } else if (EPI == EPI_STORE) {
+      // fp32 output (LM-head logits)
       float* Cf = (float*)g.C + (int64_t)layer * g.c_stride;
-      bf16* Y = nullptr;
-      int y_rows = 0;
-      if (g.desc != nullptr && layer == g.last_layer) {
-        const int s = g.desc->c - layer;
-        Y = (bf16*)g.desc->y + (int64_t)s * g.T * g.ldc;
-        y_rows = g.T;
-      }
       for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.N) continue;
         const float* s = Cs + r * CPITCH + c8;
         float* dstp = Cf + (int64_t)m * g.ldc + n;
-        const f32x4 r0 = *(const f32x4*)dstp, r1 = *(const f32x4*)(dstp + 4);
-        const f32x4 o0 = f32x4{r0[0] + s[0], r0[1] + s[1], r0[2] + s[2], r0[3] + s[3]};
-        const f32x4 o1 = f32x4{r1[0] + s[4], r1[1] + s[5], r1[2] + s[6], r1[3] + s[7]};
-        *(f32x4*)dstp = o0;
-        *(f32x4*)(dstp + 4) = o1;
-        if (m < y_rows) {
-          const bf16x8 o = {(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3],
-                            (bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
-          *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
-        }
+        *(f32x4*)dstp = f32x4{s[0], s[1], s[2], s[3]};
+        *(f32x4*)(dstp + 4) = f32x4{s[4], s[5], s[6], s[7]};
       }
     } else {
       for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
@@ -487,6 +472,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int mb, hipStream_t st) 
       return launch_epi<EPI_QKV>(g, mb, st);
     case EPI_RESID: return launch_epi<EPI_RESID>(g, mb, st);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, mb, st);
+    case EPI_STORE:
+      // whole 8-column output pieces
+      if (g.N % 8) return hipErrorInvalidValue;
+      return launch_epi<EPI_STORE>(g, mb, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,7 +5,7 @@
 // tile (each lane 4 x 4 outputs), K advances 16 at a time through LDS.  The
 // epilogue stages the tile in LDS so RoPE can pair columns i and i + hd/2
 // (hd <= 128 divides the tile width).  In this path V stays row-major inside
-// the QKV buffer.
+// the QKV buffer.  EPI_STORE writes the plain product (LM-head logits).
 #include "armt_common.h"
 #include "armt_kernels.h"
 
@@ -119,6 +119,7 @@ hipError_t launch_gemm_f32(const GemmArgs& g, int epi, hipStream_t st) {
       break;
     case EPI_RESID: hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID>, grid, dim3(256), 0, st, g); break;
     case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, st, g); break;
+    case EPI_STORE: hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, dim3(256), 0, st, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

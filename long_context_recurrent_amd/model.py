@@ -92,6 +92,30 @@ class ArmtModel:
             torch.cuda.current_stream(self.device).wait_stream(self.stream)
         return y, A, z
 
+    def logits(self, y: torch.Tensor, g_final: torch.Tensor, w_lm: torch.Tensor, out=None,
+               sync: bool = True):
+        """Final RMSNorm + LM head: y [rows, d], g_final [d], w_lm [V, d] (device
+        tensors of the config dtype) -> fp32 logits [rows, V]."""
+        c = self.cfg
+        for name, t in (("y", y), ("g_final", g_final), ("w_lm", w_lm)):
+            if t.dtype != self.dtype or not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"{name} must be a contiguous device tensor of the config dtype")
+        if y.dim() != 2 or y.shape[1] != c.d_model or g_final.shape != (c.d_model,) \
+                or w_lm.dim() != 2 or w_lm.shape[1] != c.d_model:
+            raise ValueError("shapes: y [rows, d], g_final [d], w_lm [vocab, d]")
+        rows, vocab = y.shape[0], w_lm.shape[0]
+        if out is None:
+            out = torch.empty(rows, vocab, dtype=torch.float32, device=self.device)
+        elif out.shape != (rows, vocab) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 [rows, vocab] tensor")
+        self.stream.wait_stream(torch.cuda.current_stream(self.device))
+        _c.armt_logits(self.handle, y, rows, g_final, w_lm, vocab, out)
+        if sync:
+            self.stream.synchronize()
+        else:
+            torch.cuda.current_stream(self.device).wait_stream(self.stream)
+        return out
+
     def view(self, which: str, dtype=None, shape=None):
         """Device tensor aliasing an internal workspace buffer (tests only)."""
         ptr, nbytes = _c.armt_debug_view(self.handle, which)

@@ -43,7 +43,8 @@ wave-shuffle invariance; split (resume) invariance; hand-derived closed forms of
 the memory read and write; the zero-memory node against torch's library
 routines (rms_norm, scaled_dot_product_attention, silu, linear); RoPE against
 complex rotation plus its norm and relative-position invariants; bf16 rounding
-against torch's conversion; phi against torch's elu.  No function here is
+against torch's conversion; phi against torch's elu; the logits' closed forms
+(permutation and one-hot heads, constant rows, gain and scale behaviour).  No function here is
 "parity unpinned" with respect to the stated reading; the reading itself (the
 ARMT memory equations) cannot be pinned to the authors' model, which the pages
 do not print.
@@ -76,6 +77,7 @@ __all__ = [
     "waves", "round_bf16", "phi", "sigmoid", "silu", "rms_norm", "rope",
     "causal_gqa_attention", "mem_read", "mem_write", "node",
     "forward_sequential", "forward_diagonal", "Oracle", "working_precision",
+    "logits",
 ]
 
 
@@ -354,3 +356,16 @@ def forward_diagonal(inputs, A0=None, z0=None, n_segments=None, shuffle_seed=Non
 def node(inputs, l, h_in, A, z, rows=None):
     """Convenience wrapper: one node of layer l."""
     return Oracle(inputs).node(l, h_in, A, z, rows)
+
+
+def logits(y, g_final, w_lm, dtype="f32", eps=1e-5):
+    """Final RMSNorm and LM head over output rows y [rows, d]: the logits the
+    pages compare between the sequential and the diagonal schedule (Pith
+    review: falsifier, and the referee report on Table 2's relative logit
+    drift).  The normalised row is a branch activation like the block's own
+    norm outputs, so bf16 workloads store it rounded to bf16; the product
+    accumulates in the working precision and is not rounded."""
+    R = round_bf16 if dtype == "bf16" else _identity
+    b = R(rms_norm(y, g_final, eps))
+    return b @ np.asarray(w_lm, dtype=_WP).T
+

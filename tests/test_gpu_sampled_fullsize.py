@@ -11,7 +11,9 @@ can compute one by one:
 * prefix rows of segment 1 through all layers from the oracle's own state
   after segment 0 (the recurrence across segments at every layer);
 * for the larger 3B segmentations, prefix rows of segment 0 and the layer-0
-  state after one full node.
+  state after one full node;
+* the LM head over all 131,072 output rows of the 1B run: segment 0's logits
+  end to end, and sampled rows of the last segment through the head alone.
 
 Causal attention makes the first r rows of a node independent of the rest, so
 prefix rows are exact samples (oracle ``Oracle.node(..., rows=r)``).
@@ -30,7 +32,7 @@ import pytest
 import torch
 
 import oracle
-from armt_inputs import get_config, make_inputs, make_state
+from armt_inputs import get_config, make_head, make_inputs, make_state
 
 from gpu_util import build_model, rel_l2, state_to_device, to_device, to_np, tol
 
@@ -126,6 +128,20 @@ def test_1b_fullsize():
     _check_state(A1, z1, A, z, A0, z0, bar, range(L))
     h1 = _oracle_segment(o, 1, A, z, rows=ROWS)
     _check(f"y segment 1 rows 0..{ROWS - 1}", to_np(y128[T:T + ROWS]), oracle.round_bf16(h1), bar)
+    # LM head (V = 32,000) in the benchmark's launch configuration: the
+    # logits of all 131,072 rows at once (fp32, 16.8 GB), sampled against the
+    # oracle's head on the oracle's own segment-0 rows (end to end) and on the
+    # GPU's y rows of the last segment (the head alone)
+    w_lm, g = make_head(cfg, gain_std=0.1)
+    dw, dg = to_device(w_lm, cfg), to_device(g, cfg)
+    lg = model.logits(y128, dg, dw)
+    assert torch.isfinite(lg).all()
+    _check("logits segment 0 (all rows, end to end)", to_np(lg[:T]),
+           oracle.logits(oracle.round_bf16(h[:T]), g, w_lm, "bf16", cfg.rms_eps), bar)
+    last = slice((S - 1) * T, (S - 1) * T + ROWS)
+    _check(f"logits segment {S - 1} rows 0..{ROWS - 1} (head only)", to_np(lg[last]),
+           oracle.logits(to_np(y128[last]), g, w_lm, "bf16", cfg.rms_eps), bar)
+    del lg
     del x, y1, A1, z1
     _release(model)
 

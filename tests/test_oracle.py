@@ -363,3 +363,67 @@ def test_oracle_own_rounding_error_is_far_below_the_parity_bars(name, bar_y, bar
     assert rel(low[0], ref[0]) < bar_y
     assert rel(low[1], ref[1]) < bar_state
     assert rel(low[2], ref[2]) < bar_state
+
+
+# ---------------------------------------------------------------------------
+# LM head (final RMSNorm + vocabulary projection)
+# ---------------------------------------------------------------------------
+
+def test_logits_unit_vector_geometry():
+    """With eps = 0 the normalised row is sqrt(d) * y / |y|_2 (RMSNorm puts
+    every row on the sphere of radius sqrt(d)); a 3-4-5 row makes it exact:
+    sqrt(2) * (0.6, 0.8)."""
+    y = np.array([[3.0, 4.0], [-6.0, 8.0]])
+    eye = np.eye(2)
+    out = oracle.logits(y, np.ones(2), eye, eps=0.0)
+    np.testing.assert_allclose(out[0], math.sqrt(2) * np.array([0.6, 0.8]), rtol=1e-15)
+    np.testing.assert_allclose(out[1], math.sqrt(2) * np.array([-0.6, 0.8]), rtol=1e-15)
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((7, 48)) * rng.uniform(0.1, 10.0, (7, 1))
+    out = oracle.logits(y, np.ones(48), np.eye(48), eps=0.0)
+    want = math.sqrt(48) * y / np.linalg.norm(y, axis=1, keepdims=True)
+    np.testing.assert_allclose(out, want, rtol=1e-13)
+    # eps > 0 shrinks every row by sqrt(ms / (ms + eps)) exactly
+    eps = 0.25
+    ms = np.mean(y * y, axis=1, keepdims=True)
+    np.testing.assert_allclose(oracle.logits(y, np.ones(48), np.eye(48), eps=eps),
+                               want * np.sqrt(ms / (ms + eps)), rtol=1e-13)
+
+
+def test_logits_head_orientation_and_gain():
+    """Rows of w_lm are vocabulary entries: a one-hot / two-hot head picks (sums)
+    coordinates of the normalised row, so a transposed head fails; the gain
+    scales coordinates before the head."""
+    y = np.array([[3.0, 4.0]])
+    b = math.sqrt(2) * np.array([0.6, 0.8])
+    w = np.array([[0.0, 1.0], [1.0, 0.0], [1.0, 1.0]])      # V = 3, d = 2
+    out = oracle.logits(y, np.ones(2), w, eps=0.0)
+    assert out.shape == (1, 3)
+    np.testing.assert_allclose(out[0], [b[1], b[0], b[0] + b[1]], rtol=1e-15)
+    out = oracle.logits(y, np.array([2.0, -0.5]), w, eps=0.0)
+    np.testing.assert_allclose(out[0], [-0.5 * b[1], 2 * b[0], 2 * b[0] - 0.5 * b[1]], rtol=1e-15)
+
+
+def test_logits_scale_invariance_and_row_independence():
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((5, 64))
+    g = 1 + 0.1 * rng.standard_normal(64)
+    w = 0.02 * rng.standard_normal((40, 64))
+    base = oracle.logits(y, g, w, eps=0.0)
+    np.testing.assert_allclose(oracle.logits(37.0 * y, g, w, eps=0.0), base, rtol=1e-12, atol=1e-15)
+    for r in range(5):
+        np.testing.assert_allclose(oracle.logits(y[r:r + 1], g, w, eps=0.0)[0], base[r], rtol=1e-13, atol=1e-15)
+
+
+def test_logits_bf16_rounds_the_normalised_row_only():
+    """bf16 workloads store the normalised row in bf16 (round to nearest even,
+    checked against torch's conversion); the product itself is not rounded."""
+    y = np.array([[1.0, 2.0, 2.0]])                          # |y| = 3
+    b = math.sqrt(3) * np.array([1.0, 2.0, 2.0]) / 3.0
+    b16 = torch.tensor(b).to(torch.bfloat16).to(torch.float64).numpy()
+    assert not np.array_equal(b16, b)
+    out = oracle.logits(y, np.ones(3), np.eye(3), dtype="bf16", eps=0.0)
+    np.testing.assert_array_equal(out[0], b16)
+    w = np.array([[1.0 / 3.0, 1.0 / 7.0, 1.0]])
+    out = oracle.logits(y, np.ones(3), w, dtype="bf16", eps=0.0)
+    assert out[0, 0] == pytest.approx(b16[0] / 3.0 + b16[1] / 7.0 + b16[2], rel=1e-15)
