@@ -4,6 +4,7 @@
     python bench.py --all-workloads      # diag + seq on every benchmark workload
     python bench.py --group-sweep        # grouped kernels vs wave width k
     python bench.py --logit-drift        # LM-head logits: diag vs seq vs oracle per segment count
+    python bench.py --full-attention     # full-attention Llama comparator vs diagonal ARMT, 4K..131K
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
@@ -75,6 +76,9 @@ def parse():
                          "throughput over the whole sequence")
     ap.add_argument("--drift-segments", type=int, default=8,
                     help="largest segment count of --logit-drift (the oracle runs this many segments)")
+    ap.add_argument("--full-attention", action="store_true",
+                    help="full-attention Llama comparator against the diagonal ARMT forward at 4K..131K "
+                         "tokens (1B shape): time, speed-up and workspace memory, one JSON line per length")
     ap.add_argument("--traffic-record", metavar="DIR",
                     help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
                          "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
@@ -492,6 +496,72 @@ def logit_drift(args, dev):
     model.close()
 
 
+def full_attention(args, dev):
+    """The pages' comparator (paper page, abstract; Pith review, Figure 1 and
+    Table 1): the same Llama-shaped layers with no memory over the whole
+    sequence as one causal window, against the diagonal ARMT forward over the
+    same tokens in 1,024-token segments.  Random weights of the 1B shape."""
+    import gc
+    import torch
+    from armt_inputs import get_config, make_inputs
+    from long_context_recurrent_amd import armt as C
+    from long_context_recurrent_amd.model import FullAttentionModel
+    cfg = get_config("1b_s128")
+    T, L, d = cfg.seg_len, cfg.n_layers, cfg.d_model
+    inp = make_inputs(cfg)
+    x_all = to_dev(inp.x, dev)
+    w = {k: to_dev(inp.weights[k], dev) for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down")}
+    w.update(g_attn=to_dev(inp.g_attn, dev), g_mlp=to_dev(inp.g_mlp, dev))
+    armt = build(inp, cfg, dev)
+    ccfg = armt.cfg
+    armt_ws = armt.ws_bytes
+    per_layer = cfg.node_flops()
+    blk = 2 * d * (cfg.qkv_dim + cfg.n_heads * cfg.head_dim + 3 * cfg.ffn_hidden)   # GEMM FLOPs per token
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        each = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            each.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(each), min(each)
+
+    for N in (4096, 8192, 16384, 32768, 65536, 131072):
+        S = N // T
+        x = x_all[:N]
+        full = FullAttentionModel(ccfg, w, N)
+        y = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+        t_full, t_full_min = timed(lambda: full.forward(x, out=y, sync=False), max(1, min(args.steps, 3)))
+        full_ws = full.ws_bytes
+        full.close()
+        del full
+        out = armt.alloc_outputs(S)
+        t_armt, t_armt_min = timed(lambda: armt.forward(x, "diagonal", out=out, sync=False),
+                                   max(1, min(args.steps, 3)))
+        flops_full = N * blk * L + L * 4 * (N * (N + 1) / 2) * cfg.head_dim * cfg.n_heads
+        flops_armt = sum(per_layer.values()) * S * L
+        line = {"workload": "1b", "tokens": N, "segments_armt": S,
+                "full_attention": {"ms": t_full * 1e3, "ms_min": t_full_min * 1e3, "tokens_per_s": N / t_full,
+                                   "tflops": flops_full / t_full / 1e12, "workspace_bytes": full_ws},
+                "armt_diagonal": {"ms": t_armt * 1e3, "ms_min": t_armt_min * 1e3, "tokens_per_s": N / t_armt,
+                                  "tflops": flops_armt / t_armt / 1e12, "workspace_bytes": armt_ws},
+                "speedup_armt_over_full": t_full / t_armt,
+                "workspace_ratio_full_over_armt": full_ws / armt_ws}
+        log(f"N={N}: full attention {t_full * 1e3:.1f} ms ({line['full_attention']['tflops']:.0f} TFLOP/s), "
+            f"ARMT diagonal {t_armt * 1e3:.1f} ms, x{t_full / t_armt:.2f}; workspace "
+            f"{full_ws / 2**30:.2f} vs {armt_ws / 2**30:.2f} GiB")
+        print(json.dumps(line), flush=True)
+        del y, out
+        gc.collect()
+        torch.cuda.empty_cache()
+    armt.close()
+
+
 def group_sweep(args, dev):
     """Grouped GEMM and attention throughput against the wave width k: a
     model of the first k layers of the 1B shape, run diagonally over 32 k
@@ -547,6 +617,8 @@ def main():
         all_workloads(args, dev)
     elif args.logit_drift:
         logit_drift(args, dev)
+    elif args.full_attention:
+        full_attention(args, dev)
     elif args.group_sweep:
         group_sweep(args, dev)
     else:

@@ -156,12 +156,38 @@ int armt_forward_diagonal(armt_handle *h, const void *x, int32_t n_segments,
  *   logits  [rows, vocab] fp32, row-major; must not overlap y
  * rows >= 1 and vocab >= 1 (ARMT_E_INVALID otherwise); ARMT_BF16 needs
  * vocab % 8 == 0 (ARMT_E_UNSUPPORTED).  The normalised rows pass through the
- * handle's workspace, L * (T + M) rows at a time, so the call is ordered with
+ * handle's workspace, L * (T + M) rows at a time (max_tokens for a
+ * full-attention handle), so the call is ordered with
  * the forwards on the handle's stream and must not overlap them from another
  * thread.  Asynchronous; logits are valid once the stream is synchronised.
  * The weights are read only during the call (not borrowed). */
 int armt_logits(armt_handle *h, const void *y, int64_t rows, const void *g_final,
                 const void *w_lm, int32_t vocab, float *logits);
+
+/* Full-attention comparator: the same Llama-shaped block stack with no memory,
+ * run over a whole sequence as one causal window -- the standard transformer
+ * the paper page's abstract and the Pith review's Figure 1 compare against
+ * (3.3x slower than the diagonal ARMT at 131,072 tokens there, on another
+ * GPU).  Per layer l, over positions 0..N-1 of x:
+ *   h = h + R(causal softmax(Q K^T / sqrt(hd)) V) W_o^T  (Q, K, V as above,
+ *       from R(rms(h) * g_attn[l]), RoPE positions 0..N-1)
+ *   h = h + R(silu(b W_gate^T) * (b W_up^T)) W_down^T,  b = R(rms(h) * g_mlp[l])
+ * with h_0 = x (fp32 stream) and y = R(h_L).  Uses the config's layer
+ * geometry, dtype, rms_eps and rope_theta; seg_len, n_mem, d_key and mem_eps
+ * are ignored.  Constraints: head_dim in {32, 64, 128}; d_model and
+ * ffn_hidden multiples of 64, d_model <= 4096; 1 <= max_tokens <= 262144
+ * (ARMT_BF16) or 4096 (ARMT_F32).
+ * armt_llama_workspace_size: bytes of workspace for up to max_tokens
+ * positions (host call).  armt_llama_create: as armt_create, but only
+ * w_qkv, w_o, w_gate, w_up, w_down, g_attn and g_mlp are used (borrowed);
+ * the memory fields may be NULL.  armt_llama_forward: x [n_tokens, d] ->
+ * y [n_tokens, d] (config dtype), 1 <= n_tokens <= max_tokens; asynchronous
+ * on the handle's stream.  armt_logits works on such a handle too
+ * (max_tokens rows per chunk); armt_forward_* reject it. */
+int armt_llama_workspace_size(const armt_config *cfg, int64_t max_tokens, size_t *bytes);
+int armt_llama_create(const armt_config *cfg, const armt_weights *w, int64_t max_tokens,
+                      void *workspace, size_t ws_bytes, void *hip_stream, armt_handle **out);
+int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y);
 
 void armt_destroy(armt_handle *h);
 

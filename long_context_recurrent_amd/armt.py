@@ -15,7 +15,8 @@ import re
 __all__ = [
     "ArmtError", "armt_config", "armt_weights", "load_library", "library_path",
     "armt_workspace_size", "armt_create", "armt_forward_sequential",
-    "armt_forward_diagonal", "armt_logits", "armt_destroy", "armt_last_error",
+    "armt_forward_diagonal", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
+    "armt_llama_forward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
     "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "KERNELS", "VIEWS",
@@ -75,6 +76,10 @@ def load_library():
         "armt_forward_sequential": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_diagonal": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_logits": (I32, [P, P, ctypes.c_int64, P, P, I32, P]),
+        "armt_llama_workspace_size": (I32, [ctypes.POINTER(armt_config), ctypes.c_int64, ctypes.POINTER(SZ)]),
+        "armt_llama_create": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), ctypes.c_int64,
+                                    P, SZ, P, ctypes.POINTER(P)]),
+        "armt_llama_forward": (I32, [P, P, ctypes.c_int64, P]),
         "armt_destroy": (None, [P]),
         "armt_last_error": (ctypes.c_char_p, []),
         "armt_wave_schedule": (I32, [I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), I32,
@@ -150,6 +155,24 @@ def armt_forward_diagonal(h, x, n_segments: int, A0, z0, y, A_out, z_out):
 
 def armt_logits(h, y, rows: int, g_final, w_lm, vocab: int, logits):
     _check(load_library().armt_logits(h, _ptr(y), rows, _ptr(g_final), _ptr(w_lm), vocab, _ptr(logits)))
+
+
+def armt_llama_workspace_size(cfg: armt_config, max_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().armt_llama_workspace_size(ctypes.byref(cfg), max_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def armt_llama_create(cfg: armt_config, w: armt_weights, max_tokens: int, workspace, ws_bytes: int,
+                      stream=None):
+    h = ctypes.c_void_p(0)
+    _check(load_library().armt_llama_create(ctypes.byref(cfg), ctypes.byref(w), max_tokens, _ptr(workspace),
+                                            ws_bytes, _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def armt_llama_forward(h, x, n_tokens: int, y):
+    _check(load_library().armt_llama_forward(h, _ptr(x), n_tokens, _ptr(y)))
 
 
 def armt_destroy(h):

@@ -107,6 +107,8 @@ hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_mem_keys_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_final_norm(const NormArgs& a, bool use_bf16, hipStream_t st);
+// dst[i] = (float)src[i], count a multiple of 8
+hipError_t launch_widen(const void* src, float* dst, int64_t count, bool use_bf16, hipStream_t st);
 hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
 

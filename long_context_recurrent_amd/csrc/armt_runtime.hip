@@ -121,6 +121,58 @@ Layout make_layout(const armt_config* c) {
   return lo;
 }
 
+// Full-attention comparator: the layer geometry of the config (seg_len, n_mem,
+// d_key and mem_eps unused) over up to max_tokens positions.
+int validate_llama(const armt_config* c, int64_t max_tokens) {
+  if (!c) return fail(ARMT_E_INVALID, "config is NULL");
+  if (c->n_layers <= 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn_hidden <= 0)
+    return fail(ARMT_E_INVALID, "every layer size in the config must be positive");
+  if (max_tokens < 1) return fail(ARMT_E_INVALID, "max_tokens must be >= 1");
+  if (c->dtype != ARMT_F32 && c->dtype != ARMT_BF16) return fail(ARMT_E_INVALID, "dtype must be ARMT_F32 or ARMT_BF16");
+  if (c->d_model != c->n_heads * c->head_dim)
+    return fail(ARMT_E_INVALID, "d_model (%d) must equal n_heads * head_dim (%d)", c->d_model, c->n_heads * c->head_dim);
+  if (c->n_heads % c->n_kv_heads) return fail(ARMT_E_INVALID, "n_heads must be a multiple of n_kv_heads");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(ARMT_E_INVALID, "rms_eps and rope_theta must be positive");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(ARMT_E_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (c->d_model % 64 || c->ffn_hidden % 64 || c->d_model > 4096)
+    return fail(ARMT_E_UNSUPPORTED, "d_model and ffn_hidden must be multiples of 64, d_model <= 4096");
+  if (c->dtype == ARMT_BF16 && max_tokens > (1 << 18)) return fail(ARMT_E_UNSUPPORTED, "bf16: max_tokens must be <= 262144");
+  if (c->dtype == ARMT_F32 && max_tokens > 4096) return fail(ARMT_E_UNSUPPORTED, "fp32: max_tokens must be <= 4096");
+  return ARMT_OK;
+}
+
+// One slab per buffer (the comparator runs one layer at a time over all
+// positions): residual stream fp32 [N][d] in act0, then the same scratch as a
+// node of the recurrent model with n = N.
+Layout make_llama_layout(const armt_config* c, int64_t N) {
+  const size_t d = c->d_model, n = (size_t)N, n_pad = (n + 63) / 64 * 64;
+  const size_t es = c->dtype == ARMT_BF16 ? 2 : 4;
+  const size_t qkv_dim = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  const size_t hhd = (size_t)c->n_heads * c->head_dim, F = c->ffn_hidden;
+  Layout lo{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+  lo.desc = take(sizeof(CallDesc));
+  lo.rope = take(n * (c->head_dim / 2) * 2 * sizeof(float));
+  lo.A = take(0);
+  lo.z = take(0);
+  lo.act0 = take(n * d * 4);
+  lo.act1 = take(0);
+  lo.abuf = take(n * d * es);
+  lo.qkv = take(n * qkv_dim * es);
+  lo.vt = take(c->dtype == ARMT_BF16 ? c->n_kv_heads * c->head_dim * n_pad * 2 : 0);
+  lo.attn = take(n * hhd * es);
+  lo.ubuf = take(n * F * es);
+  lo.qbuf = take(0);
+  lo.kbuf = take(0);
+  lo.pden = take(0);
+  lo.beta = take(0);
+  lo.total = off;
+  return lo;
+}
+
 enum Sched { SCHED_DIAG = 0, SCHED_SEQ = 1 };
 
 }  // namespace
@@ -133,6 +185,8 @@ struct armt_handle {
   int device = 0;
   bool bf16 = true;
   int n = 0, n_pad = 0, qkv_dim = 0, mb = 0, cus = 256;   // mb 0: per-launch choice
+  bool llama = false;       // full-attention comparator handle (armt_llama_create)
+  int64_t norm_rows = 0;    // rows of the normalised-activation buffer
   size_t es = 2;
   char* ws = nullptr;
   Layout lo{};
@@ -348,6 +402,82 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   return hipSuccess;
 }
 
+// Full-attention comparator: the L Llama-shaped blocks over all N positions
+// as one causal window, one layer at a time (no memory read or write).  The
+// same kernels as a recurrent node with n = N and one problem per launch;
+// activation slabs have stride 0, so every layer reuses the one set of
+// buffers, and the fp32 residual stream is updated in place.
+hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
+  armt_handle* h = cx.h;
+  const armt_config& c = h->cfg;
+  const int L = c.n_layers, d = c.d_model, F = c.ffn_hidden, hhd = c.n_heads * c.head_dim;
+  hipError_t e;
+  // the descriptor points the last layer's down projection at y (segment 0)
+  if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, cx.st)) != hipSuccess) return e;
+  if ((e = launch_widen(x, (float*)h->act[0], (int64_t)N * d, h->bf16, cx.st)) != hipSuccess) return e;
+  auto rows = [&](int n_cols, int cols_per_tile) {
+    return h->mb ? h->mb : pick_row_blocks(N, n_cols, cols_per_tile, 1, h->cus);
+  };
+  for (int l = 0; l < L; ++l) {
+    MemArgs m{};
+    m.P = 1; m.l0 = l; m.n = N; m.d = d; m.T = N; m.L = L;
+    m.act_cur = h->act[0]; m.act_prev = h->act[0]; m.abuf = h->abuf; m.act_stride = 0;
+    m.rms_eps = c.rms_eps;
+    GemmArgs g0{};
+    g0.P = 1; g0.l0 = l; g0.M = N; g0.T = N; g0.last_layer = L - 1; g0.head_dim = c.head_dim;
+    // attention block
+    m.gain = h->w.g_attn;
+    if ((e = launch_rmsnorm(m, h->bf16, cx.st)) != hipSuccess) return e;
+    {
+      GemmArgs g = g0;
+      g.A = h->abuf; g.a_stride = 0; g.lda = d;
+      g.B = h->w.w_qkv; g.b_stride = (int64_t)h->qkv_dim * d; g.N = h->qkv_dim; g.K = d;
+      g.C = h->qkv; g.c_stride = 0; g.ldc = h->qkv_dim;
+      g.rope_cs = h->rope; g.rope_cols = (c.n_heads + c.n_kv_heads) * c.head_dim;
+      g.v_col0 = g.rope_cols; g.vt = h->vt; g.vt_ld = h->n_pad; g.vt_stride = 0;
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_QKV, rows(h->qkv_dim, 256), cx.st) : launch_gemm_f32(g, EPI_QKV, cx.st);
+      if (e != hipSuccess) return e;
+    }
+    {
+      AttnArgs a{};
+      a.P = 1; a.l0 = l; a.qkv = h->qkv; a.qkv_stride = 0; a.ld_qkv = h->qkv_dim;
+      a.vt = h->vt; a.vt_stride = 0; a.vt_ld = h->n_pad;
+      a.out = h->attn; a.out_stride = 0; a.ld_out = hhd;
+      a.n = N; a.H = c.n_heads; a.G = c.n_kv_heads; a.hd = c.head_dim;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      if ((e = launch_attention(a, h->bf16, cx.st)) != hipSuccess) return e;
+    }
+    {
+      GemmArgs g = g0;
+      g.A = h->attn; g.a_stride = 0; g.lda = hhd;
+      g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
+      g.C = h->act[0]; g.c_stride = 0; g.ldc = d; g.desc = nullptr;
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
+      if (e != hipSuccess) return e;
+    }
+    // MLP block
+    m.gain = h->w.g_mlp;
+    if ((e = launch_rmsnorm(m, h->bf16, cx.st)) != hipSuccess) return e;
+    {
+      GemmArgs g = g0;
+      g.A = h->abuf; g.a_stride = 0; g.lda = d;
+      g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
+      g.C = h->ubuf; g.c_stride = 0; g.ldc = F;
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_SWIGLU, rows(F, 128), cx.st) : launch_gemm_f32(g, EPI_SWIGLU, cx.st);
+      if (e != hipSuccess) return e;
+    }
+    {
+      GemmArgs g = g0;
+      g.A = h->ubuf; g.a_stride = 0; g.lda = F;
+      g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
+      g.C = h->act[0]; g.c_stride = 0; g.ldc = d; g.desc = h->desc;
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 int run_step(armt_handle* h, int sched, int l_lo, int l_hi, int par, int advance) {
   const bool timing = h->time_kernel >= 0;
   if (!h->use_graphs || timing) {
@@ -382,6 +512,7 @@ int run_step(armt_handle* h, int sched, int l_lo, int l_hi, int par, int advance
 int forward(armt_handle* h, int sched, const void* x, int32_t S, const float* A0, const float* z0,
             void* y, float* A_out, float* z_out) {
   if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  if (h->llama) return fail(ARMT_E_INVALID, "handle is a full-attention comparator: use armt_llama_forward");
   if (!x || !y || !A_out || !z_out) return fail(ARMT_E_INVALID, "x, y, A_out and z_out must not be NULL");
   if (S < 1) return fail(ARMT_E_INVALID, "n_segments must be >= 1 (got %d)", S);
   const armt_config& c = h->cfg;
@@ -451,29 +582,21 @@ int armt_workspace_size(const armt_config* cfg, size_t* bytes) {
   return ARMT_OK;
 }
 
-int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, size_t ws_bytes,
-                void* hip_stream, armt_handle** out) {
-  int rc = validate_config(cfg);
-  if (rc != ARMT_OK) return rc;
-  if (!w || !out) return fail(ARMT_E_INVALID, "weights and out must not be NULL");
-  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn,
-                        w->g_mlp, w->w_mq, w->w_mk, w->w_mv, w->w_beta, w->mem_emb};
-  for (const void* p : ptrs)
-    if (!p) return fail(ARMT_E_INVALID, "every weight pointer must be non-NULL");
-  const Layout lo = make_layout(cfg);
-  if (!workspace) return fail(ARMT_E_WORKSPACE, "workspace is NULL");
-  if ((uintptr_t)workspace % kAlign) return fail(ARMT_E_WORKSPACE, "workspace must be 256-byte aligned");
-  if (ws_bytes < lo.total)
-    return fail(ARMT_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, lo.total);
+}  // extern "C"
 
-  armt_handle* h = new (std::nothrow) armt_handle();
-  if (!h) return fail(ARMT_E_INVALID, "out of host memory");
+namespace {
+
+// Common part of the two create calls: carve the workspace, upload the RoPE
+// table for positions 0..n-1 and zero the V^T padding.  Takes ownership of h
+// (deleted on failure).
+int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, const Layout& lo,
+                void* workspace, void* hip_stream, int n, armt_handle** out) {
   h->cfg = *cfg;
   h->w = *w;
   h->stream = (hipStream_t)hip_stream;
   h->bf16 = cfg->dtype == ARMT_BF16;
   h->es = h->bf16 ? 2 : 4;
-  h->n = cfg->seg_len + cfg->n_mem;
+  h->n = n;
   h->n_pad = (h->n + 63) / 64 * 64;
   h->qkv_dim = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
   h->mb = 0;
@@ -526,6 +649,73 @@ int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, 
   return ARMT_OK;
 }
 
+int check_workspace(const Layout& lo, void* workspace, size_t ws_bytes) {
+  if (!workspace) return fail(ARMT_E_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(ARMT_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < lo.total)
+    return fail(ARMT_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, lo.total);
+  return ARMT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, size_t ws_bytes,
+                void* hip_stream, armt_handle** out) {
+  int rc = validate_config(cfg);
+  if (rc != ARMT_OK) return rc;
+  if (!w || !out) return fail(ARMT_E_INVALID, "weights and out must not be NULL");
+  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn,
+                        w->g_mlp, w->w_mq, w->w_mk, w->w_mv, w->w_beta, w->mem_emb};
+  for (const void* p : ptrs)
+    if (!p) return fail(ARMT_E_INVALID, "every weight pointer must be non-NULL");
+  const Layout lo = make_layout(cfg);
+  if ((rc = check_workspace(lo, workspace, ws_bytes)) != ARMT_OK) return rc;
+  armt_handle* h = new (std::nothrow) armt_handle();
+  if (!h) return fail(ARMT_E_INVALID, "out of host memory");
+  h->norm_rows = (int64_t)cfg->n_layers * (cfg->seg_len + cfg->n_mem);
+  return init_handle(h, cfg, w, lo, workspace, hip_stream, cfg->seg_len + cfg->n_mem, out);
+}
+
+int armt_llama_workspace_size(const armt_config* cfg, int64_t max_tokens, size_t* bytes) {
+  int rc = validate_llama(cfg, max_tokens);
+  if (rc != ARMT_OK) return rc;
+  if (!bytes) return fail(ARMT_E_INVALID, "bytes is NULL");
+  *bytes = make_llama_layout(cfg, max_tokens).total;
+  return ARMT_OK;
+}
+
+int armt_llama_create(const armt_config* cfg, const armt_weights* w, int64_t max_tokens, void* workspace,
+                      size_t ws_bytes, void* hip_stream, armt_handle** out) {
+  int rc = validate_llama(cfg, max_tokens);
+  if (rc != ARMT_OK) return rc;
+  if (!w || !out) return fail(ARMT_E_INVALID, "weights and out must not be NULL");
+  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn, w->g_mlp};
+  for (const void* p : ptrs)
+    if (!p) return fail(ARMT_E_INVALID, "the block weights (w_qkv .. g_mlp) must be non-NULL");
+  const Layout lo = make_llama_layout(cfg, max_tokens);
+  if ((rc = check_workspace(lo, workspace, ws_bytes)) != ARMT_OK) return rc;
+  armt_handle* h = new (std::nothrow) armt_handle();
+  if (!h) return fail(ARMT_E_INVALID, "out of host memory");
+  h->llama = true;
+  h->norm_rows = max_tokens;
+  return init_handle(h, cfg, w, lo, workspace, hip_stream, (int)max_tokens, out);
+}
+
+int armt_llama_forward(armt_handle* h, const void* x, int64_t n_tokens, void* y) {
+  if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  if (!h->llama) return fail(ARMT_E_INVALID, "handle is not a full-attention comparator (armt_llama_create)");
+  if (!x || !y) return fail(ARMT_E_INVALID, "x and y must not be NULL");
+  if (n_tokens < 1 || n_tokens > h->n)
+    return fail(ARMT_E_INVALID, "n_tokens must be in 1..%d (got %lld)", h->n, (long long)n_tokens);
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  StepCtx cx{h, h->stream, false};
+  e = enqueue_llama(cx, x, (int)n_tokens, y);
+  return e == hipSuccess ? ARMT_OK : hip_fail(e, "kernel launch");
+}
+
 int armt_forward_sequential(armt_handle* h, const void* x, int32_t n_segments, const float* A0,
                             const float* z0, void* y, float* A_out, float* z_out) {
   return forward(h, SCHED_SEQ, x, n_segments, A0, z0, y, A_out, z_out);
@@ -547,8 +737,9 @@ int armt_logits(armt_handle* h, const void* y, int64_t rows, const void* g_final
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
   // normalised rows go through the workspace's normalised-activation buffer
-  // ([L][n][d]), a chunk of L * n rows at a time
-  const int64_t chunk = (int64_t)c.n_layers * h->n;
+  // (L * n rows of a recurrent-model handle, max_tokens of a comparator), a
+  // chunk at a time
+  const int64_t chunk = h->norm_rows;
   for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
     const int m = (int)(rows - r0 < chunk ? rows - r0 : chunk);
     NormArgs na{};

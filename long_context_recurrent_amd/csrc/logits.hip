@@ -1,12 +1,16 @@
+// Kernels outside the recurrent node.
+//
 // Final RMSNorm ahead of the LM head.  The logits that follow it are what the
 // pages compare between the sequential and the diagonal schedule (Pith review
 // of arXiv 2506.05229: falsifier, and the referee report on the relative
 // logit drift of Table 2).  The LM-head product itself is the plain-store
-// epilogue of the GEMM kernels (fp32 logits).
+// epilogue of the GEMM kernels (fp32 logits).  One wave per row: the lane
+// holds 8-element pieces c * 512 + 8 * lane of the row in registers from load
+// to store; the sum of squares goes lane-local in piece order, then across
+// the wave.
 //
-// One wave per row: the lane holds 8-element pieces c * 512 + 8 * lane of the
-// row in registers from load to store; the sum of squares goes lane-local in
-// piece order, then across the wave.
+// Stream initialisation of the full-attention comparator: the input rows,
+// widened to the fp32 residual stream.
 #include "armt_common.h"
 #include "armt_kernels.h"
 
@@ -72,7 +76,26 @@ __global__ __launch_bounds__(256) void final_norm_kernel(NormArgs a) {
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ src, float* __restrict__ dst,
+                                                    int64_t count8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count8) return;
+  float v[8];
+  ld8(src + 8 * i, v);
+  st8(dst + 8 * i, v);
+}
+
 }  // namespace
+
+hipError_t launch_widen(const void* src, float* dst, int64_t count, bool use_bf16, hipStream_t st) {
+  if (count <= 0 || count % 8) return hipErrorInvalidValue;
+  const int64_t c8 = count / 8;
+  const dim3 grid((unsigned)((c8 + 255) / 256));
+  if (use_bf16) hipLaunchKernelGGL(widen_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)src, dst, c8);
+  else hipLaunchKernelGGL(widen_kernel<float>, grid, dim3(256), 0, st, (const float*)src, dst, c8);
+  return hipGetLastError();
+}
 
 hipError_t launch_final_norm(const NormArgs& a, bool use_bf16, hipStream_t st) {
   if (a.rows <= 0 || a.d <= 0 || a.d % 8 || a.d > kMaxPieces * 64 * 8) return hipErrorInvalidValue;

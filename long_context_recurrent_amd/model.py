@@ -19,29 +19,30 @@ def make_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden, se
                           rms_eps, rope_theta, mem_eps)
 
 
-class ArmtModel:
-    """One handle: ``weights`` maps the armt_weights field names to contiguous
-    device tensors of the config dtype (kept referenced here: the library
-    borrows them)."""
+BLOCK_FIELDS = WEIGHT_FIELDS[:7]     # w_qkv .. g_mlp: all the full-attention comparator uses
 
-    def __init__(self, cfg: _c.armt_config, weights: dict, stream: torch.cuda.Stream | None = None):
+
+class _Handle:
+    """Common part of the two handle kinds: weights kept referenced (the
+    library borrows them), the workspace, the stream."""
+
+    def _setup(self, cfg, weights: dict, fields, stream, ws_bytes_fn):
         self.cfg = cfg
         self.dtype = torch.bfloat16 if cfg.dtype == _c.ARMT_BF16 else torch.float32
         self.weights = {}
-        for k in WEIGHT_FIELDS:
+        for k in fields:
             t = weights[k]
             if not (t.is_cuda and t.is_contiguous() and t.dtype == self.dtype):
                 raise ValueError(f"weight {k} must be a contiguous {self.dtype} CUDA tensor")
             self.weights[k] = t
         self.device = self.weights["w_qkv"].device
         self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
-        self.ws_bytes = _c.armt_workspace_size(cfg)
+        self.ws_bytes = ws_bytes_fn()
         self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
         base = self.workspace.data_ptr()
         self.ws_ptr = (base + 255) // 256 * 256
-        w = _c.armt_weights(*[self.weights[k].data_ptr() for k in WEIGHT_FIELDS])
-        with torch.cuda.device(self.device):
-            self.handle = _c.armt_create(cfg, w, self.ws_ptr, self.ws_bytes, self.stream)
+        return _c.armt_weights(*[self.weights[k].data_ptr() if k in self.weights else None
+                                 for k in WEIGHT_FIELDS])
 
     def close(self):
         if getattr(self, "handle", None):
@@ -54,8 +55,46 @@ class ArmtModel:
         except Exception:
             pass
 
+    def view(self, which: str, dtype=None, shape=None):
+        return _view(self, which, dtype, shape)
+
     def set_option(self, option: int, value: int):
         _c.armt_set_option(self.handle, option, value)
+
+    def logits(self, y: torch.Tensor, g_final: torch.Tensor, w_lm: torch.Tensor, out=None,
+               sync: bool = True):
+        """Final RMSNorm + LM head: y [rows, d], g_final [d], w_lm [V, d] (device
+        tensors of the config dtype) -> fp32 logits [rows, V]."""
+        c = self.cfg
+        for name, t in (("y", y), ("g_final", g_final), ("w_lm", w_lm)):
+            if t.dtype != self.dtype or not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"{name} must be a contiguous device tensor of the config dtype")
+        if y.dim() != 2 or y.shape[1] != c.d_model or g_final.shape != (c.d_model,) \
+                or w_lm.dim() != 2 or w_lm.shape[1] != c.d_model:
+            raise ValueError("shapes: y [rows, d], g_final [d], w_lm [vocab, d]")
+        rows, vocab = y.shape[0], w_lm.shape[0]
+        if out is None:
+            out = torch.empty(rows, vocab, dtype=torch.float32, device=self.device)
+        elif out.shape != (rows, vocab) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 [rows, vocab] tensor")
+        self.stream.wait_stream(torch.cuda.current_stream(self.device))
+        _c.armt_logits(self.handle, y, rows, g_final, w_lm, vocab, out)
+        if sync:
+            self.stream.synchronize()
+        else:
+            torch.cuda.current_stream(self.device).wait_stream(self.stream)
+        return out
+
+
+class ArmtModel(_Handle):
+    """One handle: ``weights`` maps the armt_weights field names to contiguous
+    device tensors of the config dtype (kept referenced here: the library
+    borrows them)."""
+
+    def __init__(self, cfg: _c.armt_config, weights: dict, stream: torch.cuda.Stream | None = None):
+        w = self._setup(cfg, weights, WEIGHT_FIELDS, stream, lambda: _c.armt_workspace_size(cfg))
+        with torch.cuda.device(self.device):
+            self.handle = _c.armt_create(cfg, w, self.ws_ptr, self.ws_bytes, self.stream)
 
     def kernel_stats(self):
         return _c.armt_kernel_stats(self.handle)
@@ -92,38 +131,44 @@ class ArmtModel:
             torch.cuda.current_stream(self.device).wait_stream(self.stream)
         return y, A, z
 
-    def logits(self, y: torch.Tensor, g_final: torch.Tensor, w_lm: torch.Tensor, out=None,
-               sync: bool = True):
-        """Final RMSNorm + LM head: y [rows, d], g_final [d], w_lm [V, d] (device
-        tensors of the config dtype) -> fp32 logits [rows, V]."""
+
+class FullAttentionModel(_Handle):
+    """The full-attention comparator (armt_llama_*): the block weights of the
+    recurrent model's layers over one causal window of up to ``max_tokens``."""
+
+    def __init__(self, cfg: _c.armt_config, weights: dict, max_tokens: int,
+                 stream: torch.cuda.Stream | None = None):
+        self.max_tokens = max_tokens
+        w = self._setup(cfg, weights, BLOCK_FIELDS, stream,
+                        lambda: _c.armt_llama_workspace_size(cfg, max_tokens))
+        with torch.cuda.device(self.device):
+            self.handle = _c.armt_llama_create(cfg, w, max_tokens, self.ws_ptr, self.ws_bytes, self.stream)
+
+    def forward(self, x: torch.Tensor, out=None, sync: bool = True):
+        """x [N, d] device tensor of the config dtype -> y [N, d]."""
         c = self.cfg
-        for name, t in (("y", y), ("g_final", g_final), ("w_lm", w_lm)):
-            if t.dtype != self.dtype or not t.is_contiguous() or t.device != self.device:
-                raise ValueError(f"{name} must be a contiguous device tensor of the config dtype")
-        if y.dim() != 2 or y.shape[1] != c.d_model or g_final.shape != (c.d_model,) \
-                or w_lm.dim() != 2 or w_lm.shape[1] != c.d_model:
-            raise ValueError("shapes: y [rows, d], g_final [d], w_lm [vocab, d]")
-        rows, vocab = y.shape[0], w_lm.shape[0]
-        if out is None:
-            out = torch.empty(rows, vocab, dtype=torch.float32, device=self.device)
-        elif out.shape != (rows, vocab) or out.dtype != torch.float32 or not out.is_contiguous():
-            raise ValueError("out must be a contiguous float32 [rows, vocab] tensor")
+        if x.dim() != 2 or x.shape[1] != c.d_model or not 1 <= x.shape[0] <= self.max_tokens:
+            raise ValueError(f"x must be [N, d_model] with 1 <= N <= {self.max_tokens}")
+        if x.dtype != self.dtype or not x.is_contiguous() or x.device != self.device:
+            raise ValueError("x must be a contiguous device tensor of the config dtype")
+        y = out if out is not None else torch.empty_like(x)
         self.stream.wait_stream(torch.cuda.current_stream(self.device))
-        _c.armt_logits(self.handle, y, rows, g_final, w_lm, vocab, out)
+        _c.armt_llama_forward(self.handle, x, x.shape[0], y)
         if sync:
             self.stream.synchronize()
         else:
             torch.cuda.current_stream(self.device).wait_stream(self.stream)
-        return out
+        return y
 
-    def view(self, which: str, dtype=None, shape=None):
-        """Device tensor aliasing an internal workspace buffer (tests only)."""
-        ptr, nbytes = _c.armt_debug_view(self.handle, which)
-        off = ptr - self.workspace.data_ptr()
-        raw = self.workspace[off:off + nbytes]
-        dt = dtype or (torch.float32 if which in ("A", "z", "act0", "act1") else self.dtype)
-        t = raw.view(dt)
-        return t if shape is None else t[: _numel(shape)].view(*shape)
+
+def _view(self, which: str, dtype=None, shape=None):
+    """Device tensor aliasing an internal workspace buffer (tests only)."""
+    ptr, nbytes = _c.armt_debug_view(self.handle, which)
+    off = ptr - self.workspace.data_ptr()
+    raw = self.workspace[off:off + nbytes]
+    dt = dtype or (torch.float32 if which in ("A", "z", "act0", "act1") else self.dtype)
+    t = raw.view(dt)
+    return t if shape is None else t[: _numel(shape)].view(*shape)
 
 
 def _numel(shape):

@@ -44,7 +44,9 @@ the memory read and write; the zero-memory node against torch's library
 routines (rms_norm, scaled_dot_product_attention, silu, linear); RoPE against
 complex rotation plus its norm and relative-position invariants; bf16 rounding
 against torch's conversion; phi against torch's elu; the logits' closed forms
-(permutation and one-hot heads, constant rows, gain and scale behaviour).  No function here is
+(permutation and one-hot heads, constant rows, gain and scale behaviour); the
+full-attention comparator against a block stack built from torch's library
+routines, its causal prefix property, and equality with a zero-memory node.  No function here is
 "parity unpinned" with respect to the stated reading; the reading itself (the
 ARMT memory equations) cannot be pinned to the authors' model, which the pages
 do not print.
@@ -77,7 +79,7 @@ __all__ = [
     "waves", "round_bf16", "phi", "sigmoid", "silu", "rms_norm", "rope",
     "causal_gqa_attention", "mem_read", "mem_write", "node",
     "forward_sequential", "forward_diagonal", "Oracle", "working_precision",
-    "logits",
+    "logits", "llama_forward",
 ]
 
 
@@ -264,16 +266,32 @@ class Oracle:
         rows are computed (causal attention makes them independent of later
         rows) and the memory write is skipped (A_new, z_new are None).  A dict
         passed as ``trace`` receives the intermediate values by name."""
-        c, R, Rs = self.cfg, self.R, self.Rs
-        T, H, G, hd = c.seg_len, c.n_heads, c.n_kv_heads, c.head_dim
+        c, Rs = self.cfg, self.Rs
+        T = c.seg_len
         h = np.asarray(h_in, dtype=self.dtype)
         if rows is not None:
             h = h[:rows]
-        n = h.shape[0]
         # 1. memory read
         h = Rs(mem_read(h, self.w("w_mq", l), A, z, c.mem_eps))
-        h_read = h
-        # 2. attention block
+        if trace is not None:
+            trace.update(h_read=h)
+        # 2-3. attention and MLP blocks
+        h = self.block(l, h, trace)
+        if rows is not None:
+            return h, None, None
+        # 4. memory write from the memory-token rows
+        A_new, z_new = mem_write(h[T:], self.w("w_mk", l), self.w("w_mv", l),
+                                 self.w("w_beta", l), A, z, c.mem_eps)
+        return h, _round_f32(A_new), _round_f32(z_new)
+
+    def block(self, l, h, trace=None):
+        """Layer l's Llama-shaped block on the residual stream h [n, d] (rows
+        are positions 0..n-1): pre-norm causal GQA attention with RoPE, then
+        a pre-norm SwiGLU MLP, each added to the stream."""
+        c, R, Rs = self.cfg, self.R, self.Rs
+        H, G, hd = c.n_heads, c.n_kv_heads, c.head_dim
+        n = h.shape[0]
+        # attention block
         a = R(rms_norm(h, self.inp.g_attn[l], c.rms_eps))
         qkv = a @ self.w("w_qkv", l).T
         Q = qkv[:, :H * hd].reshape(n, H, hd)
@@ -285,19 +303,13 @@ class Oracle:
         O = R(causal_gqa_attention(Q, K, V))
         h = Rs(h + O @ self.w("w_o", l).T)
         h_attn = h
-        # 3. MLP block
+        # MLP block
         b = R(rms_norm(h, self.inp.g_mlp[l], c.rms_eps))
         U = R(silu(b @ self.w("w_gate", l).T) * (b @ self.w("w_up", l).T))
         h = Rs(h + U @ self.w("w_down", l).T)
         if trace is not None:
-            trace.update(h_read=h_read, a_attn=a, Q=Q, K=K, V=V, O=O, h_attn=h_attn,
-                         a_mlp=b, U=U, h_out=h)
-        if rows is not None:
-            return h, None, None
-        # 4. memory write from the memory-token rows
-        A_new, z_new = mem_write(h[T:], self.w("w_mk", l), self.w("w_mv", l),
-                                 self.w("w_beta", l), A, z, c.mem_eps)
-        return h, _round_f32(A_new), _round_f32(z_new)
+            trace.update(a_attn=a, Q=Q, K=K, V=V, O=O, h_attn=h_attn, a_mlp=b, U=U, h_out=h)
+        return h
 
     def initial_state(self, A0=None, z0=None):
         c = self.cfg
@@ -368,4 +380,22 @@ def logits(y, g_final, w_lm, dtype="f32", eps=1e-5):
     R = round_bf16 if dtype == "bf16" else _identity
     b = R(rms_norm(y, g_final, eps))
     return b @ np.asarray(w_lm, dtype=_WP).T
+
+
+def llama_forward(inputs, n_tokens=None, rows=None):
+    """Full-attention comparator: the same layers' Llama-shaped blocks, with no
+    memory, run over the whole sequence as one causal window (positions
+    0..N-1) -- the standard-transformer baseline the paper page's abstract
+    and the Pith review's Figure 1 compare against.  The stream is stored like
+    the recurrent model's (float32 for bf16 workloads) and y = R(h) of the last
+    layer.  ``rows`` = r computes only the first r positions, which causal
+    attention makes independent of the rest."""
+    o = Oracle(inputs)
+    L = inputs.weights["w_qkv"].shape[0]
+    N = inputs.x.shape[0] if n_tokens is None else n_tokens
+    r = N if rows is None else min(rows, N)
+    h = o.Rs(np.asarray(inputs.x[:r], dtype=o.dtype))
+    for l in range(L):
+        h = o.block(l, h)
+    return o.R(h)
 

@@ -92,3 +92,35 @@ def test_create_rejects_bad_arguments_before_any_gpu_work():
     assert lib.armt_forward_sequential(None, 1, 1, None, None, 1, 1, 1) == -1
     assert lib.armt_set_option(None, 0, 1) == -1
     lib.armt_destroy(None)
+
+
+def test_full_attention_comparator_validation():
+    """armt_llama_*: host-side validation (no GPU work): the memory fields of
+    the config are ignored, the token count is bounded per dtype, and the
+    workspace grows with max_tokens."""
+    lib = A.load_library()
+    n1 = A.armt_llama_workspace_size(_cfg(), 64)
+    n2 = A.armt_llama_workspace_size(_cfg(), 128)
+    assert 0 < n1 < n2
+    assert A.armt_llama_workspace_size(_cfg(d_key=7, n_mem=0, seg_len=0), 64) == n1
+    bf = dict(dtype=A.ARMT_BF16, d_model=2048, n_heads=32, n_kv_heads=8, head_dim=64, ffn_hidden=8192)
+    assert A.armt_llama_workspace_size(_cfg(**bf), 131072) > 5e9
+    cases = [
+        (dict(), 0, -1), (dict(n_layers=0), 64, -1), (dict(d_model=96), 64, -1),
+        (dict(head_dim=16, n_heads=4), 64, -2), (dict(), 4097, -2),
+        (bf, (1 << 18) + 1, -2), (dict(d_model=8192, n_heads=64, head_dim=128), 64, -2),
+    ]
+    for kw, nt, code in cases:
+        with pytest.raises(A.ArmtError) as e:
+            A.armt_llama_workspace_size(_cfg(**kw), nt)
+        assert e.value.code == code, (kw, nt, e.value)
+    cfg = _cfg()
+    out = ctypes.c_void_p(0)
+    w = A.armt_weights(*([1024] * 7 + [0] * 5))        # memory weights may be NULL
+    rc = lib.armt_llama_create(ctypes.byref(cfg), ctypes.byref(w), 64, None, 1 << 20, None, ctypes.byref(out))
+    assert rc == -3 and out.value is None
+    w2 = A.armt_weights(*([1024] * 6 + [0] * 6))       # g_mlp missing
+    rc = lib.armt_llama_create(ctypes.byref(cfg), ctypes.byref(w2), 64, 4096, 1 << 30, None, ctypes.byref(out))
+    assert rc == -1
+    assert lib.armt_llama_forward(None, 1, 1, 1) == -1
+    assert lib.armt_logits(None, 1, 1, 1, 1, 8, 1) == -1

@@ -427,3 +427,38 @@ def test_logits_bf16_rounds_the_normalised_row_only():
     w = np.array([[1.0 / 3.0, 1.0 / 7.0, 1.0]])
     out = oracle.logits(y, np.ones(3), w, dtype="bf16", eps=0.0)
     assert out[0, 0] == pytest.approx(b16[0] / 3.0 + b16[1] / 7.0 + b16[2], rel=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# full-attention comparator (Llama block stack over one causal window)
+# ---------------------------------------------------------------------------
+
+def test_llama_forward_against_torch_block_stack():
+    """fp32 workload (no rounding points): the comparator over 80 positions is
+    the layers' torch-built blocks applied in turn, y = the last stream."""
+    cfg = get_config("tiny_fp32").with_(n_heads=4, n_kv_heads=2, n_segments=5)
+    inp = make_inputs(cfg)
+    y = oracle.llama_forward(inp)
+    assert y.shape == (80, cfg.d_model)
+    h = inp.x.astype(np.float64)
+    for l in range(cfg.n_layers):
+        h = _torch_block(inp, l, h)
+    np.testing.assert_allclose(y, h, rtol=1e-11, atol=1e-11)
+
+
+def test_llama_forward_causal_prefix_and_zero_memory_node():
+    cfg = get_config("small_bf16").with_(n_segments=3)
+    inp = make_inputs(cfg)
+    full = oracle.llama_forward(inp)
+    part = oracle.llama_forward(inp, rows=57)
+    assert part.shape == (57, cfg.d_model)
+    np.testing.assert_array_equal(part, oracle.llama_forward(inp, n_tokens=57))
+    assert np.mean(part == full[:57]) > 0.99          # BLAS blocking aside, the same rows
+    np.testing.assert_allclose(part, full[:57], rtol=0, atol=2 ** -7 * np.abs(full[:57]).max())
+    # one segment of the recurrent model from the zero state is the comparator
+    # over that segment's rows followed by the memory rows (the read of a zero
+    # memory adds exactly 0); its y is the comparator's first T rows
+    T = cfg.seg_len
+    y_armt, _, _ = oracle.forward_sequential(inp, n_segments=1)
+    mixed = dataclasses.replace(inp, x=np.concatenate([inp.x[:T], inp.mem_emb]))
+    np.testing.assert_array_equal(oracle.llama_forward(mixed)[:T], y_armt)
