@@ -142,6 +142,21 @@ int armt_forward_diagonal(armt_handle *h, const void *x, int32_t n_segments,
                           const float *A0, const float *z0, void *y,
                           float *A_out, float *z_out);
 
+/* Any sequence length ("dynamic" segmenting): n_tokens >= 1 tokens run as
+ * S = ceil(n_tokens / T) segments, the last one t = n_tokens - (S - 1) T
+ * tokens long (1..T); x and y span n_tokens rows, everything else as above.
+ * A short last segment is its t tokens followed by the M memory tokens
+ * (positions 0..t+M-1), so its memory write reads the node's rows t..t+M-1;
+ * nothing else changes (the pages' skill page, Implementation: the segment
+ * count is left dynamic).  With n_tokens = S * T these are bitwise identical
+ * to the calls above. */
+int armt_forward_sequential_tokens(armt_handle *h, const void *x, int64_t n_tokens,
+                                   const float *A0, const float *z0, void *y,
+                                   float *A_out, float *z_out);
+int armt_forward_diagonal_tokens(armt_handle *h, const void *x, int64_t n_tokens,
+                                 const float *A0, const float *z0, void *y,
+                                 float *A_out, float *z_out);
+
 /* Final RMSNorm and LM head over rows of a forward's output: the logits the
  * pages compare between the sequential and the diagonal schedule (Pith review
  * of arXiv 2506.05229: falsifier, and the referee report on the relative

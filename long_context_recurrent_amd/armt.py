@@ -15,7 +15,7 @@ import re
 __all__ = [
     "ArmtError", "armt_config", "armt_weights", "load_library", "library_path",
     "armt_workspace_size", "armt_create", "armt_forward_sequential",
-    "armt_forward_diagonal", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
+    "armt_forward_diagonal", "armt_forward_sequential_tokens", "armt_forward_diagonal_tokens", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
     "armt_llama_forward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
@@ -75,6 +75,8 @@ def load_library():
                               ctypes.POINTER(P)]),
         "armt_forward_sequential": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_diagonal": (I32, [P, P, I32, P, P, P, P, P]),
+        "armt_forward_sequential_tokens": (I32, [P, P, ctypes.c_int64, P, P, P, P, P]),
+        "armt_forward_diagonal_tokens": (I32, [P, P, ctypes.c_int64, P, P, P, P, P]),
         "armt_logits": (I32, [P, P, ctypes.c_int64, P, P, I32, P]),
         "armt_llama_workspace_size": (I32, [ctypes.POINTER(armt_config), ctypes.c_int64, ctypes.POINTER(SZ)]),
         "armt_llama_create": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), ctypes.c_int64,
@@ -151,6 +153,16 @@ def armt_forward_sequential(h, x, n_segments: int, A0, z0, y, A_out, z_out):
 def armt_forward_diagonal(h, x, n_segments: int, A0, z0, y, A_out, z_out):
     _check(load_library().armt_forward_diagonal(h, _ptr(x), n_segments, _ptr(A0), _ptr(z0), _ptr(y),
                                                 _ptr(A_out), _ptr(z_out)))
+
+
+def armt_forward_sequential_tokens(h, x, n_tokens: int, A0, z0, y, A_out, z_out):
+    _check(load_library().armt_forward_sequential_tokens(h, _ptr(x), n_tokens, _ptr(A0), _ptr(z0), _ptr(y),
+                                                         _ptr(A_out), _ptr(z_out)))
+
+
+def armt_forward_diagonal_tokens(h, x, n_tokens: int, A0, z0, y, A_out, z_out):
+    _check(load_library().armt_forward_diagonal_tokens(h, _ptr(x), n_tokens, _ptr(A0), _ptr(z0), _ptr(y),
+                                                       _ptr(A_out), _ptr(z_out)))
 
 
 def armt_logits(h, y, rows: int, g_final, w_lm, vocab: int, logits):

@@ -32,11 +32,19 @@ __device__ __forceinline__ float sigmoid_f(float u) { return 1.f / (1.f + __expf
 // of layer l works on segment s = c - l.  Kept in device memory so captured
 // graphs can be replayed for any call and any wave of the same shape.
 struct CallDesc {
-  const void* x;   // [S*T, d]
-  void* y;         // [S*T, d]
+  const void* x;   // [(S-1)*T + t_last, d]
+  void* y;         // same rows as x
   int32_t c;       // current wave (diagonal) or s + l (sequential)
   int32_t n_segments;
+  int32_t t_last;  // tokens of the last segment (1..T)
 };
+
+// Tokens of segment s: T, except a shorter last segment.  The node keeps its
+// n = T + M rows; a short segment's memory tokens follow its t tokens and the
+// rows after them are padding no real row attends to.
+__device__ __forceinline__ int seg_tokens(const CallDesc* d, int s, int T) {
+  return s == d->n_segments - 1 ? d->t_last : T;
+}
 
 // ---- wave reductions -------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

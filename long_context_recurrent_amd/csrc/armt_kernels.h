@@ -78,6 +78,7 @@ struct MemArgs {
   float* kbuf;               // [L][M][dk] write keys phi(Y W_mk^T)
   float* pden;               // [L][M][4] partial k . z (pre-update z), 16 keys each
   float* beta;               // [L][M]
+  int* moff;                 // [L] first memory row of the node (mem_keys -> mem_update)
   CallDesc* desc;
   int advance;               // mem_update: wave-counter increment (0: none)
   float mem_eps, rms_eps;
@@ -109,7 +110,7 @@ hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_final_norm(const NormArgs& a, bool use_bf16, hipStream_t st);
 // dst[i] = (float)src[i], count a multiple of 8
 hipError_t launch_widen(const void* src, float* dst, int64_t count, bool use_bf16, hipStream_t st);
-hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, hipStream_t st);
+hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
 
 }  // namespace armt

@@ -61,7 +61,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, qbuf, kbuf, pden, beta, total;
+  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, qbuf, kbuf, pden, beta, moff, total;
 };
 
 int validate_config(const armt_config* c) {
@@ -117,6 +117,7 @@ Layout make_layout(const armt_config* c) {
   lo.kbuf = take(L * M * dk * 4);
   lo.pden = take(L * M * 4 * 4);
   lo.beta = take(L * M * 4);
+  lo.moff = take(L * 4);
   lo.total = off;
   return lo;
 }
@@ -169,6 +170,7 @@ Layout make_llama_layout(const armt_config* c, int64_t N) {
   lo.kbuf = take(0);
   lo.pden = take(0);
   lo.beta = take(0);
+  lo.moff = take(0);
   lo.total = off;
   return lo;
 }
@@ -197,6 +199,7 @@ struct armt_handle {
   void* act[2] = {nullptr, nullptr};
   void *abuf = nullptr, *qkv = nullptr, *vt = nullptr, *attn = nullptr, *ubuf = nullptr;
   float *qbuf = nullptr, *kbuf = nullptr, *pden = nullptr, *beta = nullptr;
+  int* moff = nullptr;
   std::map<std::tuple<int, int, int, int, int>, hipGraphExec_t> graphs;
   bool use_graphs = true;
   int time_kernel = -1;
@@ -316,6 +319,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   m.act_prev = h->act[par ^ 1]; m.act_cur = h->act[par]; m.abuf = h->abuf; m.act_stride = nd;
   m.mem_emb = h->w.mem_emb; m.w_mq = h->w.w_mq; m.w_mk = h->w.w_mk; m.w_mv = h->w.w_mv; m.w_beta = h->w.w_beta;
   m.A = h->A; m.z = h->z; m.qbuf = h->qbuf; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
+  m.moff = h->moff;
   m.mem_eps = c.mem_eps; m.rms_eps = c.rms_eps; m.advance = 0;
 
   GemmArgs g0{};
@@ -413,7 +417,7 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
   const int L = c.n_layers, d = c.d_model, F = c.ffn_hidden, hhd = c.n_heads * c.head_dim;
   hipError_t e;
   // the descriptor points the last layer's down projection at y (segment 0)
-  if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, cx.st)) != hipSuccess) return e;
+  if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, N, cx.st)) != hipSuccess) return e;
   if ((e = launch_widen(x, (float*)h->act[0], (int64_t)N * d, h->bf16, cx.st)) != hipSuccess) return e;
   auto rows = [&](int n_cols, int cols_per_tile) {
     return h->mb ? h->mb : pick_row_blocks(N, n_cols, cols_per_tile, 1, h->cus);
@@ -509,8 +513,9 @@ int run_step(armt_handle* h, int sched, int l_lo, int l_hi, int par, int advance
   return e == hipSuccess ? ARMT_OK : hip_fail(e, "hipGraphLaunch");
 }
 
-int forward(armt_handle* h, int sched, const void* x, int32_t S, const float* A0, const float* z0,
-            void* y, float* A_out, float* z_out) {
+// S segments, the last one t_last (1..T) tokens long.
+int forward(armt_handle* h, int sched, const void* x, int32_t S, int32_t t_last, const float* A0,
+            const float* z0, void* y, float* A_out, float* z_out) {
   if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
   if (h->llama) return fail(ARMT_E_INVALID, "handle is a full-attention comparator: use armt_llama_forward");
   if (!x || !y || !A_out || !z_out) return fail(ARMT_E_INVALID, "x, y, A_out and z_out must not be NULL");
@@ -520,7 +525,7 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, const float* A0
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
   const int64_t a_count = (int64_t)L * c.d_model * c.d_key, z_count = (int64_t)L * c.d_key;
-  if ((e = launch_set_desc(h->desc, x, y, 0, S, h->stream)) != hipSuccess) return hip_fail(e, "set_desc");
+  if ((e = launch_set_desc(h->desc, x, y, 0, S, t_last, h->stream)) != hipSuccess) return hip_fail(e, "set_desc");
   if ((e = launch_fill_f32(h->A, A0, a_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
   if ((e = launch_fill_f32(h->z, z0, z_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
   int rc;
@@ -618,6 +623,7 @@ int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, c
   h->kbuf = (float*)(base + lo.kbuf);
   h->pden = (float*)(base + lo.pden);
   h->beta = (float*)(base + lo.beta);
+  h->moff = (int*)(base + lo.moff);
 
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e, "hipGetDevice"); }
@@ -718,12 +724,32 @@ int armt_llama_forward(armt_handle* h, const void* x, int64_t n_tokens, void* y)
 
 int armt_forward_sequential(armt_handle* h, const void* x, int32_t n_segments, const float* A0,
                             const float* z0, void* y, float* A_out, float* z_out) {
-  return forward(h, SCHED_SEQ, x, n_segments, A0, z0, y, A_out, z_out);
+  return forward(h, SCHED_SEQ, x, n_segments, h ? h->cfg.seg_len : 0, A0, z0, y, A_out, z_out);
 }
 
 int armt_forward_diagonal(armt_handle* h, const void* x, int32_t n_segments, const float* A0,
                           const float* z0, void* y, float* A_out, float* z_out) {
-  return forward(h, SCHED_DIAG, x, n_segments, A0, z0, y, A_out, z_out);
+  return forward(h, SCHED_DIAG, x, n_segments, h ? h->cfg.seg_len : 0, A0, z0, y, A_out, z_out);
+}
+
+static int forward_tokens(armt_handle* h, int sched, const void* x, int64_t n_tokens, const float* A0,
+                          const float* z0, void* y, float* A_out, float* z_out) {
+  if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
+  const int64_t T = h->cfg.seg_len;
+  if (n_tokens < 1) return fail(ARMT_E_INVALID, "n_tokens must be >= 1 (got %lld)", (long long)n_tokens);
+  const int64_t S = (n_tokens + T - 1) / T;
+  if (S > (1 << 30)) return fail(ARMT_E_INVALID, "too many segments");
+  return forward(h, sched, x, (int32_t)S, (int32_t)(n_tokens - (S - 1) * T), A0, z0, y, A_out, z_out);
+}
+
+int armt_forward_sequential_tokens(armt_handle* h, const void* x, int64_t n_tokens, const float* A0,
+                                   const float* z0, void* y, float* A_out, float* z_out) {
+  return forward_tokens(h, SCHED_SEQ, x, n_tokens, A0, z0, y, A_out, z_out);
+}
+
+int armt_forward_diagonal_tokens(armt_handle* h, const void* x, int64_t n_tokens, const float* A0,
+                                 const float* z0, void* y, float* A_out, float* z_out) {
+  return forward_tokens(h, SCHED_DIAG, x, n_tokens, A0, z0, y, A_out, z_out);
 }
 
 int armt_logits(armt_handle* h, const void* y, int64_t rows, const void* g_final, const void* w_lm,

@@ -30,8 +30,8 @@
 //                  ([G * hd][n_pad], keys reordered within groups of 16) for
 //                  the attention kernel.
 //      EPI_RESID : C += acc in place on the fp32 residual stream; for the
-//                  last layer the segment-token rows are also written to the
-//                  caller's y, rounded to bf16.
+//                  last layer the segment-token rows (fewer in a short last
+//                  segment) are also written to the caller's y, rounded to bf16.
 //      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
 //                  rows; U = R(silu(gate) * up).
 //      EPI_STORE : fp32 store (LM-head logits; N a multiple of 8).
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     int y_rows = 0;
     if (g.desc != nullptr && layer == g.last_layer) {
       Y = (bf16*)g.desc->y + (int64_t)(g.desc->c - layer) * g.T * g.ldc;
-      y_rows = g.T;
+      y_rows = seg_tokens(g.desc, g.desc->c - layer, g.T);
     }
     f32x4 rb[2][PPT][2];
     auto load_pass = [&](int rc0, f32x4 (&dstv)[PPT][2]) {

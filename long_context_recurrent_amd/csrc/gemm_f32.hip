@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   if (EPI == EPI_RESID && g.desc != nullptr && layer == g.last_layer) {
     const int s = g.desc->c - layer;
     Y = (float*)g.desc->y + (int64_t)s * g.T * g.ldc;
-    y_rows = g.T;
+    y_rows = seg_tokens(g.desc, s, g.T);
   }
   for (int c = tid; c < TM * NOUT; c += 256) {
     const int r = c / NOUT, cc = c % NOUT;

@@ -85,16 +85,24 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
       const int row = r0 + r;
       const T* src;
       if (layer == 0) {
-        if (row < a.T) {
-          const int s = a.desc->c;   // layer 0 works on segment c - 0
+        const int s = a.desc->c;   // layer 0 works on segment c - 0
+        const int ts = seg_tokens(a.desc, s, a.T);
+        if (row < ts) {
           src = (const T*)a.desc->x + ((int64_t)s * a.T + row) * d;
+        } else if (row < ts + a.M) {
+          src = (const T*)a.mem_emb + (int64_t)(row - ts) * d;
         } else {
-          src = (const T*)a.mem_emb + (int64_t)(row - a.T) * d;
+          src = nullptr;             // padding row of a short last segment
         }
       } else {
         src = (const T*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)row * d;
       }
-      copy8(dst, src + c8);
+      if (src) {
+        copy8(dst, src + c8);
+      } else {
+        float zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        store8(dst, zero);
+      }
     } else {
       float zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       store8(dst, zero);
@@ -226,7 +234,9 @@ __global__ __launch_bounds__(256) void mem_keys_kernel(MemArgs a) {
   const int jg = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int d = a.d, M = a.M, dk = a.dk;
-  const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  const int ts = seg_tokens(a.desc, a.desc->c - layer, a.T);   // memory rows start here
+  if (jg == 0 && tid == 0) a.moff[layer] = ts;                 // for mem_update (next launch)
+  const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)ts * d;
   if (jg < 4) {
     for (int jj = 0; jj < 4; ++jj) {
       const int jl = 4 * w + jj, j = 16 * jg + jl;
@@ -295,7 +305,9 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
   const int i0 = blockIdx.x * 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int d = a.d, M = a.M, dk = a.dk;
-  const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  // memory rows' offset from mem_keys (this kernel advances the wave counter,
+  // so it must not derive the segment from it)
+  const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.moff[layer] * d;
 
   for (int idx = tid; idx < M * dk; idx += 256)
     ks[idx / dk][idx % dk] = a.kbuf[(int64_t)layer * M * dk + idx];
@@ -360,11 +372,12 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ void set_desc_kernel(CallDesc* desc, const void* x, void* y, int c0, int S) {
+__global__ void set_desc_kernel(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last) {
   desc->x = x;
   desc->y = y;
   desc->c = c0;
   desc->n_segments = S;
+  desc->t_last = t_last;
 }
 
 __global__ void fill_f32_kernel(float* dst, const float* src, int64_t count) {
@@ -404,8 +417,8 @@ hipError_t launch_mem_update(const MemArgs& m, bool use_bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, hipStream_t st) {
-  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, st, desc, x, y, c0, S);
+hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, hipStream_t st) {
+  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, st, desc, x, y, c0, S, t_last);
   return hipGetLastError();
 }
 

@@ -98,18 +98,25 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   const int rowc = row < a.n ? row : a.n - 1;
   const int colw = 32 * cq + 8 * g;              // + 128 s
 
-  // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0)
+  // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0; the
+  // rows after a short last segment's memory tokens are zero padding)
   float hv[NBM][8];
+  const int ts0 = layer == 0 ? seg_tokens(a.desc, a.desc->c, a.T) : 0;
 #pragma unroll
   for (int s = 0; s < NBM; ++s) {
     if (s < nb) {
       const int c = 128 * s + colw;
       if (layer == 0) {
-        const bf16* p = rowc < a.T ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + rowc) * d
-                                   : (const bf16*)a.mem_emb + (int64_t)(rowc - a.T) * d;
-        const bf16x8 x = *(const bf16x8*)(p + c);
+        if (rowc < ts0 + a.M) {
+          const bf16* p = rowc < ts0 ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + rowc) * d
+                                     : (const bf16*)a.mem_emb + (int64_t)(rowc - ts0) * d;
+          const bf16x8 x = *(const bf16x8*)(p + c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hv[s][e] = (float)x[e];
+          for (int e = 0; e < 8; ++e) hv[s][e] = (float)x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[s][e] = 0.f;
+        }
       } else {
         load8f((const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)rowc * d + c, hv[s]);
       }
@@ -287,7 +294,9 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int d = a.d, M = a.M;
-  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  const int ts = seg_tokens(a.desc, a.desc->c - layer, a.T);   // memory rows start here
+  if (jb == 0 && tid == 0) a.moff[layer] = ts;                 // for memupdate (next launch)
+  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)ts * d;
   if (jb < 4) {
     const int mblocks = (M + 15) / 16;
     // waves take interleaved 64-wide k chunks; lane group g brings
@@ -381,7 +390,9 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int d = a.d, M = a.M;
-  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.T * d;
+  // memory rows' offset from memkeys (this kernel advances the wave counter,
+  // so it must not derive the segment from it)
+  const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)a.moff[layer] * d;
   float* A = a.A + (int64_t)layer * d * 64;
 
   for (int idx = tid; idx < M * 64; idx += 256) ks[idx >> 6][idx & 63] = a.kbuf[(int64_t)layer * M * 64 + idx];

@@ -99,32 +99,44 @@ class ArmtModel(_Handle):
     def kernel_stats(self):
         return _c.armt_kernel_stats(self.handle)
 
-    def alloc_outputs(self, n_segments: int):
+    def alloc_outputs(self, n_segments: int, n_tokens: int | None = None):
         c = self.cfg
-        y = torch.empty(n_segments * c.seg_len, c.d_model, dtype=self.dtype, device=self.device)
+        rows = n_segments * c.seg_len if n_tokens is None else n_tokens
+        y = torch.empty(rows, c.d_model, dtype=self.dtype, device=self.device)
         A = torch.empty(c.n_layers, c.d_model, c.d_key, dtype=torch.float32, device=self.device)
         z = torch.empty(c.n_layers, c.d_key, dtype=torch.float32, device=self.device)
         return y, A, z
 
     def forward(self, x: torch.Tensor, schedule: str = "diagonal", A0=None, z0=None, out=None,
-                sync: bool = True):
-        """x [S*T, d] device tensor of the config dtype.  Returns (y, A, z)."""
+                sync: bool = True, by_tokens: bool | None = None):
+        """x [N, d] device tensor of the config dtype.  Returns (y, A, z).
+        N a multiple of seg_len runs through armt_forward_{diagonal,sequential};
+        any other N (or by_tokens=True) through the *_tokens entry points
+        (a shorter last segment)."""
         c = self.cfg
-        if x.dim() != 2 or x.shape[1] != c.d_model or x.shape[0] % c.seg_len:
-            raise ValueError("x must be [n_segments * seg_len, d_model]")
+        if x.dim() != 2 or x.shape[1] != c.d_model or x.shape[0] < 1:
+            raise ValueError("x must be [n_tokens, d_model]")
         if x.dtype != self.dtype or not x.is_contiguous() or x.device != self.device:
             raise ValueError("x must be a contiguous device tensor of the config dtype")
-        S = x.shape[0] // c.seg_len
-        y, A, z = out if out is not None else self.alloc_outputs(S)
+        N = x.shape[0]
+        if by_tokens is None:
+            by_tokens = N % c.seg_len != 0
+        S = -(-N // c.seg_len)
+        y, A, z = out if out is not None else self.alloc_outputs(S, N)
         for t in (A0, z0):
             if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
                 raise ValueError("A0 / z0 must be contiguous float32 device tensors")
         if schedule not in ("diagonal", "sequential"):
             raise ValueError("schedule must be 'diagonal' or 'sequential'")
-        fn = _c.armt_forward_diagonal if schedule == "diagonal" else _c.armt_forward_sequential
+        if by_tokens:
+            fn = _c.armt_forward_diagonal_tokens if schedule == "diagonal" else _c.armt_forward_sequential_tokens
+            count = N
+        else:
+            fn = _c.armt_forward_diagonal if schedule == "diagonal" else _c.armt_forward_sequential
+            count = S
         # the library's stream must see the inputs the caller's stream produced
         self.stream.wait_stream(torch.cuda.current_stream(self.device))
-        fn(self.handle, x, S, A0, z0, y, A, z)
+        fn(self.handle, x, count, A0, z0, y, A, z)
         if sync:
             self.stream.synchronize()
         else:

@@ -246,17 +246,24 @@ class Oracle:
         bf = self.cfg.dtype == "bf16"
         self.R = round_bf16 if bf else _identity         # branch activations
         self.Rs = _round_f32 if bf else _identity        # residual stream
+        self.n_tokens = inputs.x.shape[0]                # sequence length (run() sets it)
 
     def w(self, name, l):
         return np.asarray(self.inp.weights[name][l], dtype=self.dtype)
 
+    def seg_tokens(self, s):
+        """Tokens of segment s: T, or fewer in a short last segment."""
+        T = self.cfg.seg_len
+        return min(T, self.n_tokens - s * T)
+
     def node_input(self, s, prev=None):
-        """Layer-0 input of segment s: its T token rows, then the M memory
-        token rows; deeper layers take the previous layer's node output."""
+        """Layer-0 input of segment s: its T token rows (fewer in a short last
+        segment), then the M memory token rows; deeper layers take the
+        previous layer's node output."""
         if prev is not None:
             return prev
         T = self.cfg.seg_len
-        x = np.asarray(self.inp.x[s * T:(s + 1) * T], dtype=self.dtype)
+        x = np.asarray(self.inp.x[s * T:s * T + self.seg_tokens(s)], dtype=self.dtype)
         return np.concatenate([x, np.asarray(self.inp.mem_emb, dtype=self.dtype)], axis=0)
 
     def node(self, l, h_in, A, z, rows=None, trace=None):
@@ -267,8 +274,8 @@ class Oracle:
         rows) and the memory write is skipped (A_new, z_new are None).  A dict
         passed as ``trace`` receives the intermediate values by name."""
         c, Rs = self.cfg, self.Rs
-        T = c.seg_len
         h = np.asarray(h_in, dtype=self.dtype)
+        n_in = h.shape[0]
         if rows is not None:
             h = h[:rows]
         # 1. memory read
@@ -279,8 +286,8 @@ class Oracle:
         h = self.block(l, h, trace)
         if rows is not None:
             return h, None, None
-        # 4. memory write from the memory-token rows
-        A_new, z_new = mem_write(h[T:], self.w("w_mk", l), self.w("w_mv", l),
+        # 4. memory write from the memory-token rows (the node's last M rows)
+        A_new, z_new = mem_write(h[n_in - c.n_mem:], self.w("w_mk", l), self.w("w_mv", l),
                                  self.w("w_beta", l), A, z, c.mem_eps)
         return h, _round_f32(A_new), _round_f32(z_new)
 
@@ -318,43 +325,55 @@ class Oracle:
         z = [np.zeros(c.d_key, dtype=_WP) if z0 is None else _round_f32(z0[l]) for l in range(L)]
         return A, z
 
-    def run(self, order, n_segments, A0=None, z0=None):
+    def run(self, order, n_segments, A0=None, z0=None, n_tokens=None):
         """Run the nodes in ``order`` (a list of (s, l)); every node's inputs
-        must already have been produced.  Returns (Y, A, z) with Y [S*T, d] the
-        last layer's segment-token rows and A [L, d, d_k], z [L, d_k]."""
+        must already have been produced.  Returns (Y, A, z) with Y [N, d] the
+        last layer's segment-token rows (N = S*T, or ``n_tokens`` with a short
+        last segment) and A [L, d, d_k], z [L, d_k]."""
         c = self.cfg
         L = self.inp.weights["w_qkv"].shape[0]
         T = c.seg_len
+        self.n_tokens = n_segments * T if n_tokens is None else n_tokens
         A, z = self.initial_state(A0, z0)
         out = {}
-        Y = np.zeros((n_segments * T, c.d_model), dtype=_WP)
+        Y = np.zeros((self.n_tokens, c.d_model), dtype=_WP)
         for (s, l) in order:
             prev = None if l == 0 else out.pop((s, l - 1))
             h, A[l], z[l] = self.node(l, self.node_input(s, prev), A[l], z[l])
             if l == L - 1:
-                Y[s * T:(s + 1) * T] = self.R(h[:T])      # output: the stream, stored once
+                ts = self.seg_tokens(s)
+                Y[s * T:s * T + ts] = self.R(h[:ts])      # output: the stream, stored once
             else:
                 out[(s, l)] = h
         return Y, np.stack(A), np.stack(z)
 
 
-def forward_sequential(inputs, A0=None, z0=None, n_segments=None):
+def _segments(inputs, n_segments, n_tokens):
+    T = inputs.cfg.seg_len
+    if n_tokens is not None:
+        return -(-n_tokens // T)
+    return n_segments or inputs.x.shape[0] // T
+
+
+def forward_sequential(inputs, A0=None, z0=None, n_segments=None, n_tokens=None):
     """Segment-major order: for s: for l: node(s, l) -- the L*S sequential
-    steps of the baseline schedule (Pith review, Figure 3)."""
+    steps of the baseline schedule (Pith review, Figure 3).  ``n_tokens``
+    runs the first n_tokens rows of x as ceil(n_tokens / T) segments, the
+    last one shorter if T does not divide n_tokens."""
     o = Oracle(inputs)
     L = inputs.weights["w_qkv"].shape[0]
-    S = n_segments or inputs.x.shape[0] // inputs.cfg.seg_len
+    S = _segments(inputs, n_segments, n_tokens)
     order = [(s, l) for s in range(S) for l in range(L)]
-    return o.run(order, S, A0, z0)
+    return o.run(order, S, A0, z0, n_tokens)
 
 
-def forward_diagonal(inputs, A0=None, z0=None, n_segments=None, shuffle_seed=None):
+def forward_diagonal(inputs, A0=None, z0=None, n_segments=None, shuffle_seed=None, n_tokens=None):
     """Wave order: for each diagonal s + l = i, all its nodes (Pith review,
     "What carries the argument").  ``shuffle_seed`` permutes the nodes inside
     every wave, which must not change any result."""
     o = Oracle(inputs)
     L = inputs.weights["w_qkv"].shape[0]
-    S = n_segments or inputs.x.shape[0] // inputs.cfg.seg_len
+    S = _segments(inputs, n_segments, n_tokens)
     rng = None if shuffle_seed is None else np.random.default_rng(shuffle_seed)
     order = []
     for wave in waves(L, S):
@@ -362,7 +381,7 @@ def forward_diagonal(inputs, A0=None, z0=None, n_segments=None, shuffle_seed=Non
         if rng is not None:
             rng.shuffle(wave)
         order.extend(wave)
-    return o.run(order, S, A0, z0)
+    return o.run(order, S, A0, z0, n_tokens)
 
 
 def node(inputs, l, h_in, A, z, rows=None):

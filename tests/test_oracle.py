@@ -462,3 +462,34 @@ def test_llama_forward_causal_prefix_and_zero_memory_node():
     y_armt, _, _ = oracle.forward_sequential(inp, n_segments=1)
     mixed = dataclasses.replace(inp, x=np.concatenate([inp.x[:T], inp.mem_emb]))
     np.testing.assert_array_equal(oracle.llama_forward(mixed)[:T], y_armt)
+
+
+# ---------------------------------------------------------------------------
+# any sequence length: a short last segment
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,t", [("tiny_fp32", 1), ("tiny_fp32", 9), ("small_bf16", 37)])
+def test_short_last_segment_is_a_segment_of_its_own_length(name, t):
+    """n_tokens = (S-1) T + t: the first S-1 segments are exactly the (S-1)-segment
+    run, and the last is one segment of a model with seg_len = t (same weights)
+    started from the state the first S-1 segments leave."""
+    cfg = get_config(name).with_(n_segments=3)
+    T = cfg.seg_len
+    inp = make_inputs(cfg)
+    A0, z0 = make_state(cfg)
+    N = 2 * T + t
+    y, A, z = oracle.forward_sequential(inp, A0, z0, n_tokens=N)
+    assert y.shape == (N, cfg.d_model)
+    y2, A2, z2 = oracle.forward_sequential(inp, A0, z0, n_segments=2)
+    np.testing.assert_array_equal(y[:2 * T], y2)
+    short = dataclasses.replace(inp, cfg=cfg.with_(seg_len=t, n_segments=1), x=inp.x[2 * T:N])
+    y3, A3, z3 = oracle.forward_sequential(short, A2.astype(np.float32), z2.astype(np.float32))
+    np.testing.assert_array_equal(y[2 * T:], y3)
+    np.testing.assert_array_equal(A, A3)
+    np.testing.assert_array_equal(z, z3)
+    # and the schedule is still a pure reordering
+    for shuffle in (None, 3):
+        yd, Ad, zd = oracle.forward_diagonal(inp, A0, z0, n_tokens=N, shuffle_seed=shuffle)
+        np.testing.assert_array_equal(yd, y)
+        np.testing.assert_array_equal(Ad, A)
+        np.testing.assert_array_equal(zd, z)
