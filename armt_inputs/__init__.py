@@ -41,6 +41,10 @@ Optional non-zero initial memory state (for resume tests), index 2 + 9*L:
     (scaled so that a memory read from it is of the order of the residual
     stream: q.z is about 64*24 and q A^T about 8*128)
 
+Batches of independent sequences: sequence 0 is X above; sequence b >= 1 is
+drawn at index 5 + 9*L + b, N(0, 1), same shape; its optional initial state
+is ``make_state(cfg, seed=b)``.
+
 LM head (final RMSNorm + vocabulary projection after the last layer; the
 pages give no vocabulary size, so V is synthetic, ``HEAD_VOCAB``):
     index 3 + 9*L: W_lm [V, d] N(0, 0.02);  index 4 + 9*L: g_final [d] =
@@ -60,7 +64,7 @@ import os
 import numpy as np
 
 __all__ = ["ArmtConfig", "CONFIGS", "get_config", "ArmtInputs", "make_inputs",
-           "make_state", "make_head", "HEAD_VOCAB", "WEIGHT_NAMES"]
+           "make_state", "make_head", "make_batch_x", "HEAD_VOCAB", "WEIGHT_NAMES"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -231,4 +235,15 @@ def make_head(cfg: ArmtConfig, vocab: int | None = None, seed: int = 0, gain_std
     if gain_std:
         g = g + np.float32(gain_std) * _draw(seed, 4 + 9 * L, (cfg.d_model,), 1.0)
     return w_lm, _to_storage(g.astype(np.float32), cfg.dtype)
+
+
+def make_batch_x(cfg: ArmtConfig, inputs: "ArmtInputs", batch: int, seed: int = 0) -> np.ndarray:
+    """Token embeddings of ``batch`` independent sequences, [B, S*T, d]:
+    sequence 0 is ``inputs.x``, the others are drawn as the recipe says."""
+    rows, d = inputs.x.shape
+    out = np.empty((batch, rows, d), dtype=np.float32)
+    out[0] = inputs.x
+    for b in range(1, batch):
+        out[b] = _to_storage(_draw(seed, 5 + 9 * cfg.n_layers + b, (rows, d), 1.0), cfg.dtype)
+    return out
 

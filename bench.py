@@ -5,6 +5,7 @@
     python bench.py --group-sweep        # grouped kernels vs wave width k
     python bench.py --logit-drift        # LM-head logits: diag vs seq vs oracle per segment count
     python bench.py --full-attention     # full-attention Llama comparator vs diagonal ARMT, 4K..131K
+    python bench.py --batch-sweep        # B independent sequences per node, B = 1..8
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
@@ -79,6 +80,9 @@ def parse():
     ap.add_argument("--full-attention", action="store_true",
                     help="full-attention Llama comparator against the diagonal ARMT forward at 4K..131K "
                          "tokens (1B shape): time, speed-up and workspace memory, one JSON line per length")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="diagonal forward of B = 1, 2, 4, 8 independent 32-segment sequences per node "
+                         "(1B shape): total tokens/s against the batch size")
     ap.add_argument("--traffic-record", metavar="DIR",
                     help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
                          "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
@@ -562,6 +566,48 @@ def full_attention(args, dev):
     armt.close()
 
 
+def batch_sweep(args, dev):
+    """B independent sequences of 32 segments (1B shape) in one batched
+    handle: the grouped kernels see P layers x B sequences per launch."""
+    import gc
+    import numpy as np
+    import torch
+    from armt_inputs import get_config, make_batch_x, make_inputs
+    from long_context_recurrent_amd.model import ArmtModel
+    cfg = get_config("1b_s32")
+    S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
+    inp = make_inputs(cfg)
+    base = build(inp, cfg, dev)
+    w, ccfg = base.weights, base.cfg
+    xs_all = make_batch_x(cfg, inp, 8)
+    base.close()
+    for B in (1, 2, 4, 8):
+        model = ArmtModel(ccfg, w, batch=B)
+        x = to_dev(np.ascontiguousarray(xs_all[:B]) if B > 1 else xs_all[0], dev)
+        out = model.alloc_outputs(S)
+        run = lambda: model.forward(x, "diagonal", out=out, sync=False)
+        run()
+        torch.cuda.synchronize()
+        each = []
+        for _ in range(max(1, min(args.steps, 3))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            e1.synchronize()
+            each.append(e0.elapsed_time(e1) * 1e-3)
+        t = statistics.median(each)
+        tokens = B * S * T
+        line = {"workload": "1b_s32", "batch": B, "tokens": tokens, "ms": t * 1e3, "tokens_per_s": tokens / t,
+                "tflops": node_gflop(cfg) * S * L * B / t / 1e3, "workspace_bytes": model.ws_bytes}
+        log(f"B={B}: {t * 1e3:.1f} ms, {tokens / t:.0f} tokens/s, {line['tflops']:.0f} TFLOP/s")
+        print(json.dumps(line), flush=True)
+        model.close()
+        del model, x, out
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
 def group_sweep(args, dev):
     """Grouped GEMM and attention throughput against the wave width k: a
     model of the first k layers of the 1B shape, run diagonally over 32 k
@@ -619,6 +665,8 @@ def main():
         logit_drift(args, dev)
     elif args.full_attention:
         full_attention(args, dev)
+    elif args.batch_sweep:
+        batch_sweep(args, dev)
     elif args.group_sweep:
         group_sweep(args, dev)
     else:

@@ -119,6 +119,23 @@ int armt_workspace_size(const armt_config *cfg, size_t *bytes);
 int armt_create(const armt_config *cfg, const armt_weights *w, void *workspace,
                 size_t ws_bytes, void *hip_stream, armt_handle **out);
 
+/* Several independent sequences per node (batch B): each node (s, l) runs
+ * segment s of all B sequences through layer l, each sequence with its own
+ * memory state, in the same grouped launches (the kernels see P layers x B
+ * sequences).  The pages contrast diagonal batching with batching several
+ * requests (paper page, abstract; skill page, Practical Guidance); both
+ * compose.  armt_workspace_size_batched / armt_create_batched are
+ * armt_workspace_size / armt_create for a batch of 1 <= batch <= 1024; the
+ * forward calls of such a handle take
+ *   x, y         [B][rows][d]   (rows = n_segments * T, or n_tokens)
+ *   A0, A_out    [L][B][d][d_k] fp32;  z0, z_out [L][B][d_k] fp32
+ * and all B sequences have the same length.  With B = 1 everything is as
+ * documented for the unbatched calls. */
+int armt_workspace_size_batched(const armt_config *cfg, int32_t batch, size_t *bytes);
+int armt_create_batched(const armt_config *cfg, const armt_weights *w, int32_t batch,
+                        void *workspace, size_t ws_bytes, void *hip_stream,
+                        armt_handle **out);
+
 /* Forward over n_segments segments in segment-major order: for s, for l,
  * node(s, l) -- the S*L-step baseline schedule (Pith review, Figure 3).
  *   x     [n_segments * T, d]  input token embeddings (config dtype)

@@ -14,7 +14,8 @@ import re
 
 __all__ = [
     "ArmtError", "armt_config", "armt_weights", "load_library", "library_path",
-    "armt_workspace_size", "armt_create", "armt_forward_sequential",
+    "armt_workspace_size", "armt_create", "armt_workspace_size_batched", "armt_create_batched",
+    "armt_forward_sequential",
     "armt_forward_diagonal", "armt_forward_sequential_tokens", "armt_forward_diagonal_tokens", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
     "armt_llama_forward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
@@ -73,6 +74,9 @@ def load_library():
         "armt_workspace_size": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(SZ)]),
         "armt_create": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), P, SZ, P,
                               ctypes.POINTER(P)]),
+        "armt_workspace_size_batched": (I32, [ctypes.POINTER(armt_config), I32, ctypes.POINTER(SZ)]),
+        "armt_create_batched": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), I32, P, SZ, P,
+                                      ctypes.POINTER(P)]),
         "armt_forward_sequential": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_diagonal": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_sequential_tokens": (I32, [P, P, ctypes.c_int64, P, P, P, P, P]),
@@ -142,6 +146,19 @@ def armt_create(cfg: armt_config, w: armt_weights, workspace, ws_bytes: int, str
     h = ctypes.c_void_p(0)
     _check(load_library().armt_create(ctypes.byref(cfg), ctypes.byref(w), _ptr(workspace), ws_bytes,
                                       _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def armt_workspace_size_batched(cfg: armt_config, batch: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().armt_workspace_size_batched(ctypes.byref(cfg), batch, ctypes.byref(n)))
+    return n.value
+
+
+def armt_create_batched(cfg: armt_config, w: armt_weights, batch: int, workspace, ws_bytes: int, stream=None):
+    h = ctypes.c_void_p(0)
+    _check(load_library().armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), batch, _ptr(workspace), ws_bytes,
+                                              _stream(stream), ctypes.byref(h)))
     return h.value
 
 

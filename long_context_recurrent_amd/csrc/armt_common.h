@@ -32,11 +32,12 @@ __device__ __forceinline__ float sigmoid_f(float u) { return 1.f / (1.f + __expf
 // of layer l works on segment s = c - l.  Kept in device memory so captured
 // graphs can be replayed for any call and any wave of the same shape.
 struct CallDesc {
-  const void* x;   // [(S-1)*T + t_last, d]
-  void* y;         // same rows as x
-  int32_t c;       // current wave (diagonal) or s + l (sequential)
+  const void* x;     // [B][(S-1)*T + t_last][d]
+  void* y;           // same layout as x
+  int64_t seq_rows;  // rows of one sequence in x and y ((S-1)*T + t_last)
+  int32_t c;         // current wave (diagonal) or s + l (sequential)
   int32_t n_segments;
-  int32_t t_last;  // tokens of the last segment (1..T)
+  int32_t t_last;    // tokens of the last segment (1..T)
 };
 
 // Tokens of segment s: T, except a shorter last segment.  The node keeps its

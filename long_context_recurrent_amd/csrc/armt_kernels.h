@@ -1,11 +1,12 @@
 // Launch-argument structs and host launchers of the ARMT kernels (internal to
 // libarmt.so; the public boundary is include/armt.h).
 //
-// Every kernel works on the P consecutive layers l0 .. l0+P-1 of one wave.
-// Buffers indexed "by layer" hold one [n, ...] slab per layer at a fixed
-// stride, so a node's kernels read and write the same addresses whatever the
-// wave width -- the grouped launch and the one-node launch compute bitwise
-// identical results.
+// Every kernel works on the P consecutive layers l0 .. l0+P-1 of one wave, and
+// on every sequence of the batch: problem p = layer * batch + sequence.
+// Buffers indexed "by problem" hold one [n, ...] slab per problem at a fixed
+// stride, weights are indexed by layer, so a node's kernels read and write the
+// same addresses whatever the wave width -- the grouped launch and the
+// one-node launch compute bitwise identical results.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,7 +20,8 @@ namespace armt {
 enum { EPI_STORE = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
-  int P, l0;                 // problems = layers l0 .. l0+P-1
+  int P, l0;                 // layers l0 .. l0+P-1, each with `batch` problems
+  int batch;                 // sequences per node: problem = layer * batch + sequence
   const void* A;             // activations, layer l at A + l * a_stride
   int64_t a_stride;
   int lda;
@@ -60,7 +62,8 @@ struct AttnArgs {
 };
 
 struct MemArgs {
-  int P, l0;
+  int P, l0;                 // problems l0 .. l0+P-1, problem = layer * batch + sequence
+  int batch;                 // sequences per node (weights are indexed by problem / batch)
   int n, d, T, M, dk, L;
   const void* act_prev;      // previous-wave slot [L][n][d] (layer l reads l-1)
   void* act_cur;             // this wave's slot [L][n][d]
@@ -110,7 +113,8 @@ hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st);
 hipError_t launch_final_norm(const NormArgs& a, bool use_bf16, hipStream_t st);
 // dst[i] = (float)src[i], count a multiple of 8
 hipError_t launch_widen(const void* src, float* dst, int64_t count, bool use_bf16, hipStream_t st);
-hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, hipStream_t st);
+hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, int64_t seq_rows,
+                           hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
 
 }  // namespace armt

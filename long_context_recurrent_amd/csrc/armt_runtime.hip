@@ -92,8 +92,9 @@ int validate_config(const armt_config* c) {
   return ARMT_OK;
 }
 
-Layout make_layout(const armt_config* c) {
-  const size_t L = c->n_layers, d = c->d_model, n = c->seg_len + c->n_mem;
+// Buffers with a slab per (layer, sequence) problem: L * batch slabs.
+Layout make_layout(const armt_config* c, int batch) {
+  const size_t L = (size_t)c->n_layers * batch, d = c->d_model, n = c->seg_len + c->n_mem;
   const size_t n_pad = (n + 63) / 64 * 64;
   const size_t es = c->dtype == ARMT_BF16 ? 2 : 4;
   const size_t qkv_dim = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
@@ -187,6 +188,7 @@ struct armt_handle {
   int device = 0;
   bool bf16 = true;
   int n = 0, n_pad = 0, qkv_dim = 0, mb = 0, cus = 256;   // mb 0: per-launch choice
+  int batch = 1;            // sequences per node
   bool llama = false;       // full-attention comparator handle (armt_llama_create)
   int64_t norm_rows = 0;    // rows of the normalised-activation buffer
   size_t es = 2;
@@ -243,7 +245,7 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
 int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus);
 
 int gemm_rows(const armt_handle* h, int n_cols, int cols_per_tile, int P) {
-  return h->mb ? h->mb : pick_row_blocks(h->n, n_cols, cols_per_tile, P, h->cus);
+  return h->mb ? h->mb : pick_row_blocks(h->n, n_cols, cols_per_tile, P * h->batch, h->cus);
 }
 
 struct StepCtx {
@@ -309,13 +311,16 @@ hipError_t run_mem(const void* p, hipStream_t st) {
 hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   armt_handle* h = cx.h;
   const armt_config& c = h->cfg;
-  const int P = l_hi - l_lo + 1;
+  const int P = l_hi - l_lo + 1, B = h->batch;
   const int d = c.d_model, n = h->n, F = c.ffn_hidden, hhd = c.n_heads * c.head_dim;
   const int64_t nd = (int64_t)n * d;
   const size_t es = h->es;
 
+  // memory kernels and attention: one problem per (layer, sequence); GEMMs:
+  // P layers x B sequences
   MemArgs m{};
-  m.P = P; m.l0 = l_lo; m.n = n; m.d = d; m.T = c.seg_len; m.M = c.n_mem; m.dk = c.d_key; m.L = c.n_layers;
+  m.P = P * B; m.l0 = l_lo * B; m.batch = B;
+  m.n = n; m.d = d; m.T = c.seg_len; m.M = c.n_mem; m.dk = c.d_key; m.L = c.n_layers;
   m.act_prev = h->act[par ^ 1]; m.act_cur = h->act[par]; m.abuf = h->abuf; m.act_stride = nd;
   m.mem_emb = h->w.mem_emb; m.w_mq = h->w.w_mq; m.w_mk = h->w.w_mk; m.w_mv = h->w.w_mv; m.w_beta = h->w.w_beta;
   m.A = h->A; m.z = h->z; m.qbuf = h->qbuf; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
@@ -323,7 +328,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   m.mem_eps = c.mem_eps; m.rms_eps = c.rms_eps; m.advance = 0;
 
   GemmArgs g0{};
-  g0.P = P; g0.l0 = l_lo; g0.M = n; g0.T = c.seg_len; g0.last_layer = c.n_layers - 1;
+  g0.P = P; g0.l0 = l_lo; g0.batch = B; g0.M = n; g0.T = c.seg_len; g0.last_layer = c.n_layers - 1;
   g0.head_dim = c.head_dim;
 
   hipError_t e;
@@ -331,11 +336,11 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   {
     MemCall mc{h, m, ARMT_K_MEM_READ};
     mc.m.gain = h->w.g_attn;
-    if ((e = timed(cx, ARMT_K_MEM_READ, P, run_mem, &mc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_MEM_READ, P * B, run_mem, &mc)) != hipSuccess) return e;
     if (!h->bf16) {
       MemCall nc{h, m, ARMT_K_ATTN_NORM};
       nc.m.gain = h->w.g_attn;
-      if ((e = timed(cx, ARMT_K_ATTN_NORM, P, run_mem, &nc)) != hipSuccess) return e;
+      if ((e = timed(cx, ARMT_K_ATTN_NORM, P * B, run_mem, &nc)) != hipSuccess) return e;
     }
   }
   // 2. QKV projection with RoPE
@@ -348,18 +353,18 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
     g.rope_cs = h->rope; g.rope_cols = (c.n_heads + c.n_kv_heads) * c.head_dim;
     g.v_col0 = g.rope_cols; g.vt = h->vt; g.vt_ld = h->n_pad;
     g.vt_stride = (int64_t)c.n_kv_heads * c.head_dim * h->n_pad;
-    if ((e = timed(cx, ARMT_K_QKV, P, run_gemm, &gc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_QKV, P * B, run_gemm, &gc)) != hipSuccess) return e;
   }
   // 3. attention
   {
     AttnCall ac{h, {}};
     AttnArgs& a = ac.a;
-    a.P = P; a.l0 = l_lo; a.qkv = h->qkv; a.qkv_stride = (int64_t)n * h->qkv_dim; a.ld_qkv = h->qkv_dim;
+    a.P = P * B; a.l0 = l_lo * B; a.qkv = h->qkv; a.qkv_stride = (int64_t)n * h->qkv_dim; a.ld_qkv = h->qkv_dim;
     a.vt = h->vt; a.vt_stride = (int64_t)c.n_kv_heads * c.head_dim * h->n_pad; a.vt_ld = h->n_pad;
     a.out = h->attn; a.out_stride = (int64_t)n * hhd; a.ld_out = hhd;
     a.n = n; a.H = c.n_heads; a.G = c.n_kv_heads; a.hd = c.head_dim;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
-    if ((e = timed(cx, ARMT_K_ATTN, P, run_attn, &ac)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_ATTN, P * B, run_attn, &ac)) != hipSuccess) return e;
   }
   // 4. output projection + residual
   {
@@ -368,13 +373,13 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
     g.A = h->attn; g.a_stride = (int64_t)n * hhd; g.lda = hhd;
     g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
     g.C = h->act[par]; g.c_stride = nd; g.ldc = d; g.desc = nullptr;
-    if ((e = timed(cx, ARMT_K_OPROJ, P, run_gemm, &gc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_OPROJ, P * B, run_gemm, &gc)) != hipSuccess) return e;
   }
   // 5. MLP norm
   {
     MemCall mc{h, m, ARMT_K_MLP_NORM};
     mc.m.gain = h->w.g_mlp;
-    if ((e = timed(cx, ARMT_K_MLP_NORM, P, run_mem, &mc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_MLP_NORM, P * B, run_mem, &mc)) != hipSuccess) return e;
   }
   // 6. gate/up + SiLU product
   {
@@ -383,7 +388,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
     g.A = h->abuf; g.a_stride = nd; g.lda = d;
     g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
     g.C = h->ubuf; g.c_stride = (int64_t)n * F; g.ldc = F;
-    if ((e = timed(cx, ARMT_K_GATE_UP, P, run_gemm, &gc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_GATE_UP, P * B, run_gemm, &gc)) != hipSuccess) return e;
   }
   // 7. down projection + residual (+ y rows of the last layer)
   {
@@ -392,15 +397,15 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
     g.A = h->ubuf; g.a_stride = (int64_t)n * F; g.lda = F;
     g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
     g.C = h->act[par]; g.c_stride = nd; g.ldc = d; g.desc = h->desc;
-    if ((e = timed(cx, ARMT_K_DOWN, P, run_gemm, &gc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_DOWN, P * B, run_gemm, &gc)) != hipSuccess) return e;
   }
   // 8-9. memory write
   {
     MemCall mc{h, m, ARMT_K_MEM_KEYS};
-    if ((e = timed(cx, ARMT_K_MEM_KEYS, P, run_mem, &mc)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_MEM_KEYS, P * B, run_mem, &mc)) != hipSuccess) return e;
     MemCall mu{h, m, ARMT_K_MEM_UPDATE};
     mu.m.advance = advance;
-    if ((e = timed(cx, ARMT_K_MEM_UPDATE, P, run_mem, &mu)) != hipSuccess) return e;
+    if ((e = timed(cx, ARMT_K_MEM_UPDATE, P * B, run_mem, &mu)) != hipSuccess) return e;
   }
   (void)es;
   return hipSuccess;
@@ -417,18 +422,18 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
   const int L = c.n_layers, d = c.d_model, F = c.ffn_hidden, hhd = c.n_heads * c.head_dim;
   hipError_t e;
   // the descriptor points the last layer's down projection at y (segment 0)
-  if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, N, cx.st)) != hipSuccess) return e;
+  if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, N, N, cx.st)) != hipSuccess) return e;
   if ((e = launch_widen(x, (float*)h->act[0], (int64_t)N * d, h->bf16, cx.st)) != hipSuccess) return e;
   auto rows = [&](int n_cols, int cols_per_tile) {
     return h->mb ? h->mb : pick_row_blocks(N, n_cols, cols_per_tile, 1, h->cus);
   };
   for (int l = 0; l < L; ++l) {
     MemArgs m{};
-    m.P = 1; m.l0 = l; m.n = N; m.d = d; m.T = N; m.L = L;
+    m.P = 1; m.l0 = l; m.batch = 1; m.n = N; m.d = d; m.T = N; m.L = L;
     m.act_cur = h->act[0]; m.act_prev = h->act[0]; m.abuf = h->abuf; m.act_stride = 0;
     m.rms_eps = c.rms_eps;
     GemmArgs g0{};
-    g0.P = 1; g0.l0 = l; g0.M = N; g0.T = N; g0.last_layer = L - 1; g0.head_dim = c.head_dim;
+    g0.P = 1; g0.l0 = l; g0.batch = 1; g0.M = N; g0.T = N; g0.last_layer = L - 1; g0.head_dim = c.head_dim;
     // attention block
     m.gain = h->w.g_attn;
     if ((e = launch_rmsnorm(m, h->bf16, cx.st)) != hipSuccess) return e;
@@ -524,8 +529,10 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, int32_t t_last,
   const int L = c.n_layers;
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-  const int64_t a_count = (int64_t)L * c.d_model * c.d_key, z_count = (int64_t)L * c.d_key;
-  if ((e = launch_set_desc(h->desc, x, y, 0, S, t_last, h->stream)) != hipSuccess) return hip_fail(e, "set_desc");
+  const int64_t a_count = (int64_t)L * h->batch * c.d_model * c.d_key, z_count = (int64_t)L * h->batch * c.d_key;
+  const int64_t seq_rows = (int64_t)(S - 1) * c.seg_len + t_last;
+  if ((e = launch_set_desc(h->desc, x, y, 0, S, t_last, seq_rows, h->stream)) != hipSuccess)
+    return hip_fail(e, "set_desc");
   if ((e = launch_fill_f32(h->A, A0, a_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
   if ((e = launch_fill_f32(h->z, z0, z_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
   int rc;
@@ -579,13 +586,16 @@ int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus) {
 
 extern "C" {
 
-int armt_workspace_size(const armt_config* cfg, size_t* bytes) {
+int armt_workspace_size_batched(const armt_config* cfg, int32_t batch, size_t* bytes) {
   int rc = validate_config(cfg);
   if (rc != ARMT_OK) return rc;
+  if (batch < 1 || batch > 1024) return fail(ARMT_E_INVALID, "batch must be in 1..1024 (got %d)", batch);
   if (!bytes) return fail(ARMT_E_INVALID, "bytes is NULL");
-  *bytes = make_layout(cfg).total;
+  *bytes = make_layout(cfg, batch).total;
   return ARMT_OK;
 }
+
+int armt_workspace_size(const armt_config* cfg, size_t* bytes) { return armt_workspace_size_batched(cfg, 1, bytes); }
 
 }  // extern "C"
 
@@ -669,18 +679,25 @@ extern "C" {
 
 int armt_create(const armt_config* cfg, const armt_weights* w, void* workspace, size_t ws_bytes,
                 void* hip_stream, armt_handle** out) {
+  return armt_create_batched(cfg, w, 1, workspace, ws_bytes, hip_stream, out);
+}
+
+int armt_create_batched(const armt_config* cfg, const armt_weights* w, int32_t batch, void* workspace,
+                        size_t ws_bytes, void* hip_stream, armt_handle** out) {
   int rc = validate_config(cfg);
   if (rc != ARMT_OK) return rc;
+  if (batch < 1 || batch > 1024) return fail(ARMT_E_INVALID, "batch must be in 1..1024 (got %d)", batch);
   if (!w || !out) return fail(ARMT_E_INVALID, "weights and out must not be NULL");
   const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn,
                         w->g_mlp, w->w_mq, w->w_mk, w->w_mv, w->w_beta, w->mem_emb};
   for (const void* p : ptrs)
     if (!p) return fail(ARMT_E_INVALID, "every weight pointer must be non-NULL");
-  const Layout lo = make_layout(cfg);
+  const Layout lo = make_layout(cfg, batch);
   if ((rc = check_workspace(lo, workspace, ws_bytes)) != ARMT_OK) return rc;
   armt_handle* h = new (std::nothrow) armt_handle();
   if (!h) return fail(ARMT_E_INVALID, "out of host memory");
-  h->norm_rows = (int64_t)cfg->n_layers * (cfg->seg_len + cfg->n_mem);
+  h->batch = batch;
+  h->norm_rows = (int64_t)cfg->n_layers * batch * (cfg->seg_len + cfg->n_mem);
   return init_handle(h, cfg, w, lo, workspace, hip_stream, cfg->seg_len + cfg->n_mem, out);
 }
 
@@ -777,7 +794,7 @@ int armt_logits(armt_handle* h, const void* y, int64_t rows, const void* g_final
     na.eps = c.rms_eps;
     if ((e = launch_final_norm(na, h->bf16, h->stream)) != hipSuccess) return hip_fail(e, "final norm launch");
     GemmArgs g{};
-    g.P = 1; g.l0 = 0;
+    g.P = 1; g.l0 = 0; g.batch = 1;
     g.A = h->abuf; g.a_stride = 0; g.lda = d;
     g.B = w_lm; g.b_stride = 0;
     g.M = m; g.N = vocab; g.K = d;

@@ -20,8 +20,9 @@
 //    rows hit 16 different bank groups.  The fragments of the next stage are
 //    read while the MFMAs of the current one run.
 //  * Schedule: tiles are numbered so that each of the 8 XCDs works through a
-//    contiguous range (same layer, same weight columns, neighbouring rows),
-//    keeping the shared operand tiles in that XCD's L2.
+//    contiguous range (same layer, same weight columns, neighbouring rows of
+//    every sequence of the batch), keeping the shared operand tiles in that
+//    XCD's L2.
 //  * Epilogue: fp32 results are staged through LDS, so every global store is a
 //    coalesced 16-byte write and every bf16 rounding happens once, on the fp32
 //    value:
@@ -133,16 +134,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  // logical tile order: row tile fastest, then sequence, then column tile,
+  // then layer -- the row tiles of every sequence that share one weight tile
+  // are neighbours
   const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_mb = tiles_m * g.batch;
   const int tiles_n = (g.N + BN_OUT - 1) / BN_OUT;
-  const int logical = xcd_tile(blockIdx.x, tiles_m * tiles_n * g.P);
-  const int tm = logical % tiles_m;
-  const int tn = (logical / tiles_m) % tiles_n;
-  const int layer = g.l0 + logical / (tiles_m * tiles_n);
+  const int logical = xcd_tile(blockIdx.x, tiles_mb * tiles_n * g.P);
+  const int tmb = logical % tiles_mb;
+  const int tm = tmb % tiles_m, seq = tmb / tiles_m;
+  const int tn = (logical / tiles_mb) % tiles_n;
+  const int layer = g.l0 + logical / (tiles_mb * tiles_n);   // model layer (weights)
+  const int prob = layer * g.batch + seq;                      // (layer, sequence) problem
   const int m0 = tm * BM;
   const int n0 = tn * BN_OUT;
 
-  const bf16* __restrict__ A = (const bf16*)g.A + (int64_t)layer * g.a_stride;
+  const bf16* __restrict__ A = (const bf16*)g.A + (int64_t)prob * g.a_stride;
   const bf16* __restrict__ B = (const bf16*)g.B + (int64_t)layer * g.b_stride;
   const bf16* __restrict__ B2 =
       (EPI == EPI_SWIGLU) ? (const bf16*)g.B2 + (int64_t)layer * g.b_stride : B;
@@ -273,11 +280,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     // rounded once to bf16.
     constexpr int NPASS = (BM + RC - 1) / RC;
     constexpr int PPT = RC * (BN_OUT / 8) / 256;     // pieces per thread per pass
-    float* Cf = (float*)g.C + (int64_t)layer * g.c_stride;
+    float* Cf = (float*)g.C + (int64_t)prob * g.c_stride;
     bf16* Y = nullptr;
     int y_rows = 0;
     if (g.desc != nullptr && layer == g.last_layer) {
-      Y = (bf16*)g.desc->y + (int64_t)(g.desc->c - layer) * g.T * g.ldc;
+      Y = (bf16*)g.desc->y + ((int64_t)seq * g.desc->seq_rows + (int64_t)(g.desc->c - layer) * g.T) * g.ldc;
       y_rows = seg_tokens(g.desc, g.desc->c - layer, g.T);
     }
     f32x4 rb[2][PPT][2];
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
     const int rows_here = (BM - rc0) < RC ? (BM - rc0) : RC;
     constexpr int PIECES_ROW = BN_OUT / 8;
-    bf16* C = (bf16*)g.C + (int64_t)layer * g.c_stride;
+    bf16* C = (bf16*)g.C + (int64_t)prob * g.c_stride;
     if (EPI == EPI_QKV) {
       // Q and K columns: RoPE with the partner column i +- hd/2 of the same
       // head (heads never straddle the 256-column tile: hd divides 256)
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       // piece.  Within every aligned group of 16 keys the stored order is
       // 0-3, 8-11, 4-7, 12-15 (the k-slot order of the attention kernel's
       // P V product), so keys m..m+3 and m+4..m+7 go to two 8-byte runs.
-      bf16* Vt = (bf16*)g.vt + (int64_t)layer * g.vt_stride;
+      bf16* Vt = (bf16*)g.vt + (int64_t)prob * g.vt_stride;
       const int rgroups = (rows_here + 7) / 8;
       for (int pc = tid; pc < rgroups * BN_OUT; pc += 256) {
         const int col = pc % BN_OUT, rg = pc / BN_OUT;
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       }
     } else if (EPI == EPI_STORE) {
       // fp32 output (LM-head logits)
-      float* Cf = (float*)g.C + (int64_t)layer * g.c_stride;
+      float* Cf = (float*)g.C + (int64_t)prob * g.c_stride;
       for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
@@ -442,7 +449,7 @@ template <int MB, int EPI>
 static hipError_t launch_mb(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 32 * MB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN_OUT - 1) / BN_OUT) * g.P;
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN_OUT - 1) / BN_OUT) * g.P * g.batch;
   hipLaunchKernelGGL((gemm_bf16_kernel<MB, EPI>), dim3(tiles), dim3(256), 0, st, g);
   return hipGetLastError();
 }
@@ -465,7 +472,7 @@ const int kGemmRowBlocksCount = 6;
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int mb, hipStream_t st) {
   // K must be a multiple of 64 (two pipeline stages per loop trip)
-  if (g.P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % (2 * BK)) return hipErrorInvalidValue;
+  if (g.P <= 0 || g.batch <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % (2 * BK)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV:
       if (g.head_dim <= 0 || 256 % g.head_dim) return hipErrorInvalidValue;

@@ -24,10 +24,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int tx = tid & 31, ty = tid >> 5;
-  const int layer = g.l0 + blockIdx.z;
+  const int prob = g.l0 * g.batch + blockIdx.z;   // (layer, sequence) problem
+  const int layer = prob / g.batch, seq = prob - layer * g.batch;
   const int m0 = blockIdx.x * TM;
   const int n0 = blockIdx.y * NOUT;
-  const float* A = (const float*)g.A + (int64_t)layer * g.a_stride;
+  const float* A = (const float*)g.A + (int64_t)prob * g.a_stride;
   const float* B = (const float*)g.B + (int64_t)layer * g.b_stride;
   const float* B2 = (EPI == EPI_SWIGLU) ? (const float*)g.B2 + (int64_t)layer * g.b_stride : B;
 
@@ -72,12 +73,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) Cs[ty * 4 + i][tx * 4 + j] = acc[i][j];
   __syncthreads();
 
-  float* C = (float*)g.C + (int64_t)layer * g.c_stride;
+  float* C = (float*)g.C + (int64_t)prob * g.c_stride;
   float* Y = nullptr;
   int y_rows = 0;
   if (EPI == EPI_RESID && g.desc != nullptr && layer == g.last_layer) {
     const int s = g.desc->c - layer;
-    Y = (float*)g.desc->y + (int64_t)s * g.T * g.ldc;
+    Y = (float*)g.desc->y + ((int64_t)seq * g.desc->seq_rows + (int64_t)s * g.T) * g.ldc;
     y_rows = seg_tokens(g.desc, s, g.T);
   }
   for (int c = tid; c < TM * NOUT; c += 256) {
@@ -109,9 +110,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, int epi, hipStream_t st) {
-  if (g.P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0) return hipErrorInvalidValue;
+  if (g.P <= 0 || g.batch <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0) return hipErrorInvalidValue;
   const int nout = (epi == EPI_SWIGLU) ? TN / 2 : TN;
-  dim3 grid((g.M + TM - 1) / TM, (g.N + nout - 1) / nout, g.P);
+  dim3 grid((g.M + TM - 1) / TM, (g.N + nout - 1) / nout, g.P * g.batch);
   switch (epi) {
     case EPI_QKV:
       if (g.head_dim > TN || TN % g.head_dim) return hipErrorInvalidValue;

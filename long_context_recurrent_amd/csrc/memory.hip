@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
   float* qs = (float*)(smem_raw + (size_t)RB * d * sizeof(T));   // [RB][64]
   float* dens = qs + RB * 64;                             // [RB]
 
-  const int layer = a.l0 + blockIdx.y;
+  const int layer = a.l0 + blockIdx.y;          // (layer, sequence) problem
+  const int wl = layer / a.batch;                // model layer
   const int r0 = blockIdx.x * RB;
   const int nr = min(RB, a.n - r0);
   const int tid = threadIdx.x;
@@ -84,18 +85,19 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
     if (r < nr) {
       const int row = r0 + r;
       const T* src;
-      if (layer == 0) {
+      if (wl == 0) {
         const int s = a.desc->c;   // layer 0 works on segment c - 0
         const int ts = seg_tokens(a.desc, s, a.T);
         if (row < ts) {
-          src = (const T*)a.desc->x + ((int64_t)s * a.T + row) * d;
+          // at layer 0 the problem index is the sequence index
+          src = (const T*)a.desc->x + ((int64_t)layer * a.desc->seq_rows + (int64_t)s * a.T + row) * d;
         } else if (row < ts + a.M) {
           src = (const T*)a.mem_emb + (int64_t)(row - ts) * d;
         } else {
           src = nullptr;             // padding row of a short last segment
         }
       } else {
-        src = (const T*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)row * d;
+        src = (const T*)a.act_prev + (int64_t)(layer - a.batch) * a.act_stride + (int64_t)row * d;
       }
       if (src) {
         copy8(dst, src + c8);
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void mem_read_kernel(MemArgs a) {
   // (b) q = phi(h W_mq^T): lane group of 4 per key column j, interleaved k
   {
     const int j = tid >> 2, kq = tid & 3;
-    const T* wrow = (const T*)a.w_mq + ((int64_t)layer * dk + j) * d;
+    const T* wrow = (const T*)a.w_mq + ((int64_t)wl * dk + j) * d;
     float u[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) u[r] = 0.f;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(MemArgs a) {
   }
   ss = wave_sum(ss);
   const float rs = rsqrtf(ss / (float)d + a.rms_eps);
-  const T* gain = (const T*)a.gain + (int64_t)layer * d;
+  const T* gain = (const T*)a.gain + (int64_t)(layer / a.batch) * d;
   T* o = (T*)a.abuf + off;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
@@ -234,13 +236,14 @@ __global__ __launch_bounds__(256) void mem_keys_kernel(MemArgs a) {
   const int jg = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int d = a.d, M = a.M, dk = a.dk;
-  const int ts = seg_tokens(a.desc, a.desc->c - layer, a.T);   // memory rows start here
+  const int wl = layer / a.batch;
+  const int ts = seg_tokens(a.desc, a.desc->c - wl, a.T);      // memory rows start here
   if (jg == 0 && tid == 0) a.moff[layer] = ts;                 // for mem_update (next launch)
   const T* Y = (const T*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)ts * d;
   if (jg < 4) {
     for (int jj = 0; jj < 4; ++jj) {
       const int jl = 4 * w + jj, j = 16 * jg + jl;
-      const T* wk = (const T*)a.w_mk + ((int64_t)layer * dk + j) * d;
+      const T* wk = (const T*)a.w_mk + ((int64_t)wl * dk + j) * d;
       for (int m = 0; m < M; ++m) {
         float s = 0.f;
         for (int k = lane * 8; k < d; k += 512) {
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(256) void mem_keys_kernel(MemArgs a) {
       z[tid] = z[tid] + s;
     }
   } else {
-    const T* wb = (const T*)a.w_beta + (int64_t)layer * d;
+    const T* wb = (const T*)a.w_beta + (int64_t)wl * d;
     for (int m = w; m < M; m += 4) {
       float s = 0.f;
       for (int k = lane * 8; k < d; k += 512) {
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
   }
 
   // v_m[i] for the wave's 4 rows, memory tokens in chunks of 16
-  const T* wv_base = (const T*)a.w_mv + (int64_t)layer * d * d;
+  const T* wv_base = (const T*)a.w_mv + (int64_t)(layer / a.batch) * d * d;
   for (int mc = 0; mc < M; mc += 16) {
     float acc[16][4];
 #pragma unroll
@@ -372,9 +375,11 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ void set_desc_kernel(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last) {
+__global__ void set_desc_kernel(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last,
+                                int64_t seq_rows) {
   desc->x = x;
   desc->y = y;
+  desc->seq_rows = seq_rows;
   desc->c = c0;
   desc->n_segments = S;
   desc->t_last = t_last;
@@ -387,6 +392,7 @@ __global__ void fill_f32_kernel(float* dst, const float* src, int64_t count) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_mem_read(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (m.P <= 0 || m.batch <= 0 || m.l0 < 0) return hipErrorInvalidValue;
   if (use_bf16) return launch_mem_read_bf16(m, st);
   const size_t lds = (size_t)RB * m.d * sizeof(float) + (RB * 64 + RB) * sizeof(float);
   if (lds > 64 * 1024 || m.dk != 64 || m.d % 8) return hipErrorInvalidValue;
@@ -396,6 +402,7 @@ hipError_t launch_mem_read(const MemArgs& m, bool use_bf16, hipStream_t st) {
 }
 
 hipError_t launch_rmsnorm(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (m.P <= 0 || m.batch <= 0 || m.l0 < 0) return hipErrorInvalidValue;
   if (m.d > 4096 || m.d % 8) return hipErrorInvalidValue;
   dim3 grid((m.n + 3) / 4, m.P);
   if (use_bf16) hipLaunchKernelGGL(rmsnorm_kernel<bf16>, grid, dim3(256), 0, st, m);
@@ -404,6 +411,7 @@ hipError_t launch_rmsnorm(const MemArgs& m, bool use_bf16, hipStream_t st) {
 }
 
 hipError_t launch_mem_keys(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (m.P <= 0 || m.batch <= 0 || m.l0 < 0) return hipErrorInvalidValue;
   if (use_bf16) return launch_mem_keys_bf16(m, st);
   if (m.dk != 64 || m.M > 64 || m.d % 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mem_keys_kernel<float>, dim3(5, m.P), dim3(256), 0, st, m);
@@ -411,14 +419,16 @@ hipError_t launch_mem_keys(const MemArgs& m, bool use_bf16, hipStream_t st) {
 }
 
 hipError_t launch_mem_update(const MemArgs& m, bool use_bf16, hipStream_t st) {
+  if (m.P <= 0 || m.batch <= 0 || m.l0 < 0) return hipErrorInvalidValue;
   if (use_bf16) return launch_mem_update_bf16(m, st);
   if (m.dk != 64 || m.M > 64 || m.d % 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mem_update_kernel<float>, dim3(m.d / 16, m.P), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
-hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, hipStream_t st) {
-  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, st, desc, x, y, c0, S, t_last);
+hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, int64_t seq_rows,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(set_desc_kernel, dim3(1), dim3(1), 0, st, desc, x, y, c0, S, t_last, seq_rows);
   return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   __shared__ float dens[32];
   __shared__ float ssq[2][4][16];
 
-  const int layer = a.l0 + blockIdx.y;
+  const int layer = a.l0 + blockIdx.y;          // (layer, sequence) problem
+  const int wl = layer / a.batch;                // model layer
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -101,14 +102,16 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0; the
   // rows after a short last segment's memory tokens are zero padding)
   float hv[NBM][8];
-  const int ts0 = layer == 0 ? seg_tokens(a.desc, a.desc->c, a.T) : 0;
+  const int ts0 = wl == 0 ? seg_tokens(a.desc, a.desc->c, a.T) : 0;
+  // at layer 0 the problem index is the sequence index
+  const bf16* xs = (const bf16*)a.desc->x + (int64_t)layer * a.desc->seq_rows * d;
 #pragma unroll
   for (int s = 0; s < NBM; ++s) {
     if (s < nb) {
       const int c = 128 * s + colw;
-      if (layer == 0) {
+      if (wl == 0) {
         if (rowc < ts0 + a.M) {
-          const bf16* p = rowc < ts0 ? (const bf16*)a.desc->x + ((int64_t)a.desc->c * a.T + rowc) * d
+          const bf16* p = rowc < ts0 ? xs + ((int64_t)a.desc->c * a.T + rowc) * d
                                      : (const bf16*)a.mem_emb + (int64_t)(rowc - ts0) * d;
           const bf16x8 x = *(const bf16x8*)(p + c);
 #pragma unroll
@@ -118,14 +121,14 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
           for (int e = 0; e < 8; ++e) hv[s][e] = 0.f;
         }
       } else {
-        load8f((const float*)a.act_prev + (int64_t)(layer - 1) * a.act_stride + (int64_t)rowc * d + c, hv[s]);
+        load8f((const float*)a.act_prev + (int64_t)(layer - a.batch) * a.act_stride + (int64_t)rowc * d + c, hv[s]);
       }
     }
   }
 
   // chunk DMA: 1 KB block q = w + 8t covers 4 rows of 256 bytes; lane L
   // brings row 4q + L/16, physical chunk L%16
-  const bf16* wq = (const bf16*)a.w_mq + (int64_t)layer * 64 * d;
+  const bf16* wq = (const bf16*)a.w_mq + (int64_t)wl * 64 * d;
   const float* Ast = a.A + (int64_t)layer * d * 64;
   auto issue_wq = [&](int s) {
     unsigned char* buf = ops + (s & 1) * BUF;
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   if (row < a.n) {
     float* ho = (float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)row * d;
     bf16* ao = (bf16*)a.abuf + (int64_t)layer * a.act_stride + (int64_t)row * d;
-    const bf16* gn = (const bf16*)a.gain + (int64_t)layer * d;
+    const bf16* gn = (const bf16*)a.gain + (int64_t)wl * d;
 #pragma unroll
     for (int s = 0; s < NBM; ++s) {
       if (s < nb) {
@@ -294,14 +297,15 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int d = a.d, M = a.M;
-  const int ts = seg_tokens(a.desc, a.desc->c - layer, a.T);   // memory rows start here
+  const int wl = layer / a.batch;
+  const int ts = seg_tokens(a.desc, a.desc->c - wl, a.T);      // memory rows start here
   if (jb == 0 && tid == 0) a.moff[layer] = ts;                 // for memupdate (next launch)
   const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)ts * d;
   if (jb < 4) {
     const int mblocks = (M + 15) / 16;
     // waves take interleaved 64-wide k chunks; lane group g brings
     // k0 + 16g .. +15 (same slot order for both operands, as in memupdate)
-    const bf16* wk = (const bf16*)a.w_mk + ((int64_t)layer * 64 + 16 * jb + c16) * d + 16 * g;
+    const bf16* wk = (const bf16*)a.w_mk + ((int64_t)wl * 64 + 16 * jb + c16) * d + 16 * g;
     f32x4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
       z[tid] = z[tid] + s;
     }
   } else {
-    const bf16* wb = (const bf16*)a.w_beta + (int64_t)layer * d;
+    const bf16* wb = (const bf16*)a.w_beta + (int64_t)wl * d;
     for (int m = w; m < M; m += 4) {
       float s = 0.f;
       for (int k = lane * 8; k < d; k += 512) {
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
   // feeds them to two MFMAs (slots k0 + 16g + j, then k0 + 16g + 8 + j); the
   // Y operand uses the same slot order.
   const int mblocks = (M + 15) / 16;
-  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)layer * d + i0 + 16 * w + c16) * d + 16 * g;
+  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)(layer / a.batch) * d + i0 + 16 * w + c16) * d + 16 * g;
   f32x4 acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -91,34 +91,42 @@ class ArmtModel(_Handle):
     device tensors of the config dtype (kept referenced here: the library
     borrows them)."""
 
-    def __init__(self, cfg: _c.armt_config, weights: dict, stream: torch.cuda.Stream | None = None):
-        w = self._setup(cfg, weights, WEIGHT_FIELDS, stream, lambda: _c.armt_workspace_size(cfg))
+    def __init__(self, cfg: _c.armt_config, weights: dict, stream: torch.cuda.Stream | None = None,
+                 batch: int = 1):
+        self.batch = batch
+        w = self._setup(cfg, weights, WEIGHT_FIELDS, stream, lambda: _c.armt_workspace_size_batched(cfg, batch))
         with torch.cuda.device(self.device):
-            self.handle = _c.armt_create(cfg, w, self.ws_ptr, self.ws_bytes, self.stream)
+            self.handle = _c.armt_create_batched(cfg, w, batch, self.ws_ptr, self.ws_bytes, self.stream)
 
     def kernel_stats(self):
         return _c.armt_kernel_stats(self.handle)
 
     def alloc_outputs(self, n_segments: int, n_tokens: int | None = None):
+        """y [rows, d], A [L, d, d_k], z [L, d_k]; with batch B > 1:
+        y [B, rows, d], A [L, B, d, d_k], z [L, B, d_k]."""
         c = self.cfg
         rows = n_segments * c.seg_len if n_tokens is None else n_tokens
-        y = torch.empty(rows, c.d_model, dtype=self.dtype, device=self.device)
-        A = torch.empty(c.n_layers, c.d_model, c.d_key, dtype=torch.float32, device=self.device)
-        z = torch.empty(c.n_layers, c.d_key, dtype=torch.float32, device=self.device)
+        lead = () if self.batch == 1 else (self.batch,)
+        y = torch.empty(*lead, rows, c.d_model, dtype=self.dtype, device=self.device)
+        A = torch.empty(c.n_layers, *lead, c.d_model, c.d_key, dtype=torch.float32, device=self.device)
+        z = torch.empty(c.n_layers, *lead, c.d_key, dtype=torch.float32, device=self.device)
         return y, A, z
 
     def forward(self, x: torch.Tensor, schedule: str = "diagonal", A0=None, z0=None, out=None,
                 sync: bool = True, by_tokens: bool | None = None):
-        """x [N, d] device tensor of the config dtype.  Returns (y, A, z).
+        """x [N, d] ([B, N, d] for batch B > 1) device tensor of the config
+        dtype.  Returns (y, A, z) (shapes as alloc_outputs).
         N a multiple of seg_len runs through armt_forward_{diagonal,sequential};
         any other N (or by_tokens=True) through the *_tokens entry points
         (a shorter last segment)."""
         c = self.cfg
-        if x.dim() != 2 or x.shape[1] != c.d_model or x.shape[0] < 1:
-            raise ValueError("x must be [n_tokens, d_model]")
+        want = 2 if self.batch == 1 else 3
+        if x.dim() != want or x.shape[-1] != c.d_model or x.shape[-2] < 1 or \
+                (want == 3 and x.shape[0] != self.batch):
+            raise ValueError("x must be [n_tokens, d_model] ([batch, n_tokens, d_model] for batch > 1)")
         if x.dtype != self.dtype or not x.is_contiguous() or x.device != self.device:
             raise ValueError("x must be a contiguous device tensor of the config dtype")
-        N = x.shape[0]
+        N = x.shape[-2]
         if by_tokens is None:
             by_tokens = N % c.seg_len != 0
         S = -(-N // c.seg_len)

@@ -124,3 +124,19 @@ def test_full_attention_comparator_validation():
     assert rc == -1
     assert lib.armt_llama_forward(None, 1, 1, 1) == -1
     assert lib.armt_logits(None, 1, 1, 1, 1, 8, 1) == -1
+
+
+def test_batched_workspace_validation():
+    base = A.armt_workspace_size(_cfg())
+    assert A.armt_workspace_size_batched(_cfg(), 1) == base
+    assert A.armt_workspace_size_batched(_cfg(), 3) > 2 * base
+    for bad in (0, -2, 1025):
+        with pytest.raises(A.ArmtError) as e:
+            A.armt_workspace_size_batched(_cfg(), bad)
+        assert e.value.code == -1
+    lib = A.load_library()
+    cfg = _cfg()
+    w = A.armt_weights(*([1024] * 12))
+    out = ctypes.c_void_p(0)
+    assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 0, 4096, 1 << 30, None, ctypes.byref(out)) == -1
+    assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 2, None, 1 << 30, None, ctypes.byref(out)) == -3
