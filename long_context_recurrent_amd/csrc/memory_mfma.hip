@@ -289,6 +289,7 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
 // sum_{j in block} k_mj z_j with the pre-update z, and z_j += sum_m k_mj for
 // the block's own columns.  Workgroup jb = 4: the gates beta_m.
 // ---------------------------------------------------------------------------
+template <int MBK>   // 16-row blocks of memory tokens: M <= 16 * MBK
 __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   __shared__ float red[4][4][64][4];   // [wave][m-block][lane][r]
   __shared__ float ks[64][17];
@@ -302,32 +303,48 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
   if (jb == 0 && tid == 0) a.moff[layer] = ts;                 // for memupdate (next launch)
   const float* Y = (const float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)ts * d;
   if (jb < 4) {
-    const int mblocks = (M + 15) / 16;
+    const int mblocks = MBK;
     // waves take interleaved 64-wide k chunks; lane group g brings
-    // k0 + 16g .. +15 (same slot order for both operands, as in memupdate)
+    // k0 + 16g .. +15 (same slot order for both operands, as in memupdate);
+    // the next chunk's operands load while the current one multiplies
     const bf16* wk = (const bf16*)a.w_mk + ((int64_t)wl * 64 + 16 * jb + c16) * d + 16 * g;
     f32x4 acc[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 64 * w; k0 < d; k0 += 256) {
-      const bf16x8 bv0 = *(const bf16x8*)(wk + k0), bv1 = *(const bf16x8*)(wk + k0 + 8);
+    int yrow[MBK];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (mb < mblocks) {
-          int m = 16 * mb + c16;
-          m = m < M ? m : M - 1;
-          float v[16];
-          load8f(Y + (int64_t)m * d + k0 + 16 * g, v);
-          load8f(Y + (int64_t)m * d + k0 + 16 * g + 8, v + 8);
-          bf16x8 hi0, lo0, hi1, lo1;
-          split8(v, hi0, lo0);
-          split8(v + 8, hi1, lo1);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, bv0, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, bv0, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, bv1, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, bv1, acc[mb], 0, 0, 0);
-        }
+    for (int mb = 0; mb < MBK; ++mb) yrow[mb] = 16 * mb + c16 < M ? 16 * mb + c16 : M - 1;
+    bf16x8 bw[2][2];
+    float yv[2][MBK][16];
+    auto load = [&](int k0, bf16x8 (&b)[2], float (&y)[MBK][16]) {
+      b[0] = *(const bf16x8*)(wk + k0);
+      b[1] = *(const bf16x8*)(wk + k0 + 8);
+#pragma unroll
+      for (int mb = 0; mb < MBK; ++mb) {
+        load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g, y[mb]);
+        load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g + 8, y[mb] + 8);
       }
+    };
+    auto mul = [&](const bf16x8 (&b)[2], const float (&y)[MBK][16]) {
+#pragma unroll
+      for (int mb = 0; mb < MBK; ++mb) {
+        bf16x8 hi0, lo0, hi1, lo1;
+        split8(y[mb], hi0, lo0);
+        split8(y[mb] + 8, hi1, lo1);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, b[0], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, b[0], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, b[1], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, b[1], acc[mb], 0, 0, 0);
+      }
+    };
+    int k0 = 64 * w;
+    if (k0 < d) load(k0, bw[0], yv[0]);
+    for (; k0 < d; k0 += 512) {
+      if (k0 + 256 < d) load(k0 + 256, bw[1], yv[1]);
+      mul(bw[0], yv[0]);
+      if (k0 + 256 >= d) break;
+      if (k0 + 512 < d) load(k0 + 512, bw[0], yv[0]);
+      mul(bw[1], yv[1]);
     }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -382,6 +399,7 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
 // k_mj.  W_mv is read exactly once per node.  Optionally advances the wave
 // counter (no kernel of this launch reads it).
 // ---------------------------------------------------------------------------
+template <int MBK>   // 16-row blocks of memory tokens: M <= 16 * MBK
 __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
   constexpr int P65 = 65;
   __shared__ float ks[64][64];
@@ -415,39 +433,53 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
   // k moves 64 per step: lane group g brings k0 + 16g .. +15 of its row (32
   // bytes of W_mv, a whole 128-byte line per row across the four groups) and
   // feeds them to two MFMAs (slots k0 + 16g + j, then k0 + 16g + 8 + j); the
-  // Y operand uses the same slot order.
-  const int mblocks = (M + 15) / 16;
+  // Y operand uses the same slot order.  The operands of step k + 1 are
+  // loaded into a second register set while step k multiplies (d / 64 is
+  // even: d is a multiple of 128).
   const bf16* wv = (const bf16*)a.w_mv + ((int64_t)(layer / a.batch) * d + i0 + 16 * w + c16) * d + 16 * g;
-  f32x4 acc[4];
+  f32x4 acc[MBK];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    const bf16x8 bv0 = *(const bf16x8*)(wv + k0), bv1 = *(const bf16x8*)(wv + k0 + 8);
+  for (int mb = 0; mb < MBK; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int yrow[MBK];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb < mblocks) {
-        int m = 16 * mb + c16;
-        m = m < M ? m : M - 1;
-        float v[16];
-        load8f(Y + (int64_t)m * d + k0 + 16 * g, v);
-        load8f(Y + (int64_t)m * d + k0 + 16 * g + 8, v + 8);
-        bf16x8 hi0, lo0, hi1, lo1;
-        split8(v, hi0, lo0);
-        split8(v + 8, hi1, lo1);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, bv0, acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, bv0, acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, bv1, acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, bv1, acc[mb], 0, 0, 0);
-      }
+  for (int mb = 0; mb < MBK; ++mb) yrow[mb] = 16 * mb + c16 < M ? 16 * mb + c16 : M - 1;
+  bf16x8 bw[2][2];
+  float yv[2][MBK][16];
+  auto load = [&](int k0, bf16x8 (&b)[2], float (&y)[MBK][16]) {
+    b[0] = *(const bf16x8*)(wv + k0);
+    b[1] = *(const bf16x8*)(wv + k0 + 8);
+#pragma unroll
+    for (int mb = 0; mb < MBK; ++mb) {
+      load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g, y[mb]);
+      load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g + 8, y[mb] + 8);
     }
+  };
+  auto mul = [&](const bf16x8 (&b)[2], const float (&y)[MBK][16]) {
+#pragma unroll
+    for (int mb = 0; mb < MBK; ++mb) {
+      bf16x8 hi0, lo0, hi1, lo1;
+      split8(y[mb], hi0, lo0);
+      split8(y[mb] + 8, hi1, lo1);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, b[0], acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, b[0], acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, b[1], acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, b[1], acc[mb], 0, 0, 0);
+    }
+  };
+  load(0, bw[0], yv[0]);
+  for (int k0 = 0; k0 < d; k0 += 128) {
+    load(k0 + 64, bw[1], yv[1]);
+    mul(bw[0], yv[0]);
+    if (k0 + 128 < d) load(k0 + 128, bw[0], yv[0]);
+    mul(bw[1], yv[1]);
   }
   // lane holds v[m = 16mb + 4g + r][i = i0 + 16w + c16]
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MBK; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mb + 4 * g + r;
-      if (mb < mblocks && m < M) vvs[m][16 * w + c16] = acc[mb][r];
+      if (m < M) vvs[m][16 * w + c16] = acc[mb][r];
     }
   __syncthreads();
   for (int idx = tid; idx < M * 64; idx += 256) {
@@ -482,13 +514,20 @@ hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st) {
 
 hipError_t launch_mem_keys_bf16(const MemArgs& m, hipStream_t st) {
   if (m.dk != 64 || m.M > 64 || m.d % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(memkeys_bf16_kernel, dim3(5, m.P), dim3(256), 0, st, m);
+  const dim3 grid(5, m.P);
+  if (m.M <= 16) hipLaunchKernelGGL(memkeys_bf16_kernel<1>, grid, dim3(256), 0, st, m);
+  else if (m.M <= 32) hipLaunchKernelGGL(memkeys_bf16_kernel<2>, grid, dim3(256), 0, st, m);
+  else hipLaunchKernelGGL(memkeys_bf16_kernel<4>, grid, dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
 hipError_t launch_mem_update_bf16(const MemArgs& m, hipStream_t st) {
   if (m.dk != 64 || m.M > 64 || m.d % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(memupdate_bf16_kernel, dim3(m.d / 64, m.P), dim3(256), 0, st, m);
+  const dim3 grid(m.d / 64, m.P);
+  if (m.d % 128) return hipErrorInvalidValue;
+  if (m.M <= 16) hipLaunchKernelGGL(memupdate_bf16_kernel<1>, grid, dim3(256), 0, st, m);
+  else if (m.M <= 32) hipLaunchKernelGGL(memupdate_bf16_kernel<2>, grid, dim3(256), 0, st, m);
+  else hipLaunchKernelGGL(memupdate_bf16_kernel<4>, grid, dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
