@@ -362,55 +362,67 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     bf16* C = (bf16*)g.C + (int64_t)prob * g.c_stride;
     if (EPI == EPI_QKV) {
       // Q and K columns: RoPE with the partner column i +- hd/2 of the same
-      // head (heads never straddle the 256-column tile: hd divides 256)
+      // head (heads never straddle the 256-column tile: hd divides 256).  The
+      // 8 columns of a piece lie in one half of one head (hd is a power of
+      // two, a multiple of 16), so they share the partner offset and read 8
+      // consecutive (cos, sin) pairs of the row's table.
       const int hd = g.head_dim, half = hd >> 1;
       for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.v_col0) continue;
-        const float* src_row = Cs + r * CPITCH;
+        const float* src = Cs + r * CPITCH + c8;
+        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
         bf16x8 o;
         if (n < g.rope_cols) {
+          const int hb = n & (hd - 1);
+          const bool first = hb < half;
+          const int fi = first ? hb : hb - half;
+          const float* pp = src + (first ? half : -half);
+          const f32x4 p0 = *(const f32x4*)pp, p1 = *(const f32x4*)(pp + 4);
+          const f32x4* cs = (const f32x4*)(g.rope_cs + ((int64_t)m * half + fi) * 2);
+          const f32x4 t0 = cs[0], t1 = cs[1], t2 = cs[2], t3 = cs[3];   // (cos, sin) x 8
+          const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+          const float cv[8] = {t0[0], t0[2], t1[0], t1[2], t2[0], t2[2], t3[0], t3[2]};
+          const float sv[8] = {t0[1], t0[3], t1[1], t1[3], t2[1], t2[3], t3[1], t3[3]};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int c = c8 + e, hi = (n + e) % hd;
-            const bool first = hi < half;
-            const int fi = first ? hi : hi - half;
-            const float2 cs = *(const float2*)(g.rope_cs + ((int64_t)m * half + fi) * 2);
-            const float x = src_row[c], xp = src_row[first ? c + half : c - half];
-            o[e] = (bf16)(first ? x * cs.x - xp * cs.y : x * cs.x + xp * cs.y);
-          }
+          for (int e = 0; e < 8; ++e)
+            o[e] = (bf16)(first ? xv[e] * cv[e] - pv[e] * sv[e] : xv[e] * cv[e] + pv[e] * sv[e]);
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)src_row[c8 + e];
+          o = bf16x8{(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
+                     (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
         }
         *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
       }
-      // V columns, transposed: 8 consecutive rows (keys) of one column per
-      // piece.  Within every aligned group of 16 keys the stored order is
-      // 0-3, 8-11, 4-7, 12-15 (the k-slot order of the attention kernel's
-      // P V product), so keys m..m+3 and m+4..m+7 go to two 8-byte runs.
+      // V columns, transposed: one aligned group of 16 keys of one column per
+      // item.  Within the group the stored order is 0-3, 8-11, 4-7, 12-15 (the
+      // k-slot order of the attention kernel's P V product), so a full group
+      // is two 16-byte stores; consecutive threads take consecutive columns
+      // (conflict-free LDS reads down the staged columns).
       bf16* Vt = (bf16*)g.vt + (int64_t)prob * g.vt_stride;
-      const int rgroups = (rows_here + 7) / 8;
-      for (int pc = tid; pc < rgroups * BN_OUT; pc += 256) {
-        const int col = pc % BN_OUT, rg = pc / BN_OUT;
+      const int kgroups = (rows_here + 15) / 16;
+      for (int it = tid; it < kgroups * BN_OUT; it += 256) {
+        const int col = it % BN_OUT, grp = it / BN_OUT;
         const int n = n0 + col;
         if (n < g.v_col0 || n >= g.N) continue;
-        const int m = m0 + rc0 + rg * 8;
+        const int m = m0 + rc0 + 16 * grp;           // a multiple of 16
         if (m >= g.M) continue;
         bf16* dstp = Vt + (int64_t)(n - g.v_col0) * g.vt_ld;
-        const float* s = Cs + (rg * 8) * CPITCH + col;
-        if (m + 8 <= g.M) {
-          bf16x4 lo, hi;
+        const float* sp = Cs + (16 * grp) * CPITCH + col;
+        if (m + 16 <= g.M) {
+          bf16x8 a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            lo[e] = (bf16)s[e * CPITCH];
-            hi[e] = (bf16)s[(4 + e) * CPITCH];
+            a[e] = (bf16)sp[e * CPITCH];              // keys 0-3
+            a[4 + e] = (bf16)sp[(8 + e) * CPITCH];    // keys 8-11
+            b[e] = (bf16)sp[(4 + e) * CPITCH];        // keys 4-7
+            b[4 + e] = (bf16)sp[(12 + e) * CPITCH];   // keys 12-15
           }
-          *(bf16x4*)(dstp + vt_pos(m)) = lo;
-          *(bf16x4*)(dstp + vt_pos(m + 4)) = hi;
+          *(bf16x8*)(dstp + m) = a;
+          *(bf16x8*)(dstp + m + 8) = b;
         } else {
-          for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)s[e * CPITCH];
+          for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)sp[e * CPITCH];
         }
       }
     } else if (EPI == EPI_STORE) {
