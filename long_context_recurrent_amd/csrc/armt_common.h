@@ -25,7 +25,9 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 
 // phi(u) = elu(u) + 1
 __device__ __forceinline__ float phi_f(float u) { return u > 0.f ? u + 1.f : __expf(u); }
-__device__ __forceinline__ float sigmoid_f(float u) { return 1.f / (1.f + __expf(-u)); }
+// sigmoid with the hardware reciprocal (about 1 ulp; an IEEE division costs
+// ten instructions per element in the SwiGLU epilogue).  exp(-u) = inf gives 0.
+__device__ __forceinline__ float sigmoid_f(float u) { return __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
 
 // Per-call descriptor shared by the kernels of one forward: the caller's
 // input/output pointers and the running wave counter c.  In wave c the node
