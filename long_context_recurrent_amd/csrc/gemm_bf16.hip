@@ -340,24 +340,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     });
     return;
   }
-  for (int rc0 = 0; rc0 < BM; rc0 += RC) {
+  // The SwiGLU tile has 128 output columns: with a 132-float pitch all BM rows
+  // fit the stage buffers at once, so it takes a single pass.  Passes are
+  // separated by barriers that wait for LDS traffic only; the global stores
+  // of one pass drain while the next is staged.
+  constexpr int EP_PITCH = (EPI == EPI_SWIGLU) ? 128 + 4 : CPITCH;
+  constexpr int EP_RC = (EPI == EPI_SWIGLU) ? BM : RC;
+  static_assert(EP_RC * EP_PITCH * 4 <= NS * STAGE, "epilogue staging fits");
+  for (int rc0 = 0; rc0 < BM; rc0 += EP_RC) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      if (32 * i < rc0 || 32 * i >= rc0 + RC) continue;
+      if (32 * i < rc0 || 32 * i >= rc0 + EP_RC) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int rl = 32 * i - rc0 + 8 * (e >> 2) + 4 * h + (e & 3);
         if (EPI == EPI_SWIGLU) {
           const float gt = acc[i][0][e], up = acc[i][1][e];
-          Cs[rl * CPITCH + 32 * w + r32] = gt * sigmoid_f(gt) * up;
+          Cs[rl * EP_PITCH + 32 * w + r32] = gt * sigmoid_f(gt) * up;
         } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) Cs[rl * CPITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
+          for (int j = 0; j < 2; ++j) Cs[rl * EP_PITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
         }
       }
     }
-    __syncthreads();
-    const int rows_here = (BM - rc0) < RC ? (BM - rc0) : RC;
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
+    lds_barrier();
+    const int rows_here = (BM - rc0) < EP_RC ? (BM - rc0) : EP_RC;
     constexpr int PIECES_ROW = BN_OUT / 8;
     bf16* C = (bf16*)g.C + (int64_t)prob * g.c_stride;
     if (EPI == EPI_QKV) {
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.v_col0) continue;
-        const float* src = Cs + r * CPITCH + c8;
+        const float* src = Cs + r * EP_PITCH + c8;
         const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
         bf16x8 o;
         if (n < g.rope_cols) {
@@ -409,20 +417,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int m = m0 + rc0 + 16 * grp;           // a multiple of 16
         if (m >= g.M) continue;
         bf16* dstp = Vt + (int64_t)(n - g.v_col0) * g.vt_ld;
-        const float* sp = Cs + (16 * grp) * CPITCH + col;
+        const float* sp = Cs + (16 * grp) * EP_PITCH + col;
         if (m + 16 <= g.M) {
           bf16x8 a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            a[e] = (bf16)sp[e * CPITCH];              // keys 0-3
-            a[4 + e] = (bf16)sp[(8 + e) * CPITCH];    // keys 8-11
-            b[e] = (bf16)sp[(4 + e) * CPITCH];        // keys 4-7
-            b[4 + e] = (bf16)sp[(12 + e) * CPITCH];   // keys 12-15
+            a[e] = (bf16)sp[e * EP_PITCH];              // keys 0-3
+            a[4 + e] = (bf16)sp[(8 + e) * EP_PITCH];    // keys 8-11
+            b[e] = (bf16)sp[(4 + e) * EP_PITCH];        // keys 4-7
+            b[4 + e] = (bf16)sp[(12 + e) * EP_PITCH];   // keys 12-15
           }
           *(bf16x8*)(dstp + m) = a;
           *(bf16x8*)(dstp + m + 8) = b;
         } else {
-          for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)sp[e * CPITCH];
+          for (int e = 0; m + e < g.M; ++e) dstp[vt_pos(m + e)] = (bf16)sp[e * EP_PITCH];
         }
       }
     } else if (EPI == EPI_STORE) {
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.N) continue;
-        const float* s = Cs + r * CPITCH + c8;
+        const float* s = Cs + r * EP_PITCH + c8;
         float* dstp = Cf + (int64_t)m * g.ldc + n;
         *(f32x4*)dstp = f32x4{s[0], s[1], s[2], s[3]};
         *(f32x4*)(dstp + 4) = f32x4{s[4], s[5], s[6], s[7]};
@@ -442,14 +450,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
         if (m >= g.M || n >= g.N) continue;
-        const float* s = Cs + r * CPITCH + c8;
+        const float* s = Cs + r * EP_PITCH + c8;
         bf16x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (bf16)s[e];
         *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
+    lds_barrier();
   }
 }
 
