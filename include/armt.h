@@ -221,6 +221,34 @@ int armt_llama_create(const armt_config *cfg, const armt_weights *w, int64_t max
                       void *workspace, size_t ws_bytes, void *hip_stream, armt_handle **out);
 int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y);
 
+/* Backward pass (training; ARMT_F32 handles with batch 1): the gradients of
+ *   <y, dy> + <A_out, dA_out> + <z_out, dz_out>
+ * with respect to x, A0, z0 and every weight, for the forward of
+ * armt_forward_diagonal / _sequential over n_segments full segments.  Node
+ * (s, l)'s backward needs the gradients from (s, l+1) and (s+1, l), so it runs
+ * as the S + L - 1 waves in reverse order, one grouped launch per step
+ * (schedule 0), or node by node in reverse segment-major order (schedule 1);
+ * the two give bitwise equal results (the pages' appendix on the grouped
+ * backward; Pith review, "What carries the argument").  A forward pass first
+ * records each node's input rows and the state it read in the workspace; each
+ * node's activations are recomputed from that record.
+ *   x, dy  [S*T, d] fp32;  A0, dA_out [L, d, d_k], z0, dz_out [L, d_k] fp32
+ *          (A0, z0, dA_out, dz_out may be NULL for zeros)
+ *   dx [S*T, d], dA0 [L, d, d_k], dz0 [L, d_k] fp32 (outputs)
+ *   grads  gradient buffers with the layout of armt_weights, fp32, device
+ *          memory; overwritten
+ *   workspace  device memory of armt_backward_workspace_size bytes,
+ *          256-byte aligned
+ * Asynchronous on the handle's stream; uses the handle's workspace too (must
+ * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for bf16 or
+ * batched handles.  Kernels: plain fp32 SIMT, built for correctness at the
+ * fp32 workloads' sizes. */
+int armt_backward_workspace_size(armt_handle *h, int32_t n_segments, size_t *bytes);
+int armt_backward(armt_handle *h, int32_t schedule, const void *x, int32_t n_segments,
+                  const float *A0, const float *z0, const void *dy, const float *dA_out,
+                  const float *dz_out, void *dx, float *dA0, float *dz0,
+                  const armt_weights *grads, void *workspace, size_t ws_bytes);
+
 void armt_destroy(armt_handle *h);
 
 /* Message of the last non-OK status on this thread ("" if none).  Host

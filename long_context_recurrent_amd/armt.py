@@ -17,7 +17,7 @@ __all__ = [
     "armt_workspace_size", "armt_create", "armt_workspace_size_batched", "armt_create_batched",
     "armt_forward_sequential",
     "armt_forward_diagonal", "armt_forward_sequential_tokens", "armt_forward_diagonal_tokens", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
-    "armt_llama_forward", "armt_destroy", "armt_last_error",
+    "armt_llama_forward", "armt_backward_workspace_size", "armt_backward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
     "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "KERNELS", "VIEWS",
@@ -86,6 +86,8 @@ def load_library():
         "armt_llama_create": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), ctypes.c_int64,
                                     P, SZ, P, ctypes.POINTER(P)]),
         "armt_llama_forward": (I32, [P, P, ctypes.c_int64, P]),
+        "armt_backward_workspace_size": (I32, [P, I32, ctypes.POINTER(SZ)]),
+        "armt_backward": (I32, [P, I32, P, I32, P, P, P, P, P, P, P, P, ctypes.POINTER(armt_weights), P, SZ]),
         "armt_destroy": (None, [P]),
         "armt_last_error": (ctypes.c_char_p, []),
         "armt_wave_schedule": (I32, [I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), I32,
@@ -202,6 +204,19 @@ def armt_llama_create(cfg: armt_config, w: armt_weights, max_tokens: int, worksp
 
 def armt_llama_forward(h, x, n_tokens: int, y):
     _check(load_library().armt_llama_forward(h, _ptr(x), n_tokens, _ptr(y)))
+
+
+def armt_backward_workspace_size(h, n_segments: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().armt_backward_workspace_size(h, n_segments, ctypes.byref(n)))
+    return n.value
+
+
+def armt_backward(h, schedule: int, x, n_segments: int, A0, z0, dy, dA_out, dz_out, dx, dA0, dz0,
+                  grads: armt_weights, workspace, ws_bytes: int):
+    _check(load_library().armt_backward(h, schedule, _ptr(x), n_segments, _ptr(A0), _ptr(z0), _ptr(dy),
+                                        _ptr(dA_out), _ptr(dz_out), _ptr(dx), _ptr(dA0), _ptr(dz0),
+                                        ctypes.byref(grads), _ptr(workspace), ws_bytes))
 
 
 def armt_destroy(h):

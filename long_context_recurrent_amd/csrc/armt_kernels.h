@@ -96,6 +96,59 @@ struct NormArgs {
   float eps;
 };
 
+// ---- backward (fp32) ----------------------------------------------------
+// Generic strided fp32 GEMM over P problems: C = (accumulate ? C : 0) + A B,
+// A(m, k) = A + p*a_ps + m*a_rs + k*a_cs, B(k, n) and C(m, n) likewise.
+struct GenGemm {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs;
+  int M, N, K, accumulate;
+};
+
+// Shapes shared by the backward kernels.
+struct BwArgs {
+  int d, n, M, hd, H, G, qkv_ld;
+  int row_ps;                // per-problem stride of row-scalar arrays (n)
+  float mem_eps, rms_eps, scale;
+  const float* rope;         // [n][hd/2] (cos, sin)
+};
+
+hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st);
+hipError_t bw_phi_den(const BwArgs& a, const float* u, float* q, float* den, const float* z, int64_t u_ps,
+                      int64_t z_ps, int rows, int P, hipStream_t st);
+hipError_t bw_add_div(const BwArgs& a, const float* base, const float* num, const float* den, float* out, int64_t ps,
+                      int rows, int P, hipStream_t st);
+hipError_t bw_rms_fwd(const BwArgs& a, const float* x, const float* g, float* out, float* rs, int64_t ps,
+                      int64_t g_ps, int rows, int P, hipStream_t st);
+hipError_t bw_rms_bwd(const BwArgs& a, const float* x, const float* g, const float* rs, const float* dy, float* dx,
+                      float* dg, int64_t ps, int64_t g_ps, int rows, int accumulate, int P, hipStream_t st);
+hipError_t bw_rope(const BwArgs& a, float* x, int64_t ps, int ld, int col0, int heads, float sign, int rows, int P,
+                   hipStream_t st);
+hipError_t bw_attn_fwd(const BwArgs& a, const float* qkv, float* O, float* mx, float* ls, int64_t qkv_ps,
+                       int64_t o_ps, int64_t st_ps, int P, hipStream_t st);
+hipError_t bw_attn_bwd(const BwArgs& a, const float* qkv, const float* O, const float* dO, const float* mx,
+                       const float* ls, float* Dq, float* dqkv, int64_t qkv_ps, int64_t o_ps, int64_t st_ps, int P,
+                       hipStream_t st);
+hipError_t bw_swiglu(const float* G, const float* Up, float* Uo, int64_t count, int64_t ps, int P, hipStream_t st);
+hipError_t bw_swiglu_bwd(const float* G, const float* Up, const float* dUo, float* dG, float* dUp, int64_t count,
+                         int64_t ps, int P, hipStream_t st);
+hipError_t bw_memw_fwd(const BwArgs& a, const float* uk, float* k, const float* bl, float* beta, const float* z,
+                       float* denw, const float* kA, const float* v, float* e, int64_t z_ps, int P, hipStream_t st);
+hipError_t bw_memw_bwd(const BwArgs& a, const float* de, const float* v, const float* kA, const float* beta,
+                       const float* denw, float* dv, float* dkA, float* ddenw, float* dbl, int P, hipStream_t st);
+hipError_t bw_memw_dk(const BwArgs& a, float* dk, const float* uk, const float* k, const float* ddenw, const float* z,
+                      float* dz, int64_t z_ps, int64_t dz_ps, int P, hipStream_t st);
+hipError_t bw_memw_beta(const BwArgs& a, const float* dbl, const float* wb, const float* Y, float* dY, float* dwb,
+                        int64_t y_ps, int64_t wb_ps, int P, hipStream_t st);
+hipError_t bw_memr_bwd(const BwArgs& a, const float* dh1, const float* num, const float* den, float* dnum, float* dden,
+                       int64_t ps, int rows, int P, hipStream_t st);
+hipError_t bw_memr_dq(const BwArgs& a, float* dq, const float* u, const float* q, const float* dden, const float* z,
+                      float* dz, int64_t u_ps, int64_t z_ps, int64_t dz_ps, int rows, int P, hipStream_t st);
+hipError_t bw_copy(const float* src, float* dst, int64_t count, int64_t src_ps, int64_t dst_ps, int accumulate, int P,
+                   hipStream_t st);
+
 // number of 16-row MFMA blocks per GEMM tile that have instantiations
 extern const int kGemmRowBlocks[];
 extern const int kGemmRowBlocksCount;

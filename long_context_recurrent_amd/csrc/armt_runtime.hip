@@ -898,3 +898,342 @@ int armt_debug_view(armt_handle* h, int32_t which, void** ptr, size_t* bytes) {
 }
 
 }  // extern "C"
+
+// ===========================================================================
+// Backward pass (fp32 handles): the vector-Jacobian product of the forward
+// over the diagonal waves in reverse order (or segment-major in reverse for
+// the sequential schedule).  A forward pass first records each node's input
+// rows and the state it read into a tape; every node's activations are then
+// recomputed from the tape before its backward.
+// ===========================================================================
+namespace {
+
+struct BwLayout {
+  size_t tape_h, tape_A, tape_z;
+  size_t u, q, dq, den, r1, r2, dden;
+  size_t num, h1, a, h2, b, h3, dh, da, db, dnum;
+  size_t qkv, dqkv, O, dO, mx, ls, Dq;
+  size_t G, Up, Uo, dG, dUp, dUo;
+  size_t uk, k, dk, v, kA, e, de, dv, dkA, bl, beta, denw, ddenw, dbl;
+  size_t dH, dA, dz, total;
+};
+
+BwLayout make_bw_layout(const armt_config* c, int S) {
+  const size_t L = c->n_layers, d = c->d_model, n = c->seg_len + c->n_mem, M = c->n_mem, F = c->ffn_hidden;
+  const size_t qd = (size_t)(c->n_heads + 2 * c->n_kv_heads) * c->head_dim, H = c->n_heads;
+  BwLayout lo{};
+  size_t off = 0;
+  auto take = [&](size_t floats) { size_t at = off; off = align_up(off + floats * 4); return at; };
+  lo.tape_h = take(L * S * n * d);
+  lo.tape_A = take(L * S * d * 64);
+  lo.tape_z = take(L * S * 64);
+  lo.u = take(L * n * 64); lo.q = take(L * n * 64); lo.dq = take(L * n * 64);
+  lo.den = take(L * n); lo.r1 = take(L * n); lo.r2 = take(L * n); lo.dden = take(L * n);
+  lo.num = take(L * n * d); lo.h1 = take(L * n * d); lo.a = take(L * n * d); lo.h2 = take(L * n * d);
+  lo.b = take(L * n * d); lo.h3 = take(L * n * d); lo.dh = take(L * n * d); lo.da = take(L * n * d);
+  lo.db = take(L * n * d); lo.dnum = take(L * n * d);
+  lo.qkv = take(L * n * qd); lo.dqkv = take(L * n * qd);
+  lo.O = take(L * n * H * c->head_dim); lo.dO = take(L * n * H * c->head_dim);
+  lo.mx = take(L * H * n); lo.ls = take(L * H * n); lo.Dq = take(L * H * n);
+  lo.G = take(L * n * F); lo.Up = take(L * n * F); lo.Uo = take(L * n * F);
+  lo.dG = take(L * n * F); lo.dUp = take(L * n * F); lo.dUo = take(L * n * F);
+  lo.uk = take(L * M * 64); lo.k = take(L * M * 64); lo.dk = take(L * M * 64);
+  lo.v = take(L * M * d); lo.kA = take(L * M * d); lo.e = take(L * M * d);
+  lo.de = take(L * M * d); lo.dv = take(L * M * d); lo.dkA = take(L * M * d);
+  lo.bl = take(L * M); lo.beta = take(L * M); lo.denw = take(L * M); lo.ddenw = take(L * M); lo.dbl = take(L * M);
+  lo.dH = take(2 * L * n * d);
+  lo.dA = take(L * d * 64);
+  lo.dz = take(L * 64);
+  lo.total = off;
+  return lo;
+}
+
+struct BwCtx {
+  armt_handle* h;
+  hipStream_t st;
+  int S;
+  char* ws;
+  BwLayout lo;
+  const armt_weights* gw;   // gradient buffers (fp32, weight shapes)
+  float* f(size_t at) const { return (float*)(ws + at); }
+};
+
+// C = (acc ? C : 0) + A B over P problems (strides in floats)
+hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const float* B, int64_t b_ps, int64_t b_rs,
+              int64_t b_cs, float* C, int64_t c_ps, int64_t c_rs, int64_t c_cs, int M, int N, int K, int acc, int P,
+              hipStream_t st) {
+  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc};
+  return launch_gemm_gen(g, P, st);
+}
+
+#define BW_TRY(x)                              \
+  do {                                         \
+    hipError_t _e = (x);                       \
+    if (_e != hipSuccess) return _e;           \
+  } while (0)
+
+// Backward of the nodes (c - l, l) for l = l0 .. l0 + P - 1 (wave c).
+hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float* dx) {
+  armt_handle* h = cx.h;
+  const armt_config& cf = h->cfg;
+  const int L = cf.n_layers, S = cx.S, d = cf.d_model, n = h->n, M = cf.n_mem, T = cf.seg_len, F = cf.ffn_hidden;
+  const int H = cf.n_heads, G = cf.n_kv_heads, hd = cf.head_dim, qd = h->qkv_dim, hhd = H * hd;
+  const int64_t nd = (int64_t)n * d, n64 = (int64_t)n * 64, nq = (int64_t)n * qd, nF = (int64_t)n * F;
+  const int64_t Md = (int64_t)M * d, M64 = (int64_t)M * 64, D64 = (int64_t)d * 64;
+  hipStream_t st = cx.st;
+  BwArgs ba{};
+  ba.d = d; ba.n = n; ba.M = M; ba.hd = hd; ba.H = H; ba.G = G; ba.qkv_ld = qd; ba.row_ps = n;
+  ba.mem_eps = cf.mem_eps; ba.rms_eps = cf.rms_eps; ba.scale = 1.0f / std::sqrt((float)hd); ba.rope = h->rope;
+  // per-layer slab pointers, offset to layer l0
+  auto S1 = [&](size_t at, int64_t per) { return cx.f(at) + (int64_t)l0 * per; };
+  const int64_t tap = (int64_t)l0 * S + (c - l0);       // tape index of problem 0; problem p adds p (S - 1)
+  const float* hin = cx.f(cx.lo.tape_h) + tap * nd;
+  const float* Ast = cx.f(cx.lo.tape_A) + tap * D64;
+  const float* zst = cx.f(cx.lo.tape_z) + tap * 64;
+  const int64_t hin_ps = (int64_t)(S - 1) * nd, A_ps = (int64_t)(S - 1) * D64, z_ps = (int64_t)(S - 1) * 64;
+  const float* W_mq = (const float*)h->w.w_mq + (int64_t)l0 * 64 * d;
+  const float* W_qkv = (const float*)h->w.w_qkv + (int64_t)l0 * qd * d;
+  const float* W_o = (const float*)h->w.w_o + (int64_t)l0 * d * hhd;
+  const float* W_g = (const float*)h->w.w_gate + (int64_t)l0 * F * d;
+  const float* W_u = (const float*)h->w.w_up + (int64_t)l0 * F * d;
+  const float* W_d = (const float*)h->w.w_down + (int64_t)l0 * d * F;
+  const float* W_mk = (const float*)h->w.w_mk + (int64_t)l0 * 64 * d;
+  const float* W_mv = (const float*)h->w.w_mv + (int64_t)l0 * d * d;
+  const float* w_b = (const float*)h->w.w_beta + (int64_t)l0 * d;
+  const float* g_at = (const float*)h->w.g_attn + (int64_t)l0 * d;
+  const float* g_ml = (const float*)h->w.g_mlp + (int64_t)l0 * d;
+  float* dW_mq = (float*)cx.gw->w_mq + (int64_t)l0 * 64 * d;
+  float* dW_qkv = (float*)cx.gw->w_qkv + (int64_t)l0 * qd * d;
+  float* dW_o = (float*)cx.gw->w_o + (int64_t)l0 * d * hhd;
+  float* dW_g = (float*)cx.gw->w_gate + (int64_t)l0 * F * d;
+  float* dW_u = (float*)cx.gw->w_up + (int64_t)l0 * F * d;
+  float* dW_d = (float*)cx.gw->w_down + (int64_t)l0 * d * F;
+  float* dW_mk = (float*)cx.gw->w_mk + (int64_t)l0 * 64 * d;
+  float* dW_mv = (float*)cx.gw->w_mv + (int64_t)l0 * d * d;
+  float* dw_b = (float*)cx.gw->w_beta + (int64_t)l0 * d;
+  float* dg_at = (float*)cx.gw->g_attn + (int64_t)l0 * d;
+  float* dg_ml = (float*)cx.gw->g_mlp + (int64_t)l0 * d;
+  float *u = S1(cx.lo.u, n64), *q = S1(cx.lo.q, n64), *dq = S1(cx.lo.dq, n64);
+  float *den = S1(cx.lo.den, n), *r1 = S1(cx.lo.r1, n), *r2 = S1(cx.lo.r2, n), *dden = S1(cx.lo.dden, n);
+  float *num = S1(cx.lo.num, nd), *h1 = S1(cx.lo.h1, nd), *a = S1(cx.lo.a, nd), *h2 = S1(cx.lo.h2, nd);
+  float *b = S1(cx.lo.b, nd), *h3 = S1(cx.lo.h3, nd), *dh = S1(cx.lo.dh, nd), *da = S1(cx.lo.da, nd);
+  float *db = S1(cx.lo.db, nd), *dnum = S1(cx.lo.dnum, nd);
+  float *qkv = S1(cx.lo.qkv, nq), *dqkv = S1(cx.lo.dqkv, nq), *O = S1(cx.lo.O, nd), *dO = S1(cx.lo.dO, nd);
+  const int64_t Hn = (int64_t)H * n;
+  float *mx = S1(cx.lo.mx, Hn), *ls = S1(cx.lo.ls, Hn), *Dq = S1(cx.lo.Dq, Hn);
+  float *Gt = S1(cx.lo.G, nF), *Up = S1(cx.lo.Up, nF), *Uo = S1(cx.lo.Uo, nF);
+  float *dG = S1(cx.lo.dG, nF), *dUp = S1(cx.lo.dUp, nF), *dUo = S1(cx.lo.dUo, nF);
+  float *uk = S1(cx.lo.uk, M64), *kk = S1(cx.lo.k, M64), *dk = S1(cx.lo.dk, M64);
+  float *v = S1(cx.lo.v, Md), *kA = S1(cx.lo.kA, Md), *e = S1(cx.lo.e, Md), *de = S1(cx.lo.de, Md);
+  float *dv = S1(cx.lo.dv, Md), *dkA = S1(cx.lo.dkA, Md);
+  float *bl = S1(cx.lo.bl, M), *beta = S1(cx.lo.beta, M), *denw = S1(cx.lo.denw, M), *ddenw = S1(cx.lo.ddenw, M);
+  float* dbl = S1(cx.lo.dbl, M);
+  float* dA = S1(cx.lo.dA, D64);
+  float* dz = S1(cx.lo.dz, 64);
+
+  // ---- upstream gradient of each node's output into dh
+  const int l_hi = l0 + P - 1;
+  const int Pn = (l_hi == L - 1) ? P - 1 : P;   // problems fed by the layer above
+  float* dH_in = cx.f(cx.lo.dH) + (int64_t)((c + 1) & 1) * L * nd;
+  if (Pn > 0) BW_TRY(bw_copy(dH_in + (int64_t)(l0 + 1) * nd, dh, nd, nd, nd, 0, Pn, st));
+  if (l_hi == L - 1) {
+    float* top = dh + (int64_t)(P - 1) * nd;
+    const int s = c - (L - 1);
+    BW_TRY(bw_copy(dy + (int64_t)s * T * d, top, (int64_t)T * d, 0, 0, 0, 1, st));
+    BW_TRY(hipMemsetAsync(top + (int64_t)T * d, 0, (size_t)M * d * 4, st));
+  }
+
+  // ---- recompute the forward of each node
+  BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st));
+  BW_TRY(bw_phi_den(ba, u, q, den, zst, n64, z_ps, n, P, st));
+  BW_TRY(gg(q, n64, 64, 1, Ast, A_ps, 1, 64, num, nd, d, 1, n, d, 64, 0, P, st));
+  BW_TRY(bw_copy(hin, h1, nd, hin_ps, nd, 0, P, st));
+  BW_TRY(bw_add_div(ba, h1, num, den, h1, nd, n, P, st));
+  BW_TRY(bw_rms_fwd(ba, h1, g_at, a, r1, nd, d, n, P, st));
+  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st));
+  BW_TRY(bw_rope(ba, qkv, nq, qd, 0, H, 1.f, n, P, st));
+  BW_TRY(bw_rope(ba, qkv, nq, qd, H * hd, G, 1.f, n, P, st));
+  BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
+  BW_TRY(bw_copy(h1, h2, nd, nd, nd, 0, P, st));
+  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st));
+  BW_TRY(bw_rms_fwd(ba, h2, g_ml, b, r2, nd, d, n, P, st));
+  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st));
+  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st));
+  BW_TRY(bw_swiglu(Gt, Up, Uo, nF, nF, P, st));
+  BW_TRY(bw_copy(h2, h3, nd, nd, nd, 0, P, st));
+  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st));
+  const float* Y = h3 + (int64_t)T * d;
+  BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st));
+  BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st));
+  BW_TRY(gg(Y, nd, d, 1, w_b, d, 1, 0, bl, M, 1, 0, M, 1, d, 0, P, st));
+  BwArgs bm = ba;
+  bm.row_ps = M;
+  BW_TRY(bw_phi_den(bm, uk, kk, denw, zst, M64, z_ps, M, P, st));
+  BW_TRY(gg(kk, M64, 64, 1, Ast, A_ps, 1, 64, kA, Md, d, 1, M, d, 64, 0, P, st));
+  BW_TRY(bw_memw_fwd(ba, uk, kk, bl, beta, zst, denw, kA, v, e, z_ps, P, st));
+
+  // ---- memory write backward (dA, dz hold the gradient of the state it wrote)
+  BW_TRY(gg(kk, M64, 64, 1, dA, D64, 1, 64, de, Md, d, 1, M, d, 64, 0, P, st));
+  BW_TRY(gg(e, Md, d, 1, dA, D64, 64, 1, dk, M64, 64, 1, M, 64, d, 0, P, st));
+  BW_TRY(bw_memw_bwd(ba, de, v, kA, beta, denw, dv, dkA, ddenw, dbl, P, st));
+  BW_TRY(gg(dkA, Md, 1, d, kk, M64, 64, 1, dA, D64, 64, 1, d, 64, M, 1, P, st));
+  BW_TRY(gg(dkA, Md, d, 1, Ast, A_ps, 64, 1, dk, M64, 64, 1, M, 64, d, 1, P, st));
+  BW_TRY(bw_memw_dk(ba, dk, uk, kk, ddenw, zst, dz, z_ps, 64, P, st));
+  float* dY = dh + (int64_t)T * d;
+  BW_TRY(gg(dk, M64, 64, 1, W_mk, 64 * (int64_t)d, d, 1, dY, nd, d, 1, M, d, 64, 1, P, st));
+  BW_TRY(gg(dv, Md, d, 1, W_mv, (int64_t)d * d, d, 1, dY, nd, d, 1, M, d, d, 1, P, st));
+  BW_TRY(bw_memw_beta(ba, dbl, w_b, Y, dY, dw_b, nd, d, P, st));
+  BW_TRY(gg(dk, M64, 1, 64, Y, nd, d, 1, dW_mk, 64 * (int64_t)d, d, 1, 64, d, M, 1, P, st));
+  BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st));
+  // ---- MLP block backward
+  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st));
+  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
+  BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
+  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st));
+  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st));
+  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
+  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
+  BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
+  // ---- attention block backward
+  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st));
+  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st));
+  BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
+  BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
+  BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
+  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st));
+  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st));
+  BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
+  // ---- memory read backward
+  BW_TRY(bw_memr_bwd(ba, dh, num, den, dnum, dden, nd, n, P, st));
+  BW_TRY(gg(dnum, nd, d, 1, Ast, A_ps, 64, 1, dq, n64, 64, 1, n, 64, d, 0, P, st));
+  BW_TRY(gg(dnum, nd, 1, d, q, n64, 64, 1, dA, D64, 64, 1, d, 64, n, 1, P, st));
+  BW_TRY(bw_memr_dq(ba, dq, u, q, dden, zst, dz, n64, z_ps, 64, n, P, st));
+  BW_TRY(gg(dq, n64, 64, 1, W_mq, 64 * (int64_t)d, d, 1, dh, nd, d, 1, n, d, 64, 1, P, st));
+  BW_TRY(gg(dq, n64, 1, 64, hin, hin_ps, d, 1, dW_mq, 64 * (int64_t)d, d, 1, 64, d, n, 1, P, st));
+
+  // ---- the gradient of each node's input rows: to the layer below, or to x
+  // and the memory embeddings at layer 0
+  float* dH_out = cx.f(cx.lo.dH) + (int64_t)(c & 1) * L * nd;
+  const int p0 = (l0 == 0) ? 1 : 0;
+  if (P - p0 > 0) BW_TRY(bw_copy(dh + p0 * nd, dH_out + (int64_t)(l0 + p0) * nd, nd, nd, nd, 0, P - p0, st));
+  if (l0 == 0) {
+    const int s = c;
+    BW_TRY(bw_copy(dh, dx + (int64_t)s * T * d, (int64_t)T * d, 0, 0, 0, 1, st));
+    BW_TRY(bw_copy(dh + (int64_t)T * d, (float*)cx.gw->mem_emb, (int64_t)M * d, 0, 0, 1, 1, st));
+  }
+  return hipSuccess;
+}
+
+// Record node (c - l, l)'s input rows and the state it reads, l = l0 ..
+// l0 + P - 1, before wave c runs.
+hipError_t save_wave(BwCtx& cx, int c, int l0, int P, const float* x) {
+  armt_handle* h = cx.h;
+  const armt_config& cf = h->cfg;
+  const int S = cx.S, d = cf.d_model, n = h->n, T = cf.seg_len, M = cf.n_mem;
+  const int64_t nd = (int64_t)n * d, D64 = (int64_t)d * 64;
+  const int64_t tap = (int64_t)l0 * S + (c - l0);
+  float* th = cx.f(cx.lo.tape_h) + tap * nd;
+  const int64_t hps = (int64_t)(S - 1) * nd;
+  hipStream_t st = cx.st;
+  const int p0 = (l0 == 0) ? 1 : 0;
+  if (l0 == 0) {
+    const int s = c;
+    BW_TRY(bw_copy(x + (int64_t)s * T * d, th, (int64_t)T * d, 0, 0, 0, 1, st));
+    BW_TRY(bw_copy((const float*)h->w.mem_emb, th + (int64_t)T * d, (int64_t)M * d, 0, 0, 0, 1, st));
+  }
+  if (P - p0 > 0) {
+    const float* prev = (const float*)h->act[(c - 1) & 1] + (int64_t)(l0 + p0 - 1) * nd;
+    BW_TRY(bw_copy(prev, th + p0 * hps, nd, nd, hps, 0, P - p0, st));
+  }
+  BW_TRY(bw_copy(h->A + (int64_t)l0 * D64, cx.f(cx.lo.tape_A) + tap * D64, D64, D64, (int64_t)(S - 1) * D64, 0, P, st));
+  BW_TRY(bw_copy(h->z + (int64_t)l0 * 64, cx.f(cx.lo.tape_z) + tap * 64, 64, 64, (int64_t)(S - 1) * 64, 0, P, st));
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int armt_backward_workspace_size(armt_handle* h, int32_t n_segments, size_t* bytes) {
+  if (!h || !bytes) return fail(ARMT_E_INVALID, "NULL argument");
+  if (h->llama) return fail(ARMT_E_INVALID, "handle is a full-attention comparator");
+  if (h->bf16) return fail(ARMT_E_UNSUPPORTED, "the backward runs on ARMT_F32 handles");
+  if (h->batch != 1) return fail(ARMT_E_UNSUPPORTED, "the backward runs on batch-1 handles");
+  if (n_segments < 1) return fail(ARMT_E_INVALID, "n_segments must be >= 1");
+  *bytes = make_bw_layout(&h->cfg, n_segments).total;
+  return ARMT_OK;
+}
+
+int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_segments, const float* A0,
+                  const float* z0, const void* dy, const float* dA_out, const float* dz_out, void* dx, float* dA0,
+                  float* dz0, const armt_weights* grads, void* workspace, size_t ws_bytes) {
+  size_t need = 0;
+  int rc = armt_backward_workspace_size(h, n_segments, &need);
+  if (rc != ARMT_OK) return rc;
+  if (schedule != 0 && schedule != 1) return fail(ARMT_E_INVALID, "schedule must be 0 (diagonal) or 1 (sequential)");
+  if (!x || !dy || !dx || !dA0 || !dz0 || !grads) return fail(ARMT_E_INVALID, "x, dy, dx, dA0, dz0 and grads must not be NULL");
+  const void* gp[] = {grads->w_qkv, grads->w_o, grads->w_gate, grads->w_up, grads->w_down, grads->g_attn,
+                      grads->g_mlp, grads->w_mq, grads->w_mk, grads->w_mv, grads->w_beta, grads->mem_emb};
+  for (const void* p : gp)
+    if (!p) return fail(ARMT_E_INVALID, "every gradient pointer must be non-NULL");
+  if (!workspace || (uintptr_t)workspace % kAlign) return fail(ARMT_E_WORKSPACE, "workspace missing or misaligned");
+  if (ws_bytes < need) return fail(ARMT_E_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+  const armt_config& c = h->cfg;
+  const int L = c.n_layers, S = n_segments, d = c.d_model, F = c.ffn_hidden;
+  const int qd = h->qkv_dim, hhd = c.n_heads * c.head_dim;
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  BwCtx cx{h, h->stream, S, (char*)workspace, make_bw_layout(&c, S), grads};
+  hipStream_t st = h->stream;
+  // 1. forward, recording the tape (direct launches, the chosen order)
+  const int64_t a_count = (int64_t)L * d * 64, z_count = (int64_t)L * 64;
+  // the forward's y is not needed: it goes to a scratch slab of the tape
+  // workspace that the backward overwrites later (the SwiGLU gradient buffer)
+  if ((int64_t)S * c.seg_len * d > (int64_t)L * h->n * F) return fail(ARMT_E_UNSUPPORTED, "sequence too long for the backward scratch");
+  if ((e = launch_set_desc(h->desc, x, cx.f(cx.lo.dG), 0, S, c.seg_len, (int64_t)S * c.seg_len, st)) != hipSuccess)
+    return hip_fail(e, "set_desc");
+  if ((e = launch_fill_f32(h->A, A0, a_count, st)) != hipSuccess) return hip_fail(e, "state init");
+  if ((e = launch_fill_f32(h->z, z0, z_count, st)) != hipSuccess) return hip_fail(e, "state init");
+  StepCtx sc{h, st, false};
+  if (schedule == 0) {
+    for (int w = 0; w < S + L - 1; ++w) {
+      const int l_lo = w - S + 1 > 0 ? w - S + 1 : 0, l_hi = w < L - 1 ? w : L - 1;
+      if ((e = save_wave(cx, w, l_lo, l_hi - l_lo + 1, (const float*)x)) != hipSuccess) return hip_fail(e, "tape");
+      if ((e = enqueue_step(sc, l_lo, l_hi, w & 1, 1)) != hipSuccess) return hip_fail(e, "forward");
+    }
+  } else {
+    for (int s = 0; s < S; ++s)
+      for (int l = 0; l < L; ++l) {
+        if ((e = save_wave(cx, s + l, l, 1, (const float*)x)) != hipSuccess) return hip_fail(e, "tape");
+        if ((e = enqueue_step(sc, l, l, (s + l) & 1, l == L - 1 ? 2 - L : 1)) != hipSuccess) return hip_fail(e, "forward");
+      }
+  }
+  // 2. zero the gradients; the state gradient starts from dA_out, dz_out
+  const size_t wsz[] = {(size_t)L * qd * d, (size_t)L * d * hhd, (size_t)L * F * d, (size_t)L * F * d,
+                        (size_t)L * d * F, (size_t)L * d, (size_t)L * d, (size_t)L * 64 * d, (size_t)L * 64 * d,
+                        (size_t)L * d * d, (size_t)L * d, (size_t)c.n_mem * d};
+  for (int i = 0; i < 12; ++i)
+    if ((e = hipMemsetAsync((void*)gp[i], 0, wsz[i] * 4, st)) != hipSuccess) return hip_fail(e, "zero gradients");
+  if ((e = launch_fill_f32(cx.f(cx.lo.dA), dA_out, a_count, st)) != hipSuccess) return hip_fail(e, "dA init");
+  if ((e = launch_fill_f32(cx.f(cx.lo.dz), dz_out, z_count, st)) != hipSuccess) return hip_fail(e, "dz init");
+  // 3. the reversed schedule
+  if (schedule == 0) {
+    for (int w = S + L - 2; w >= 0; --w) {
+      const int l_lo = w - S + 1 > 0 ? w - S + 1 : 0, l_hi = w < L - 1 ? w : L - 1;
+      if ((e = backward_wave(cx, w, l_lo, l_hi - l_lo + 1, (const float*)dy, (float*)dx)) != hipSuccess)
+        return hip_fail(e, "backward");
+    }
+  } else {
+    for (int s = S - 1; s >= 0; --s)
+      for (int l = L - 1; l >= 0; --l)
+        if ((e = backward_wave(cx, s + l, l, 1, (const float*)dy, (float*)dx)) != hipSuccess)
+          return hip_fail(e, "backward");
+  }
+  if ((e = hipMemcpyAsync(dA0, cx.f(cx.lo.dA), a_count * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return hip_fail(e, "copy dA0");
+  if ((e = hipMemcpyAsync(dz0, cx.f(cx.lo.dz), z_count * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return hip_fail(e, "copy dz0");
+  return ARMT_OK;
+}
+
+}  // extern "C"

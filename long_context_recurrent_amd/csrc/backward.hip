@@ -1,0 +1,538 @@
+// Backward pass of the fp32 forward (vector-Jacobian product), run over the
+// diagonal waves in reverse order: node (s, l) needs the gradient of its
+// output from node (s, l+1) and the gradient of the state it wrote from node
+// (s+1, l), so the reversed grid is again S + L - 1 waves of independent
+// nodes (Pith review of arXiv 2506.05229, "What carries the argument", Lemma
+// 3.1, applied to the transposed dependency graph; the pages' appendix
+// describes the grouped backward).  Each launch covers every active layer of
+// a wave (problem p = layer l0 + p); every buffer is a per-layer slab, so the
+// per-layer weight gradients take one node's contribution per wave with
+// plain read-modify-write and the result does not depend on the wave width.
+//
+// These are plain SIMT fp32 kernels: the backward is built for correctness at
+// the fp32 workloads' sizes, not tuned.
+#include <cmath>
+
+#include "armt_common.h"
+#include "armt_kernels.h"
+
+namespace armt {
+
+namespace {
+
+__device__ __forceinline__ float dphi_f(float u) { return u > 0.f ? 1.f : __expf(u); }
+
+// ---------------------------------------------------------------------------
+// Generic strided GEMM, P problems: C = beta * C + A B with
+// A(m, k) = A + p*a_ps + m*a_rs + k*a_cs, B(k, n) likewise, C(m, n) likewise.
+// 32 x 32 outputs per workgroup, 2 x 2 per thread, K in steps of 32 via LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm_gen_kernel(GenGemm g) {
+  __shared__ float As[32][33];
+  __shared__ float Bs[32][33];
+  const int p = blockIdx.z;
+  const float* A = g.A + (int64_t)p * g.a_ps;
+  const float* B = g.B + (int64_t)p * g.b_ps;
+  float* C = g.C + (int64_t)p * g.c_ps;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  for (int k0 = 0; k0 < g.K; k0 += 32) {
+    for (int i = tid; i < 32 * 32; i += 256) {
+      const int r = i >> 5, c = i & 31;
+      const int m = m0 + r, k = k0 + c;
+      As[r][c] = (m < g.M && k < g.K) ? A[(int64_t)m * g.a_rs + (int64_t)k * g.a_cs] : 0.f;
+      const int kk = k0 + r, n = n0 + c;
+      Bs[r][c] = (kk < g.K && n < g.N) ? B[(int64_t)kk * g.b_rs + (int64_t)n * g.b_cs] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float a0 = As[ty * 2][k], a1 = As[ty * 2 + 1][k];
+      const float b0 = Bs[k][tx * 2], b1 = Bs[k][tx * 2 + 1];
+      acc[0][0] = fmaf(a0, b0, acc[0][0]);
+      acc[0][1] = fmaf(a0, b1, acc[0][1]);
+      acc[1][0] = fmaf(a1, b0, acc[1][0]);
+      acc[1][1] = fmaf(a1, b1, acc[1][1]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + ty * 2 + i, n = n0 + tx * 2 + j;
+      if (m < g.M && n < g.N) {
+        float* c = C + (int64_t)m * g.c_rs + (int64_t)n * g.c_cs;
+        *c = g.accumulate ? *c + acc[i][j] : acc[i][j];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernels.  One wave per row (rows of every problem: blockIdx.y = p).
+// ---------------------------------------------------------------------------
+
+// q = phi(u) (u kept), den = q . z + eps
+__global__ __launch_bounds__(256) void phi_den_kernel(BwArgs a, const float* u, float* q, float* den,
+                                                      const float* z, int64_t u_ps, int64_t z_ps, int rows) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + w;
+  if (r >= rows) return;
+  const float* ur = u + p * u_ps + (int64_t)r * 64;
+  float* qr = q + p * u_ps + (int64_t)r * 64;
+  const float qq = phi_f(ur[lane]);
+  qr[lane] = qq;
+  const float s = wave_sum(qq * z[p * z_ps + lane]);
+  if (lane == 0) den[p * (int64_t)a.row_ps + r] = s + a.mem_eps;
+}
+
+// out = base + num / den[row]   (d columns)
+__global__ __launch_bounds__(256) void add_div_kernel(BwArgs a, const float* base, const float* num, const float* den,
+                                                      float* out, int64_t ps, int rows) {
+  const int p = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * a.d) return;
+  const int r = (int)(i / a.d);
+  out[p * ps + i] = base[p * ps + i] + num[p * ps + i] / den[p * (int64_t)a.row_ps + r];
+}
+
+// out = x * rs * g, rs[row] = 1 / sqrt(mean(x^2) + eps)
+__global__ __launch_bounds__(256) void rms_fwd_kernel(BwArgs a, const float* x, const float* g, float* out, float* rs,
+                                                      int64_t ps, int64_t g_ps, int rows) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + w;
+  if (r >= rows) return;
+  const float* xr = x + p * ps + (int64_t)r * a.d;
+  float ss = 0.f;
+  for (int i = lane; i < a.d; i += 64) ss = fmaf(xr[i], xr[i], ss);
+  ss = wave_sum(ss);
+  const float rr = 1.f / sqrtf(ss / (float)a.d + a.rms_eps);
+  const float* gg = g + p * g_ps;
+  float* o = out + p * ps + (int64_t)r * a.d;
+  for (int i = lane; i < a.d; i += 64) o[i] = xr[i] * rr * gg[i];
+  if (lane == 0) rs[p * (int64_t)a.row_ps + r] = rr;
+}
+
+// dx (+)= rs * (g . dy) - x * rs^3 * mean(x . g . dy)
+__global__ __launch_bounds__(256) void rms_bwd_kernel(BwArgs a, const float* x, const float* g, const float* rs,
+                                                      const float* dy, float* dx, int64_t ps, int64_t g_ps, int rows,
+                                                      int accumulate) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + w;
+  if (r >= rows) return;
+  const float* xr = x + p * ps + (int64_t)r * a.d;
+  const float* dr = dy + p * ps + (int64_t)r * a.d;
+  const float* gg = g + p * g_ps;
+  float dot = 0.f;
+  for (int i = lane; i < a.d; i += 64) dot = fmaf(xr[i], gg[i] * dr[i], dot);
+  dot = wave_sum(dot);
+  const float rr = rs[p * (int64_t)a.row_ps + r];
+  const float c = rr * rr * rr * dot / (float)a.d;
+  float* o = dx + p * ps + (int64_t)r * a.d;
+  for (int i = lane; i < a.d; i += 64) {
+    const float v = rr * gg[i] * dr[i] - xr[i] * c;
+    o[i] = accumulate ? o[i] + v : v;
+  }
+}
+
+// dg[i] += sum over rows of dy[r, i] * x[r, i] * rs[r]   (one column per thread)
+__global__ __launch_bounds__(256) void rms_dgain_kernel(BwArgs a, const float* x, const float* rs, const float* dy,
+                                                        float* dg, int64_t ps, int64_t g_ps, int rows) {
+  const int p = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.d) return;
+  float s = 0.f;
+  for (int r = 0; r < rows; ++r)
+    s = fmaf(dy[p * ps + (int64_t)r * a.d + i], x[p * ps + (int64_t)r * a.d + i] * rs[p * (int64_t)a.row_ps + r], s);
+  dg[p * g_ps + i] += s;
+}
+
+// RoPE on the first `heads` heads of rows of width ld (in place); sign -1
+// rotates back (the transpose, for gradients).
+__global__ __launch_bounds__(256) void rope_kernel(BwArgs a, float* x, int64_t ps, int ld, int col0, int heads,
+                                                   float sign, int rows) {
+  const int p = blockIdx.y;
+  const int hd = a.hd, half = hd / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * heads * half) return;
+  const int r = (int)(i / (heads * half)), rem = (int)(i % (heads * half));
+  const int hh = rem / half, f = rem % half;
+  float* row = x + p * ps + (int64_t)r * ld + col0 + hh * hd;
+  const float c = a.rope[((int64_t)r * half + f) * 2], s = sign * a.rope[((int64_t)r * half + f) * 2 + 1];
+  const float x0 = row[f], x1 = row[f + half];
+  row[f] = x0 * c - x1 * s;
+  row[f + half] = x1 * c + x0 * s;
+}
+
+// Causal attention forward with the row statistics kept: one wave per
+// (query, head).  O[q, j] = sum_k P[q, k] V[k, kv], P = softmax(scale q.k).
+__global__ __launch_bounds__(256) void attn_fwd_kernel(BwArgs a, const float* qkv, float* O, float* mx, float* lsum,
+                                                       int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  const int p = blockIdx.z, j = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = blockIdx.x * 4 + w;
+  const int n = a.n, hd = a.hd, ld = a.qkv_ld;
+  if (q >= n) return;
+  const int kv = j / (a.H / a.G);
+  const float* base = qkv + p * qkv_ps;
+  const float* qv = base + (int64_t)q * ld + j * hd;
+  const int kc = (a.H + kv) * hd, vc = (a.H + a.G + kv) * hd;
+  float m = -INFINITY;
+  for (int k = lane; k <= q; k += 64) {
+    float s = 0.f;
+    for (int e = 0; e < hd; ++e) s = fmaf(qv[e], base[(int64_t)k * ld + kc + e], s);
+    m = fmaxf(m, s * a.scale);
+  }
+  m = wave_max(m);
+  float l = 0.f;
+  for (int k = lane; k <= q; k += 64) {
+    float s = 0.f;
+    for (int e = 0; e < hd; ++e) s = fmaf(qv[e], base[(int64_t)k * ld + kc + e], s);
+    l += __expf(s * a.scale - m);
+  }
+  l = wave_sum(l);
+  for (int e = lane; e < hd; e += 64) {
+    float acc = 0.f;
+    for (int k = 0; k <= q; ++k) {
+      float s = 0.f;
+      for (int t = 0; t < hd; ++t) s = fmaf(qv[t], base[(int64_t)k * ld + kc + t], s);
+      acc = fmaf(__expf(s * a.scale - m) / l, base[(int64_t)k * ld + vc + e], acc);
+    }
+    O[p * o_ps + (int64_t)q * (a.H * hd) + j * hd + e] = acc;
+  }
+  if (lane == 0) {
+    mx[p * st_ps + (int64_t)j * n + q] = m;
+    lsum[p * st_ps + (int64_t)j * n + q] = l;
+  }
+}
+
+__device__ __forceinline__ float att_score(const BwArgs& a, const float* base, int q, int k, int j, int kv) {
+  const int hd = a.hd, ld = a.qkv_ld;
+  const float* qv = base + (int64_t)q * ld + j * hd;
+  const float* kvp = base + (int64_t)k * ld + (a.H + kv) * hd;
+  float s = 0.f;
+  for (int e = 0; e < hd; ++e) s = fmaf(qv[e], kvp[e], s);
+  return s * a.scale;
+}
+__device__ __forceinline__ float att_dp(const BwArgs& a, const float* base, const float* dO, int q, int k, int j,
+                                        int kv) {
+  const int hd = a.hd, ld = a.qkv_ld;
+  const float* dov = dO + (int64_t)q * (a.H * hd) + j * hd;
+  const float* vv = base + (int64_t)k * ld + (a.H + a.G + kv) * hd;
+  float s = 0.f;
+  for (int e = 0; e < hd; ++e) s = fmaf(dov[e], vv[e], s);
+  return s;
+}
+
+// Attention backward, part 1: one wave per (query, head):
+// Dq = sum_k P dP (= dO . O), dQ[q] = scale * sum_k P (dP - Dq) K[k].
+__global__ __launch_bounds__(256) void attn_bwd_q_kernel(BwArgs a, const float* qkv, const float* O, const float* dO,
+                                                         const float* mx, const float* lsum, float* Dq, float* dqkv,
+                                                         int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  const int p = blockIdx.z, j = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = blockIdx.x * 4 + w;
+  const int n = a.n, hd = a.hd, ld = a.qkv_ld;
+  if (q >= n) return;
+  const int kv = j / (a.H / a.G);
+  const float* base = qkv + p * qkv_ps;
+  const float* dOp = dO + p * o_ps;
+  float dd = 0.f;
+  for (int e = lane; e < hd; e += 64)
+    dd = fmaf(dOp[(int64_t)q * (a.H * hd) + j * hd + e], O[p * o_ps + (int64_t)q * (a.H * hd) + j * hd + e], dd);
+  dd = wave_sum(dd);
+  const float m = mx[p * st_ps + (int64_t)j * n + q], l = lsum[p * st_ps + (int64_t)j * n + q];
+  for (int e = lane; e < hd; e += 64) {
+    float acc = 0.f;
+    for (int k = 0; k <= q; ++k) {
+      const float P = __expf(att_score(a, base, q, k, j, kv) - m) / l;
+      const float dS = P * (att_dp(a, base, dOp, q, k, j, kv) - dd);
+      acc = fmaf(dS, base[(int64_t)k * ld + (a.H + kv) * hd + e], acc);
+    }
+    dqkv[p * qkv_ps + (int64_t)q * ld + j * hd + e] = acc * a.scale;
+  }
+  if (lane == 0) Dq[p * st_ps + (int64_t)j * n + q] = dd;
+}
+
+// Attention backward, part 2: one wave per (key, kv-head), summing over the
+// query heads of its group and the queries at or after the key:
+// dK[k] = scale * sum P (dP - Dq) Q[q],  dV[k] = sum P dO[q].
+__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(BwArgs a, const float* qkv, const float* dO, const float* mx,
+                                                          const float* lsum, const float* Dq, float* dqkv,
+                                                          int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  const int p = blockIdx.z, kv = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + w;
+  const int n = a.n, hd = a.hd, ld = a.qkv_ld, rep = a.H / a.G;
+  if (k >= n) return;
+  const float* base = qkv + p * qkv_ps;
+  const float* dOp = dO + p * o_ps;
+  for (int e = lane; e < hd; e += 64) {
+    float dk = 0.f, dv = 0.f;
+    for (int j = kv * rep; j < (kv + 1) * rep; ++j)
+      for (int q = k; q < n; ++q) {
+        const float m = mx[p * st_ps + (int64_t)j * n + q], l = lsum[p * st_ps + (int64_t)j * n + q];
+        const float P = __expf(att_score(a, base, q, k, j, kv) - m) / l;
+        const float dS = P * (att_dp(a, base, dOp, q, k, j, kv) - Dq[p * st_ps + (int64_t)j * n + q]);
+        dk = fmaf(dS, base[(int64_t)q * ld + j * hd + e], dk);
+        dv = fmaf(P, dOp[(int64_t)q * (a.H * hd) + j * hd + e], dv);
+      }
+    dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + kv) * hd + e] = dk * a.scale;
+    dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + a.G + kv) * hd + e] = dv;
+  }
+}
+
+// Uo = silu(G) * Up   /   dG, dUp from dUo
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* Gt, const float* Up, float* Uo, int64_t count,
+                                                     int64_t ps) {
+  const int p = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float g = Gt[p * ps + i];
+  Uo[p * ps + i] = g / (1.f + __expf(-g)) * Up[p * ps + i];
+}
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* Gt, const float* Up, const float* dUo, float* dG,
+                                                         float* dUp, int64_t count, int64_t ps) {
+  const int p = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float g = Gt[p * ps + i], u = Up[p * ps + i], d = dUo[p * ps + i];
+  const float sg = 1.f / (1.f + __expf(-g));
+  dG[p * ps + i] = d * u * sg * (1.f + g * (1.f - sg));
+  dUp[p * ps + i] = d * g * sg;
+}
+
+// Memory write, recomputed per memory row m (one wave each):
+// k = phi(uk), beta = sigmoid(bl), denw = k . z + eps, vbar = kA / denw,
+// e = beta (v - vbar).
+__global__ __launch_bounds__(256) void memw_fwd_kernel(BwArgs a, const float* uk, float* k, const float* bl,
+                                                       float* beta, const float* z, float* denw, const float* kA,
+                                                       const float* v, float* e, int64_t z_ps) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + w;
+  if (m >= a.M) return;
+  const int64_t km = ((int64_t)p * a.M + m) * 64;
+  const float kk = phi_f(uk[km + lane]);
+  k[km + lane] = kk;
+  const float dn = wave_sum(kk * z[p * z_ps + lane]) + a.mem_eps;
+  const float b = 1.f / (1.f + __expf(-bl[p * a.M + m]));
+  if (lane == 0) {
+    denw[p * a.M + m] = dn;
+    beta[p * a.M + m] = b;
+  }
+  const int64_t vm = ((int64_t)p * a.M + m) * a.d;
+  for (int i = lane; i < a.d; i += 64) e[vm + i] = b * (v[vm + i] - kA[vm + i] / dn);
+}
+
+// Memory write backward, per memory row m (one wave each), given
+// de = k dA'^T: dbeta, dv = beta de, dkA = -beta de / denw,
+// ddenw = sum_i beta de_i kA_i / denw^2, dbl = dbeta beta (1 - beta).
+__global__ __launch_bounds__(256) void memw_bwd_kernel(BwArgs a, const float* de, const float* v, const float* kA,
+                                                       const float* beta, const float* denw, float* dv, float* dkA,
+                                                       float* ddenw, float* dbl) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + w;
+  if (m >= a.M) return;
+  const int64_t vm = ((int64_t)p * a.M + m) * a.d;
+  const float b = beta[p * a.M + m], dn = denw[p * a.M + m];
+  float db = 0.f, dden = 0.f;
+  for (int i = lane; i < a.d; i += 64) {
+    const float dei = de[vm + i], kai = kA[vm + i];
+    db = fmaf(dei, v[vm + i] - kai / dn, db);
+    dv[vm + i] = b * dei;
+    dkA[vm + i] = -b * dei / dn;
+    dden = fmaf(b * dei, kai, dden);
+  }
+  db = wave_sum(db);
+  dden = wave_sum(dden);
+  if (lane == 0) {
+    ddenw[p * a.M + m] = dden / (dn * dn);
+    dbl[p * a.M + m] = db * b * (1.f - b);
+  }
+}
+
+// dk += ddenw[m] z + dz' (and -> duk = dk phi'(uk)); dz = dz' + sum_m ddenw[m] k[m]
+// (in place on the layer's dz, which held dz').  One workgroup per problem.
+__global__ __launch_bounds__(64) void memw_dk_kernel(BwArgs a, float* dk, const float* uk, const float* k,
+                                                     const float* ddenw, const float* z, float* dz, int64_t z_ps,
+                                                     int64_t dz_ps) {
+  const int p = blockIdx.x, j = threadIdx.x;
+  const float dzp = dz[p * dz_ps + j], zj = z[p * z_ps + j];
+  float acc = dzp;
+  for (int m = 0; m < a.M; ++m) {
+    const int64_t km = ((int64_t)p * a.M + m) * 64 + j;
+    const float dd = ddenw[p * a.M + m];
+    const float g = dk[km] + dd * zj + dzp;
+    dk[km] = g * dphi_f(uk[km]);
+    acc = fmaf(dd, k[km], acc);
+  }
+  dz[p * dz_ps + j] = acc;
+}
+
+// dY += dbl[m] w_beta, dw_beta += sum_m dbl[m] Y[m]
+__global__ __launch_bounds__(256) void memw_beta_kernel(BwArgs a, const float* dbl, const float* wb, const float* Y,
+                                                        float* dY, float* dwb, int64_t y_ps, int64_t wb_ps) {
+  const int p = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.d) return;
+  float s = 0.f;
+  for (int m = 0; m < a.M; ++m) {
+    const float d = dbl[p * a.M + m];
+    dY[p * y_ps + (int64_t)m * a.d + i] += d * wb[p * wb_ps + i];
+    s = fmaf(d, Y[p * y_ps + (int64_t)m * a.d + i], s);
+  }
+  dwb[p * wb_ps + i] += s;
+}
+
+// Memory read backward, per row (one wave each): dnum = dh1 / den,
+// dden = -sum_i dh1_i num_i / den^2.
+__global__ __launch_bounds__(256) void memr_bwd_kernel(BwArgs a, const float* dh1, const float* num, const float* den,
+                                                       float* dnum, float* dden, int64_t ps, int rows) {
+  const int p = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + w;
+  if (r >= rows) return;
+  const float dn = den[p * (int64_t)a.row_ps + r];
+  const int64_t o = p * ps + (int64_t)r * a.d;
+  float s = 0.f;
+  for (int i = lane; i < a.d; i += 64) {
+    dnum[o + i] = dh1[o + i] / dn;
+    s = fmaf(dh1[o + i], num[o + i], s);
+  }
+  s = wave_sum(s);
+  if (lane == 0) dden[p * (int64_t)a.row_ps + r] = -s / (dn * dn);
+}
+
+// dq += dden[r] z, du = dq phi'(u)  (in place on dq); dz += sum_r dden[r] q[r]
+__global__ __launch_bounds__(64) void memr_dq_kernel(BwArgs a, float* dq, const float* u, const float* q,
+                                                     const float* dden, const float* z, float* dz, int64_t u_ps,
+                                                     int64_t z_ps, int64_t dz_ps, int rows) {
+  const int p = blockIdx.x, j = threadIdx.x;
+  const float zj = z[p * z_ps + j];
+  float acc = 0.f;
+  for (int r = 0; r < rows; ++r) {
+    const int64_t o = p * u_ps + (int64_t)r * 64 + j;
+    const float dd = dden[p * (int64_t)a.row_ps + r];
+    dq[o] = (dq[o] + dd * zj) * dphi_f(u[o]);
+    acc = fmaf(dd, q[o], acc);
+  }
+  dz[p * dz_ps + j] += acc;
+}
+
+// Gather / scatter between the tape, the layer slabs and the caller's
+// arrays.  Node (s, l) of problem p: layer l0 + p, segment s = c - l.
+__global__ __launch_bounds__(256) void bw_copy_kernel(const float* src, float* dst, int64_t count, int64_t src_ps,
+                                                      int64_t dst_ps, int accumulate) {
+  const int p = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  dst[p * dst_ps + i] = accumulate ? dst[p * dst_ps + i] + src[p * src_ps + i] : src[p * src_ps + i];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st) {
+  if (P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_gen_kernel, dim3((g.N + 31) / 32, (g.M + 31) / 32, P), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+static dim3 rows_grid(int rows, int P) { return dim3((rows + 3) / 4, P); }
+static dim3 elem_grid(int64_t count, int P) { return dim3((unsigned)((count + 255) / 256), P); }
+
+hipError_t bw_phi_den(const BwArgs& a, const float* u, float* q, float* den, const float* z, int64_t u_ps,
+                      int64_t z_ps, int rows, int P, hipStream_t st) {
+  hipLaunchKernelGGL(phi_den_kernel, rows_grid(rows, P), dim3(256), 0, st, a, u, q, den, z, u_ps, z_ps, rows);
+  return hipGetLastError();
+}
+hipError_t bw_add_div(const BwArgs& a, const float* base, const float* num, const float* den, float* out, int64_t ps,
+                      int rows, int P, hipStream_t st) {
+  hipLaunchKernelGGL(add_div_kernel, elem_grid((int64_t)rows * a.d, P), dim3(256), 0, st, a, base, num, den, out, ps,
+                     rows);
+  return hipGetLastError();
+}
+hipError_t bw_rms_fwd(const BwArgs& a, const float* x, const float* g, float* out, float* rs, int64_t ps,
+                      int64_t g_ps, int rows, int P, hipStream_t st) {
+  hipLaunchKernelGGL(rms_fwd_kernel, rows_grid(rows, P), dim3(256), 0, st, a, x, g, out, rs, ps, g_ps, rows);
+  return hipGetLastError();
+}
+hipError_t bw_rms_bwd(const BwArgs& a, const float* x, const float* g, const float* rs, const float* dy, float* dx,
+                      float* dg, int64_t ps, int64_t g_ps, int rows, int accumulate, int P, hipStream_t st) {
+  hipLaunchKernelGGL(rms_dgain_kernel, dim3((a.d + 255) / 256, P), dim3(256), 0, st, a, x, rs, dy, dg, ps, g_ps,
+                     rows);
+  hipLaunchKernelGGL(rms_bwd_kernel, rows_grid(rows, P), dim3(256), 0, st, a, x, g, rs, dy, dx, ps, g_ps, rows,
+                     accumulate);
+  return hipGetLastError();
+}
+hipError_t bw_rope(const BwArgs& a, float* x, int64_t ps, int ld, int col0, int heads, float sign, int rows, int P,
+                   hipStream_t st) {
+  hipLaunchKernelGGL(rope_kernel, elem_grid((int64_t)rows * heads * (a.hd / 2), P), dim3(256), 0, st, a, x, ps, ld,
+                     col0, heads, sign, rows);
+  return hipGetLastError();
+}
+hipError_t bw_attn_fwd(const BwArgs& a, const float* qkv, float* O, float* mx, float* ls, int64_t qkv_ps,
+                       int64_t o_ps, int64_t st_ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 0, st, a, qkv, O, mx, ls, qkv_ps, o_ps,
+                     st_ps);
+  return hipGetLastError();
+}
+hipError_t bw_attn_bwd(const BwArgs& a, const float* qkv, const float* O, const float* dO, const float* mx,
+                       const float* ls, float* Dq, float* dqkv, int64_t qkv_ps, int64_t o_ps, int64_t st_ps, int P,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 0, st, a, qkv, O, dO, mx, ls, Dq,
+                     dqkv, qkv_ps, o_ps, st_ps);
+  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((a.n + 3) / 4, a.G, P), dim3(256), 0, st, a, qkv, dO, mx, ls, Dq, dqkv,
+                     qkv_ps, o_ps, st_ps);
+  return hipGetLastError();
+}
+hipError_t bw_swiglu(const float* G, const float* Up, float* Uo, int64_t count, int64_t ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(swiglu_kernel, elem_grid(count, P), dim3(256), 0, st, G, Up, Uo, count, ps);
+  return hipGetLastError();
+}
+hipError_t bw_swiglu_bwd(const float* G, const float* Up, const float* dUo, float* dG, float* dUp, int64_t count,
+                         int64_t ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(swiglu_bwd_kernel, elem_grid(count, P), dim3(256), 0, st, G, Up, dUo, dG, dUp, count, ps);
+  return hipGetLastError();
+}
+hipError_t bw_memw_fwd(const BwArgs& a, const float* uk, float* k, const float* bl, float* beta, const float* z,
+                       float* denw, const float* kA, const float* v, float* e, int64_t z_ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memw_fwd_kernel, rows_grid(a.M, P), dim3(256), 0, st, a, uk, k, bl, beta, z, denw, kA, v, e,
+                     z_ps);
+  return hipGetLastError();
+}
+hipError_t bw_memw_bwd(const BwArgs& a, const float* de, const float* v, const float* kA, const float* beta,
+                       const float* denw, float* dv, float* dkA, float* ddenw, float* dbl, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memw_bwd_kernel, rows_grid(a.M, P), dim3(256), 0, st, a, de, v, kA, beta, denw, dv, dkA, ddenw,
+                     dbl);
+  return hipGetLastError();
+}
+hipError_t bw_memw_dk(const BwArgs& a, float* dk, const float* uk, const float* k, const float* ddenw, const float* z,
+                      float* dz, int64_t z_ps, int64_t dz_ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memw_dk_kernel, dim3(P), dim3(64), 0, st, a, dk, uk, k, ddenw, z, dz, z_ps, dz_ps);
+  return hipGetLastError();
+}
+hipError_t bw_memw_beta(const BwArgs& a, const float* dbl, const float* wb, const float* Y, float* dY, float* dwb,
+                        int64_t y_ps, int64_t wb_ps, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memw_beta_kernel, dim3((a.d + 255) / 256, P), dim3(256), 0, st, a, dbl, wb, Y, dY, dwb, y_ps,
+                     wb_ps);
+  return hipGetLastError();
+}
+hipError_t bw_memr_bwd(const BwArgs& a, const float* dh1, const float* num, const float* den, float* dnum, float* dden,
+                       int64_t ps, int rows, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memr_bwd_kernel, rows_grid(rows, P), dim3(256), 0, st, a, dh1, num, den, dnum, dden, ps, rows);
+  return hipGetLastError();
+}
+hipError_t bw_memr_dq(const BwArgs& a, float* dq, const float* u, const float* q, const float* dden, const float* z,
+                      float* dz, int64_t u_ps, int64_t z_ps, int64_t dz_ps, int rows, int P, hipStream_t st) {
+  hipLaunchKernelGGL(memr_dq_kernel, dim3(P), dim3(64), 0, st, a, dq, u, q, dden, z, dz, u_ps, z_ps, dz_ps, rows);
+  return hipGetLastError();
+}
+hipError_t bw_copy(const float* src, float* dst, int64_t count, int64_t src_ps, int64_t dst_ps, int accumulate, int P,
+                   hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bw_copy_kernel, elem_grid(count, P), dim3(256), 0, st, src, dst, count, src_ps, dst_ps,
+                     accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace armt

@@ -152,6 +152,31 @@ class ArmtModel(_Handle):
         return y, A, z
 
 
+def backward(model: "ArmtModel", x: torch.Tensor, dy: torch.Tensor, A0=None, z0=None, dA_out=None, dz_out=None,
+             schedule: str = "diagonal"):
+    """Gradients of <y, dy> + <A_out, dA_out> + <z_out, dz_out> (fp32 handles):
+    returns (dx, dA0, dz0, {weight field: gradient})."""
+    c = model.cfg
+    if model.dtype != torch.float32:
+        raise ValueError("the backward runs on fp32 handles")
+    S = x.shape[0] // c.seg_len
+    dev = model.device
+    ws_bytes = _c.armt_backward_workspace_size(model.handle, S)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    grads = {k: torch.empty_like(model.weights[k]) for k in WEIGHT_FIELDS}
+    gw = _c.armt_weights(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    dx = torch.empty_like(x)
+    dA0 = torch.empty(c.n_layers, c.d_model, c.d_key, dtype=torch.float32, device=dev)
+    dz0 = torch.empty(c.n_layers, c.d_key, dtype=torch.float32, device=dev)
+    model.stream.wait_stream(torch.cuda.current_stream(dev))
+    _c.armt_backward(model.handle, 0 if schedule == "diagonal" else 1, x, S, A0, z0, dy, dA_out, dz_out,
+                     dx, dA0, dz0, gw, ws_ptr, ws_bytes)
+    model.stream.synchronize()
+    del ws
+    return dx, dA0, dz0, grads
+
+
 class FullAttentionModel(_Handle):
     """The full-attention comparator (armt_llama_*): the block weights of the
     recurrent model's layers over one causal window of up to ``max_tokens``."""
