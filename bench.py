@@ -6,6 +6,7 @@
     python bench.py --logit-drift        # LM-head logits: diag vs seq vs oracle per segment count
     python bench.py --full-attention     # full-attention Llama comparator vs diagonal ARMT, 4K..131K
     python bench.py --batch-sweep        # B independent sequences per node, B = 1..8
+    python bench.py --backward           # grouped vs node-by-node backward (fp32)
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
@@ -83,6 +84,9 @@ def parse():
     ap.add_argument("--batch-sweep", action="store_true",
                     help="diagonal forward of B = 1, 2, 4, 8 independent 32-segment sequences per node "
                          "(1B shape): total tokens/s against the batch size")
+    ap.add_argument("--backward", action="store_true",
+                    help="grouped backward (reversed diagonal waves) against the node-by-node backward on an "
+                         "fp32 workload: time per forward + backward, one JSON line per schedule")
     ap.add_argument("--traffic-record", metavar="DIR",
                     help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
                          "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
@@ -608,6 +612,78 @@ def batch_sweep(args, dev):
         torch.cuda.empty_cache()
 
 
+def backward_bench(args, dev):
+    """Forward + backward (fp32 handles) over an 8-layer, 32-segment fp32
+    workload: the grouped backward over the reversed diagonal waves against
+    the node-by-node backward in reverse segment-major order (same results,
+    bitwise)."""
+    import numpy as np
+    import torch
+    from armt_inputs import get_config, make_inputs
+    from long_context_recurrent_amd import armt as C
+    from long_context_recurrent_amd.model import ArmtModel, WEIGHT_FIELDS, make_config
+    cfg = get_config("tiny_fp32").with_(name="fp32_l8_s32", n_layers=8, d_model=256, n_heads=4, n_kv_heads=2,
+                                        head_dim=64, ffn_hidden=512, seg_len=128, n_mem=8, n_segments=32)
+    S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
+    inp = make_inputs(cfg)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, torch.float32)
+    w = {k: f(v) for k, v in inp.weights.items()}
+    w.update(g_attn=f(inp.g_attn), g_mlp=f(inp.g_mlp), mem_emb=f(inp.mem_emb))
+    ccfg = make_config(L, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_hidden, T, cfg.n_mem,
+                       dtype="f32")
+    model = ArmtModel(ccfg, w)
+    x = f(inp.x)
+    dy = torch.randn_like(x)
+    ws_bytes = C.armt_backward_workspace_size(model.handle, S)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    grads = {k: torch.empty_like(w[k]) for k in WEIGHT_FIELDS}
+    gw = C.armt_weights(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    dx = torch.empty_like(x)
+    dA0 = torch.empty(L, cfg.d_model, 64, device=dev)
+    dz0 = torch.empty(L, 64, device=dev)
+    st = model.stream
+    results = {}
+    for sched, code in (("diagonal", 0), ("sequential", 1)):
+        run = lambda: C.armt_backward(model.handle, code, x, S, None, None, dy, None, None, dx, dA0, dz0, gw,
+                                      ws_ptr, ws_bytes)
+        run()
+        st.synchronize()
+        each = []
+        for _ in range(max(1, min(args.steps, 3))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            run()
+            e1.record(st)
+            e1.synchronize()
+            each.append(e0.elapsed_time(e1) * 1e-3)
+        results[sched] = (statistics.median(each), dx.clone())
+    y_t = statistics.median([timed_forward(model, x) for _ in range(3)])
+    same = bool(torch.equal(results["diagonal"][1], results["sequential"][1]))
+    for sched in ("diagonal", "sequential"):
+        t = results[sched][0]
+        line = {"workload": cfg.name, "dtype": "f32", "schedule": sched, "tokens": S * T,
+                "ms_forward_plus_backward": t * 1e3, "tokens_per_s": S * T / t,
+                "ms_forward_alone": y_t * 1e3, "bitwise_equal_schedules": same,
+                "kernels": "fp32 SIMT (not tuned)"}
+        log(f"{sched}: forward + backward {t * 1e3:.1f} ms ({S * T / t:.0f} tokens/s); forward alone "
+            f"{y_t * 1e3:.1f} ms")
+        print(json.dumps(line), flush=True)
+    log(f"grouped backward speed-up {results['sequential'][0] / results['diagonal'][0]:.2f}x")
+    model.close()
+
+
+def timed_forward(model, x):
+    import torch
+    st = model.stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    model.forward(x, "diagonal", sync=False)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
 def group_sweep(args, dev):
     """Grouped GEMM and attention throughput against the wave width k: a
     model of the first k layers of the 1B shape, run diagonally over 32 k
@@ -667,6 +743,8 @@ def main():
         full_attention(args, dev)
     elif args.batch_sweep:
         batch_sweep(args, dev)
+    elif args.backward:
+        backward_bench(args, dev)
     elif args.group_sweep:
         group_sweep(args, dev)
     else:

@@ -915,7 +915,7 @@ struct BwLayout {
   size_t qkv, dqkv, O, dO, mx, ls, Dq;
   size_t G, Up, Uo, dG, dUp, dUo;
   size_t uk, k, dk, v, kA, e, de, dv, dkA, bl, beta, denw, ddenw, dbl;
-  size_t dH, dA, dz, total;
+  size_t dH, dA, dz, yscr, total;
 };
 
 BwLayout make_bw_layout(const armt_config* c, int S) {
@@ -944,6 +944,7 @@ BwLayout make_bw_layout(const armt_config* c, int S) {
   lo.dH = take(2 * L * n * d);
   lo.dA = take(L * d * 64);
   lo.dz = take(L * 64);
+  lo.yscr = take((size_t)S * c->seg_len * d);   // the recording forward's y (not returned)
   lo.total = off;
   return lo;
 }
@@ -1187,10 +1188,7 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
   hipStream_t st = h->stream;
   // 1. forward, recording the tape (direct launches, the chosen order)
   const int64_t a_count = (int64_t)L * d * 64, z_count = (int64_t)L * 64;
-  // the forward's y is not needed: it goes to a scratch slab of the tape
-  // workspace that the backward overwrites later (the SwiGLU gradient buffer)
-  if ((int64_t)S * c.seg_len * d > (int64_t)L * h->n * F) return fail(ARMT_E_UNSUPPORTED, "sequence too long for the backward scratch");
-  if ((e = launch_set_desc(h->desc, x, cx.f(cx.lo.dG), 0, S, c.seg_len, (int64_t)S * c.seg_len, st)) != hipSuccess)
+  if ((e = launch_set_desc(h->desc, x, cx.f(cx.lo.yscr), 0, S, c.seg_len, (int64_t)S * c.seg_len, st)) != hipSuccess)
     return hip_fail(e, "set_desc");
   if ((e = launch_fill_f32(h->A, A0, a_count, st)) != hipSuccess) return hip_fail(e, "state init");
   if ((e = launch_fill_f32(h->z, z0, z_count, st)) != hipSuccess) return hip_fail(e, "state init");
