@@ -229,8 +229,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// fp32 path: one wave per query, lanes over keys for the scores and over the
-// head dimension for the weighted sum.  Used for the small fp32 workloads.
+// fp32 path: one wave per query (4 queries per workgroup), lanes over keys
+// for the scores and over the head dimension for the weighted sum.  Used for
+// the small fp32 workloads.
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   extern __shared__ float pbuf[];   // [4][n + 1]
   const int h = blockIdx.x, layer = a.l0 + blockIdx.y;
@@ -240,40 +241,36 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* p = pbuf + w * (n + 1);
   float* out = (float*)a.out + (int64_t)layer * a.out_stride;
-  // uniform trip count over query groups so every barrier is reached by all waves
-  for (int q0 = 0; q0 < n; q0 += 4) {
-    const int q = q0 + w;
-    if (q < n) {
-      const float* qv = qkv + (int64_t)q * a.ld_qkv + h * hd;
-      float mx = -INFINITY;
-      for (int k = lane; k <= q; k += 64) {
-        const float* kv = qkv + (int64_t)k * a.ld_qkv + kcol;
-        float sc = 0.f;
-        for (int e = 0; e < hd; ++e) sc = fmaf(qv[e], kv[e], sc);
-        sc *= a.scale;
-        p[k] = sc;
-        mx = fmaxf(mx, sc);
-      }
-      mx = wave_max(mx);
-      float sum = 0.f;
-      for (int k = lane; k <= q; k += 64) {
-        const float e = __expf(p[k] - mx);
-        p[k] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      p[n] = sum;  // slot past the keys (buffer holds n + 1 per wave)
+  const int q = blockIdx.z * 4 + w;
+  if (q < n) {
+    const float* qv = qkv + (int64_t)q * a.ld_qkv + h * hd;
+    float mx = -INFINITY;
+    for (int k = lane; k <= q; k += 64) {
+      const float* kv = qkv + (int64_t)k * a.ld_qkv + kcol;
+      float sc = 0.f;
+      for (int e = 0; e < hd; ++e) sc = fmaf(qv[e], kv[e], sc);
+      sc *= a.scale;
+      p[k] = sc;
+      mx = fmaxf(mx, sc);
     }
-    __syncthreads();  // p[] written by one lane is read by all lanes of the wave
-    if (q < n) {
-      const float inv = 1.f / p[n];
-      for (int e = lane; e < hd; e += 64) {
-        float acc = 0.f;
-        for (int k = 0; k <= q; ++k) acc = fmaf(p[k], qkv[(int64_t)k * a.ld_qkv + vcol + e], acc);
-        out[(int64_t)q * a.ld_out + h * hd + e] = acc * inv;
-      }
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int k = lane; k <= q; k += 64) {
+      const float e = __expf(p[k] - mx);
+      p[k] = e;
+      sum += e;
     }
-    __syncthreads();
+    sum = wave_sum(sum);
+    p[n] = sum;  // slot past the keys (buffer holds n + 1 per wave)
+  }
+  __syncthreads();  // p[] written by one lane is read by all lanes of the wave
+  if (q < n) {
+    const float inv = 1.f / p[n];
+    for (int e = lane; e < hd; e += 64) {
+      float acc = 0.f;
+      for (int k = 0; k <= q; ++k) acc = fmaf(p[k], qkv[(int64_t)k * a.ld_qkv + vcol + e], acc);
+      out[(int64_t)q * a.ld_out + h * hd + e] = acc * inv;
+    }
   }
 }
 
@@ -289,7 +286,7 @@ hipError_t launch_attention(const AttnArgs& a, bool use_bf16, hipStream_t st) {
     }
   } else {
     if (a.n > 4096) return hipErrorInvalidValue;
-    dim3 grid(a.H, a.P);
+    dim3 grid(a.H, a.P, (a.n + 3) / 4);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 4 * (a.n + 1) * sizeof(float), st, a);
   }
   return hipGetLastError();

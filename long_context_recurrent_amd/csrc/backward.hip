@@ -167,37 +167,43 @@ __global__ __launch_bounds__(256) void rope_kernel(BwArgs a, float* x, int64_t p
 
 // Causal attention forward with the row statistics kept: one wave per
 // (query, head).  O[q, j] = sum_k P[q, k] V[k, kv], P = softmax(scale q.k).
+// The lanes first take keys (scores, max, sum of exponentials; P kept in the
+// wave's LDS row), then head-dimension elements (the weighted sum over keys
+// in key order).
 __global__ __launch_bounds__(256) void attn_fwd_kernel(BwArgs a, const float* qkv, float* O, float* mx, float* lsum,
                                                        int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  extern __shared__ float wrow[];   // [4][n]
   const int p = blockIdx.z, j = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + w;
   const int n = a.n, hd = a.hd, ld = a.qkv_ld;
-  if (q >= n) return;
+  const bool active = q < n;
   const int kv = j / (a.H / a.G);
   const float* base = qkv + p * qkv_ps;
-  const float* qv = base + (int64_t)q * ld + j * hd;
   const int kc = (a.H + kv) * hd, vc = (a.H + a.G + kv) * hd;
-  float m = -INFINITY;
-  for (int k = lane; k <= q; k += 64) {
-    float s = 0.f;
-    for (int e = 0; e < hd; ++e) s = fmaf(qv[e], base[(int64_t)k * ld + kc + e], s);
-    m = fmaxf(m, s * a.scale);
+  float* pr = wrow + w * n;
+  float m = -INFINITY, l = 0.f;
+  if (active) {
+    const float* qv = base + (int64_t)q * ld + j * hd;
+    for (int k = lane; k <= q; k += 64) {
+      float s = 0.f;
+      for (int e = 0; e < hd; ++e) s = fmaf(qv[e], base[(int64_t)k * ld + kc + e], s);
+      pr[k] = s * a.scale;
+      m = fmaxf(m, s * a.scale);
+    }
+    m = wave_max(m);
+    for (int k = lane; k <= q; k += 64) {
+      const float e = __expf(pr[k] - m);
+      pr[k] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    for (int k = lane; k <= q; k += 64) pr[k] = pr[k] / l;
   }
-  m = wave_max(m);
-  float l = 0.f;
-  for (int k = lane; k <= q; k += 64) {
-    float s = 0.f;
-    for (int e = 0; e < hd; ++e) s = fmaf(qv[e], base[(int64_t)k * ld + kc + e], s);
-    l += __expf(s * a.scale - m);
-  }
-  l = wave_sum(l);
+  __syncthreads();   // P rows written by one lane, read by all lanes of the wave
+  if (!active) return;
   for (int e = lane; e < hd; e += 64) {
     float acc = 0.f;
-    for (int k = 0; k <= q; ++k) {
-      float s = 0.f;
-      for (int t = 0; t < hd; ++t) s = fmaf(qv[t], base[(int64_t)k * ld + kc + t], s);
-      acc = fmaf(__expf(s * a.scale - m) / l, base[(int64_t)k * ld + vc + e], acc);
-    }
+    for (int k = 0; k <= q; ++k) acc = fmaf(pr[k], base[(int64_t)k * ld + vc + e], acc);
     O[p * o_ps + (int64_t)q * (a.H * hd) + j * hd + e] = acc;
   }
   if (lane == 0) {
@@ -226,28 +232,36 @@ __device__ __forceinline__ float att_dp(const BwArgs& a, const float* base, cons
 
 // Attention backward, part 1: one wave per (query, head):
 // Dq = sum_k P dP (= dO . O), dQ[q] = scale * sum_k P (dP - Dq) K[k].
+// Lanes take keys for dS = P (dP - Dq) (kept in the wave's LDS row), then
+// head-dimension elements for the sum over keys in key order.
 __global__ __launch_bounds__(256) void attn_bwd_q_kernel(BwArgs a, const float* qkv, const float* O, const float* dO,
                                                          const float* mx, const float* lsum, float* Dq, float* dqkv,
                                                          int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  extern __shared__ float wrow[];   // [4][n]
   const int p = blockIdx.z, j = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + w;
   const int n = a.n, hd = a.hd, ld = a.qkv_ld;
-  if (q >= n) return;
+  const bool active = q < n;
   const int kv = j / (a.H / a.G);
   const float* base = qkv + p * qkv_ps;
   const float* dOp = dO + p * o_ps;
+  float* ds = wrow + w * n;
   float dd = 0.f;
-  for (int e = lane; e < hd; e += 64)
-    dd = fmaf(dOp[(int64_t)q * (a.H * hd) + j * hd + e], O[p * o_ps + (int64_t)q * (a.H * hd) + j * hd + e], dd);
-  dd = wave_sum(dd);
-  const float m = mx[p * st_ps + (int64_t)j * n + q], l = lsum[p * st_ps + (int64_t)j * n + q];
+  if (active) {
+    for (int e = lane; e < hd; e += 64)
+      dd = fmaf(dOp[(int64_t)q * (a.H * hd) + j * hd + e], O[p * o_ps + (int64_t)q * (a.H * hd) + j * hd + e], dd);
+    dd = wave_sum(dd);
+    const float m = mx[p * st_ps + (int64_t)j * n + q], l = lsum[p * st_ps + (int64_t)j * n + q];
+    for (int k = lane; k <= q; k += 64) {
+      const float P = __expf(att_score(a, base, q, k, j, kv) - m) / l;
+      ds[k] = P * (att_dp(a, base, dOp, q, k, j, kv) - dd);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
   for (int e = lane; e < hd; e += 64) {
     float acc = 0.f;
-    for (int k = 0; k <= q; ++k) {
-      const float P = __expf(att_score(a, base, q, k, j, kv) - m) / l;
-      const float dS = P * (att_dp(a, base, dOp, q, k, j, kv) - dd);
-      acc = fmaf(dS, base[(int64_t)k * ld + (a.H + kv) * hd + e], acc);
-    }
+    for (int k = 0; k <= q; ++k) acc = fmaf(ds[k], base[(int64_t)k * ld + (a.H + kv) * hd + e], acc);
     dqkv[p * qkv_ps + (int64_t)q * ld + j * hd + e] = acc * a.scale;
   }
   if (lane == 0) Dq[p * st_ps + (int64_t)j * n + q] = dd;
@@ -256,27 +270,53 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(BwArgs a, const float* 
 // Attention backward, part 2: one wave per (key, kv-head), summing over the
 // query heads of its group and the queries at or after the key:
 // dK[k] = scale * sum P (dP - Dq) Q[q],  dV[k] = sum P dO[q].
+// Per query head, lanes take queries for P and dS (kept in the wave's LDS
+// rows), then head-dimension elements for the sums over queries in order.
 __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(BwArgs a, const float* qkv, const float* dO, const float* mx,
                                                           const float* lsum, const float* Dq, float* dqkv,
                                                           int64_t qkv_ps, int64_t o_ps, int64_t st_ps) {
+  extern __shared__ float wrow[];   // [4][2n]
   const int p = blockIdx.z, kv = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = blockIdx.x * 4 + w;
   const int n = a.n, hd = a.hd, ld = a.qkv_ld, rep = a.H / a.G;
-  if (k >= n) return;
+  const bool active = k < n;
   const float* base = qkv + p * qkv_ps;
   const float* dOp = dO + p * o_ps;
-  for (int e = lane; e < hd; e += 64) {
-    float dk = 0.f, dv = 0.f;
-    for (int j = kv * rep; j < (kv + 1) * rep; ++j)
-      for (int q = k; q < n; ++q) {
+  float* pr = wrow + w * 2 * n;
+  float* ds = pr + n;
+  float dk[2] = {0.f, 0.f}, dv[2] = {0.f, 0.f};   // e = lane, lane + 64 (hd <= 128)
+  for (int j = kv * rep; j < (kv + 1) * rep; ++j) {
+    if (active) {
+      for (int q = k + lane; q < n; q += 64) {
         const float m = mx[p * st_ps + (int64_t)j * n + q], l = lsum[p * st_ps + (int64_t)j * n + q];
         const float P = __expf(att_score(a, base, q, k, j, kv) - m) / l;
-        const float dS = P * (att_dp(a, base, dOp, q, k, j, kv) - Dq[p * st_ps + (int64_t)j * n + q]);
-        dk = fmaf(dS, base[(int64_t)q * ld + j * hd + e], dk);
-        dv = fmaf(P, dOp[(int64_t)q * (a.H * hd) + j * hd + e], dv);
+        pr[q] = P;
+        ds[q] = P * (att_dp(a, base, dOp, q, k, j, kv) - Dq[p * st_ps + (int64_t)j * n + q]);
       }
-    dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + kv) * hd + e] = dk * a.scale;
-    dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + a.G + kv) * hd + e] = dv;
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int e = lane + 64 * t;
+        if (e < hd) {
+          for (int q = k; q < n; ++q) {
+            dk[t] = fmaf(ds[q], base[(int64_t)q * ld + j * hd + e], dk[t]);
+            dv[t] = fmaf(pr[q], dOp[(int64_t)q * (a.H * hd) + j * hd + e], dv[t]);
+          }
+        }
+      }
+    }
+    __syncthreads();   // the rows are rewritten for the next query head
+  }
+  if (!active) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int e = lane + 64 * t;
+    if (e < hd) {
+      dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + kv) * hd + e] = dk[t] * a.scale;
+      dqkv[p * qkv_ps + (int64_t)k * ld + (a.H + a.G + kv) * hd + e] = dv[t];
+    }
   }
 }
 
@@ -472,17 +512,19 @@ hipError_t bw_rope(const BwArgs& a, float* x, int64_t ps, int ld, int col0, int 
 }
 hipError_t bw_attn_fwd(const BwArgs& a, const float* qkv, float* O, float* mx, float* ls, int64_t qkv_ps,
                        int64_t o_ps, int64_t st_ps, int P, hipStream_t st) {
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 0, st, a, qkv, O, mx, ls, qkv_ps, o_ps,
-                     st_ps);
+  if (a.n > 4096 || a.hd > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 4 * a.n * sizeof(float), st, a, qkv, O,
+                     mx, ls, qkv_ps, o_ps, st_ps);
   return hipGetLastError();
 }
 hipError_t bw_attn_bwd(const BwArgs& a, const float* qkv, const float* O, const float* dO, const float* mx,
                        const float* ls, float* Dq, float* dqkv, int64_t qkv_ps, int64_t o_ps, int64_t st_ps, int P,
                        hipStream_t st) {
-  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 0, st, a, qkv, O, dO, mx, ls, Dq,
-                     dqkv, qkv_ps, o_ps, st_ps);
-  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((a.n + 3) / 4, a.G, P), dim3(256), 0, st, a, qkv, dO, mx, ls, Dq, dqkv,
-                     qkv_ps, o_ps, st_ps);
+  if (a.n > 4096 || a.hd > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((a.n + 3) / 4, a.H, P), dim3(256), 4 * a.n * sizeof(float), st, a, qkv,
+                     O, dO, mx, ls, Dq, dqkv, qkv_ps, o_ps, st_ps);
+  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((a.n + 3) / 4, a.G, P), dim3(256), 8 * a.n * sizeof(float), st, a, qkv,
+                     dO, mx, ls, Dq, dqkv, qkv_ps, o_ps, st_ps);
   return hipGetLastError();
 }
 hipError_t bw_swiglu(const float* G, const float* Up, float* Uo, int64_t count, int64_t ps, int P, hipStream_t st) {
