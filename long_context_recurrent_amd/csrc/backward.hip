@@ -25,43 +25,65 @@ __device__ __forceinline__ float dphi_f(float u) { return u > 0.f ? 1.f : __expf
 // ---------------------------------------------------------------------------
 // Generic strided GEMM, P problems: C = beta * C + A B with
 // A(m, k) = A + p*a_ps + m*a_rs + k*a_cs, B(k, n) likewise, C(m, n) likewise.
-// 32 x 32 outputs per workgroup, 2 x 2 per thread, K in steps of 32 via LDS.
+// TM x TN outputs per workgroup of 16 x 16 threads, (TM/16) x (TN/16) per
+// thread; K in steps of 16 staged in LDS k-major.  Tile loads put consecutive
+// threads on whichever index of the operand is contiguous in memory, so both
+// a matrix and its transpose load coalesced.  Every output accumulates its
+// products one k at a time in increasing k with fused multiply-adds, whatever
+// the tile shape.
 // ---------------------------------------------------------------------------
+template <int TM, int TN>
 __global__ __launch_bounds__(256) void gemm_gen_kernel(GenGemm g) {
-  __shared__ float As[32][33];
-  __shared__ float Bs[32][33];
+  constexpr int KS = 16, RM = TM / 16, RN = TN / 16;
+  __shared__ __attribute__((aligned(16))) float As[KS][TM + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[KS][TN + 4];
   const int p = blockIdx.z;
   const float* A = g.A + (int64_t)p * g.a_ps;
   const float* B = g.B + (int64_t)p * g.b_ps;
   float* C = g.C + (int64_t)p * g.c_ps;
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  for (int k0 = 0; k0 < g.K; k0 += 32) {
-    for (int i = tid; i < 32 * 32; i += 256) {
-      const int r = i >> 5, c = i & 31;
+  const bool a_kc = g.a_cs == 1, b_nc = g.b_cs == 1;   // contiguous along k (A) / along n (B)
+  float acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < g.K; k0 += KS) {
+#pragma unroll
+    for (int t = 0; t < TM * KS / 256; ++t) {
+      const int idx = tid + 256 * t;
+      const int r = a_kc ? idx / KS : idx % TM, c = a_kc ? idx % KS : idx / TM;
       const int m = m0 + r, k = k0 + c;
-      As[r][c] = (m < g.M && k < g.K) ? A[(int64_t)m * g.a_rs + (int64_t)k * g.a_cs] : 0.f;
+      As[c][r] = (m < g.M && k < g.K) ? A[(int64_t)m * g.a_rs + (int64_t)k * g.a_cs] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < TN * KS / 256; ++t) {
+      const int idx = tid + 256 * t;
+      const int c = b_nc ? idx % TN : idx / KS, r = b_nc ? idx / TN : idx % KS;
       const int kk = k0 + r, n = n0 + c;
       Bs[r][c] = (kk < g.K && n < g.N) ? B[(int64_t)kk * g.b_rs + (int64_t)n * g.b_cs] : 0.f;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-      const float a0 = As[ty * 2][k], a1 = As[ty * 2 + 1][k];
-      const float b0 = Bs[k][tx * 2], b1 = Bs[k][tx * 2 + 1];
-      acc[0][0] = fmaf(a0, b0, acc[0][0]);
-      acc[0][1] = fmaf(a0, b1, acc[0][1]);
-      acc[1][0] = fmaf(a1, b0, acc[1][0]);
-      acc[1][1] = fmaf(a1, b1, acc[1][1]);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      float av[RM], bv[RN];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) av[i] = As[k][ty * RM + i];
+#pragma unroll
+      for (int j = 0; j < RN; ++j) bv[j] = Bs[k][tx * RN + j];
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = m0 + ty * 2 + i, n = n0 + tx * 2 + j;
+    for (int j = 0; j < RN; ++j) {
+      const int m = m0 + ty * RM + i, n = n0 + tx * RN + j;
       if (m < g.M && n < g.N) {
         float* c = C + (int64_t)m * g.c_rs + (int64_t)n * g.c_cs;
         *c = g.accumulate ? *c + acc[i][j] : acc[i][j];
@@ -137,14 +159,29 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(BwArgs a, const float* x, 
 }
 
 // dg[i] += sum over rows of dy[r, i] * x[r, i] * rs[r]   (one column per thread)
-__global__ __launch_bounds__(256) void rms_dgain_kernel(BwArgs a, const float* x, const float* rs, const float* dy,
+__global__ __launch_bounds__(64) void rms_dgain_kernel(BwArgs a, const float* x, const float* rs, const float* dy,
                                                         float* dg, int64_t ps, int64_t g_ps, int rows) {
   const int p = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= a.d) return;
+  const float* dyp = dy + p * ps + i;
+  const float* xp = x + p * ps + i;
+  const float* rp = rs + p * (int64_t)a.row_ps;
   float s = 0.f;
-  for (int r = 0; r < rows; ++r)
-    s = fmaf(dy[p * ps + (int64_t)r * a.d + i], x[p * ps + (int64_t)r * a.d + i] * rs[p * (int64_t)a.row_ps + r], s);
+  int r = 0;
+  // rows in order; the loads of 8 rows are issued before their products
+  for (; r + 8 <= rows; r += 8) {
+    float dv[8], xv[8], rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dv[u] = dyp[(int64_t)(r + u) * a.d];
+      xv[u] = xp[(int64_t)(r + u) * a.d];
+      rv[u] = rp[r + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = fmaf(dv[u], xv[u] * rv[u], s);
+  }
+  for (; r < rows; ++r) s = fmaf(dyp[(int64_t)r * a.d], xp[(int64_t)r * a.d] * rp[r], s);
   dg[p * g_ps + i] += s;
 }
 
@@ -447,7 +484,25 @@ __global__ __launch_bounds__(64) void memr_dq_kernel(BwArgs a, float* dq, const 
   const int p = blockIdx.x, j = threadIdx.x;
   const float zj = z[p * z_ps + j];
   float acc = 0.f;
-  for (int r = 0; r < rows; ++r) {
+  int r = 0;
+  // rows in order; the loads of 8 rows are issued before their updates
+  for (; r + 8 <= rows; r += 8) {
+    float dqv[8], uv[8], qv[8], ddv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t o = p * u_ps + (int64_t)(r + t) * 64 + j;
+      dqv[t] = dq[o];
+      uv[t] = u[o];
+      qv[t] = q[o];
+      ddv[t] = dden[p * (int64_t)a.row_ps + r + t];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      dq[p * u_ps + (int64_t)(r + t) * 64 + j] = (dqv[t] + ddv[t] * zj) * dphi_f(uv[t]);
+      acc = fmaf(ddv[t], qv[t], acc);
+    }
+  }
+  for (; r < rows; ++r) {
     const int64_t o = p * u_ps + (int64_t)r * 64 + j;
     const float dd = dden[p * (int64_t)a.row_ps + r];
     dq[o] = (dq[o] + dd * zj) * dphi_f(u[o]);
@@ -473,7 +528,13 @@ __global__ __launch_bounds__(256) void bw_copy_kernel(const float* src, float* d
 // ---------------------------------------------------------------------------
 hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st) {
   if (P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_gen_kernel, dim3((g.N + 31) / 32, (g.M + 31) / 32, P), dim3(256), 0, st, g);
+  // 64 x 64 tiles only where they still give two workgroups per CU; the
+  // products here are small, and the number of workgroups sets their speed
+  const int64_t big = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64) * P;
+  if (g.M >= 64 && g.N >= 64 && big >= 512)
+    hipLaunchKernelGGL((gemm_gen_kernel<64, 64>), dim3((g.N + 63) / 64, (g.M + 63) / 64, P), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_gen_kernel<32, 32>), dim3((g.N + 31) / 32, (g.M + 31) / 32, P), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
@@ -498,8 +559,7 @@ hipError_t bw_rms_fwd(const BwArgs& a, const float* x, const float* g, float* ou
 }
 hipError_t bw_rms_bwd(const BwArgs& a, const float* x, const float* g, const float* rs, const float* dy, float* dx,
                       float* dg, int64_t ps, int64_t g_ps, int rows, int accumulate, int P, hipStream_t st) {
-  hipLaunchKernelGGL(rms_dgain_kernel, dim3((a.d + 255) / 256, P), dim3(256), 0, st, a, x, rs, dy, dg, ps, g_ps,
-                     rows);
+  hipLaunchKernelGGL(rms_dgain_kernel, dim3((a.d + 63) / 64, P), dim3(64), 0, st, a, x, rs, dy, dg, ps, g_ps, rows);
   hipLaunchKernelGGL(rms_bwd_kernel, rows_grid(rows, P), dim3(256), 0, st, a, x, g, rs, dy, dx, ps, g_ps, rows,
                      accumulate);
   return hipGetLastError();
