@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3   # fp32 vector, published (packed fp32 counted)
 METRIC = "tokens/s, 131K-token 1B-shape ARMT forward (diag vs seq); GEMM MFMA util %"
 
 
@@ -660,17 +661,53 @@ def backward_bench(args, dev):
         results[sched] = (statistics.median(each), dx.clone())
     y_t = statistics.median([timed_forward(model, x) for _ in range(3)])
     same = bool(torch.equal(results["diagonal"][1], results["sequential"][1]))
+    # algorithmic work of forward + backward: every product of the forward has
+    # two in the backward (input and weight gradients; for attention dV, dP,
+    # dQ and dK), so three times the forward's FLOPs; the recomputation of
+    # the forward inside the backward is not counted
+    flops = 3 * node_gflop(cfg) * 1e9 * S * L
+    cpu = None if args.no_cpu else grad_cpu_baseline(inp, S)
     for sched in ("diagonal", "sequential"):
         t = results[sched][0]
+        achieved = flops / t / 1e12
         line = {"workload": cfg.name, "dtype": "f32", "schedule": sched, "tokens": S * T,
                 "ms_forward_plus_backward": t * 1e3, "tokens_per_s": S * T / t,
                 "ms_forward_alone": y_t * 1e3, "bitwise_equal_schedules": same,
-                "kernels": "fp32 SIMT (not tuned)"}
-        log(f"{sched}: forward + backward {t * 1e3:.1f} ms ({S * T / t:.0f} tokens/s); forward alone "
-            f"{y_t * 1e3:.1f} ms")
+                "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                             "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
+                             "work": "3 x forward FLOPs (forward + input and weight gradients)"},
+                "cpu_baseline": cpu if sched == "diagonal" else None,
+                "kernels": "fp32 vector ALU (no packed fp32, no matrix cores)"}
+        log(f"{sched}: forward + backward {t * 1e3:.1f} ms ({S * T / t:.0f} tokens/s, {achieved:.2f} TFLOP/s); "
+            f"forward alone {y_t * 1e3:.1f} ms")
         print(json.dumps(line), flush=True)
     log(f"grouped backward speed-up {results['sequential'][0] / results['diagonal'][0]:.2f}x")
     model.close()
+
+
+def grad_cpu_baseline(inp, n_seg):
+    """The gradient oracle (float64 autograd) on the first `n_seg` segments
+    of the workload: tokens/s of forward + backward on the host."""
+    import numpy as np
+    from oracle import armt_grad
+    import torch
+    cores = torch.get_num_threads()   # autograd's CPU kernels run on torch's thread pool
+    cfg = inp.cfg
+    rows = n_seg * cfg.seg_len
+    sub = inp.__class__(**{**inp.__dict__, "cfg": cfg.with_(n_segments=n_seg), "x": inp.x[:rows]})
+    rng = np.random.default_rng(0)
+    dy = rng.standard_normal((rows, cfg.d_model))
+    L = cfg.n_layers
+    dA = np.zeros((L, cfg.d_model, cfg.d_key))
+    dz = np.zeros((L, cfg.d_key))
+    a = time.perf_counter()
+    armt_grad.vjp(sub, None, None, dy, dA, dz)
+    el = time.perf_counter() - a
+    value = rows / el
+    log(f"cpu gradient oracle: {n_seg} segments in {el:.1f}s -> {value:.0f} tokens/s")
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_cpu(),
+            "sample": f"forward + backward of the first {n_seg} of {cfg.n_segments} segments by float64 autograd "
+                      f"({rows} tokens) in {el:.1f}s"}
 
 
 def timed_forward(model, x):

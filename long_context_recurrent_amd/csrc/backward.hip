@@ -9,8 +9,10 @@
 // per-layer weight gradients take one node's contribution per wave with
 // plain read-modify-write and the result does not depend on the wave width.
 //
-// These are plain SIMT fp32 kernels: the backward is built for correctness at
-// the fp32 workloads' sizes, not tuned.
+// These are fp32 kernels on the vector ALU (no matrix cores, no packed fp32):
+// a generic strided GEMM with coalesced tile loads for either operand
+// orientation, attention kernels that form each (query, key) score once and
+// keep a row of probabilities in LDS, and row / element kernels.
 #include <cmath>
 
 #include "armt_common.h"
