@@ -3,7 +3,8 @@ gradient oracle (PyTorch autograd over a float64 restatement of the forward,
 pinned to finite differences): the gradients of <y, dy> + <A_out, dA_out> +
 <z_out, dz_out> with respect to x, A0, z0 and all twelve weight tensors,
 relative L2 <= 1e-4 each; the grouped (reversed diagonal waves) and the
-node-by-node backward bitwise equal.
+node-by-node backward bitwise equal.  The shapes run from a single node to the
+timed backward workload itself (8 layers, 32 segments of 128 + 8 tokens).
 """
 
 import sys
@@ -29,6 +30,13 @@ CASES = [
                n_kv_heads=2, head_dim=32, ffn_hidden=192),
     TINY.with_(name="bw_l1_s1", n_layers=1, n_segments=1, seg_len=7, n_mem=2, d_model=64, n_heads=1, n_kv_heads=1,
                head_dim=64, ffn_hidden=128),
+    # head dimension 128 (two elements per lane in the attention backward),
+    # 64 x 64 GEMM tiles, a node longer than one 64-key lane sweep
+    TINY.with_(name="bw_hd128", n_layers=4, n_segments=3, seg_len=200, n_mem=8, d_model=256, n_heads=2,
+               n_kv_heads=1, head_dim=128, ffn_hidden=512),
+    # the timed backward workload (8 layers, 32 segments of 128 + 8 tokens)
+    TINY.with_(name="bw_bench", n_layers=8, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_hidden=512,
+               seg_len=128, n_mem=8, n_segments=32),
 ]
 
 
