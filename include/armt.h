@@ -241,8 +241,7 @@ int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y)
  *          256-byte aligned
  * Asynchronous on the handle's stream; uses the handle's workspace too (must
  * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for bf16 or
- * batched handles.  Kernels: plain fp32 SIMT, built for correctness at the
- * fp32 workloads' sizes. */
+ * batched handles.  Kernels: fp32 on the vector ALU (no matrix cores). */
 int armt_backward_workspace_size(armt_handle *h, int32_t n_segments, size_t *bytes);
 int armt_backward(armt_handle *h, int32_t schedule, const void *x, int32_t n_segments,
                   const float *A0, const float *z0, const void *dy, const float *dA_out,
