@@ -221,7 +221,7 @@ int armt_llama_create(const armt_config *cfg, const armt_weights *w, int64_t max
                       void *workspace, size_t ws_bytes, void *hip_stream, armt_handle **out);
 int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y);
 
-/* Backward pass (training; ARMT_F32 handles with batch 1): the gradients of
+/* Backward pass (training; handles with batch 1): the gradients of
  *   <y, dy> + <A_out, dA_out> + <z_out, dz_out>
  * with respect to x, A0, z0 and every weight, for the forward of
  * armt_forward_diagonal / _sequential over n_segments full segments.  Node
@@ -232,16 +232,21 @@ int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y)
  * backward; Pith review, "What carries the argument").  A forward pass first
  * records each node's input rows and the state it read in the workspace; each
  * node's activations are recomputed from that record.
- *   x, dy  [S*T, d] fp32;  A0, dA_out [L, d, d_k], z0, dz_out [L, d_k] fp32
- *          (A0, z0, dA_out, dz_out may be NULL for zeros)
+ *   x, dy  [S*T, d] in the handle's dtype;  A0, dA_out [L, d, d_k],
+ *          z0, dz_out [L, d_k] fp32 (A0, z0, dA_out, dz_out may be NULL for
+ *          zeros)
  *   dx [S*T, d], dA0 [L, d, d_k], dz0 [L, d_k] fp32 (outputs)
  *   grads  gradient buffers with the layout of armt_weights, fp32, device
  *          memory; overwritten
  *   workspace  device memory of armt_backward_workspace_size bytes,
  *          256-byte aligned
+ * For an ARMT_BF16 handle the recording forward is the bf16 forward, and each
+ * node is differentiated in fp32 at the input rows that forward gave it, with
+ * the bf16 weights widened exactly: the forward's bf16 roundings of branch
+ * activations count as identity in the gradient.
  * Asynchronous on the handle's stream; uses the handle's workspace too (must
- * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for bf16 or
- * batched handles.  Kernels: fp32 on the vector ALU (no matrix cores). */
+ * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for batched
+ * handles.  Kernels: fp32 on the vector ALU (no matrix cores). */
 int armt_backward_workspace_size(armt_handle *h, int32_t n_segments, size_t *bytes);
 int armt_backward(armt_handle *h, int32_t schedule, const void *x, int32_t n_segments,
                   const float *A0, const float *z0, const void *dy, const float *dA_out,

@@ -101,10 +101,11 @@ struct NormArgs {
 // A(m, k) = A + p*a_ps + m*a_rs + k*a_cs, B(k, n) and C(m, n) likewise.
 struct GenGemm {
   const float* A;
-  const float* B;
+  const void* B;             // fp32, or bf16 when b_bf16 (strides in elements)
   float* C;
   int64_t a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs;
   int M, N, K, accumulate;
+  int b_bf16;
 };
 
 // Shapes shared by the backward kernels.

@@ -915,7 +915,7 @@ struct BwLayout {
   size_t qkv, dqkv, O, dO, mx, ls, Dq;
   size_t G, Up, Uo, dG, dUp, dUo;
   size_t uk, k, dk, v, kA, e, de, dv, dkA, bl, beta, denw, ddenw, dbl;
-  size_t dH, dA, dz, yscr, total;
+  size_t dH, dA, dz, yscr, g32, total;
 };
 
 BwLayout make_bw_layout(const armt_config* c, int S) {
@@ -945,6 +945,7 @@ BwLayout make_bw_layout(const armt_config* c, int S) {
   lo.dA = take(L * d * 64);
   lo.dz = take(L * 64);
   lo.yscr = take((size_t)S * c->seg_len * d);   // the recording forward's y (not returned)
+  lo.g32 = take(3 * L * d);                      // fp32 g_attn, g_mlp, w_beta of a bf16 model
   lo.total = off;
   return lo;
 }
@@ -956,14 +957,16 @@ struct BwCtx {
   char* ws;
   BwLayout lo;
   const armt_weights* gw;   // gradient buffers (fp32, weight shapes)
+  const float *g_attn, *g_mlp, *w_beta;   // fp32 views of the gains and the gate vector
   float* f(size_t at) const { return (float*)(ws + at); }
 };
 
-// C = (acc ? C : 0) + A B over P problems (strides in floats)
-hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const float* B, int64_t b_ps, int64_t b_rs,
+// C = (acc ? C : 0) + A B over P problems
+// (strides in elements; B is bf16 when b16 is set)
+hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_ps, int64_t b_rs,
               int64_t b_cs, float* C, int64_t c_ps, int64_t c_rs, int64_t c_cs, int M, int N, int K, int acc, int P,
-              hipStream_t st) {
-  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc};
+              hipStream_t st, int b16 = 0) {
+  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16};
   return launch_gemm_gen(g, P, st);
 }
 
@@ -974,7 +977,7 @@ hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const fl
   } while (0)
 
 // Backward of the nodes (c - l, l) for l = l0 .. l0 + P - 1 (wave c).
-hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float* dx) {
+hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float* dx) {
   armt_handle* h = cx.h;
   const armt_config& cf = h->cfg;
   const int L = cf.n_layers, S = cx.S, d = cf.d_model, n = h->n, M = cf.n_mem, T = cf.seg_len, F = cf.ffn_hidden;
@@ -992,17 +995,21 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float
   const float* Ast = cx.f(cx.lo.tape_A) + tap * D64;
   const float* zst = cx.f(cx.lo.tape_z) + tap * 64;
   const int64_t hin_ps = (int64_t)(S - 1) * nd, A_ps = (int64_t)(S - 1) * D64, z_ps = (int64_t)(S - 1) * 64;
-  const float* W_mq = (const float*)h->w.w_mq + (int64_t)l0 * 64 * d;
-  const float* W_qkv = (const float*)h->w.w_qkv + (int64_t)l0 * qd * d;
-  const float* W_o = (const float*)h->w.w_o + (int64_t)l0 * d * hhd;
-  const float* W_g = (const float*)h->w.w_gate + (int64_t)l0 * F * d;
-  const float* W_u = (const float*)h->w.w_up + (int64_t)l0 * F * d;
-  const float* W_d = (const float*)h->w.w_down + (int64_t)l0 * d * F;
-  const float* W_mk = (const float*)h->w.w_mk + (int64_t)l0 * 64 * d;
-  const float* W_mv = (const float*)h->w.w_mv + (int64_t)l0 * d * d;
-  const float* w_b = (const float*)h->w.w_beta + (int64_t)l0 * d;
-  const float* g_at = (const float*)h->w.g_attn + (int64_t)l0 * d;
-  const float* g_ml = (const float*)h->w.g_mlp + (int64_t)l0 * d;
+  // weight matrices in the model's dtype (bf16 ones are widened exactly as
+  // the products load them); gains and the gate vector as fp32 views
+  const int wb = h->bf16 ? 1 : 0;
+  auto wp = [&](const void* base, int64_t elems) { return (const void*)((const char*)base + elems * (wb ? 2 : 4)); };
+  const void* W_mq = wp(h->w.w_mq, (int64_t)l0 * 64 * d);
+  const void* W_qkv = wp(h->w.w_qkv, (int64_t)l0 * qd * d);
+  const void* W_o = wp(h->w.w_o, (int64_t)l0 * d * hhd);
+  const void* W_g = wp(h->w.w_gate, (int64_t)l0 * F * d);
+  const void* W_u = wp(h->w.w_up, (int64_t)l0 * F * d);
+  const void* W_d = wp(h->w.w_down, (int64_t)l0 * d * F);
+  const void* W_mk = wp(h->w.w_mk, (int64_t)l0 * 64 * d);
+  const void* W_mv = wp(h->w.w_mv, (int64_t)l0 * d * d);
+  const float* w_b = cx.w_beta + (int64_t)l0 * d;
+  const float* g_at = cx.g_attn + (int64_t)l0 * d;
+  const float* g_ml = cx.g_mlp + (int64_t)l0 * d;
   float* dW_mq = (float*)cx.gw->w_mq + (int64_t)l0 * 64 * d;
   float* dW_qkv = (float*)cx.gw->w_qkv + (int64_t)l0 * qd * d;
   float* dW_o = (float*)cx.gw->w_o + (int64_t)l0 * d * hhd;
@@ -1040,32 +1047,33 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float
   if (l_hi == L - 1) {
     float* top = dh + (int64_t)(P - 1) * nd;
     const int s = c - (L - 1);
-    BW_TRY(bw_copy(dy + (int64_t)s * T * d, top, (int64_t)T * d, 0, 0, 0, 1, st));
+    if (wb) BW_TRY(launch_widen((const bf16*)dy + (int64_t)s * T * d, top, (int64_t)T * d, true, st));
+    else BW_TRY(bw_copy((const float*)dy + (int64_t)s * T * d, top, (int64_t)T * d, 0, 0, 0, 1, st));
     BW_TRY(hipMemsetAsync(top + (int64_t)T * d, 0, (size_t)M * d * 4, st));
   }
 
   // ---- recompute the forward of each node
-  BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st));
+  BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st, wb));
   BW_TRY(bw_phi_den(ba, u, q, den, zst, n64, z_ps, n, P, st));
   BW_TRY(gg(q, n64, 64, 1, Ast, A_ps, 1, 64, num, nd, d, 1, n, d, 64, 0, P, st));
   BW_TRY(bw_copy(hin, h1, nd, hin_ps, nd, 0, P, st));
   BW_TRY(bw_add_div(ba, h1, num, den, h1, nd, n, P, st));
   BW_TRY(bw_rms_fwd(ba, h1, g_at, a, r1, nd, d, n, P, st));
-  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st));
+  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb));
   BW_TRY(bw_rope(ba, qkv, nq, qd, 0, H, 1.f, n, P, st));
   BW_TRY(bw_rope(ba, qkv, nq, qd, H * hd, G, 1.f, n, P, st));
   BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   BW_TRY(bw_copy(h1, h2, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st));
+  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb));
   BW_TRY(bw_rms_fwd(ba, h2, g_ml, b, r2, nd, d, n, P, st));
-  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st));
-  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st));
+  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb));
+  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb));
   BW_TRY(bw_swiglu(Gt, Up, Uo, nF, nF, P, st));
   BW_TRY(bw_copy(h2, h3, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st));
+  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb));
   const float* Y = h3 + (int64_t)T * d;
-  BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st));
-  BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st));
+  BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st, wb));
+  BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st, wb));
   BW_TRY(gg(Y, nd, d, 1, w_b, d, 1, 0, bl, M, 1, 0, M, 1, d, 0, P, st));
   BwArgs bm = ba;
   bm.row_ps = M;
@@ -1081,27 +1089,27 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float
   BW_TRY(gg(dkA, Md, d, 1, Ast, A_ps, 64, 1, dk, M64, 64, 1, M, 64, d, 1, P, st));
   BW_TRY(bw_memw_dk(ba, dk, uk, kk, ddenw, zst, dz, z_ps, 64, P, st));
   float* dY = dh + (int64_t)T * d;
-  BW_TRY(gg(dk, M64, 64, 1, W_mk, 64 * (int64_t)d, d, 1, dY, nd, d, 1, M, d, 64, 1, P, st));
-  BW_TRY(gg(dv, Md, d, 1, W_mv, (int64_t)d * d, d, 1, dY, nd, d, 1, M, d, d, 1, P, st));
+  BW_TRY(gg(dk, M64, 64, 1, W_mk, 64 * (int64_t)d, d, 1, dY, nd, d, 1, M, d, 64, 1, P, st, wb));
+  BW_TRY(gg(dv, Md, d, 1, W_mv, (int64_t)d * d, d, 1, dY, nd, d, 1, M, d, d, 1, P, st, wb));
   BW_TRY(bw_memw_beta(ba, dbl, w_b, Y, dY, dw_b, nd, d, P, st));
   BW_TRY(gg(dk, M64, 1, 64, Y, nd, d, 1, dW_mk, 64 * (int64_t)d, d, 1, 64, d, M, 1, P, st));
   BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st));
   // ---- MLP block backward
-  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st));
+  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb));
   BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
-  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st));
-  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st));
+  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb));
+  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb));
   BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
   BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
   BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
   // ---- attention block backward
-  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st));
+  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb));
   BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st));
   BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
-  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st));
+  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb));
   BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st));
   BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
   // ---- memory read backward
@@ -1109,7 +1117,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float
   BW_TRY(gg(dnum, nd, d, 1, Ast, A_ps, 64, 1, dq, n64, 64, 1, n, 64, d, 0, P, st));
   BW_TRY(gg(dnum, nd, 1, d, q, n64, 64, 1, dA, D64, 64, 1, d, 64, n, 1, P, st));
   BW_TRY(bw_memr_dq(ba, dq, u, q, dden, zst, dz, n64, z_ps, 64, n, P, st));
-  BW_TRY(gg(dq, n64, 64, 1, W_mq, 64 * (int64_t)d, d, 1, dh, nd, d, 1, n, d, 64, 1, P, st));
+  BW_TRY(gg(dq, n64, 64, 1, W_mq, 64 * (int64_t)d, d, 1, dh, nd, d, 1, n, d, 64, 1, P, st, wb));
   BW_TRY(gg(dq, n64, 1, 64, hin, hin_ps, d, 1, dW_mq, 64 * (int64_t)d, d, 1, 64, d, n, 1, P, st));
 
   // ---- the gradient of each node's input rows: to the layer below, or to x
@@ -1127,7 +1135,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const float* dy, float
 
 // Record node (c - l, l)'s input rows and the state it reads, l = l0 ..
 // l0 + P - 1, before wave c runs.
-hipError_t save_wave(BwCtx& cx, int c, int l0, int P, const float* x) {
+hipError_t save_wave(BwCtx& cx, int c, int l0, int P, const void* x) {
   armt_handle* h = cx.h;
   const armt_config& cf = h->cfg;
   const int S = cx.S, d = cf.d_model, n = h->n, T = cf.seg_len, M = cf.n_mem;
@@ -1139,8 +1147,13 @@ hipError_t save_wave(BwCtx& cx, int c, int l0, int P, const float* x) {
   const int p0 = (l0 == 0) ? 1 : 0;
   if (l0 == 0) {
     const int s = c;
-    BW_TRY(bw_copy(x + (int64_t)s * T * d, th, (int64_t)T * d, 0, 0, 0, 1, st));
-    BW_TRY(bw_copy((const float*)h->w.mem_emb, th + (int64_t)T * d, (int64_t)M * d, 0, 0, 0, 1, st));
+    if (h->bf16) {
+      BW_TRY(launch_widen((const bf16*)x + (int64_t)s * T * d, th, (int64_t)T * d, true, st));
+      BW_TRY(launch_widen(h->w.mem_emb, th + (int64_t)T * d, (int64_t)M * d, true, st));
+    } else {
+      BW_TRY(bw_copy((const float*)x + (int64_t)s * T * d, th, (int64_t)T * d, 0, 0, 0, 1, st));
+      BW_TRY(bw_copy((const float*)h->w.mem_emb, th + (int64_t)T * d, (int64_t)M * d, 0, 0, 0, 1, st));
+    }
   }
   if (P - p0 > 0) {
     const float* prev = (const float*)h->act[(c - 1) & 1] + (int64_t)(l0 + p0 - 1) * nd;
@@ -1158,7 +1171,6 @@ extern "C" {
 int armt_backward_workspace_size(armt_handle* h, int32_t n_segments, size_t* bytes) {
   if (!h || !bytes) return fail(ARMT_E_INVALID, "NULL argument");
   if (h->llama) return fail(ARMT_E_INVALID, "handle is a full-attention comparator");
-  if (h->bf16) return fail(ARMT_E_UNSUPPORTED, "the backward runs on ARMT_F32 handles");
   if (h->batch != 1) return fail(ARMT_E_UNSUPPORTED, "the backward runs on batch-1 handles");
   if (n_segments < 1) return fail(ARMT_E_INVALID, "n_segments must be >= 1");
   *bytes = make_bw_layout(&h->cfg, n_segments).total;
@@ -1184,8 +1196,22 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
   const int qd = h->qkv_dim, hhd = c.n_heads * c.head_dim;
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-  BwCtx cx{h, h->stream, S, (char*)workspace, make_bw_layout(&c, S), grads};
+  BwCtx cx{h, h->stream, S, (char*)workspace, make_bw_layout(&c, S), grads, nullptr, nullptr, nullptr};
   hipStream_t st = h->stream;
+  if (h->bf16) {
+    float* g32 = cx.f(cx.lo.g32);
+    const int64_t Ld = (int64_t)L * d;
+    if ((e = launch_widen(h->w.g_attn, g32, Ld, true, st)) != hipSuccess) return hip_fail(e, "widen gains");
+    if ((e = launch_widen(h->w.g_mlp, g32 + Ld, Ld, true, st)) != hipSuccess) return hip_fail(e, "widen gains");
+    if ((e = launch_widen(h->w.w_beta, g32 + 2 * Ld, Ld, true, st)) != hipSuccess) return hip_fail(e, "widen gains");
+    cx.g_attn = g32;
+    cx.g_mlp = g32 + Ld;
+    cx.w_beta = g32 + 2 * Ld;
+  } else {
+    cx.g_attn = (const float*)h->w.g_attn;
+    cx.g_mlp = (const float*)h->w.g_mlp;
+    cx.w_beta = (const float*)h->w.w_beta;
+  }
   // 1. forward, recording the tape (direct launches, the chosen order)
   const int64_t a_count = (int64_t)L * d * 64, z_count = (int64_t)L * 64;
   if ((e = launch_set_desc(h->desc, x, cx.f(cx.lo.yscr), 0, S, c.seg_len, (int64_t)S * c.seg_len, st)) != hipSuccess)
@@ -1196,13 +1222,13 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
   if (schedule == 0) {
     for (int w = 0; w < S + L - 1; ++w) {
       const int l_lo = w - S + 1 > 0 ? w - S + 1 : 0, l_hi = w < L - 1 ? w : L - 1;
-      if ((e = save_wave(cx, w, l_lo, l_hi - l_lo + 1, (const float*)x)) != hipSuccess) return hip_fail(e, "tape");
+      if ((e = save_wave(cx, w, l_lo, l_hi - l_lo + 1, x)) != hipSuccess) return hip_fail(e, "tape");
       if ((e = enqueue_step(sc, l_lo, l_hi, w & 1, 1)) != hipSuccess) return hip_fail(e, "forward");
     }
   } else {
     for (int s = 0; s < S; ++s)
       for (int l = 0; l < L; ++l) {
-        if ((e = save_wave(cx, s + l, l, 1, (const float*)x)) != hipSuccess) return hip_fail(e, "tape");
+        if ((e = save_wave(cx, s + l, l, 1, x)) != hipSuccess) return hip_fail(e, "tape");
         if ((e = enqueue_step(sc, l, l, (s + l) & 1, l == L - 1 ? 2 - L : 1)) != hipSuccess) return hip_fail(e, "forward");
       }
   }
@@ -1218,13 +1244,13 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
   if (schedule == 0) {
     for (int w = S + L - 2; w >= 0; --w) {
       const int l_lo = w - S + 1 > 0 ? w - S + 1 : 0, l_hi = w < L - 1 ? w : L - 1;
-      if ((e = backward_wave(cx, w, l_lo, l_hi - l_lo + 1, (const float*)dy, (float*)dx)) != hipSuccess)
+      if ((e = backward_wave(cx, w, l_lo, l_hi - l_lo + 1, dy, (float*)dx)) != hipSuccess)
         return hip_fail(e, "backward");
     }
   } else {
     for (int s = S - 1; s >= 0; --s)
       for (int l = L - 1; l >= 0; --l)
-        if ((e = backward_wave(cx, s + l, l, 1, (const float*)dy, (float*)dx)) != hipSuccess)
+        if ((e = backward_wave(cx, s + l, l, 1, dy, (float*)dx)) != hipSuccess)
           return hip_fail(e, "backward");
   }
   if ((e = hipMemcpyAsync(dA0, cx.f(cx.lo.dA), a_count * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)

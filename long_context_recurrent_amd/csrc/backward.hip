@@ -32,16 +32,17 @@ __device__ __forceinline__ float dphi_f(float u) { return u > 0.f ? 1.f : __expf
 // threads on whichever index of the operand is contiguous in memory, so both
 // a matrix and its transpose load coalesced.  Every output accumulates its
 // products one k at a time in increasing k with fused multiply-adds, whatever
-// the tile shape.
+// the tile shape.  B may hold bf16 values (the weights of a bf16 model),
+// widened exactly on load.
 // ---------------------------------------------------------------------------
-template <int TM, int TN>
+template <int TM, int TN, typename BT>
 __global__ __launch_bounds__(256) void gemm_gen_kernel(GenGemm g) {
   constexpr int KS = 16, RM = TM / 16, RN = TN / 16;
   __shared__ __attribute__((aligned(16))) float As[KS][TM + 4];
   __shared__ __attribute__((aligned(16))) float Bs[KS][TN + 4];
   const int p = blockIdx.z;
   const float* A = g.A + (int64_t)p * g.a_ps;
-  const float* B = g.B + (int64_t)p * g.b_ps;
+  const BT* B = (const BT*)g.B + (int64_t)p * g.b_ps;
   float* C = g.C + (int64_t)p * g.c_ps;
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(GenGemm g) {
       const int idx = tid + 256 * t;
       const int c = b_nc ? idx % TN : idx / KS, r = b_nc ? idx / TN : idx % KS;
       const int kk = k0 + r, n = n0 + c;
-      Bs[r][c] = (kk < g.K && n < g.N) ? B[(int64_t)kk * g.b_rs + (int64_t)n * g.b_cs] : 0.f;
+      Bs[r][c] = (kk < g.K && n < g.N) ? (float)B[(int64_t)kk * g.b_rs + (int64_t)n * g.b_cs] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -533,10 +534,14 @@ hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st) {
   // 64 x 64 tiles only where they still give two workgroups per CU; the
   // products here are small, and the number of workgroups sets their speed
   const int64_t big = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64) * P;
-  if (g.M >= 64 && g.N >= 64 && big >= 512)
-    hipLaunchKernelGGL((gemm_gen_kernel<64, 64>), dim3((g.N + 63) / 64, (g.M + 63) / 64, P), dim3(256), 0, st, g);
-  else
-    hipLaunchKernelGGL((gemm_gen_kernel<32, 32>), dim3((g.N + 31) / 32, (g.M + 31) / 32, P), dim3(256), 0, st, g);
+  const dim3 g64((g.N + 63) / 64, (g.M + 63) / 64, P), g32((g.N + 31) / 32, (g.M + 31) / 32, P);
+  if (g.M >= 64 && g.N >= 64 && big >= 512) {
+    if (g.b_bf16) hipLaunchKernelGGL((gemm_gen_kernel<64, 64, bf16>), g64, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_gen_kernel<64, 64, float>), g64, dim3(256), 0, st, g);
+  } else {
+    if (g.b_bf16) hipLaunchKernelGGL((gemm_gen_kernel<32, 32, bf16>), g32, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_gen_kernel<32, 32, float>), g32, dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 

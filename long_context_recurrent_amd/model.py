@@ -154,19 +154,20 @@ class ArmtModel(_Handle):
 
 def backward(model: "ArmtModel", x: torch.Tensor, dy: torch.Tensor, A0=None, z0=None, dA_out=None, dz_out=None,
              schedule: str = "diagonal"):
-    """Gradients of <y, dy> + <A_out, dA_out> + <z_out, dz_out> (fp32 handles):
-    returns (dx, dA0, dz0, {weight field: gradient})."""
+    """Gradients of <y, dy> + <A_out, dA_out> + <z_out, dz_out>: returns
+    (dx, dA0, dz0, {weight field: gradient}).  x and dy have the model's
+    dtype; every gradient is fp32."""
     c = model.cfg
-    if model.dtype != torch.float32:
-        raise ValueError("the backward runs on fp32 handles")
+    if x.dtype != model.dtype or dy.dtype != model.dtype:
+        raise ValueError("x and dy must have the model's dtype")
     S = x.shape[0] // c.seg_len
     dev = model.device
     ws_bytes = _c.armt_backward_workspace_size(model.handle, S)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     ws_ptr = (ws.data_ptr() + 255) // 256 * 256
-    grads = {k: torch.empty_like(model.weights[k]) for k in WEIGHT_FIELDS}
+    grads = {k: torch.empty(model.weights[k].shape, dtype=torch.float32, device=dev) for k in WEIGHT_FIELDS}
     gw = _c.armt_weights(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
-    dx = torch.empty_like(x)
+    dx = torch.empty(x.shape, dtype=torch.float32, device=dev)
     dA0 = torch.empty(c.n_layers, c.d_model, c.d_key, dtype=torch.float32, device=dev)
     dz0 = torch.empty(c.n_layers, c.d_key, dtype=torch.float32, device=dev)
     model.stream.wait_stream(torch.cuda.current_stream(dev))

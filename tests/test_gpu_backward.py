@@ -16,7 +16,7 @@ import torch
 from oracle import armt_grad
 from armt_inputs import get_config, make_inputs, make_state
 from long_context_recurrent_amd import armt as C
-from long_context_recurrent_amd.model import WEIGHT_FIELDS, backward
+from long_context_recurrent_amd.model import ArmtModel, WEIGHT_FIELDS, backward
 
 from gpu_util import build_model, rel_l2, to_device, to_np
 
@@ -84,6 +84,59 @@ def test_backward_parity(cfg, state):
     assert torch.equal(y1, model2.forward(x, "diagonal")[0])
 
 
+SMALL = get_config("small_bf16")
+BF16_CASES = [
+    SMALL.with_(name="bw16_l2_s3", n_layers=2, n_segments=3, seg_len=64, n_mem=8, d_model=256, n_heads=4,
+                n_kv_heads=2, head_dim=64, ffn_hidden=512),
+    SMALL.with_(name="bw16_l3_s4_hd128", n_layers=3, n_segments=4, seg_len=100, n_mem=16, d_model=256, n_heads=2,
+                n_kv_heads=1, head_dim=128, ffn_hidden=768),
+]
+
+
+def _bf16_case(cfg, state):
+    inp = make_inputs(cfg)
+    if state == "given":
+        A0, z0 = make_state(cfg)
+        A0 = (A0 / 64.0).astype(np.float32)
+    else:
+        A0, z0 = None, None
+    rng = np.random.default_rng(5)
+    # dy is given in bf16: the oracle sees the same (exactly representable) values
+    dy = torch.from_numpy(rng.standard_normal(inp.x.shape).astype(np.float32)).to(torch.bfloat16)
+    dA = (rng.standard_normal((cfg.n_layers, cfg.d_model, cfg.d_key)) * 1e-3).astype(np.float32)
+    dz = (rng.standard_normal((cfg.n_layers, cfg.d_key)) * 1e-3).astype(np.float32)
+    return inp, A0, z0, dy, dA, dz
+
+
+@pytest.mark.parametrize("cfg", BF16_CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("state", ["zero", "given"])
+def test_backward_bf16_parity(cfg, state):
+    """bf16 handles: the recording forward is the bf16 forward and each node
+    is differentiated in fp32 with the weights widened, so the gradients differ
+    from the float64 gradient of the unrounded forward by the bf16 forward's
+    own error; bar 2e-2 relative L2 (the bf16 forward's bar)."""
+    say(f"[backward bf16] {cfg.name} state={state}")
+    inp, A0, z0, dy, dA, dz = _bf16_case(cfg, state)
+    dx_r, dA0_r, dz0_r, dp_r = armt_grad.vjp(inp, A0, z0, dy.float().numpy(), dA, dz)
+    model = build_model(inp)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = to_device(inp.x, cfg)
+    got = {sched: backward(model, x, dy.cuda(), dev(A0), dev(z0), dev(dA), dev(dz), schedule=sched)
+           for sched in ("diagonal", "sequential")}
+    dxd, dA0d, dz0d, gd = got["diagonal"]
+    dxs, dA0s, dz0s, gs = got["sequential"]
+    assert dxd.dtype == torch.float32 and all(gd[k].dtype == torch.float32 for k in WEIGHT_FIELDS)
+    assert torch.equal(dxd, dxs) and torch.equal(dA0d, dA0s) and torch.equal(dz0d, dz0s)
+    for k in WEIGHT_FIELDS:
+        assert torch.equal(gd[k], gs[k]), f"d{k}: diagonal and sequential backward differ"
+    errs = {"x": rel_l2(to_np(dxd), dx_r), "A0": rel_l2(to_np(dA0d), dA0_r), "z0": rel_l2(to_np(dz0d), dz0_r)}
+    for k in WEIGHT_FIELDS:
+        errs[k] = rel_l2(to_np(gd[k]), dp_r[k])
+    say("  rel L2 " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= 2e-2, f"d{k}: rel L2 {v:.3e}"
+
+
 def test_backward_argument_errors():
     cfg = CASES[0]
     inp = make_inputs(cfg)
@@ -93,9 +146,10 @@ def test_backward_argument_errors():
     assert n > 0
     with pytest.raises(C.ArmtError):
         C.armt_backward_workspace_size(model.handle, 0)
-    bf = get_config("small_bf16").with_(n_segments=1)
-    bmodel = build_model(make_inputs(bf))
+    bmodel = ArmtModel(model.cfg, model.weights, batch=2)
     with pytest.raises(C.ArmtError) as e:
         C.armt_backward_workspace_size(bmodel.handle, 1)
     assert e.value.code == -2
     assert lib.armt_backward(None, 0, 1, 1, None, None, 1, None, None, 1, 1, 1, None, 1, 1) == -1
+    with pytest.raises(ValueError):
+        backward(model, x=to_device(inp.x, cfg).to(torch.bfloat16), dy=to_device(inp.x, cfg))
