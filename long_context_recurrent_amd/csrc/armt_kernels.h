@@ -116,7 +116,19 @@ struct BwArgs {
   const float* rope;         // [n][hd/2] (cos, sin)
 };
 
-hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st);
+// Causal attention of the backward on the matrix cores (bf16 operands, fp32
+// accumulation; head dimension 64 or 128): the recomputed forward (O, base-2
+// row statistics) and dQ, dK, dV.  bw_attn_mfma_ok tells whether a shape is
+// supported.
+bool bw_attn_mfma_ok(const BwArgs& a);
+hipError_t bw_attn_mfma_fwd(const BwArgs& a, const float* qkv, float* O, float* mx, float* ls, int64_t qkv_ps,
+                            int64_t o_ps, int64_t st_ps, int P, hipStream_t st);
+hipError_t bw_attn_mfma_bwd(const BwArgs& a, const float* qkv, const float* O, const float* dO, const float* mx,
+                            const float* ls, float* Dq, float* dqkv, int64_t qkv_ps, int64_t o_ps, int64_t st_ps,
+                            int P, hipStream_t st);
+// matrix_cores: bf16 MFMA with fp32 operands split into bf16 pairs (about
+// 16 bits each survive), else fp32 fused multiply-adds in k order
+hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream_t st);
 hipError_t bw_phi_den(const BwArgs& a, const float* u, float* q, float* den, const float* z, int64_t u_ps,
                       int64_t z_ps, int rows, int P, hipStream_t st);
 hipError_t bw_add_div(const BwArgs& a, const float* base, const float* num, const float* den, float* out, int64_t ps,

@@ -965,9 +965,9 @@ struct BwCtx {
 // (strides in elements; B is bf16 when b16 is set)
 hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_ps, int64_t b_rs,
               int64_t b_cs, float* C, int64_t c_ps, int64_t c_rs, int64_t c_cs, int M, int N, int K, int acc, int P,
-              hipStream_t st, int b16 = 0) {
+              hipStream_t st, int b16 = 0, int matrix_cores = 0) {
   GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16};
-  return launch_gemm_gen(g, P, st);
+  return launch_gemm_gen(g, P, matrix_cores != 0, st);
 }
 
 #define BW_TRY(x)                              \
@@ -1053,72 +1053,77 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   }
 
   // ---- recompute the forward of each node
-  BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st, wb));
+  BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st, wb, wb));
   BW_TRY(bw_phi_den(ba, u, q, den, zst, n64, z_ps, n, P, st));
-  BW_TRY(gg(q, n64, 64, 1, Ast, A_ps, 1, 64, num, nd, d, 1, n, d, 64, 0, P, st));
+  BW_TRY(gg(q, n64, 64, 1, Ast, A_ps, 1, 64, num, nd, d, 1, n, d, 64, 0, P, st, 0, wb));
   BW_TRY(bw_copy(hin, h1, nd, hin_ps, nd, 0, P, st));
   BW_TRY(bw_add_div(ba, h1, num, den, h1, nd, n, P, st));
   BW_TRY(bw_rms_fwd(ba, h1, g_at, a, r1, nd, d, n, P, st));
-  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb));
+  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb, wb));
   BW_TRY(bw_rope(ba, qkv, nq, qd, 0, H, 1.f, n, P, st));
   BW_TRY(bw_rope(ba, qkv, nq, qd, H * hd, G, 1.f, n, P, st));
-  BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
+  // bf16 models: attention on the matrix cores (bf16 operands), as their
+  // forward computes it; fp32 models: the fp32 kernels
+  const bool attn_mm = wb && bw_attn_mfma_ok(ba);
+  if (attn_mm) BW_TRY(bw_attn_mfma_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
+  else BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   BW_TRY(bw_copy(h1, h2, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb));
+  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb, wb));
   BW_TRY(bw_rms_fwd(ba, h2, g_ml, b, r2, nd, d, n, P, st));
-  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb));
-  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb));
+  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb, wb));
+  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb, wb));
   BW_TRY(bw_swiglu(Gt, Up, Uo, nF, nF, P, st));
   BW_TRY(bw_copy(h2, h3, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb));
+  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb, wb));
   const float* Y = h3 + (int64_t)T * d;
-  BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st, wb));
-  BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st, wb));
-  BW_TRY(gg(Y, nd, d, 1, w_b, d, 1, 0, bl, M, 1, 0, M, 1, d, 0, P, st));
+  BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st, wb, wb));
+  BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st, wb, wb));
+  BW_TRY(gg(Y, nd, d, 1, w_b, d, 1, 0, bl, M, 1, 0, M, 1, d, 0, P, st, 0, wb));
   BwArgs bm = ba;
   bm.row_ps = M;
   BW_TRY(bw_phi_den(bm, uk, kk, denw, zst, M64, z_ps, M, P, st));
-  BW_TRY(gg(kk, M64, 64, 1, Ast, A_ps, 1, 64, kA, Md, d, 1, M, d, 64, 0, P, st));
+  BW_TRY(gg(kk, M64, 64, 1, Ast, A_ps, 1, 64, kA, Md, d, 1, M, d, 64, 0, P, st, 0, wb));
   BW_TRY(bw_memw_fwd(ba, uk, kk, bl, beta, zst, denw, kA, v, e, z_ps, P, st));
 
   // ---- memory write backward (dA, dz hold the gradient of the state it wrote)
-  BW_TRY(gg(kk, M64, 64, 1, dA, D64, 1, 64, de, Md, d, 1, M, d, 64, 0, P, st));
-  BW_TRY(gg(e, Md, d, 1, dA, D64, 64, 1, dk, M64, 64, 1, M, 64, d, 0, P, st));
+  BW_TRY(gg(kk, M64, 64, 1, dA, D64, 1, 64, de, Md, d, 1, M, d, 64, 0, P, st, 0, wb));
+  BW_TRY(gg(e, Md, d, 1, dA, D64, 64, 1, dk, M64, 64, 1, M, 64, d, 0, P, st, 0, wb));
   BW_TRY(bw_memw_bwd(ba, de, v, kA, beta, denw, dv, dkA, ddenw, dbl, P, st));
-  BW_TRY(gg(dkA, Md, 1, d, kk, M64, 64, 1, dA, D64, 64, 1, d, 64, M, 1, P, st));
-  BW_TRY(gg(dkA, Md, d, 1, Ast, A_ps, 64, 1, dk, M64, 64, 1, M, 64, d, 1, P, st));
+  BW_TRY(gg(dkA, Md, 1, d, kk, M64, 64, 1, dA, D64, 64, 1, d, 64, M, 1, P, st, 0, wb));
+  BW_TRY(gg(dkA, Md, d, 1, Ast, A_ps, 64, 1, dk, M64, 64, 1, M, 64, d, 1, P, st, 0, wb));
   BW_TRY(bw_memw_dk(ba, dk, uk, kk, ddenw, zst, dz, z_ps, 64, P, st));
   float* dY = dh + (int64_t)T * d;
-  BW_TRY(gg(dk, M64, 64, 1, W_mk, 64 * (int64_t)d, d, 1, dY, nd, d, 1, M, d, 64, 1, P, st, wb));
-  BW_TRY(gg(dv, Md, d, 1, W_mv, (int64_t)d * d, d, 1, dY, nd, d, 1, M, d, d, 1, P, st, wb));
+  BW_TRY(gg(dk, M64, 64, 1, W_mk, 64 * (int64_t)d, d, 1, dY, nd, d, 1, M, d, 64, 1, P, st, wb, wb));
+  BW_TRY(gg(dv, Md, d, 1, W_mv, (int64_t)d * d, d, 1, dY, nd, d, 1, M, d, d, 1, P, st, wb, wb));
   BW_TRY(bw_memw_beta(ba, dbl, w_b, Y, dY, dw_b, nd, d, P, st));
-  BW_TRY(gg(dk, M64, 1, 64, Y, nd, d, 1, dW_mk, 64 * (int64_t)d, d, 1, 64, d, M, 1, P, st));
-  BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st));
+  BW_TRY(gg(dk, M64, 1, 64, Y, nd, d, 1, dW_mk, 64 * (int64_t)d, d, 1, 64, d, M, 1, P, st, 0, wb));
+  BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st, 0, wb));
   // ---- MLP block backward
-  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb));
-  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
+  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb, wb));
+  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st, 0, wb));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
-  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb));
-  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb));
-  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
-  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
+  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb, wb));
+  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb, wb));
+  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb));
+  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb));
   BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
   // ---- attention block backward
-  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb));
-  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st));
-  BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
+  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb, wb));
+  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st, 0, wb));
+  if (attn_mm) BW_TRY(bw_attn_mfma_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
+  else BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
-  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb));
-  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st));
+  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb, wb));
+  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st, 0, wb));
   BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
   // ---- memory read backward
   BW_TRY(bw_memr_bwd(ba, dh, num, den, dnum, dden, nd, n, P, st));
-  BW_TRY(gg(dnum, nd, d, 1, Ast, A_ps, 64, 1, dq, n64, 64, 1, n, 64, d, 0, P, st));
-  BW_TRY(gg(dnum, nd, 1, d, q, n64, 64, 1, dA, D64, 64, 1, d, 64, n, 1, P, st));
+  BW_TRY(gg(dnum, nd, d, 1, Ast, A_ps, 64, 1, dq, n64, 64, 1, n, 64, d, 0, P, st, 0, wb));
+  BW_TRY(gg(dnum, nd, 1, d, q, n64, 64, 1, dA, D64, 64, 1, d, 64, n, 1, P, st, 0, wb));
   BW_TRY(bw_memr_dq(ba, dq, u, q, dden, zst, dz, n64, z_ps, 64, n, P, st));
-  BW_TRY(gg(dq, n64, 64, 1, W_mq, 64 * (int64_t)d, d, 1, dh, nd, d, 1, n, d, 64, 1, P, st, wb));
-  BW_TRY(gg(dq, n64, 1, 64, hin, hin_ps, d, 1, dW_mq, 64 * (int64_t)d, d, 1, 64, d, n, 1, P, st));
+  BW_TRY(gg(dq, n64, 64, 1, W_mq, 64 * (int64_t)d, d, 1, dh, nd, d, 1, n, d, 64, 1, P, st, wb, wb));
+  BW_TRY(gg(dq, n64, 1, 64, hin, hin_ps, d, 1, dW_mq, 64 * (int64_t)d, d, 1, 64, d, n, 1, P, st, 0, wb));
 
   // ---- the gradient of each node's input rows: to the layer below, or to x
   // and the memory embeddings at layer 0

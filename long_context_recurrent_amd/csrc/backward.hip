@@ -14,6 +14,8 @@
 // orientation, attention kernels that form each (query, key) score once and
 // keep a row of probabilities in LDS, and row / element kernels.
 #include <cmath>
+#include <type_traits>
+#include <utility>
 
 #include "armt_common.h"
 #include "armt_kernels.h"
@@ -21,6 +23,17 @@
 namespace armt {
 
 namespace {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time
+// (register-array indices stay static).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ float dphi_f(float u) { return u > 0.f ? 1.f : __expf(u); }
 
@@ -92,6 +105,264 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(GenGemm g) {
         *c = g.accumulate ? *c + acc[i][j] : acc[i][j];
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// The same strided GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16), for
+// the backward of bf16 models.  Every fp32 operand enters as a bf16 pair
+// (hi = R(v), lo = R(v - hi), |v - hi - lo| <= 2^-17 |v|): the products are
+// A_hi B_hi + A_lo B_hi + A_hi B_lo for an fp32 B, A_hi B + A_lo B for a bf16
+// B (weights, exact), so about 16 bits of each operand survive; fp32
+// accumulation.  Tile 128 x 128, four waves of 64 x 64 (2 x 2 blocks of
+// 32 x 32); K in steps of 32.  LDS holds each operand tile as 128 rows (m of
+// A, n of B) of 32 k (64 bytes = four 16-byte chunks, XOR-swizzled so
+// fragment reads of 16 consecutive rows are conflict-free).  Tile loads take
+// 16-byte vectors along whichever index is contiguous in memory when the
+// shape and alignment allow (VK: along k, VR: along the rows), else single
+// elements; stages are loaded into registers one or two steps ahead of the
+// one being multiplied (two or three register sets, two LDS buffers).
+// ---------------------------------------------------------------------------
+namespace mm {
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int BM = 128, BN = 128, BK = 32, ROWB = BK * 2, OPB = BM * ROWB;
+enum { GEN = 0, VK = 1, VR = 2 };
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// byte offset of k (even) in row r
+__device__ __forceinline__ int koff(int r, int k) { return r * ROWB + swz(r, k >> 3) * 16 + (k & 7) * 2; }
+__device__ __forceinline__ unsigned bits(bf16 v) { return (unsigned)__builtin_bit_cast(unsigned short, v); }
+__device__ __forceinline__ unsigned pack2(bf16 a, bf16 b) { return bits(a) | (bits(b) << 16); }
+__device__ __forceinline__ bf16 lo_of(float v, bf16 hi) { return (bf16)(v - (float)hi); }
+
+// One operand tile: element (r, k) of the 128 x 32 tile at rows r0.., k0..
+// sits at base + r * rs + k * cs.  raw: 16 words of stage registers.
+template <typename T, int MODE>
+struct Opnd {
+  const T* base;
+  int64_t rs, cs;
+  int rows, K;   // valid extent
+  __device__ __forceinline__ void load(int r0, int k0, unsigned (&raw)[16], int tid) const {
+    if constexpr (MODE == GEN) {
+      // 2048 k pairs; consecutive lanes on the contiguous index
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = tid + 256 * j;
+        const int r = cs == 1 ? i >> 4 : i & 127, kp = cs == 1 ? i & 15 : i >> 7;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int k = k0 + 2 * kp + t;
+          const float v = (r0 + r < rows && k < K) ? (float)base[(int64_t)(r0 + r) * rs + (int64_t)k * cs] : 0.f;
+          raw[2 * j + t] = __builtin_bit_cast(unsigned, v);
+        }
+      }
+    } else if constexpr (MODE == VK && sizeof(T) == 4) {
+      // 1024 vectors of 4 k: row i / 8, k 4 (i % 8)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, k = k0 + 4 * (i & 7);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r0 + r < rows && k < K) v = *(const u32x4*)(base + (int64_t)(r0 + r) * rs + k);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) raw[4 * j + t] = v[t];
+      }
+    } else if constexpr (MODE == VK) {
+      // 512 vectors of 8 k: row i / 4, k 8 (i % 4)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = tid + 256 * j, r = i >> 2, k = k0 + 8 * (i & 3);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r0 + r < rows && k < K) v = *(const u32x4*)(base + (int64_t)(r0 + r) * rs + k);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) raw[4 * j + t] = v[t];
+      }
+    } else if constexpr (sizeof(T) == 4) {
+      // VR: 512 units of 4 rows x k pair: rows 4 (i % 32), k pair i / 32
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = tid + 256 * j, r = 4 * (i & 31), k = k0 + 2 * (i >> 5);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (r0 + r < rows && k + t < K) v = *(const u32x4*)(base + (int64_t)(r0 + r) + (int64_t)(k + t) * cs);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) raw[8 * j + 4 * t + e] = v[e];
+        }
+      }
+    } else {
+      // VR, 2-byte elements: 256 units of 8 rows x k pair: rows 8 (i % 16), k pair i / 16
+      const int i = tid, r = 8 * (i & 15), k = k0 + 2 * (i >> 4);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r0 + r < rows && k + t < K) v = *(const u32x4*)(base + (int64_t)(r0 + r) + (int64_t)(k + t) * cs);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) raw[4 * t + e] = v[e];
+      }
+    }
+  }
+  // raw -> LDS (hi part at hi, lo part at lo when T is fp32)
+  __device__ __forceinline__ void store(const unsigned (&raw)[16], unsigned char* hi, unsigned char* lo,
+                                        int tid) const {
+    constexpr bool F32 = sizeof(T) == 4;
+    if constexpr (MODE == GEN) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = tid + 256 * j;
+        const int r = cs == 1 ? i >> 4 : i & 127, kp = cs == 1 ? i & 15 : i >> 7;
+        const float v0 = __builtin_bit_cast(float, raw[2 * j]), v1 = __builtin_bit_cast(float, raw[2 * j + 1]);
+        const bf16 h0 = (bf16)v0, h1 = (bf16)v1;
+        const int o = koff(r, 2 * kp);
+        *(unsigned*)(hi + o) = pack2(h0, h1);
+        if (F32) *(unsigned*)(lo + o) = pack2(lo_of(v0, h0), lo_of(v1, h1));
+      }
+    } else if constexpr (MODE == VK && F32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = tid + 256 * j, r = i >> 3, k = 4 * (i & 7);
+        bf16 h[4], l[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = __builtin_bit_cast(float, raw[4 * j + t]);
+          h[t] = (bf16)v;
+          l[t] = lo_of(v, h[t]);
+        }
+        const int o = koff(r, k);
+        *(uint2*)(hi + o) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+        *(uint2*)(lo + o) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+      }
+    } else if constexpr (MODE == VK) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = tid + 256 * j, r = i >> 2;
+        *(u32x4*)(hi + r * ROWB + swz(r, i & 3) * 16) =
+            u32x4{raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]};
+      }
+    } else if constexpr (F32) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = tid + 256 * j, r = 4 * (i & 31), k = 2 * (i >> 5);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = __builtin_bit_cast(float, raw[8 * j + e]), v1 = __builtin_bit_cast(float, raw[8 * j + 4 + e]);
+          const bf16 h0 = (bf16)v0, h1 = (bf16)v1;
+          const int o = koff(r + e, k);
+          *(unsigned*)(hi + o) = pack2(h0, h1);
+          *(unsigned*)(lo + o) = pack2(lo_of(v0, h0), lo_of(v1, h1));
+        }
+      }
+    } else {
+      const int i = tid, r = 8 * (i & 15), k = 2 * (i >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned w0 = raw[e >> 1], w1 = raw[4 + (e >> 1)];
+        const unsigned b0 = (e & 1) ? w0 >> 16 : w0 & 0xffffu, b1 = (e & 1) ? w1 >> 16 : w1 & 0xffffu;
+        *(unsigned*)(hi + koff(r + e, k)) = b0 | (b1 << 16);
+      }
+    }
+  }
+};
+}  // namespace mm
+
+template <int AM, int BMODE, bool B16>
+__global__ __launch_bounds__(256, (AM == mm::GEN || BMODE == mm::GEN) ? 1 : 2) void gemm_mfma_kernel(GenGemm g) {
+  using namespace mm;
+  using BT = typename std::conditional<B16, bf16, float>::type;
+  constexpr int NB = B16 ? 3 : 4;              // A_hi, A_lo, B_hi (, B_lo)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][NB * OPB];
+  const int p = blockIdx.z;
+  const Opnd<float, AM> opa{g.A + (int64_t)p * g.a_ps, g.a_rs, g.a_cs, g.M, g.K};
+  const Opnd<BT, BMODE> opb{(const BT*)g.B + (int64_t)p * g.b_ps, g.b_cs, g.b_rs, g.N, g.K};
+  float* C = g.C + (int64_t)p * g.c_ps;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+
+  // register sets for staged tiles: loads run PD = NSET - 1 stages ahead
+  // (two fp32 operands take more registers: one stage ahead keeps two
+  // workgroups per CU)
+  constexpr int NSET = (B16 || AM == GEN || BMODE == GEN) ? 3 : 2;
+  unsigned ra[NSET][16], rb[NSET][16];
+  auto put = [&](int buf, const unsigned (&xa)[16], const unsigned (&xb)[16]) {
+    unsigned char* base = lds[buf];
+    opa.store(xa, base, base + OPB, tid);
+    opb.store(xb, base + 2 * OPB, base + 3 * OPB, tid);
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](int buf) {
+    const unsigned char* base = lds[buf];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * wm + 32 * i + r32;
+        const int o = r * ROWB + swz(r, 2 * ks + h) * 16;
+        ah[i] = *(const bf16x8*)(base + o);
+        al[i] = *(const bf16x8*)(base + OPB + o);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 64 * wn + 32 * j + r32;
+        const int o = r * ROWB + swz(r, 2 * ks + h) * 16;
+        bh[j] = *(const bf16x8*)(base + 2 * OPB + o);
+        if (!B16) bl[j] = *(const bf16x8*)(base + 3 * OPB + o);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+          if (!B16) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  };
+
+  // stage s: register set s % NSET, LDS buffer s % 2
+  constexpr int PD = NSET - 1;
+  const int nst = (g.K + BK - 1) / BK;
+  static_for<PD>([&](auto I) {
+    constexpr int t = decltype(I)::value;
+    if (t < nst) {
+      opa.load(m0, t * BK, ra[t], tid);
+      opb.load(n0, t * BK, rb[t], tid);
+    }
+  });
+  put(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int s0 = 0; s0 < nst; s0 += NSET) {
+    static_for<NSET>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      const int s = s0 + u;
+      if (s < nst) {
+        if (s + PD < nst) {
+          opa.load(m0, (s + PD) * BK, ra[(u + PD) % NSET], tid);
+          opb.load(n0, (s + PD) * BK, rb[(u + PD) % NSET], tid);
+        }
+        compute(s & 1);
+        if (s + 1 < nst) put((s + 1) & 1, ra[(u + 1) % NSET], rb[(u + 1) % NSET]);
+        __syncthreads();
+      }
+    });
+  }
+  // element e of block (i, j) in lane (r32, h): row 8(e/4) + 4h + e%4, column r32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int n = n0 + 64 * wn + 32 * j + r32;
+        if (m < g.M && n < g.N) {
+          float* c = C + (int64_t)m * g.c_rs + (int64_t)n * g.c_cs;
+          *c = g.accumulate ? *c + acc[i][j][e] : acc[i][j][e];
+        }
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -529,8 +800,42 @@ __global__ __launch_bounds__(256) void bw_copy_kernel(const float* src, float* d
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_gemm_gen(const GenGemm& g, int P, hipStream_t st) {
+hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream_t st) {
   if (P <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0) return hipErrorInvalidValue;
+  if (matrix_cores) {
+    const dim3 grid((g.N + mm::BN - 1) / mm::BN, (g.M + mm::BM - 1) / mm::BM, P);
+    // 16-byte vectors along the contiguous index where every vector is whole
+    // and aligned
+    auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    int am = mm::GEN, bm = mm::GEN;
+    if (al16(g.A) && g.a_ps % 4 == 0) {
+      if (g.a_cs == 1 && g.a_rs % 4 == 0 && g.K % 4 == 0) am = mm::VK;
+      else if (g.a_rs == 1 && g.a_cs % 4 == 0 && g.M % 4 == 0) am = mm::VR;
+    }
+    const int vb = g.b_bf16 ? 8 : 4;
+    if (al16(g.B) && g.b_ps % vb == 0) {
+      if (g.b_rs == 1 && g.b_cs % vb == 0 && g.K % vb == 0) bm = mm::VK;
+      else if (g.b_cs == 1 && g.b_rs % vb == 0 && g.N % vb == 0) bm = mm::VR;
+    }
+#define MM_LAUNCH(AM_, BM_)                                                                            \
+  do {                                                                                                \
+    if (g.b_bf16) hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, true>), grid, dim3(256), 0, st, g);  \
+    else hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, false>), grid, dim3(256), 0, st, g);          \
+  } while (0)
+    switch (am * 3 + bm) {
+      case 0: MM_LAUNCH(mm::GEN, mm::GEN); break;
+      case 1: MM_LAUNCH(mm::GEN, mm::VK); break;
+      case 2: MM_LAUNCH(mm::GEN, mm::VR); break;
+      case 3: MM_LAUNCH(mm::VK, mm::GEN); break;
+      case 4: MM_LAUNCH(mm::VK, mm::VK); break;
+      case 5: MM_LAUNCH(mm::VK, mm::VR); break;
+      case 6: MM_LAUNCH(mm::VR, mm::GEN); break;
+      case 7: MM_LAUNCH(mm::VR, mm::VK); break;
+      default: MM_LAUNCH(mm::VR, mm::VR); break;
+    }
+#undef MM_LAUNCH
+    return hipGetLastError();
+  }
   // 64 x 64 tiles only where they still give two workgroups per CU; the
   // products here are small, and the number of workgroups sets their speed
   const int64_t big = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64) * P;
