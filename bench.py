@@ -6,7 +6,7 @@
     python bench.py --logit-drift        # LM-head logits: diag vs seq vs oracle per segment count
     python bench.py --full-attention     # full-attention Llama comparator vs diagonal ARMT, 4K..131K
     python bench.py --batch-sweep        # B independent sequences per node, B = 1..8
-    python bench.py --backward           # grouped vs node-by-node backward (fp32)
+    python bench.py --backward           # grouped vs node-by-node backward (fp32; 1B shape in bf16)
 
 A step is one full forward of the workload (all S + L - 1 diagonal waves, every
 kernel of every node) over a synthetic sequence that is resident in HBM before
@@ -87,7 +87,8 @@ def parse():
                          "(1B shape): total tokens/s against the batch size")
     ap.add_argument("--backward", action="store_true",
                     help="grouped backward (reversed diagonal waves) against the node-by-node backward on an "
-                         "fp32 workload: time per forward + backward, one JSON line per schedule")
+                         "fp32 workload and on the 1B shape in bf16: time per forward + backward, one JSON line "
+                         "per workload and schedule")
     ap.add_argument("--traffic-record", metavar="DIR",
                     help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
                          "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
@@ -614,33 +615,45 @@ def batch_sweep(args, dev):
 
 
 def backward_bench(args, dev):
-    """Forward + backward (fp32 handles) over an 8-layer, 32-segment fp32
-    workload: the grouped backward over the reversed diagonal waves against
-    the node-by-node backward in reverse segment-major order (same results,
-    bitwise)."""
+    """Forward + backward: the grouped backward over the reversed diagonal
+    waves against the node-by-node backward in reverse segment-major order
+    (same results, bitwise), on an 8-layer fp32 workload (vector-ALU kernels)
+    and on the 1B shape in bf16 (16 layers, 32 segments; matrix cores)."""
+    from armt_inputs import get_config
+    fp32 = get_config("tiny_fp32").with_(name="fp32_l8_s32", n_layers=8, d_model=256, n_heads=4, n_kv_heads=2,
+                                         head_dim=64, ffn_hidden=512, seg_len=128, n_mem=8, n_segments=32)
+    one_b = get_config("1b_s128").with_(name="1b_bf16_s32", n_segments=32)
+    backward_workload(args, dev, fp32, cpu_segments=fp32.n_segments, cpu_layers=None,
+                      kernels="fp32 vector ALU (no packed fp32, no matrix cores)", peak=PEAK_F32_TFLOPS, bound="alu")
+    backward_workload(args, dev, one_b, cpu_segments=2, cpu_layers=2,
+                      kernels="bf16 matrix cores (fp32 operands as bf16 pairs; attention operands bf16)",
+                      peak=PEAK_BF16_TFLOPS, bound="mfma")
+
+
+def backward_workload(args, dev, cfg, cpu_segments, cpu_layers, kernels, peak, bound):
+    import gc
     import numpy as np
     import torch
-    from armt_inputs import get_config, make_inputs
+    from armt_inputs import make_inputs
     from long_context_recurrent_amd import armt as C
     from long_context_recurrent_amd.model import ArmtModel, WEIGHT_FIELDS, make_config
-    cfg = get_config("tiny_fp32").with_(name="fp32_l8_s32", n_layers=8, d_model=256, n_heads=4, n_kv_heads=2,
-                                        head_dim=64, ffn_hidden=512, seg_len=128, n_mem=8, n_segments=32)
     S, T, L = cfg.n_segments, cfg.seg_len, cfg.n_layers
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     inp = make_inputs(cfg)
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, torch.float32)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
     w = {k: f(v) for k, v in inp.weights.items()}
     w.update(g_attn=f(inp.g_attn), g_mlp=f(inp.g_mlp), mem_emb=f(inp.mem_emb))
     ccfg = make_config(L, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_hidden, T, cfg.n_mem,
-                       dtype="f32")
+                       dtype=cfg.dtype)
     model = ArmtModel(ccfg, w)
     x = f(inp.x)
-    dy = torch.randn_like(x)
+    dy = torch.randn(x.shape, device=dev).to(dt)
     ws_bytes = C.armt_backward_workspace_size(model.handle, S)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     ws_ptr = (ws.data_ptr() + 255) // 256 * 256
-    grads = {k: torch.empty_like(w[k]) for k in WEIGHT_FIELDS}
+    grads = {k: torch.empty(w[k].shape, dtype=torch.float32, device=dev) for k in WEIGHT_FIELDS}
     gw = C.armt_weights(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
-    dx = torch.empty_like(x)
+    dx = torch.empty(x.shape, dtype=torch.float32, device=dev)
     dA0 = torch.empty(L, cfg.d_model, 64, device=dev)
     dz0 = torch.empty(L, 64, device=dev)
     st = model.stream
@@ -666,48 +679,56 @@ def backward_bench(args, dev):
     # dQ and dK), so three times the forward's FLOPs; the recomputation of
     # the forward inside the backward is not counted
     flops = 3 * node_gflop(cfg) * 1e9 * S * L
-    cpu = None if args.no_cpu else grad_cpu_baseline(inp, S)
+    cpu = None if args.no_cpu else grad_cpu_baseline(inp, cpu_segments, cpu_layers)
     for sched in ("diagonal", "sequential"):
         t = results[sched][0]
         achieved = flops / t / 1e12
-        line = {"workload": cfg.name, "dtype": "f32", "schedule": sched, "tokens": S * T,
+        line = {"workload": cfg.name, "dtype": cfg.dtype, "schedule": sched, "tokens": S * T,
                 "ms_forward_plus_backward": t * 1e3, "tokens_per_s": S * T / t,
                 "ms_forward_alone": y_t * 1e3, "bitwise_equal_schedules": same,
-                "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                             "frac": achieved / PEAK_F32_TFLOPS, "traffic": None,
+                "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                             "frac": achieved / peak, "traffic": None,
                              "work": "3 x forward FLOPs (forward + input and weight gradients)"},
-                "cpu_baseline": cpu if sched == "diagonal" else None,
-                "kernels": "fp32 vector ALU (no packed fp32, no matrix cores)"}
-        log(f"{sched}: forward + backward {t * 1e3:.1f} ms ({S * T / t:.0f} tokens/s, {achieved:.2f} TFLOP/s); "
-            f"forward alone {y_t * 1e3:.1f} ms")
+                "cpu_baseline": cpu if sched == "diagonal" else None, "kernels": kernels}
+        log(f"{cfg.name} {sched}: forward + backward {t * 1e3:.1f} ms ({S * T / t:.0f} tokens/s, "
+            f"{achieved:.2f} TFLOP/s); forward alone {y_t * 1e3:.1f} ms")
         print(json.dumps(line), flush=True)
-    log(f"grouped backward speed-up {results['sequential'][0] / results['diagonal'][0]:.2f}x")
+    log(f"{cfg.name}: grouped backward speed-up {results['sequential'][0] / results['diagonal'][0]:.2f}x")
     model.close()
+    del model, ws, grads, w, x, dy, dx
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
-def grad_cpu_baseline(inp, n_seg):
+def grad_cpu_baseline(inp, n_seg, n_layers=None):
     """The gradient oracle (float64 autograd) on the first `n_seg` segments
-    of the workload: tokens/s of forward + backward on the host."""
+    (and, if given, the first `n_layers` layers) of the workload: tokens/s of
+    forward + backward on the host, scaled to all layers by the layer
+    count."""
     import numpy as np
     from oracle import armt_grad
     import torch
     cores = torch.get_num_threads()   # autograd's CPU kernels run on torch's thread pool
     cfg = inp.cfg
+    L = cfg.n_layers
+    Ls = L if n_layers is None else n_layers
     rows = n_seg * cfg.seg_len
-    sub = inp.__class__(**{**inp.__dict__, "cfg": cfg.with_(n_segments=n_seg), "x": inp.x[:rows]})
+    sub = inp.__class__(cfg=cfg.with_(n_segments=n_seg, n_layers=Ls), x=inp.x[:rows], mem_emb=inp.mem_emb,
+                        weights={k: v[:Ls] for k, v in inp.weights.items()}, g_attn=inp.g_attn[:Ls],
+                        g_mlp=inp.g_mlp[:Ls])
     rng = np.random.default_rng(0)
     dy = rng.standard_normal((rows, cfg.d_model))
-    L = cfg.n_layers
-    dA = np.zeros((L, cfg.d_model, cfg.d_key))
-    dz = np.zeros((L, cfg.d_key))
+    dA = np.zeros((Ls, cfg.d_model, cfg.d_key))
+    dz = np.zeros((Ls, cfg.d_key))
     a = time.perf_counter()
     armt_grad.vjp(sub, None, None, dy, dA, dz)
     el = time.perf_counter() - a
-    value = rows / el
-    log(f"cpu gradient oracle: {n_seg} segments in {el:.1f}s -> {value:.0f} tokens/s")
+    value = rows / el * Ls / L
+    log(f"cpu gradient oracle: {n_seg} segment(s) x {Ls} layer(s) in {el:.1f}s -> {value:.1f} tokens/s")
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_cpu(),
-            "sample": f"forward + backward of the first {n_seg} of {cfg.n_segments} segments by float64 autograd "
-                      f"({rows} tokens) in {el:.1f}s"}
+            "sample": f"forward + backward of the first {n_seg} of {cfg.n_segments} segments through "
+                      f"{Ls} of {L} layers by float64 autograd ({rows} tokens) in {el:.1f}s; "
+                      f"tokens/s scaled by {Ls}/{L}"}
 
 
 def timed_forward(model, x):

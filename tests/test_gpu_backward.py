@@ -114,7 +114,8 @@ def test_backward_bf16_parity(cfg, state):
     """bf16 handles: the recording forward is the bf16 forward and each node
     is differentiated in fp32 with the weights widened, so the gradients differ
     from the float64 gradient of the unrounded forward by the bf16 forward's
-    own error; bar 2e-2 relative L2 (the bf16 forward's bar)."""
+    own error and the bf16 operands of attention; bar 2e-2 relative L2 (the
+    bf16 forward's bar)."""
     say(f"[backward bf16] {cfg.name} state={state}")
     inp, A0, z0, dy, dA, dz = _bf16_case(cfg, state)
     dx_r, dA0_r, dz0_r, dp_r = armt_grad.vjp(inp, A0, z0, dy.float().numpy(), dA, dz)
@@ -129,6 +130,34 @@ def test_backward_bf16_parity(cfg, state):
     assert torch.equal(dxd, dxs) and torch.equal(dA0d, dA0s) and torch.equal(dz0d, dz0s)
     for k in WEIGHT_FIELDS:
         assert torch.equal(gd[k], gs[k]), f"d{k}: diagonal and sequential backward differ"
+    errs = {"x": rel_l2(to_np(dxd), dx_r), "A0": rel_l2(to_np(dA0d), dA0_r), "z0": rel_l2(to_np(dz0d), dz0_r)}
+    for k in WEIGHT_FIELDS:
+        errs[k] = rel_l2(to_np(gd[k]), dp_r[k])
+    say("  rel L2 " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= 2e-2, f"d{k}: rel L2 {v:.3e}"
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_backward_bf16_1b_layer_shape():
+    """The 1B layer shape (d 2048, 32/8 heads of 64, F 8192, 1024 + 16 rows),
+    2 layers x 2 segments from a non-zero state: every gradient against the
+    float64 oracle (bar 2e-2), grouped == node-by-node bitwise."""
+    cfg = get_config("1b_s128").with_(n_layers=2, n_segments=2)
+    say(f"[backward bf16 1B shape] L={cfg.n_layers} S={cfg.n_segments}")
+    inp, A0, z0, dy, dA, dz = _bf16_case(cfg, "given")
+    dx_r, dA0_r, dz0_r, dp_r = armt_grad.vjp(inp, A0, z0, dy.float().numpy(), dA, dz)
+    model = build_model(inp)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = to_device(inp.x, cfg)
+    got = {sched: backward(model, x, dy.cuda(), dev(A0), dev(z0), dev(dA), dev(dz), schedule=sched)
+           for sched in ("diagonal", "sequential")}
+    dxd, dA0d, dz0d, gd = got["diagonal"]
+    dxs, dA0s, dz0s, gs = got["sequential"]
+    assert torch.equal(dxd, dxs) and torch.equal(dA0d, dA0s) and torch.equal(dz0d, dz0s)
+    for k in WEIGHT_FIELDS:
+        assert torch.equal(gd[k], gs[k])
     errs = {"x": rel_l2(to_np(dxd), dx_r), "A0": rel_l2(to_np(dA0d), dA0_r), "z0": rel_l2(to_np(dz0d), dz0_r)}
     for k in WEIGHT_FIELDS:
         errs[k] = rel_l2(to_np(gd[k]), dp_r[k])
