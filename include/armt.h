@@ -241,12 +241,14 @@ int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y)
  *   workspace  device memory of armt_backward_workspace_size bytes,
  *          256-byte aligned
  * For an ARMT_BF16 handle the recording forward is the bf16 forward, and each
- * node is differentiated in fp32 at the input rows that forward gave it, with
- * the bf16 weights widened exactly: the forward's bf16 roundings of branch
- * activations count as identity in the gradient.
+ * node is differentiated at the input rows that forward gave it, the
+ * forward's bf16 roundings of branch activations counting as identity in the
+ * gradient; its products run on the matrix cores with every fp32 operand as
+ * a bf16 pair (about 16 bits kept) and attention with bf16 operands, fp32
+ * accumulation.  ARMT_F32 handles use fp32 vector-ALU kernels throughout.
  * Asynchronous on the handle's stream; uses the handle's workspace too (must
  * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for batched
- * handles.  Kernels: fp32 on the vector ALU (no matrix cores). */
+ * handles. */
 int armt_backward_workspace_size(armt_handle *h, int32_t n_segments, size_t *bytes);
 int armt_backward(armt_handle *h, int32_t schedule, const void *x, int32_t n_segments,
                   const float *A0, const float *z0, const void *dy, const float *dA_out,
