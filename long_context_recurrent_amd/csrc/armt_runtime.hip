@@ -965,8 +965,9 @@ struct BwCtx {
 // (strides in elements; B is bf16 when b16 is set)
 hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_ps, int64_t b_rs,
               int64_t b_cs, float* C, int64_t c_ps, int64_t c_rs, int64_t c_cs, int M, int N, int K, int acc, int P,
-              hipStream_t st, int b16 = 0, int matrix_cores = 0) {
-  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16};
+              hipStream_t st, int b16 = 0, int matrix_cores = 0, int single = 0) {
+  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16, single & 1,
+            (single >> 1) & 1};
   return launch_gemm_gen(g, P, matrix_cores != 0, st);
 }
 
@@ -1052,6 +1053,13 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     BW_TRY(hipMemsetAsync(top + (int64_t)T * d, 0, (size_t)M * d * 4, st));
   }
 
+  // The activations that the bf16 forward rounds to bf16 before a product
+  // (the attention and MLP inputs a and b, the attention output O, the SwiGLU
+  // output Uo) enter the matrix-core products rounded once (RA: as the first
+  // operand, RB: as the second); every other fp32 operand enters as a hi/lo
+  // pair.
+  const int RA = 1, RB = 2;
+
   // ---- recompute the forward of each node
   BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st, wb, wb));
   BW_TRY(bw_phi_den(ba, u, q, den, zst, n64, z_ps, n, P, st));
@@ -1059,7 +1067,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   BW_TRY(bw_copy(hin, h1, nd, hin_ps, nd, 0, P, st));
   BW_TRY(bw_add_div(ba, h1, num, den, h1, nd, n, P, st));
   BW_TRY(bw_rms_fwd(ba, h1, g_at, a, r1, nd, d, n, P, st));
-  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb, wb));
+  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb, wb, RA));
   BW_TRY(bw_rope(ba, qkv, nq, qd, 0, H, 1.f, n, P, st));
   BW_TRY(bw_rope(ba, qkv, nq, qd, H * hd, G, 1.f, n, P, st));
   // bf16 models: attention on the matrix cores (bf16 operands), as their
@@ -1068,13 +1076,13 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   if (attn_mm) BW_TRY(bw_attn_mfma_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   else BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   BW_TRY(bw_copy(h1, h2, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb, wb));
+  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb, wb, RA));
   BW_TRY(bw_rms_fwd(ba, h2, g_ml, b, r2, nd, d, n, P, st));
-  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb, wb));
-  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb, wb));
+  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb, wb, RA));
+  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb, wb, RA));
   BW_TRY(bw_swiglu(Gt, Up, Uo, nF, nF, P, st));
   BW_TRY(bw_copy(h2, h3, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb, wb));
+  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb, wb, RA));
   const float* Y = h3 + (int64_t)T * d;
   BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st, wb, wb));
   BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st, wb, wb));
@@ -1100,22 +1108,22 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st, 0, wb));
   // ---- MLP block backward
   BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb, wb));
-  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st, 0, wb));
+  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st, 0, wb, RB));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
   BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb, wb));
   BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb, wb));
-  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb));
-  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb));
+  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb, RB));
+  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb, RB));
   BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
   // ---- attention block backward
   BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb, wb));
-  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st, 0, wb));
+  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st, 0, wb, RB));
   if (attn_mm) BW_TRY(bw_attn_mfma_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   else BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
   BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb, wb));
-  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st, 0, wb));
+  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st, 0, wb, RB));
   BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
   // ---- memory read backward
   BW_TRY(bw_memr_bwd(ba, dh, num, den, dnum, dden, nd, n, P, st));

@@ -136,7 +136,7 @@ __device__ __forceinline__ bf16 lo_of(float v, bf16 hi) { return (bf16)(v - (flo
 
 // One operand tile: element (r, k) of the 128 x 32 tile at rows r0.., k0..
 // sits at base + r * rs + k * cs.  raw: 16 words of stage registers.
-template <typename T, int MODE>
+template <typename T, int MODE, bool LO>   // LO: an fp32 tile also stores its low parts
 struct Opnd {
   const T* base;
   int64_t rs, cs;
@@ -203,7 +203,7 @@ struct Opnd {
   // raw -> LDS (hi part at hi, lo part at lo when T is fp32)
   __device__ __forceinline__ void store(const unsigned (&raw)[16], unsigned char* hi, unsigned char* lo,
                                         int tid) const {
-    constexpr bool F32 = sizeof(T) == 4;
+    constexpr bool F32 = sizeof(T) == 4 && LO;
     if constexpr (MODE == GEN) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -215,7 +215,7 @@ struct Opnd {
         *(unsigned*)(hi + o) = pack2(h0, h1);
         if (F32) *(unsigned*)(lo + o) = pack2(lo_of(v0, h0), lo_of(v1, h1));
       }
-    } else if constexpr (MODE == VK && F32) {
+    } else if constexpr (MODE == VK && sizeof(T) == 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = tid + 256 * j, r = i >> 3, k = 4 * (i & 7);
@@ -228,7 +228,7 @@ struct Opnd {
         }
         const int o = koff(r, k);
         *(uint2*)(hi + o) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-        *(uint2*)(lo + o) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+        if (F32) *(uint2*)(lo + o) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
       }
     } else if constexpr (MODE == VK) {
 #pragma unroll
@@ -237,7 +237,7 @@ struct Opnd {
         *(u32x4*)(hi + r * ROWB + swz(r, i & 3) * 16) =
             u32x4{raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]};
       }
-    } else if constexpr (F32) {
+    } else if constexpr (sizeof(T) == 4) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int i = tid + 256 * j, r = 4 * (i & 31), k = 2 * (i >> 5);
@@ -247,7 +247,7 @@ struct Opnd {
           const bf16 h0 = (bf16)v0, h1 = (bf16)v1;
           const int o = koff(r + e, k);
           *(unsigned*)(hi + o) = pack2(h0, h1);
-          *(unsigned*)(lo + o) = pack2(lo_of(v0, h0), lo_of(v1, h1));
+          if (F32) *(unsigned*)(lo + o) = pack2(lo_of(v0, h0), lo_of(v1, h1));
         }
       }
     } else {
@@ -263,15 +263,18 @@ struct Opnd {
 };
 }  // namespace mm
 
-template <int AM, int BMODE, bool B16>
+// ALO / BLO: the operand enters as a hi/lo pair (else rounded once to bf16,
+// for activations the bf16 forward itself rounds)
+template <int AM, int BMODE, bool B16, bool ALO, bool BLO>
 __global__ __launch_bounds__(256, (AM == mm::GEN || BMODE == mm::GEN) ? 1 : 2) void gemm_mfma_kernel(GenGemm g) {
   using namespace mm;
   using BT = typename std::conditional<B16, bf16, float>::type;
-  constexpr int NB = B16 ? 3 : 4;              // A_hi, A_lo, B_hi (, B_lo)
+  constexpr bool BL = BLO && !B16;
+  constexpr int NB = BL ? 4 : 3;               // A_hi, A_lo, B_hi (, B_lo)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][NB * OPB];
   const int p = blockIdx.z;
-  const Opnd<float, AM> opa{g.A + (int64_t)p * g.a_ps, g.a_rs, g.a_cs, g.M, g.K};
-  const Opnd<BT, BMODE> opb{(const BT*)g.B + (int64_t)p * g.b_ps, g.b_cs, g.b_rs, g.N, g.K};
+  const Opnd<float, AM, ALO> opa{g.A + (int64_t)p * g.a_ps, g.a_rs, g.a_cs, g.M, g.K};
+  const Opnd<BT, BMODE, BL> opb{(const BT*)g.B + (int64_t)p * g.b_ps, g.b_cs, g.b_rs, g.N, g.K};
   float* C = g.C + (int64_t)p * g.c_ps;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31, h = lane >> 5;
@@ -302,22 +305,22 @@ __global__ __launch_bounds__(256, (AM == mm::GEN || BMODE == mm::GEN) ? 1 : 2) v
         const int r = 64 * wm + 32 * i + r32;
         const int o = r * ROWB + swz(r, 2 * ks + h) * 16;
         ah[i] = *(const bf16x8*)(base + o);
-        al[i] = *(const bf16x8*)(base + OPB + o);
+        if (ALO) al[i] = *(const bf16x8*)(base + OPB + o);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = 64 * wn + 32 * j + r32;
         const int o = r * ROWB + swz(r, 2 * ks + h) * 16;
         bh[j] = *(const bf16x8*)(base + 2 * OPB + o);
-        if (!B16) bl[j] = *(const bf16x8*)(base + 3 * OPB + o);
+        if (BL) bl[j] = *(const bf16x8*)(base + 3 * OPB + o);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
-          if (!B16) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+          if (ALO) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+          if (BL) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
         }
     }
   };
@@ -817,10 +820,21 @@ hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream
       if (g.b_rs == 1 && g.b_cs % vb == 0 && g.K % vb == 0) bm = mm::VK;
       else if (g.b_cs == 1 && g.b_rs % vb == 0 && g.N % vb == 0) bm = mm::VR;
     }
-#define MM_LAUNCH(AM_, BM_)                                                                            \
-  do {                                                                                                \
-    if (g.b_bf16) hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, true>), grid, dim3(256), 0, st, g);  \
-    else hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, false>), grid, dim3(256), 0, st, g);          \
+#define MM_KERNEL(AM_, BM_, B16_, ALO_, BLO_) \
+  hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, B16_, ALO_, BLO_>), grid, dim3(256), 0, st, g)
+    // operands that enter rounded once: only on the vector paths (the
+    // element-wise fallback always keeps the hi/lo pairs)
+#define MM_LAUNCH(AM_, BM_)                                                                 \
+  do {                                                                                     \
+    const bool vec = AM_ != mm::GEN && BM_ != mm::GEN;                                     \
+    const bool alo = !(vec && g.a_single), blo = !(vec && g.b_single);                     \
+    if (g.b_bf16) {                                                                        \
+      if (alo) MM_KERNEL(AM_, BM_, true, true, false);                                     \
+      else MM_KERNEL(AM_, BM_, true, false, false);                                        \
+    } else {                                                                               \
+      if (blo) MM_KERNEL(AM_, BM_, false, true, true);                                     \
+      else MM_KERNEL(AM_, BM_, false, true, false);                                        \
+    }                                                                                      \
   } while (0)
     switch (am * 3 + bm) {
       case 0: MM_LAUNCH(mm::GEN, mm::GEN); break;
@@ -834,6 +848,7 @@ hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream
       default: MM_LAUNCH(mm::VR, mm::VR); break;
     }
 #undef MM_LAUNCH
+#undef MM_KERNEL
     return hipGetLastError();
   }
   // 64 x 64 tiles only where they still give two workgroups per CU; the
