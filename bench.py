@@ -294,6 +294,20 @@ def host_cpu():
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
+def roofline_mfma(achieved_tflops):
+    """Roofline object of a contraction-bound path against the bf16 peak."""
+    return {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None}
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        return os.cpu_count()
+
+
 def cpu_baseline(inp, seconds):
     """The oracle as it stands, on this host: nodes of segment 0, layer by
     layer, until about `seconds` of CPU work; tokens/s = T / (L * mean node
@@ -470,8 +484,21 @@ def logit_drift(args, dev):
     flops = 2.0 * S * T * V * cfg.d_model
     head = {"rows": S * T, "vocab": V, "ms": ms, "tflops": flops / ms / 1e9,
             "frac_mfma_bf16": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    cpu = None
+    if not args.no_cpu:
+        # the oracle's LM head (float64) on the first rows of the same output
+        rows = min(S * T, 4096)
+        yh = y[:rows].to(torch.float64).cpu().numpy()
+        a = time.perf_counter()
+        oracle.logits(yh, g, w_lm, cfg.dtype, cfg.rms_eps)
+        el = time.perf_counter() - a
+        cpu = {"value": rows / el, "unit": "rows/s", "cores": oracle_threads(), "kind": "oracle",
+               "host": host_cpu(), "sample": f"final norm + LM head of {rows} of {S * T} rows (V={V}, float64 "
+                                              f"NumPy) in {el:.2f}s"}
+        log(f"cpu oracle LM head: {rows} rows in {el:.2f}s")
     log(f"LM head over {S * T} rows, V={V}: {ms:.2f} ms, {head['tflops']:.0f} TFLOP/s")
-    print(json.dumps({"workload": args.workload, "lm_head": head}), flush=True)
+    print(json.dumps({"workload": args.workload, "lm_head": head, "roofline": roofline_mfma(head["tflops"]),
+                      "rows_per_s": S * T / (ms * 1e-3), "cpu_baseline": cpu}), flush=True)
     del lg, y
 
     o = oracle.Oracle(inp)
@@ -541,6 +568,25 @@ def full_attention(args, dev):
             each.append(e0.elapsed_time(e1) * 1e-3)
         return statistics.median(each), min(each)
 
+    cpu = None
+    if not args.no_cpu:
+        # the oracle's full-attention forward (float64) on 1,024 tokens through
+        # 2 of the 16 layers; tokens/s scaled by 2/16 (at 1,024 tokens the
+        # products dominate, so the scaling holds there; longer windows cost
+        # the oracle more per token)
+        import numpy as np
+        import oracle
+        Ls, Ns = 2, 1024
+        sub = inp.__class__(cfg=cfg.with_(n_layers=Ls, n_segments=1), x=inp.x[:Ns], mem_emb=inp.mem_emb,
+                            weights={k: v[:Ls] for k, v in inp.weights.items()}, g_attn=inp.g_attn[:Ls],
+                            g_mlp=inp.g_mlp[:Ls])
+        a = time.perf_counter()
+        oracle.llama_forward(sub, n_tokens=Ns)
+        el = time.perf_counter() - a
+        cpu = {"value": Ns / el * Ls / L, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+               "host": host_cpu(), "sample": f"full-attention forward of {Ns} tokens through {Ls} of {L} layers "
+                                              f"(float64 NumPy) in {el:.1f}s; tokens/s scaled by {Ls}/{L}"}
+        log(f"cpu oracle full attention: {Ns} tokens x {Ls} layers in {el:.1f}s")
     for N in (4096, 8192, 16384, 32768, 65536, 131072):
         S = N // T
         x = x_all[:N]
@@ -561,7 +607,9 @@ def full_attention(args, dev):
                 "armt_diagonal": {"ms": t_armt * 1e3, "ms_min": t_armt_min * 1e3, "tokens_per_s": N / t_armt,
                                   "tflops": flops_armt / t_armt / 1e12, "workspace_bytes": armt_ws},
                 "speedup_armt_over_full": t_full / t_armt,
-                "workspace_ratio_full_over_armt": full_ws / armt_ws}
+                "workspace_ratio_full_over_armt": full_ws / armt_ws,
+                "roofline": dict(roofline_mfma(flops_full / t_full / 1e12), path="full attention forward"),
+                "cpu_baseline": cpu if N == 4096 else None}
         log(f"N={N}: full attention {t_full * 1e3:.1f} ms ({line['full_attention']['tflops']:.0f} TFLOP/s), "
             f"ARMT diagonal {t_armt * 1e3:.1f} ms, x{t_full / t_armt:.2f}; workspace "
             f"{full_ws / 2**30:.2f} vs {armt_ws / 2**30:.2f} GiB")
@@ -587,6 +635,9 @@ def batch_sweep(args, dev):
     w, ccfg = base.weights, base.cfg
     xs_all = make_batch_x(cfg, inp, 8)
     base.close()
+    # a batch adds no arithmetic of its own: the oracle's forward rate is the
+    # headline's (per sequence, one node at a time)
+    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds)
     for B in (1, 2, 4, 8):
         model = ArmtModel(ccfg, w, batch=B)
         x = to_dev(np.ascontiguousarray(xs_all[:B]) if B > 1 else xs_all[0], dev)
@@ -604,8 +655,10 @@ def batch_sweep(args, dev):
             each.append(e0.elapsed_time(e1) * 1e-3)
         t = statistics.median(each)
         tokens = B * S * T
+        tf = node_gflop(cfg) * S * L * B / t / 1e3
         line = {"workload": "1b_s32", "batch": B, "tokens": tokens, "ms": t * 1e3, "tokens_per_s": tokens / t,
-                "tflops": node_gflop(cfg) * S * L * B / t / 1e3, "workspace_bytes": model.ws_bytes}
+                "tflops": tf, "workspace_bytes": model.ws_bytes, "roofline": roofline_mfma(tf),
+                "cpu_baseline": cpu if B == 1 else None}
         log(f"B={B}: {t * 1e3:.1f} ms, {tokens / t:.0f} tokens/s, {line['tflops']:.0f} TFLOP/s")
         print(json.dumps(line), flush=True)
         model.close()
