@@ -430,58 +430,80 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
     for (int e = 0; e < 4; ++e) At[i][c4 + e] = t[e];
   }
 
-  // k moves 64 per step: lane group g brings k0 + 16g .. +15 of its row (32
-  // bytes of W_mv, a whole 128-byte line per row across the four groups) and
-  // feeds them to two MFMAs (slots k0 + 16g + j, then k0 + 16g + 8 + j); the
-  // Y operand uses the same slot order.  The operands of step k + 1 are
-  // loaded into a second register set while step k multiplies (d / 64 is
-  // even: d is a multiple of 128).
-  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)(layer / a.batch) * d + i0 + 16 * w + c16) * d + 16 * g;
-  f32x4 acc[MBK];
+  // v = Y W_mv^T for the workgroup's 64 rows of W_mv.  The waves split k:
+  // wave w takes the 64-wide steps w, w + 4, ...  In a step, lane group g
+  // brings k0 + 16g .. +15 of a row (32 bytes of W_mv; a whole 128-byte line
+  // per row across the four groups) and feeds them to two MFMAs (slots
+  // k0 + 16g + j, then k0 + 16g + 8 + j); the Y operand, split into its bf16
+  // pair once per step, uses the same slot order and serves the four 16-row
+  // blocks of W_mv -- so each wave reads its quarter of Y once, not all of it.
+  // The next step's operands load into a second register set while a step
+  // multiplies; the four waves' partial sums are added in LDS in wave order.
+  const bf16* wv = (const bf16*)a.w_mv + ((int64_t)(layer / a.batch) * d + i0 + c16) * d + 16 * g;
+  f32x4 acc[4][MBK];
 #pragma unroll
-  for (int mb = 0; mb < MBK; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MBK; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   int yrow[MBK];
 #pragma unroll
   for (int mb = 0; mb < MBK; ++mb) yrow[mb] = 16 * mb + c16 < M ? 16 * mb + c16 : M - 1;
-  bf16x8 bw[2][2];
+  bf16x8 bw[2][4][2];
   float yv[2][MBK][16];
-  auto load = [&](int k0, bf16x8 (&b)[2], float (&y)[MBK][16]) {
-    b[0] = *(const bf16x8*)(wv + k0);
-    b[1] = *(const bf16x8*)(wv + k0 + 8);
+  auto load = [&](int k0, bf16x8 (&b)[4][2], float (&y)[MBK][16]) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      b[rb][0] = *(const bf16x8*)(wv + (int64_t)16 * rb * d + k0);
+      b[rb][1] = *(const bf16x8*)(wv + (int64_t)16 * rb * d + k0 + 8);
+    }
 #pragma unroll
     for (int mb = 0; mb < MBK; ++mb) {
       load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g, y[mb]);
       load8f(Y + (int64_t)yrow[mb] * d + k0 + 16 * g + 8, y[mb] + 8);
     }
   };
-  auto mul = [&](const bf16x8 (&b)[2], const float (&y)[MBK][16]) {
+  auto mul = [&](const bf16x8 (&b)[4][2], const float (&y)[MBK][16]) {
 #pragma unroll
     for (int mb = 0; mb < MBK; ++mb) {
       bf16x8 hi0, lo0, hi1, lo1;
       split8(y[mb], hi0, lo0);
       split8(y[mb] + 8, hi1, lo1);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, b[0], acc[mb], 0, 0, 0);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, b[0], acc[mb], 0, 0, 0);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, b[1], acc[mb], 0, 0, 0);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, b[1], acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi0, b[rb][0], acc[rb][mb], 0, 0, 0);
+        acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, b[rb][0], acc[rb][mb], 0, 0, 0);
+        acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi1, b[rb][1], acc[rb][mb], 0, 0, 0);
+        acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, b[rb][1], acc[rb][mb], 0, 0, 0);
+      }
     }
   };
-  load(0, bw[0], yv[0]);
-  for (int k0 = 0; k0 < d; k0 += 128) {
-    load(k0 + 64, bw[1], yv[1]);
+  const int ksteps = d >> 6;
+  int st = w;
+  if (st < ksteps) load(64 * st, bw[0], yv[0]);
+  for (; st < ksteps; st += 8) {
+    if (st + 4 < ksteps) load(64 * (st + 4), bw[1], yv[1]);
     mul(bw[0], yv[0]);
-    if (k0 + 128 < d) load(k0 + 128, bw[0], yv[0]);
+    if (st + 4 >= ksteps) break;
+    if (st + 8 < ksteps) load(64 * (st + 8), bw[0], yv[0]);
     mul(bw[1], yv[1]);
   }
-  // lane holds v[m = 16mb + 4g + r][i = i0 + 16w + c16]
+  // lane holds wave w's partial v[m = 16mb + 4g + r][i = i0 + 16rb + c16];
+  // vvs = ((w0 + w1) + w2) + w3
 #pragma unroll
-  for (int mb = 0; mb < MBK; ++mb)
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mb + 4 * g + r;
-      if (m < M) vvs[m][16 * w + c16] = acc[mb][r];
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MBK; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 16 * mb + 4 * g + r;
+            if (m < M) vvs[m][16 * rb + c16] = (ww == 0 ? 0.f : vvs[m][16 * rb + c16]) + acc[rb][mb][r];
+          }
     }
-  __syncthreads();
+    __syncthreads();
+  }
   for (int idx = tid; idx < M * 64; idx += 256) {
     const int m = idx >> 6, ii = idx & 63;
     float s = 0.f;
