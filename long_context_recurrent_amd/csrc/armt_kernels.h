@@ -97,8 +97,9 @@ struct NormArgs {
 };
 
 // ---- backward (fp32) ----------------------------------------------------
-// Generic strided fp32 GEMM over P problems: C = (accumulate ? C : 0) + A B,
-// A(m, k) = A + p*a_ps + m*a_rs + k*a_cs, B(k, n) and C(m, n) likewise.
+// Generic strided GEMM over P problems (the backward's products):
+// C = (accumulate ? C : 0) + A B with A(m, k) = A + p*a_ps + m*a_rs + k*a_cs,
+// B(k, n) and C(m, n) likewise; A and C fp32, B fp32 or bf16.
 struct GenGemm {
   const float* A;
   const void* B;             // fp32, or bf16 when b_bf16 (strides in elements)
@@ -165,7 +166,7 @@ hipError_t bw_memr_dq(const BwArgs& a, float* dq, const float* u, const float* q
 hipError_t bw_copy(const float* src, float* dst, int64_t count, int64_t src_ps, int64_t dst_ps, int accumulate, int P,
                    hipStream_t st);
 
-// number of 16-row MFMA blocks per GEMM tile that have instantiations
+// tile heights of the bf16 GEMM, in 32-row MFMA blocks, that have instantiations
 extern const int kGemmRowBlocks[];
 extern const int kGemmRowBlocksCount;
 
