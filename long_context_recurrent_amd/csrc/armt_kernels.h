@@ -165,6 +165,12 @@ hipError_t bw_memr_dq(const BwArgs& a, float* dq, const float* u, const float* q
                       float* dz, int64_t u_ps, int64_t z_ps, int64_t dz_ps, int rows, int P, hipStream_t st);
 hipError_t bw_copy(const float* src, float* dst, int64_t count, int64_t src_ps, int64_t dst_ps, int accumulate, int P,
                    hipStream_t st);
+hipError_t bw_to_bf16(const float* src, bf16* dst, int64_t count, int64_t ps, int P, hipStream_t st);
+// dst[c][r] = src[r][c] (r < rows; zero up to rows_pad, a multiple of 64) as
+// bf16 hi (and lo when dst_lo) parts, per problem; destination rows ld_dst apart
+hipError_t bw_transpose_bf16(const void* src, bool src_bf16, int64_t ld_src, int64_t src_ps, int rows, int rows_pad,
+                             int cols, bf16* dst_hi, bf16* dst_lo, int64_t ld_dst, int64_t dst_ps, int P,
+                             hipStream_t st);
 
 // tile heights of the bf16 GEMM, in 32-row MFMA blocks, that have instantiations
 extern const int kGemmRowBlocks[];

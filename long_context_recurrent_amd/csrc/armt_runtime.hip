@@ -915,7 +915,7 @@ struct BwLayout {
   size_t qkv, dqkv, O, dO, mx, ls, Dq;
   size_t G, Up, Uo, dG, dUp, dUo;
   size_t uk, k, dk, v, kA, e, de, dv, dkA, bl, beta, denw, ddenw, dbl;
-  size_t dH, dA, dz, yscr, g32, total;
+  size_t dH, dA, dz, yscr, g32, a16, O16, b16, U16, ta, tb, total;
 };
 
 BwLayout make_bw_layout(const armt_config* c, int S) {
@@ -946,6 +946,18 @@ BwLayout make_bw_layout(const armt_config* c, int S) {
   lo.dz = take(L * 64);
   lo.yscr = take((size_t)S * c->seg_len * d);   // the recording forward's y (not returned)
   lo.g32 = take(3 * L * d);                      // fp32 g_attn, g_mlp, w_beta of a bf16 model
+  // bf16 copies of the recomputed a, O, b, Uo (bf16 models)
+  lo.a16 = take(L * n * d / 2 + 1); lo.O16 = take(L * n * H * c->head_dim / 2 + 1);
+  lo.b16 = take(L * n * d / 2 + 1); lo.U16 = take(L * n * F / 2 + 1);
+  // transposed bf16 operands of the weight gradients (bf16 models): rows of
+  // the node padded to a multiple of 64 with zeros
+  {
+    const size_t n_pad = (n + 63) / 64 * 64;
+    size_t cmax = d > F ? d : F;
+    cmax = cmax > qd ? cmax : qd;
+    cmax = cmax > H * (size_t)c->head_dim ? cmax : H * (size_t)c->head_dim;
+    lo.ta = take(L * cmax * n_pad); lo.tb = take(L * cmax * n_pad);   // [cols][2 n_pad] bf16
+  }
   lo.total = off;
   return lo;
 }
@@ -1053,12 +1065,60 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     BW_TRY(hipMemsetAsync(top + (int64_t)T * d, 0, (size_t)M * d * 4, st));
   }
 
-  // The activations that the bf16 forward rounds to bf16 before a product
-  // (the attention and MLP inputs a and b, the attention output O, the SwiGLU
-  // output Uo) enter the matrix-core products rounded once (RA: as the first
-  // operand, RB: as the second); every other fp32 operand enters as a hi/lo
-  // pair.
-  const int RA = 1, RB = 2;
+  // bf16 models: the activations that the bf16 forward rounds before a
+  // product (the attention and MLP inputs a and b, the attention output O,
+  // the SwiGLU output Uo) are kept rounded in bf16 slabs; the recomputed
+  // products that take them as inputs run on the forward's own grouped GEMM
+  // (fp32 store, or += on the residual), and the weight gradients take them
+  // as bf16 operands.  Every other fp32 operand of a matrix-core product
+  // enters as a hi/lo pair.
+  bf16* const a16 = (bf16*)(cx.ws + cx.lo.a16);
+  bf16* const O16 = (bf16*)(cx.ws + cx.lo.O16);
+  bf16* const b16 = (bf16*)(cx.ws + cx.lo.b16);
+  bf16* const U16 = (bf16*)(cx.ws + cx.lo.U16);
+  const int64_t nh = (int64_t)n * hhd;
+  // C (fp32 slab, layer-indexed) = or += A16 W^T over the wave's layers
+  auto fwd_gemm = [&](const bf16* A16, int64_t a_ps, int K, const void* W, float* C, int64_t c_ps, int N,
+                      int epi) -> hipError_t {
+    GemmArgs g{};
+    g.P = P; g.l0 = l0; g.batch = 1;
+    g.A = A16; g.a_stride = a_ps; g.lda = K;
+    g.B = W; g.b_stride = (int64_t)N * K;
+    g.M = n; g.N = N; g.K = K;
+    g.C = C; g.c_stride = c_ps; g.ldc = N;
+    g.desc = nullptr; g.last_layer = L - 1; g.T = T;
+    return launch_gemm_bf16(g, epi, gemm_rows(h, N, 256, P), st);
+  };
+  const int64_t Lo = (int64_t)l0;   // slab offsets of layer l0
+  // dW (fp32, [L][out][in], layer-indexed) += dY^T X on the forward's grouped
+  // GEMM, in one pass over dW: K runs over the node's rows twice, first with
+  // the bf16 hi parts of dY, then with its lo parts, against X both times
+  // (dY^T -> [out][hi | lo], X^T -> [in][X | X], each half n_pad rows with
+  // zeros past the node)
+  const int n_pad = (n + 63) / 64 * 64;
+  bf16* const ta = (bf16*)(cx.ws + cx.lo.ta);
+  bf16* const tb = (bf16*)(cx.ws + cx.lo.tb);
+  auto dw_gemm = [&](const float* dY, int64_t y_ps, int out, const bf16* X16, int64_t x_ps, int in,
+                     const void* dW) -> hipError_t {
+    const int k2 = 2 * n_pad;
+    const int64_t sa = (int64_t)out * k2, sb = (int64_t)in * k2;
+    bf16* a0 = ta + Lo * sa;
+    bf16* b0 = tb + Lo * sb;
+    hipError_t e = bw_transpose_bf16(dY, false, out, y_ps, n, n_pad, out, a0, a0 + n_pad, k2, sa, P, st);
+    if (e != hipSuccess) return e;
+    if ((e = bw_transpose_bf16(X16, true, in, x_ps, n, n_pad, in, b0, nullptr, k2, sb, P, st)) != hipSuccess)
+      return e;
+    if ((e = bw_transpose_bf16(X16, true, in, x_ps, n, n_pad, in, b0 + n_pad, nullptr, k2, sb, P, st)) != hipSuccess)
+      return e;
+    GemmArgs g{};
+    g.P = P; g.l0 = l0; g.batch = 1;
+    g.A = ta; g.a_stride = sa; g.lda = k2;
+    g.B = tb; g.b_stride = sb;
+    g.M = out; g.N = in; g.K = k2;
+    g.C = const_cast<void*>(dW); g.c_stride = (int64_t)out * in; g.ldc = in;   // caller's gradient buffer
+    g.desc = nullptr; g.last_layer = L - 1; g.T = T;
+    return launch_gemm_bf16(g, EPI_RESID, h->mb ? h->mb : pick_row_blocks(out, in, 256, P, h->cus), st);
+  };
 
   // ---- recompute the forward of each node
   BW_TRY(gg(hin, hin_ps, d, 1, W_mq, 64 * (int64_t)d, 1, d, u, n64, 64, 1, n, 64, d, 0, P, st, wb, wb));
@@ -1067,7 +1127,12 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   BW_TRY(bw_copy(hin, h1, nd, hin_ps, nd, 0, P, st));
   BW_TRY(bw_add_div(ba, h1, num, den, h1, nd, n, P, st));
   BW_TRY(bw_rms_fwd(ba, h1, g_at, a, r1, nd, d, n, P, st));
-  BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st, wb, wb, RA));
+  if (wb) {
+    BW_TRY(bw_to_bf16(a, a16 + Lo * nd, nd, nd, P, st));
+    BW_TRY(fwd_gemm(a16, nd, d, h->w.w_qkv, cx.f(cx.lo.qkv), nq, qd, EPI_STORE));
+  } else {
+    BW_TRY(gg(a, nd, d, 1, W_qkv, (int64_t)qd * d, 1, d, qkv, nq, qd, 1, n, qd, d, 0, P, st));
+  }
   BW_TRY(bw_rope(ba, qkv, nq, qd, 0, H, 1.f, n, P, st));
   BW_TRY(bw_rope(ba, qkv, nq, qd, H * hd, G, 1.f, n, P, st));
   // bf16 models: attention on the matrix cores (bf16 operands), as their
@@ -1076,13 +1141,29 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   if (attn_mm) BW_TRY(bw_attn_mfma_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   else BW_TRY(bw_attn_fwd(ba, qkv, O, mx, ls, nq, nd, Hn, P, st));
   BW_TRY(bw_copy(h1, h2, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st, wb, wb, RA));
+  if (wb) {
+    BW_TRY(bw_to_bf16(O, O16 + Lo * nh, nh, nh, P, st));
+    BW_TRY(fwd_gemm(O16, nh, hhd, h->w.w_o, cx.f(cx.lo.h2), nd, d, EPI_RESID));
+  } else {
+    BW_TRY(gg(O, nd, hhd, 1, W_o, (int64_t)d * hhd, 1, hhd, h2, nd, d, 1, n, d, hhd, 1, P, st));
+  }
   BW_TRY(bw_rms_fwd(ba, h2, g_ml, b, r2, nd, d, n, P, st));
-  BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st, wb, wb, RA));
-  BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st, wb, wb, RA));
+  if (wb) {
+    BW_TRY(bw_to_bf16(b, b16 + Lo * nd, nd, nd, P, st));
+    BW_TRY(fwd_gemm(b16, nd, d, h->w.w_gate, cx.f(cx.lo.G), nF, F, EPI_STORE));
+    BW_TRY(fwd_gemm(b16, nd, d, h->w.w_up, cx.f(cx.lo.Up), nF, F, EPI_STORE));
+  } else {
+    BW_TRY(gg(b, nd, d, 1, W_g, (int64_t)F * d, 1, d, Gt, nF, F, 1, n, F, d, 0, P, st));
+    BW_TRY(gg(b, nd, d, 1, W_u, (int64_t)F * d, 1, d, Up, nF, F, 1, n, F, d, 0, P, st));
+  }
   BW_TRY(bw_swiglu(Gt, Up, Uo, nF, nF, P, st));
   BW_TRY(bw_copy(h2, h3, nd, nd, nd, 0, P, st));
-  BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st, wb, wb, RA));
+  if (wb) {
+    BW_TRY(bw_to_bf16(Uo, U16 + Lo * nF, nF, nF, P, st));
+    BW_TRY(fwd_gemm(U16, nF, F, h->w.w_down, cx.f(cx.lo.h3), nd, d, EPI_RESID));
+  } else {
+    BW_TRY(gg(Uo, nF, F, 1, W_d, (int64_t)d * F, 1, F, h3, nd, d, 1, n, d, F, 1, P, st));
+  }
   const float* Y = h3 + (int64_t)T * d;
   BW_TRY(gg(Y, nd, d, 1, W_mk, 64 * (int64_t)d, 1, d, uk, M64, 64, 1, M, 64, d, 0, P, st, wb, wb));
   BW_TRY(gg(Y, nd, d, 1, W_mv, (int64_t)d * d, 1, d, v, Md, d, 1, M, d, d, 0, P, st, wb, wb));
@@ -1108,22 +1189,30 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st, 0, wb));
   // ---- MLP block backward
   BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb, wb));
-  BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st, 0, wb, RB));
+  if (wb) BW_TRY(dw_gemm(dh, nd, d, U16 + Lo * nF, nF, F, cx.gw->w_down));
+  else BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
   BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb, wb));
   BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb, wb));
-  BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb, RB));
-  BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st, 0, wb, RB));
+  if (wb) {
+    BW_TRY(dw_gemm(dG, nF, F, b16 + Lo * nd, nd, d, cx.gw->w_gate));
+    BW_TRY(dw_gemm(dUp, nF, F, b16 + Lo * nd, nd, d, cx.gw->w_up));
+  } else {
+    BW_TRY(gg(dG, nF, 1, F, b, nd, d, 1, dW_g, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
+    BW_TRY(gg(dUp, nF, 1, F, b, nd, d, 1, dW_u, (int64_t)F * d, d, 1, F, d, n, 1, P, st));
+  }
   BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
   // ---- attention block backward
   BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb, wb));
-  BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st, 0, wb, RB));
+  if (wb) BW_TRY(dw_gemm(dh, nd, d, O16 + Lo * nh, nh, hhd, cx.gw->w_o));
+  else BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st));
   if (attn_mm) BW_TRY(bw_attn_mfma_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   else BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
   BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb, wb));
-  BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st, 0, wb, RB));
+  if (wb) BW_TRY(dw_gemm(dqkv, nq, qd, a16 + Lo * nd, nd, d, cx.gw->w_qkv));
+  else BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st));
   BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
   // ---- memory read backward
   BW_TRY(bw_memr_bwd(ba, dh, num, den, dnum, dden, nd, n, P, st));

@@ -798,7 +798,76 @@ __global__ __launch_bounds__(256) void bw_copy_kernel(const float* src, float* d
   dst[p * dst_ps + i] = accumulate ? dst[p * dst_ps + i] + src[p * src_ps + i] : src[p * src_ps + i];
 }
 
+// dst = R(src) (bf16), count a multiple of 4, per-problem strides ps
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* src, bf16* dst, int64_t count4, int64_t ps) {
+  const int p = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count4) return;
+  const f32x4 v = *(const f32x4*)(src + p * ps + 4 * i);
+  *(bf16x4*)(dst + p * ps + 4 * i) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// dst[c][r] = src[r][c] for r < rows_pad (zero for r >= rows), c < cols:
+// bf16 hi part (and lo part when dst_lo) of an fp32 or bf16 source.  Tiles of
+// 64 x 64 through LDS; reads coalesced along c, writes along r.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const T* src, int64_t ld_src, int64_t src_ps, int rows,
+                                                             int cols, bf16* dst_hi, bf16* dst_lo, int64_t ld_dst,
+                                                             int64_t dst_ps) {
+  __shared__ float tile[64][65];
+  const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  const T* sp = src + p * src_ps;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 4 * i + (tid >> 6), c = tid & 63;
+    tile[r][c] = (r0 + r < rows && c0 + c < cols) ? (float)sp[(int64_t)(r0 + r) * ld_src + c0 + c] : 0.f;
+  }
+  __syncthreads();
+  const int c = tid >> 2, r16 = (tid & 3) * 16;
+  if (c0 + c >= cols) return;
+  bf16x8 h[2], l[2];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const float v = tile[r16 + t][c];
+    const bf16 hv = (bf16)v;
+    h[t >> 3][t & 7] = hv;
+    l[t >> 3][t & 7] = (bf16)(v - (float)hv);
+  }
+  bf16* dh = dst_hi + p * dst_ps + (int64_t)(c0 + c) * ld_dst + r0 + r16;
+  *(bf16x8*)dh = h[0];
+  *(bf16x8*)(dh + 8) = h[1];
+  if (dst_lo) {
+    bf16* dl = dst_lo + p * dst_ps + (int64_t)(c0 + c) * ld_dst + r0 + r16;
+    *(bf16x8*)dl = l[0];
+    *(bf16x8*)(dl + 8) = l[1];
+  }
+}
+
 }  // namespace
+
+hipError_t bw_transpose_bf16(const void* src, bool src_bf16, int64_t ld_src, int64_t src_ps, int rows, int rows_pad,
+                             int cols, bf16* dst_hi, bf16* dst_lo, int64_t ld_dst, int64_t dst_ps, int P,
+                             hipStream_t st) {
+  // rows_pad: whole 64-row tiles; 16-byte aligned destination rows
+  if (rows_pad % 64 || rows_pad < rows || ld_dst < rows_pad || ld_dst % 8 || dst_ps % 8 || ((uintptr_t)dst_hi & 15) ||
+      ((uintptr_t)dst_lo & 15))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(rows_pad / 64), (unsigned)((cols + 63) / 64), P);
+  if (src_bf16)
+    hipLaunchKernelGGL(transpose_bf16_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)src, ld_src, src_ps, rows,
+                       cols, dst_hi, dst_lo, ld_dst, dst_ps);
+  else
+    hipLaunchKernelGGL(transpose_bf16_kernel<float>, grid, dim3(256), 0, st, (const float*)src, ld_src, src_ps, rows,
+                       cols, dst_hi, dst_lo, ld_dst, dst_ps);
+  return hipGetLastError();
+}
+
+hipError_t bw_to_bf16(const float* src, bf16* dst, int64_t count, int64_t ps, int P, hipStream_t st) {
+  if (count % 4 || ps % 4 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 7)) return hipErrorInvalidValue;
+  const int64_t c4 = count / 4;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((c4 + 255) / 256), P), dim3(256), 0, st, src, dst, c4, ps);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // launchers
