@@ -166,6 +166,10 @@ hipError_t bw_memr_dq(const BwArgs& a, float* dq, const float* u, const float* q
 hipError_t bw_copy(const float* src, float* dst, int64_t count, int64_t src_ps, int64_t dst_ps, int accumulate, int P,
                    hipStream_t st);
 hipError_t bw_to_bf16(const float* src, bf16* dst, int64_t count, int64_t ps, int P, hipStream_t st);
+// dst[r][c] = hi(src[r][c]), dst[r][lo_off + c] = lo(src[r][c]): fp32 rows as
+// bf16 pairs, per problem
+hipError_t bw_split_bf16(const float* src, int64_t ld_src, int64_t src_ps, int rows, int cols, bf16* dst,
+                         int64_t ld_dst, int64_t dst_ps, int lo_off, int P, hipStream_t st);
 // dst[c][r] = src[r][c] (r < rows; zero up to rows_pad, a multiple of 64) as
 // bf16 hi (and lo when dst_lo) parts, per problem; destination rows ld_dst apart
 hipError_t bw_transpose_bf16(const void* src, bool src_bf16, int64_t ld_src, int64_t src_ps, int rows, int rows_pad,

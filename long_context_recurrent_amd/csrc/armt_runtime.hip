@@ -915,7 +915,7 @@ struct BwLayout {
   size_t qkv, dqkv, O, dO, mx, ls, Dq;
   size_t G, Up, Uo, dG, dUp, dUo;
   size_t uk, k, dk, v, kA, e, de, dv, dkA, bl, beta, denw, ddenw, dbl;
-  size_t dH, dA, dz, yscr, g32, a16, O16, b16, U16, ta, tb, total;
+  size_t dH, dA, dz, yscr, g32, a16, O16, b16, U16, ta, tb, wtd, wtgu, wto, wtq, ysp, total;
 };
 
 BwLayout make_bw_layout(const armt_config* c, int S) {
@@ -957,6 +957,18 @@ BwLayout make_bw_layout(const armt_config* c, int S) {
     cmax = cmax > qd ? cmax : qd;
     cmax = cmax > H * (size_t)c->head_dim ? cmax : H * (size_t)c->head_dim;
     lo.ta = take(L * cmax * n_pad); lo.tb = take(L * cmax * n_pad);   // [cols][2 n_pad] bf16
+  }
+  // input gradients of the block products (bf16 models): the transposed
+  // weights, each twice along k, [W_d^T | W_d^T], [W_g^T | W_g^T | W_u^T |
+  // W_u^T], [W_o^T | W_o^T], [W_qkv^T | W_qkv^T]; and the gradients as bf16
+  // pairs, [n][hi | lo]
+  {
+    const size_t hd = H * (size_t)c->head_dim;
+    lo.wtd = take(L * F * 2 * d / 2); lo.wtgu = take(L * d * 4 * F / 2);
+    lo.wto = take(L * hd * 2 * d / 2); lo.wtq = take(L * d * 2 * qd / 2);
+    size_t cmax = 4 * F > 2 * qd ? 4 * F : 2 * qd;
+    cmax = cmax > 2 * d ? cmax : 2 * d;
+    lo.ysp = take(L * n * cmax / 2);
   }
   lo.total = off;
   return lo;
@@ -1090,6 +1102,20 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     return launch_gemm_bf16(g, epi, gemm_rows(h, N, 256, P), st);
   };
   const int64_t Lo = (int64_t)l0;   // slab offsets of layer l0
+  // dX (fp32, layer-indexed slab) = dY W on the forward's grouped GEMM: dY as
+  // a bf16 pair along k ([n][hi | lo], from the per-layer scratch ysp)
+  // against the doubled transposed weights wt ([in][W^T | W^T])
+  bf16* const ysp = (bf16*)(cx.ws + cx.lo.ysp);
+  auto dx_gemm = [&](int Kx, const bf16* wt, float* C, int64_t c_ps, int N) -> hipError_t {
+    GemmArgs g{};
+    g.P = P; g.l0 = l0; g.batch = 1;
+    g.A = ysp; g.a_stride = (int64_t)n * Kx; g.lda = Kx;
+    g.B = wt; g.b_stride = (int64_t)N * Kx;
+    g.M = n; g.N = N; g.K = Kx;
+    g.C = C; g.c_stride = c_ps; g.ldc = N;
+    g.desc = nullptr; g.last_layer = L - 1; g.T = T;
+    return launch_gemm_bf16(g, EPI_STORE, gemm_rows(h, N, 256, P), st);
+  };
   // dW (fp32, [L][out][in], layer-indexed) += dY^T X on the forward's grouped
   // GEMM, in one pass over dW: K runs over the node's rows twice, first with
   // the bf16 hi parts of dY, then with its lo parts, against X both times
@@ -1188,12 +1214,25 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   BW_TRY(gg(dk, M64, 1, 64, Y, nd, d, 1, dW_mk, 64 * (int64_t)d, d, 1, 64, d, M, 1, P, st, 0, wb));
   BW_TRY(gg(dv, Md, 1, d, Y, nd, d, 1, dW_mv, (int64_t)d * d, d, 1, d, d, M, 1, P, st, 0, wb));
   // ---- MLP block backward
-  BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st, wb, wb));
+  if (wb) {
+    BW_TRY(bw_split_bf16(dh, d, nd, n, d, ysp + Lo * n * 2 * d, 2 * d, (int64_t)n * 2 * d, d, P, st));
+    BW_TRY(dx_gemm(2 * d, (const bf16*)(cx.ws + cx.lo.wtd), cx.f(cx.lo.dUo), nF, F));
+  } else {
+    BW_TRY(gg(dh, nd, d, 1, W_d, (int64_t)d * F, F, 1, dUo, nF, F, 1, n, F, d, 0, P, st));
+  }
   if (wb) BW_TRY(dw_gemm(dh, nd, d, U16 + Lo * nF, nF, F, cx.gw->w_down));
   else BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
-  BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st, wb, wb));
-  BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st, wb, wb));
+  if (wb) {
+    // db = dG W_g + dUp W_u as one product: [dG | dUp] pairs against [W_g^T | W_u^T] doubled
+    bf16* y0 = ysp + Lo * n * 4 * F;
+    BW_TRY(bw_split_bf16(dG, F, nF, n, F, y0, 4 * F, (int64_t)n * 4 * F, F, P, st));
+    BW_TRY(bw_split_bf16(dUp, F, nF, n, F, y0 + 2 * F, 4 * F, (int64_t)n * 4 * F, F, P, st));
+    BW_TRY(dx_gemm(4 * F, (const bf16*)(cx.ws + cx.lo.wtgu), cx.f(cx.lo.db), nd, d));
+  } else {
+    BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st));
+    BW_TRY(gg(dUp, nF, F, 1, W_u, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 1, P, st));
+  }
   if (wb) {
     BW_TRY(dw_gemm(dG, nF, F, b16 + Lo * nd, nd, d, cx.gw->w_gate));
     BW_TRY(dw_gemm(dUp, nF, F, b16 + Lo * nd, nd, d, cx.gw->w_up));
@@ -1203,14 +1242,24 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   }
   BW_TRY(bw_rms_bwd(ba, h2, g_ml, r2, db, dh, dg_ml, nd, d, n, 1, P, st));
   // ---- attention block backward
-  BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st, wb, wb));
+  if (wb) {
+    BW_TRY(bw_split_bf16(dh, d, nd, n, d, ysp + Lo * n * 2 * d, 2 * d, (int64_t)n * 2 * d, d, P, st));
+    BW_TRY(dx_gemm(2 * d, (const bf16*)(cx.ws + cx.lo.wto), cx.f(cx.lo.dO), nd, hhd));
+  } else {
+    BW_TRY(gg(dh, nd, d, 1, W_o, (int64_t)d * hhd, hhd, 1, dO, nd, hhd, 1, n, hhd, d, 0, P, st));
+  }
   if (wb) BW_TRY(dw_gemm(dh, nd, d, O16 + Lo * nh, nh, hhd, cx.gw->w_o));
   else BW_TRY(gg(dh, nd, 1, d, O, nd, hhd, 1, dW_o, (int64_t)d * hhd, hhd, 1, d, hhd, n, 1, P, st));
   if (attn_mm) BW_TRY(bw_attn_mfma_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   else BW_TRY(bw_attn_bwd(ba, qkv, O, dO, mx, ls, Dq, dqkv, nq, nd, Hn, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, 0, H, -1.f, n, P, st));
   BW_TRY(bw_rope(ba, dqkv, nq, qd, H * hd, G, -1.f, n, P, st));
-  BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st, wb, wb));
+  if (wb) {
+    BW_TRY(bw_split_bf16(dqkv, qd, nq, n, qd, ysp + Lo * n * 2 * qd, 2 * qd, (int64_t)n * 2 * qd, qd, P, st));
+    BW_TRY(dx_gemm(2 * qd, (const bf16*)(cx.ws + cx.lo.wtq), cx.f(cx.lo.da), nd, d));
+  } else {
+    BW_TRY(gg(dqkv, nq, qd, 1, W_qkv, (int64_t)qd * d, d, 1, da, nd, d, 1, n, d, qd, 0, P, st));
+  }
   if (wb) BW_TRY(dw_gemm(dqkv, nq, qd, a16 + Lo * nd, nd, d, cx.gw->w_qkv));
   else BW_TRY(gg(dqkv, nq, 1, qd, a, nd, d, 1, dW_qkv, (int64_t)qd * d, d, 1, qd, d, n, 1, P, st));
   BW_TRY(bw_rms_bwd(ba, h1, g_at, r1, da, dh, dg_at, nd, d, n, 1, P, st));
@@ -1275,6 +1324,14 @@ int armt_backward_workspace_size(armt_handle* h, int32_t n_segments, size_t* byt
   if (h->llama) return fail(ARMT_E_INVALID, "handle is a full-attention comparator");
   if (h->batch != 1) return fail(ARMT_E_UNSUPPORTED, "the backward runs on batch-1 handles");
   if (n_segments < 1) return fail(ARMT_E_INVALID, "n_segments must be >= 1");
+  if (h->bf16) {
+    // the input-gradient products run on the grouped bf16 GEMM with the
+    // weights transposed: every weight dimension a multiple of 64
+    const armt_config& c = h->cfg;
+    const int hd = c.n_heads * c.head_dim;
+    if (c.d_model % 64 || c.ffn_hidden % 64 || h->qkv_dim % 64 || hd % 64)
+      return fail(ARMT_E_UNSUPPORTED, "bf16 backward needs d, F, (H + 2G) hd and H hd multiples of 64");
+  }
   *bytes = make_bw_layout(&h->cfg, n_segments).total;
   return ARMT_OK;
 }
@@ -1309,6 +1366,22 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
     cx.g_attn = g32;
     cx.g_mlp = g32 + Ld;
     cx.w_beta = g32 + 2 * Ld;
+    // transposed weights, each twice along k, for the input-gradient products
+    const int hd = c.n_heads * c.head_dim;
+    struct { const void* w; int out, in; size_t at; int ld, off0, off1; } tw[] = {
+        {h->w.w_down, d, F, cx.lo.wtd, 2 * d, 0, d},
+        {h->w.w_gate, F, d, cx.lo.wtgu, 4 * F, 0, F},
+        {h->w.w_up, F, d, cx.lo.wtgu, 4 * F, 2 * F, 3 * F},
+        {h->w.w_o, d, hd, cx.lo.wto, 2 * d, 0, d},
+        {h->w.w_qkv, qd, d, cx.lo.wtq, 2 * qd, 0, qd}};
+    for (const auto& t : tw) {
+      bf16* dst = (bf16*)((char*)workspace + t.at);
+      const int64_t dps = (int64_t)t.in * t.ld;
+      for (int off : {t.off0, t.off1})
+        if ((e = bw_transpose_bf16(t.w, true, t.in, (int64_t)t.out * t.in, t.out, t.out, t.in, dst + off, nullptr,
+                                   t.ld, dps, L, st)) != hipSuccess)
+          return hip_fail(e, "transposed weights");
+    }
   } else {
     cx.g_attn = (const float*)h->w.g_attn;
     cx.g_mlp = (const float*)h->w.g_mlp;

@@ -843,7 +843,39 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const T* src, int64
   }
 }
 
+// dst[r][c] = hi(src[r][c]), dst[r][lo_off + c] = lo(src[r][c]) (bf16 pair);
+// cols a multiple of 4
+__global__ __launch_bounds__(256) void split_bf16_kernel(const float* src, int64_t ld_src, int64_t src_ps, int rows,
+                                                         int cols, bf16* dst, int64_t ld_dst, int64_t dst_ps,
+                                                         int lo_off) {
+  const int p = blockIdx.y, c4n = cols / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * c4n) return;
+  const int r = (int)(i / c4n), c = 4 * (int)(i % c4n);
+  const f32x4 v = *(const f32x4*)(src + p * src_ps + (int64_t)r * ld_src + c);
+  bf16x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (bf16)v[e];
+    l[e] = (bf16)(v[e] - (float)h[e]);
+  }
+  bf16* d = dst + p * dst_ps + (int64_t)r * ld_dst + c;
+  *(bf16x4*)d = h;
+  *(bf16x4*)(d + lo_off) = l;
+}
+
 }  // namespace
+
+hipError_t bw_split_bf16(const float* src, int64_t ld_src, int64_t src_ps, int rows, int cols, bf16* dst,
+                         int64_t ld_dst, int64_t dst_ps, int lo_off, int P, hipStream_t st) {
+  if (cols % 4 || ld_src % 4 || src_ps % 4 || ld_dst % 4 || dst_ps % 4 || lo_off % 4 || ((uintptr_t)src & 15) ||
+      ((uintptr_t)dst & 7))
+    return hipErrorInvalidValue;
+  const int64_t items = (int64_t)rows * (cols / 4);
+  hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((items + 255) / 256), P), dim3(256), 0, st, src, ld_src,
+                     src_ps, rows, cols, dst, ld_dst, dst_ps, lo_off);
+  return hipGetLastError();
+}
 
 hipError_t bw_transpose_bf16(const void* src, bool src_bf16, int64_t ld_src, int64_t src_ps, int rows, int rows_pad,
                              int cols, bf16* dst_hi, bf16* dst_lo, int64_t ld_dst, int64_t dst_ps, int P,
