@@ -243,9 +243,12 @@ int armt_llama_forward(armt_handle *h, const void *x, int64_t n_tokens, void *y)
  * For an ARMT_BF16 handle the recording forward is the bf16 forward, and each
  * node is differentiated at the input rows that forward gave it, the
  * forward's bf16 roundings of branch activations counting as identity in the
- * gradient; its products run on the matrix cores with every fp32 operand as
- * a bf16 pair (about 16 bits kept) and attention with bf16 operands, fp32
- * accumulation.  ARMT_F32 handles use fp32 vector-ALU kernels throughout.
+ * gradient; its products run on the matrix cores, the bf16-rounded
+ * activations as single bf16 values and every other fp32 operand (the
+ * gradients among them) as a bf16 pair (about 16 bits kept), attention with
+ * bf16 operands, fp32 accumulation.  ARMT_E_UNSUPPORTED unless d, F,
+ * (H + 2G) hd and H hd are multiples of 64.  ARMT_F32 handles use fp32
+ * vector-ALU kernels throughout.
  * Asynchronous on the handle's stream; uses the handle's workspace too (must
  * not overlap a forward on the handle).  ARMT_E_UNSUPPORTED for batched
  * handles. */

@@ -107,9 +107,6 @@ struct GenGemm {
   int64_t a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs;
   int M, N, K, accumulate;
   int b_bf16;
-  // matrix-core path: operand rounded once to bf16 instead of a hi/lo pair
-  // (activations that the bf16 forward itself rounds)
-  int a_single, b_single;
 };
 
 // Shapes shared by the backward kernels.

@@ -989,9 +989,8 @@ struct BwCtx {
 // (strides in elements; B is bf16 when b16 is set)
 hipError_t gg(const float* A, int64_t a_ps, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_ps, int64_t b_rs,
               int64_t b_cs, float* C, int64_t c_ps, int64_t c_rs, int64_t c_cs, int M, int N, int K, int acc, int P,
-              hipStream_t st, int b16 = 0, int matrix_cores = 0, int single = 0) {
-  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16, single & 1,
-            (single >> 1) & 1};
+              hipStream_t st, int b16 = 0, int matrix_cores = 0) {
+  GenGemm g{A, B, C, a_ps, a_rs, a_cs, b_ps, b_rs, b_cs, c_ps, c_rs, c_cs, M, N, K, acc, b16};
   return launch_gemm_gen(g, P, matrix_cores != 0, st);
 }
 

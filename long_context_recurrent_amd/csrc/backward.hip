@@ -263,13 +263,11 @@ struct Opnd {
 };
 }  // namespace mm
 
-// ALO / BLO: the operand enters as a hi/lo pair (else rounded once to bf16,
-// for activations the bf16 forward itself rounds)
-template <int AM, int BMODE, bool B16, bool ALO, bool BLO>
+template <int AM, int BMODE, bool B16>
 __global__ __launch_bounds__(256, (AM == mm::GEN || BMODE == mm::GEN) ? 1 : 2) void gemm_mfma_kernel(GenGemm g) {
   using namespace mm;
   using BT = typename std::conditional<B16, bf16, float>::type;
-  constexpr bool BL = BLO && !B16;
+  constexpr bool ALO = true, BL = !B16;   // fp32 operands as hi/lo pairs
   constexpr int NB = BL ? 4 : 3;               // A_hi, A_lo, B_hi (, B_lo)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][NB * OPB];
   const int p = blockIdx.z;
@@ -921,21 +919,10 @@ hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream
       if (g.b_rs == 1 && g.b_cs % vb == 0 && g.K % vb == 0) bm = mm::VK;
       else if (g.b_cs == 1 && g.b_rs % vb == 0 && g.N % vb == 0) bm = mm::VR;
     }
-#define MM_KERNEL(AM_, BM_, B16_, ALO_, BLO_) \
-  hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, B16_, ALO_, BLO_>), grid, dim3(256), 0, st, g)
-    // operands that enter rounded once: only on the vector paths (the
-    // element-wise fallback always keeps the hi/lo pairs)
-#define MM_LAUNCH(AM_, BM_)                                                                 \
-  do {                                                                                     \
-    const bool vec = AM_ != mm::GEN && BM_ != mm::GEN;                                     \
-    const bool alo = !(vec && g.a_single), blo = !(vec && g.b_single);                     \
-    if (g.b_bf16) {                                                                        \
-      if (alo) MM_KERNEL(AM_, BM_, true, true, false);                                     \
-      else MM_KERNEL(AM_, BM_, true, false, false);                                        \
-    } else {                                                                               \
-      if (blo) MM_KERNEL(AM_, BM_, false, true, true);                                     \
-      else MM_KERNEL(AM_, BM_, false, true, false);                                        \
-    }                                                                                      \
+#define MM_LAUNCH(AM_, BM_)                                                                             \
+  do {                                                                                                 \
+    if (g.b_bf16) hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, true>), grid, dim3(256), 0, st, g);  \
+    else hipLaunchKernelGGL((gemm_mfma_kernel<AM_, BM_, false>), grid, dim3(256), 0, st, g);          \
   } while (0)
     switch (am * 3 + bm) {
       case 0: MM_LAUNCH(mm::GEN, mm::GEN); break;
@@ -949,7 +936,6 @@ hipError_t launch_gemm_gen(const GenGemm& g, int P, bool matrix_cores, hipStream
       default: MM_LAUNCH(mm::VR, mm::VR); break;
     }
 #undef MM_LAUNCH
-#undef MM_KERNEL
     return hipGetLastError();
   }
   // 64 x 64 tiles only where they still give two workgroups per CU; the
