@@ -42,7 +42,9 @@ def sources() -> list:
 # Per-source extra device flags.  Attention keeps its MFMA results in
 # ordinary VGPRs: the softmax works on every score and accumulator element
 # between products, which would otherwise cost a register move each way.
-EXTRA: dict = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA: dict = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               # the memory read unrolls its chunk loops completely (24 chunks at d = 3072)
+               "memory_mfma.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 
 
 def _compile(src: str) -> str:

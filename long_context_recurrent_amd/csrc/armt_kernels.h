@@ -76,6 +76,7 @@ struct MemArgs {
   const void* w_beta;        // [L][d]
   const void* gain;          // [L][d] (g_attn or g_mlp)
   float* A;                  // [L][d][dk] fp32 state
+  bf16* A2;                  // [L][d][2][dk] the state as bf16 hi / lo parts (bf16 path)
   float* z;                  // [L][dk]
   float* qbuf;               // [L][n][dk] read keys phi(h W_mq^T) (bf16 path)
   float* kbuf;               // [L][M][dk] write keys phi(Y W_mk^T)
@@ -193,5 +194,8 @@ hipError_t launch_widen(const void* src, float* dst, int64_t count, bool use_bf1
 hipError_t launch_set_desc(CallDesc* desc, const void* x, void* y, int c0, int S, int t_last, int64_t seq_rows,
                            hipStream_t st);
 hipError_t launch_fill_f32(float* dst, const float* src, int64_t count, hipStream_t st);
+// A2[r] = (hi, lo) of A[r] for rows of 64 (hi = R(v), lo = R(v - hi)): the
+// bf16 path's copy of the memory state, refreshed by every memory update
+hipError_t launch_split_state(const float* A, bf16* A2, int64_t rows, hipStream_t st);
 
 }  // namespace armt

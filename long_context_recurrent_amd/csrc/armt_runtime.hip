@@ -61,7 +61,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, qbuf, kbuf, pden, beta, moff, total;
+  size_t desc, rope, A, z, act0, act1, abuf, qkv, vt, attn, ubuf, qbuf, kbuf, pden, beta, moff, A2, total;
 };
 
 int validate_config(const armt_config* c) {
@@ -119,6 +119,7 @@ Layout make_layout(const armt_config* c, int batch) {
   lo.pden = take(L * M * 4 * 4);
   lo.beta = take(L * M * 4);
   lo.moff = take(L * 4);
+  lo.A2 = take(c->dtype == ARMT_BF16 ? L * d * dk * 4 : 0);   // A as bf16 hi / lo pairs
   lo.total = off;
   return lo;
 }
@@ -198,6 +199,7 @@ struct armt_handle {
   float* rope = nullptr;
   float* A = nullptr;
   float* z = nullptr;
+  armt::bf16* A2 = nullptr;   // bf16 workloads: A split into hi / lo parts for the memory read
   void* act[2] = {nullptr, nullptr};
   void *abuf = nullptr, *qkv = nullptr, *vt = nullptr, *attn = nullptr, *ubuf = nullptr;
   float *qbuf = nullptr, *kbuf = nullptr, *pden = nullptr, *beta = nullptr;
@@ -323,7 +325,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   m.n = n; m.d = d; m.T = c.seg_len; m.M = c.n_mem; m.dk = c.d_key; m.L = c.n_layers;
   m.act_prev = h->act[par ^ 1]; m.act_cur = h->act[par]; m.abuf = h->abuf; m.act_stride = nd;
   m.mem_emb = h->w.mem_emb; m.w_mq = h->w.w_mq; m.w_mk = h->w.w_mk; m.w_mv = h->w.w_mv; m.w_beta = h->w.w_beta;
-  m.A = h->A; m.z = h->z; m.qbuf = h->qbuf; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
+  m.A = h->A; m.A2 = h->A2; m.z = h->z; m.qbuf = h->qbuf; m.kbuf = h->kbuf; m.pden = h->pden; m.beta = h->beta; m.desc = h->desc;
   m.moff = h->moff;
   m.mem_eps = c.mem_eps; m.rms_eps = c.rms_eps; m.advance = 0;
 
@@ -535,6 +537,8 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, int32_t t_last,
     return hip_fail(e, "set_desc");
   if ((e = launch_fill_f32(h->A, A0, a_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
   if ((e = launch_fill_f32(h->z, z0, z_count, h->stream)) != hipSuccess) return hip_fail(e, "state init");
+  if (h->bf16 && (e = launch_split_state(h->A, h->A2, a_count / c.d_key, h->stream)) != hipSuccess)
+    return hip_fail(e, "state init");
   int rc;
   if (sched == SCHED_DIAG) {
     for (int w = 0; w < S + L - 1; ++w) {
@@ -622,6 +626,7 @@ int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, c
   h->rope = (float*)(base + lo.rope);
   h->A = (float*)(base + lo.A);
   h->z = (float*)(base + lo.z);
+  h->A2 = (armt::bf16*)(base + lo.A2);
   h->act[0] = base + lo.act0;
   h->act[1] = base + lo.act1;
   h->abuf = base + lo.abuf;
@@ -1392,6 +1397,7 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
     return hip_fail(e, "set_desc");
   if ((e = launch_fill_f32(h->A, A0, a_count, st)) != hipSuccess) return hip_fail(e, "state init");
   if ((e = launch_fill_f32(h->z, z0, z_count, st)) != hipSuccess) return hip_fail(e, "state init");
+  if (h->bf16 && (e = launch_split_state(h->A, h->A2, a_count / 64, st)) != hipSuccess) return hip_fail(e, "state init");
   StepCtx sc{h, st, false};
   if (schedule == 0) {
     for (int w = 0; w < S + L - 1; ++w) {

@@ -62,30 +62,78 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 // columns 128 s + 32 cq .. + 31 of every chunk and keeps its 16 rows of them
 // in registers from the first load to the last store: lane (c16, g) holds row
 // c16, columns 128 s + 32 cq + 8 g .. + 7.  The operands of a chunk -- the
-// W_mq columns [64 keys x 128] bf16 for the first product, then the A rows
-// [128 x 64] fp32 for the second -- stream into LDS by global->LDS DMA in
-// whole 256-byte rows, one chunk ahead, and are shared by both row groups.
+// W_mq columns [64 keys x 128] bf16 for the first product, then 128 rows of
+// the state as bf16 hi / lo halves [128 x (64 + 64)] for the second -- stream
+// into LDS by buffer->LDS DMA in whole 256-byte rows and are shared by both
+// row groups.
 //  * u = h W_mq^T on v_mfma_f32_16x16x32_bf16 with h as a bf16 pair
 //    (hi = R(h), lo = R(h - hi)); the four column sets' partial u are added
 //    in LDS in a fixed order.
 //  * r^T = A q^T on the same instruction as three hi/lo products
-//    (A_hi q_hi + A_hi q_lo + A_lo q_hi, relative error ~2^-16).  The A rows
+//    (A_hi q_hi + A_hi q_lo + A_lo q_hi, relative error ~2^-16).  The split of
+//    the fp32 state is kept beside it (A2, written by every memory update), so
+//    it is formed once per node instead of by every workgroup.  The A rows
 //    feeding 16x16 output block sb are the columns 8(i/4) + 4 sb + i%4 of the
 //    wave's 32, so lane (c16, g) receives r for exactly the columns it holds.
 // Tile rows keep their 16-byte chunks XOR-swizzled (W_mq rows by key & 15, A
 // rows by (r & 3) | ((r >> 3) & 3) << 2) so the fragment reads are free of
 // bank conflicts.
-// ---------------------------------------------------------------------------
-template <int NBM>   // 128-column chunks this instantiation can hold (d / 128 <= NBM)
-__global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
-  constexpr int BUF = 128 * 64 * 4;           // one chunk buffer: A chunk 32 KB (W_mq chunk: 16 KB)
-  constexpr int LW = 64 * 128 * 2 / 1024 / 8;  // 1 KB DMA loads per wave per W_mq chunk (2)
-  constexpr int LA = BUF / 1024 / 8;            // ... per A chunk (4)
-  __shared__ __attribute__((aligned(1024))) unsigned char ops[2 * BUF];
-  __shared__ float ured[2][4][16][65];
-  __shared__ float qs[32][68];
-  __shared__ float dens[32];
-  __shared__ float ssq[2][4][16];
+//
+// Vector-memory operations complete in issue order, so a wait for one of
+// them is "at most n outstanding" with n the operations issued after it; the
+// kernel counts what it issues (a lower bound wherever a count could vary, so
+// a wait is never short) and waits for exactly what the next step reads.
+// Operands stay NW (phase 1) or NA (phase 2) chunks ahead of the products and
+// h HA chunks ahead; each updated h chunk is stored as soon as it is formed;
+// the gains and z reach LDS early, so the bf16 output waits for nothing but
+// its row's RMS.  With the chunk count a template constant every wait is a
+// single instruction.
+template <int I = 0>
+__device__ __forceinline__ void wait_vm_le(int n) {   // n wave-uniform
+  if constexpr (I >= 31) {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(31));
+  } else {
+    if (n <= I) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(I));
+    else wait_vm_le<I + 1>(n);
+  }
+}
+
+// Word 3 of a raw buffer resource on gfx9 parts (no format conversion).
+constexpr int kRawBuffer = 0x00020000;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte LDS reads of the chunk buffers, issued together and waited for in
+// the same block.  Written as asm because the compiler would otherwise wait
+// for every buffer->LDS load in flight before each read (it cannot tell which
+// buffer a DMA fills); the explicit vmcnt waits already cover the chunk read.
+__device__ __forceinline__ void lds_read4(unsigned a0, unsigned a1, unsigned a2, unsigned a3, bf16x8& r0, bf16x8& r1,
+                                          bf16x8& r2, bf16x8& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+}
+
+constexpr int kMrW = 16 * 1024;   // W_mq chunk: 64 keys x 128 columns bf16
+constexpr int kMrA = 32 * 1024;   // A chunk: 128 rows x 64 keys fp32
+constexpr int kMrNW = 6;          // W_mq chunk buffers (phase 1)
+constexpr int kMrNA = 3;          // A chunk buffers (phase 2), same LDS
+constexpr int kMrOps = kMrNW * kMrW;
+static_assert(kMrNA * kMrA <= kMrOps, "operand buffers");
+
+template <int NBM, bool EXACT, bool L0>   // EXACT: d == 128 NBM (every count below is a constant)
+__device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned char* ops, float (&ured)[2][4][16][65],
+                                                  float (&qs)[32][68], float (&dens)[32], float (&ssq)[2][4][16],
+                                                  float (&zs)[64], unsigned char* gsh) {
+  constexpr int LW = kMrW / 1024 / 8;   // 1 KB DMA loads per wave per W_mq chunk (2)
+  constexpr int LA = kMrA / 1024 / 8;   // ... per A chunk (4)
+  constexpr int HO = L0 ? 1 : 2;        // loads per h chunk (bf16 x / fp32 stream)
+  constexpr int SO = 2;                 // stores per h chunk
+  constexpr int HA = 6;                 // h chunks loaded ahead
 
   const int layer = a.l0 + blockIdx.y;          // (layer, sequence) problem
   const int wl = layer / a.batch;                // model layer
@@ -93,101 +141,137 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int rg = w >> 2, cq = w & 3;
-  const int d = a.d, nb = d >> 7;
+  const int d = EXACT ? 128 * NBM : a.d, nb = d >> 7;
   const int rl = 16 * rg + c16;                  // row within the workgroup's 32
   const int row = blockIdx.x * 32 + rl;
   const int rowc = row < a.n ? row : a.n - 1;
   const int colw = 32 * cq + 8 * g;              // + 128 s
+  // the wave holds at least one row of the node (its stores are issued)
+  const bool live = blockIdx.x * 32 + 16 * rg < a.n;
+
+  // z, for the denominators (one value per lane of wave 0)
+  const float zv = w == 0 ? a.z[(int64_t)layer * 64 + lane] : 0.f;
 
   // h_in rows (fp32 stream, or bf16 x / memory embeddings at layer 0; the
-  // rows after a short last segment's memory tokens are zero padding)
+  // rows after a short last segment's memory tokens are zero padding).  Every
+  // lane loads (padding lanes from a valid row), so each chunk is HO loads.
   float hv[NBM][8];
-  const int ts0 = wl == 0 ? seg_tokens(a.desc, a.desc->c, a.T) : 0;
-  // at layer 0 the problem index is the sequence index
-  const bf16* xs = (const bf16*)a.desc->x + (int64_t)layer * a.desc->seq_rows * d;
-#pragma unroll
-  for (int s = 0; s < NBM; ++s) {
-    if (s < nb) {
-      const int c = 128 * s + colw;
-      if (wl == 0) {
-        if (rowc < ts0 + a.M) {
-          const bf16* p = rowc < ts0 ? xs + ((int64_t)a.desc->c * a.T + rowc) * d
-                                     : (const bf16*)a.mem_emb + (int64_t)(rowc - ts0) * d;
-          const bf16x8 x = *(const bf16x8*)(p + c);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hv[s][e] = (float)x[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hv[s][e] = 0.f;
-        }
-      } else {
-        load8f((const float*)a.act_prev + (int64_t)(layer - a.batch) * a.act_stride + (int64_t)rowc * d + c, hv[s]);
-      }
-    }
+  bf16x8 hx[NBM];
+  const bf16* h0p = nullptr;
+  bool pad = false;
+  if constexpr (L0) {
+    const int ts0 = seg_tokens(a.desc, a.desc->c, a.T);
+    // at layer 0 the problem index is the sequence index
+    const bf16* xs = (const bf16*)a.desc->x + (int64_t)layer * a.desc->seq_rows * d;
+    pad = rowc >= ts0 + a.M;
+    h0p = rowc < ts0 ? xs + ((int64_t)a.desc->c * a.T + rowc) * d
+                     : (const bf16*)a.mem_emb + (int64_t)(pad ? 0 : rowc - ts0) * d;
   }
+  const float* hp = L0 ? nullptr
+                       : (const float*)a.act_prev + (int64_t)(layer - a.batch) * a.act_stride + (int64_t)rowc * d;
+  auto load_h = [&](int s) {
+    const int c = 128 * s + colw;
+    if constexpr (L0) hx[s] = *(const bf16x8*)(h0p + c);
+    else load8f(hp + c, hv[s]);
+  };
 
   // chunk DMA: 1 KB block q = w + 8t covers 4 rows of 256 bytes; lane L
-  // brings row 4q + L/16, physical chunk L%16
-  const bf16* wq = (const bf16*)a.w_mq + (int64_t)wl * 64 * d;
-  const float* Ast = a.A + (int64_t)layer * d * 64;
+  // brings row 4q + L/16, physical chunk L%16.  Buffer (not global) DMA: with
+  // global->LDS loads in flight the compiler waits for every outstanding
+  // operation before any use of a register load (the h rows).
+  const __amdgpu_buffer_rsrc_t wq_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)a.w_mq + (int64_t)wl * 64 * d), 0, 64 * d * 2, kRawBuffer);
+  const __amdgpu_buffer_rsrc_t a_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.A2 + (int64_t)layer * d * 128), 0, d * 128 * 2, kRawBuffer);
   auto issue_wq = [&](int s) {
-    unsigned char* buf = ops + (s & 1) * BUF;
+    unsigned char* buf = ops + (s % kMrNW) * kMrW;
 #pragma unroll
     for (int t = 0; t < LW; ++t) {
       const int q = w + 8 * t, key = 4 * q + (lane >> 4), pc = lane & 15;
-      const bf16* src = wq + (int64_t)key * d + 128 * s + 8 * (pc ^ (key & 15));
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(buf + q * 1024),
-                                       16, 0, 0);
+      const int off = 2 * (key * d + 128 * s + 8 * (pc ^ (key & 15)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wq_rs, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16,
+                                               off, 0, 0, 0);
     }
   };
   auto aswz = [](int r) { return (r & 3) | (((r >> 3) & 3) << 2); };
   auto issue_a = [&](int s) {
-    unsigned char* buf = ops + (s & 1) * BUF;
+    unsigned char* buf = ops + (s % kMrNA) * kMrA;
 #pragma unroll
     for (int t = 0; t < LA; ++t) {
       const int q = w + 8 * t, r = 4 * q + (lane >> 4), pc = lane & 15;
-      const float* src = Ast + (int64_t)(128 * s + r) * 64 + 4 * (pc ^ aswz(r));
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(buf + q * 1024),
-                                       16, 0, 0);
+      const int off = (128 * s + r) * 256 + 16 * (pc ^ aswz(r));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16,
+                                               off, 0, 0, 0);
     }
   };
+  // memory operations keep the order of these calls
+  auto fence = [] { asm volatile("" ::: "memory"); };
+  int issued = 0;        // loads and DMA issued so far by this wave
+  int stores = 0;        // h stores issued so far, counted as if the wave is live
+  int tag[NBM];          // `issued` just after chunk s's operand DMA
+  int stag[NBM];         // `stores` at that point
 
-  // ---- u = h W_mq^T: chunk s from buffer s & 1, chunk s + 1 in flight
-  issue_wq(0);
-  if (nb > 1) issue_wq(1);
+  // ---- u = h W_mq^T: chunk s from buffer s % NW.  Issue order: h 0..HA-1,
+  // W_mq 0..NW-1; after step s: h s+HA, W_mq s+NW.
+#pragma unroll
+  for (int s = 0; s < HA && s < NBM; ++s)
+    if (s < nb) { load_h(s); issued += HO; }
+  fence();
+#pragma unroll
+  for (int s = 0; s < kMrNW && s < NBM; ++s)
+    if (s < nb) { issue_wq(s); issued += LW; tag[s] = issued; fence(); }
   f32x4 u[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) u[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NBM; ++s) {
     if (s < nb) {
-      if (s + 1 < nb) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LW));
-      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+      wait_vm_le(issued - tag[s]);   // W_mq chunk s in LDS (h chunk s: its registers are waited for)
       lds_barrier();
-      const unsigned char* buf = ops + (s & 1) * BUF;
+      if constexpr (L0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[s][e] = pad ? 0.f : (float)hx[s][e];
+      }
+      const unsigned char* buf = ops + (s % kMrNW) * kMrW;
       bf16x8 hi, lo;
       split8(hv[s], hi, lo);
       const int lc = 4 * cq + g;
+      // key 16 jb + c16 of the chunk (key & 15 == c16)
+      const unsigned b0 = lds_addr(buf) + c16 * 256 + ((lc ^ c16) << 4);
+      bf16x8 bv[4];
+      lds_read4(b0, b0 + 16 * 256, b0 + 32 * 256, b0 + 48 * 256, bv[0], bv[1], bv[2], bv[3]);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
-        const int key = 16 * jb + c16;
-        const bf16x8 bv = *(const bf16x8*)(buf + key * 256 + ((lc ^ (key & 15)) << 4));
-        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, u[jb], 0, 0, 0);
-        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, u[jb], 0, 0, 0);
+        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv[jb], u[jb], 0, 0, 0);
+        u[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv[jb], u[jb], 0, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(kLgkmOnly);
       lds_barrier();
-      if (s + 2 < nb) issue_wq(s + 2);
+      if (s + HA < nb) { load_h(s + HA); issued += HO; }
+      fence();
+      if (s + kMrNW < nb) { issue_wq(s + kMrNW); issued += LW; tag[s + kMrNW] = issued; }
+      fence();
     }
   }
-  // both buffers are free: start the A chunks while q is formed
-  issue_a(0);
-  if (nb > 1) issue_a(1);
+  // every operand buffer is free: the gains (one 1 KB block per wave,
+  // clamped into the row) and the first A chunks load while q is formed
+  {
+    const __amdgpu_buffer_rsrc_t g_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)a.gain + (int64_t)wl * d), 0, 2 * d, kRawBuffer);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rs, (__attribute__((address_space(3))) void*)(gsh + 1024 * w), 16,
+                                             min(1024 * w + 16 * lane, 2 * d - 16), 0, 0, 0);
+    issued += 1;
+  }
+  fence();
+#pragma unroll
+  for (int s = 0; s < kMrNA && s < NBM; ++s)
+    if (s < nb) { issue_a(s); issued += LA; tag[s] = issued; stag[s] = stores; fence(); }
   // lane (c16, g) of block jb holds u[row 4g + i of its group][key 16 jb + c16]
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) ured[rg][cq][4 * g + i][16 * jb + c16] = u[jb][i];
+  if (w == 0) zs[lane] = zv;
   __builtin_amdgcn_s_waitcnt(kLgkmOnly);
   lds_barrier();
   for (int idx = tid; idx < 32 * 64; idx += 512) {
@@ -197,9 +281,8 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   __builtin_amdgcn_s_waitcnt(kLgkmOnly);
   lds_barrier();
   if (tid < 32) {
-    const float* z = a.z + (int64_t)layer * 64;
     float sd = 0.f;
-    for (int k = 0; k < 64; ++k) sd = fmaf(qs[tid][k], z[k], sd);
+    for (int k = 0; k < 64; ++k) sd = fmaf(qs[tid][k], zs[k], sd);
     dens[tid] = sd + a.mem_eps;
   }
   // q^T as the second operand of r^T = A q^T: lane (c16, g) brings
@@ -216,30 +299,35 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   lds_barrier();   // dens visible
   const float den = dens[rl];
 
-  // ---- h += r^T / den, chunk by chunk; partial sum of squares of the new h
+  // ---- h += r^T / den, chunk by chunk from buffer s % NA, each chunk stored
+  // once updated; partial sum of squares of the new h.  After step s: A s+NA,
+  // then the store of h chunk s (issued by live waves only).
+  float* ho = (float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)row * d;
   float ss = 0.f;
 #pragma unroll
   for (int s = 0; s < NBM; ++s) {
     if (s < nb) {
-      if (s + 1 < nb) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LA));
-      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+      // A chunk s (and the gains before it) in LDS
+      if (live) wait_vm_le(issued - tag[s] + stores - stag[s]);
+      else wait_vm_le(issued - tag[s]);
       lds_barrier();
-      const unsigned char* buf = ops + (s & 1) * BUF;
+      const unsigned char* buf = ops + (s % kMrNA) * kMrA;
+      // A rows ar(sb) = 32 cq + 8 (c16 / 4) + 4 sb + c16 % 4 (aswz(ar) does
+      // not depend on sb); keys 32 ks + 8 g .. + 7 are 16-byte chunk 4 ks + g
+      // of the row's hi half and 8 + 4 ks + g of its lo half
+      const int ar0 = 32 * cq + 8 * (c16 >> 2) + (c16 & 3), sw = aswz(ar0);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int ar = 32 * cq + 8 * (c16 >> 2) + 4 * sb + (c16 & 3);   // A row within the chunk
+        bf16x8 ah[2], al[2];
+        const unsigned rb = lds_addr(buf) + (ar0 + 4 * sb) * 256;
+        lds_read4(rb + ((g ^ sw) << 4), rb + (((8 + g) ^ sw) << 4), rb + (((4 + g) ^ sw) << 4),
+                  rb + (((12 + g) ^ sw) << 4), ah[0], al[0], ah[1], al[1]);
         f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int lc = 8 * ks + 2 * g;
-          const f32x4 a0 = *(const f32x4*)(buf + ar * 256 + ((lc ^ aswz(ar)) << 4));
-          const f32x4 a1 = *(const f32x4*)(buf + ar * 256 + (((lc + 1) ^ aswz(ar)) << 4));
-          const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          bf16x8 ah, al;
-          split8(av, ah, al);
-          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh[ks], r, 0, 0, 0);
-          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql[ks], r, 0, 0, 0);
-          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh[ks], r, 0, 0, 0);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], qh[ks], r, 0, 0, 0);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], ql[ks], r, 0, 0, 0);
+          r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], qh[ks], r, 0, 0, 0);
         }
         // lane (c16, g) holds r^T[block row 4g + i][row c16] = column 8g + 4sb + i
 #pragma unroll
@@ -251,7 +339,16 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(kLgkmOnly);
       lds_barrier();
-      if (s + 2 < nb) issue_a(s + 2);
+      if (s + kMrNA < nb) { issue_a(s + kMrNA); issued += LA; tag[s + kMrNA] = issued; stag[s + kMrNA] = stores; }
+      fence();
+      if (row < a.n) {
+        const int c = 128 * s + colw;
+        const float* v = hv[s];
+        *(f32x4*)(ho + c) = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4*)(ho + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
+      stores += SO;
+      fence();
     }
   }
   ss += __shfl_xor(ss, 16, kWave);
@@ -262,17 +359,13 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
   const float rs = rsqrtf((((ssq[rg][0][c16] + ssq[rg][1][c16]) + ssq[rg][2][c16]) + ssq[rg][3][c16]) / (float)d +
                           a.rms_eps);
   if (row < a.n) {
-    float* ho = (float*)a.act_cur + (int64_t)layer * a.act_stride + (int64_t)row * d;
     bf16* ao = (bf16*)a.abuf + (int64_t)layer * a.act_stride + (int64_t)row * d;
-    const bf16* gn = (const bf16*)a.gain + (int64_t)wl * d;
 #pragma unroll
     for (int s = 0; s < NBM; ++s) {
       if (s < nb) {
         const int c = 128 * s + colw;
         const float* v = hv[s];
-        *(f32x4*)(ho + c) = f32x4{v[0], v[1], v[2], v[3]};
-        *(f32x4*)(ho + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
-        const bf16x8 gv = *(const bf16x8*)(gn + c);
+        const bf16x8 gv = *(const bf16x8*)(gsh + 2 * c);
         bf16x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * rs * (float)gv[e]);
@@ -280,6 +373,19 @@ __global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
       }
     }
   }
+}
+
+template <int NBM, bool EXACT>   // 128-column chunks: d / 128 <= NBM (EXACT: ==)
+__global__ __launch_bounds__(512) void memread_norm_bf16_kernel(MemArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ops[kMrOps];
+  __shared__ __attribute__((aligned(1024))) unsigned char gsh[8 * 1024];
+  __shared__ float ured[2][4][16][65];
+  __shared__ float qs[32][68];
+  __shared__ float dens[32];
+  __shared__ float ssq[2][4][16];
+  __shared__ float zs[64];
+  if ((a.l0 + (int)blockIdx.y) / a.batch == 0) memread_norm_body<NBM, EXACT, true>(a, ops, ured, qs, dens, ssq, zs, gsh);
+  else memread_norm_body<NBM, EXACT, false>(a, ops, ured, qs, dens, ssq, zs, gsh);
 }
 
 // ---------------------------------------------------------------------------
@@ -396,8 +502,9 @@ __global__ __launch_bounds__(256) void memkeys_bf16_kernel(MemArgs a) {
 // Y_m . W_mv[i] on MFMA (wave w: rows i0 + 16w .. +15), then with the A tile
 // staged in LDS: vbar_m[i] = (k_m . A[i]) / (sum of partial denominators +
 // eps), delta_m[i] = beta_m (v_m[i] - vbar_m[i]), A[i][j] += sum_m delta_m[i]
-// k_mj.  W_mv is read exactly once per node.  Optionally advances the wave
-// counter (no kernel of this launch reads it).
+// k_mj, also stored as its bf16 hi / lo split for the next memory read.  W_mv
+// is read exactly once per node.  Optionally advances the wave counter (no
+// kernel of this launch reads it).
 // ---------------------------------------------------------------------------
 template <int MBK>   // 16-row blocks of memory tokens: M <= 16 * MBK
 __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
@@ -516,7 +623,12 @@ __global__ __launch_bounds__(256) void memupdate_bf16_kernel(MemArgs a) {
     const int ii = idx >> 6, j = idx & 63;
     float s = 0.f;
     for (int m = 0; m < M; ++m) s = fmaf(delta[m][ii], ks[m][j], s);
-    A[(int64_t)(i0 + ii) * 64 + j] = At[ii][j] + s;
+    const float v = At[ii][j] + s;
+    A[(int64_t)(i0 + ii) * 64 + j] = v;
+    const bf16 hi = (bf16)v;
+    bf16* a2 = a.A2 + ((int64_t)layer * d + i0 + ii) * 128 + j;
+    a2[0] = hi;
+    a2[64] = (bf16)(v - (float)hi);
   }
   if (a.advance != 0 && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.desc->c += a.advance;
 }
@@ -527,10 +639,38 @@ hipError_t launch_mem_read_bf16(const MemArgs& m, hipStream_t st) {
   if (m.dk != 64 || m.d % 128 || m.d > 3072) return hipErrorInvalidValue;
   const dim3 grid((m.n + 31) / 32, m.P);
   const int nb = m.d / 128;
-  if (nb <= 4) hipLaunchKernelGGL(memread_norm_bf16_kernel<4>, grid, dim3(512), 0, st, m);
-  else if (nb <= 8) hipLaunchKernelGGL(memread_norm_bf16_kernel<8>, grid, dim3(512), 0, st, m);
-  else if (nb <= 16) hipLaunchKernelGGL(memread_norm_bf16_kernel<16>, grid, dim3(512), 0, st, m);
-  else hipLaunchKernelGGL(memread_norm_bf16_kernel<24>, grid, dim3(512), 0, st, m);
+  switch (nb) {   // the common widths with constant wait counts, others counted at run time
+    case 1: hipLaunchKernelGGL((memread_norm_bf16_kernel<1, true>), grid, dim3(512), 0, st, m); break;
+    case 2: hipLaunchKernelGGL((memread_norm_bf16_kernel<2, true>), grid, dim3(512), 0, st, m); break;
+    case 4: hipLaunchKernelGGL((memread_norm_bf16_kernel<4, true>), grid, dim3(512), 0, st, m); break;
+    case 6: hipLaunchKernelGGL((memread_norm_bf16_kernel<6, true>), grid, dim3(512), 0, st, m); break;
+    case 8: hipLaunchKernelGGL((memread_norm_bf16_kernel<8, true>), grid, dim3(512), 0, st, m); break;
+    case 16: hipLaunchKernelGGL((memread_norm_bf16_kernel<16, true>), grid, dim3(512), 0, st, m); break;
+    case 24: hipLaunchKernelGGL((memread_norm_bf16_kernel<24, true>), grid, dim3(512), 0, st, m); break;
+    default:
+      if (nb <= 8) hipLaunchKernelGGL((memread_norm_bf16_kernel<8, false>), grid, dim3(512), 0, st, m);
+      else if (nb <= 16) hipLaunchKernelGGL((memread_norm_bf16_kernel<16, false>), grid, dim3(512), 0, st, m);
+      else hipLaunchKernelGGL((memread_norm_bf16_kernel<24, false>), grid, dim3(512), 0, st, m);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void split_state_kernel(const float* A, bf16* A2, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const float v = A[i];
+  const bf16 hi = (bf16)v;
+  bf16* o = A2 + (i >> 6) * 128 + (i & 63);
+  o[0] = hi;
+  o[64] = (bf16)(v - (float)hi);
+}
+}  // namespace
+
+hipError_t launch_split_state(const float* A, bf16* A2, int64_t rows, hipStream_t st) {
+  const int64_t count = rows * 64;
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(split_state_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, A, A2, count);
   return hipGetLastError();
 }
 
