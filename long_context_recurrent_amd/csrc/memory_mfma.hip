@@ -55,8 +55,8 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 
 // ---------------------------------------------------------------------------
 // Memory read fused with the attention RMSNorm, for 32 rows of one node:
-//   q  = phi(h_in W_mq^T),  h = h_in + (q A^T) / (q . z + eps)   (fp32 stream)
-//   a  = R(rms(h) * g_attn)                                       (bf16)
+//   q  = phi(h_in W_mq^T),  h = h_in + (q A^T) * (1 / (q . z + eps))   (fp32 stream)
+//   a  = R(rms(h) * g_attn)                                             (bf16)
 // Workgroup = 8 waves: row group rg = w / 4 (16 rows) x column set cq = w % 4.
 // Columns come in 128-wide chunks s = 0 .. d/128 - 1; wave (rg, cq) owns
 // columns 128 s + 32 cq .. + 31 of every chunk and keeps its 16 rows of them
@@ -297,7 +297,7 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
   }
   __builtin_amdgcn_s_waitcnt(kLgkmOnly);
   lds_barrier();   // dens visible
-  const float den = dens[rl];
+  const float rden = 1.f / dens[rl];   // one division per row
 
   // ---- h += r^T / den, chunk by chunk from buffer s % NA, each chunk stored
   // once updated; partial sum of squares of the new h.  After step s: A s+NA,
@@ -332,7 +332,7 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
         // lane (c16, g) holds r^T[block row 4g + i][row c16] = column 8g + 4sb + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float hn = hv[s][4 * sb + i] + r[i] / den;
+          const float hn = fmaf(r[i], rden, hv[s][4 * sb + i]);
           hv[s][4 * sb + i] = hn;
           ss = fmaf(hn, hn, ss);
         }
