@@ -194,8 +194,28 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
     }
   };
   auto aswz = [](int r) { return (r & 3) | (((r >> 3) & 3) << 2); };
+  // A buffer j overlays W_mq buffers 2j, 2j+1 and is free once the last W_mq
+  // chunk held there has been multiplied (after phase-1 step fr[j]; -1: never
+  // used).  Update-phase chunk s goes to A buffer abuf[s % NA], the first
+  // chunks to the buffers freed first, so they load during phase 1.
+  auto last_w = [&](int b) { return b < nb ? b + kMrNW * ((nb - 1 - b) / kMrNW) : -1; };
+  int fr[kMrNA], abuf[kMrNA];
+#pragma unroll
+  for (int j = 0; j < kMrNA; ++j) {
+    fr[j] = max(last_w(2 * j), last_w(2 * j + 1));
+    abuf[j] = j;
+  }
+#pragma unroll
+  for (int i = 0; i < kMrNA; ++i)
+#pragma unroll
+    for (int j = 0; j + 1 < kMrNA; ++j)
+      if (fr[abuf[j]] > fr[abuf[j + 1]]) {
+        const int t = abuf[j];
+        abuf[j] = abuf[j + 1];
+        abuf[j + 1] = t;
+      }
   auto issue_a = [&](int s) {
-    unsigned char* buf = ops + (s % kMrNA) * kMrA;
+    unsigned char* buf = ops + abuf[s % kMrNA] * kMrA;
 #pragma unroll
     for (int t = 0; t < LA; ++t) {
       const int q = w + 8 * t, r = 4 * q + (lane >> 4), pc = lane & 15;
@@ -208,8 +228,25 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
   auto fence = [] { asm volatile("" ::: "memory"); };
   int issued = 0;        // loads and DMA issued so far by this wave
   int stores = 0;        // h stores issued so far, counted as if the wave is live
-  int tag[NBM];          // `issued` just after chunk s's operand DMA
-  int stag[NBM];         // `stores` at that point
+  int tag[NBM];          // `issued` just after W_mq chunk s's DMA
+  int atag[NBM];         // `issued` just after A chunk s's DMA
+  int astag[NBM];        // `stores` at that point
+  auto issue_a_tagged = [&](int s) {
+    issue_a(s);
+    issued += LA;
+    atag[s] = issued;
+    astag[s] = stores;
+  };
+
+  // the gains (one 1 KB block per wave, clamped into the row), needed last
+  {
+    const __amdgpu_buffer_rsrc_t g_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)a.gain + (int64_t)wl * d), 0, 2 * d, kRawBuffer);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rs, (__attribute__((address_space(3))) void*)(gsh + 1024 * w), 16,
+                                             min(1024 * w + 16 * lane, 2 * d - 16), 0, 0, 0);
+    issued += 1;
+  }
+  fence();
 
   // ---- u = h W_mq^T: chunk s from buffer s % NW.  Issue order: h 0..HA-1,
   // W_mq 0..NW-1; after step s: h s+HA, W_mq s+NW.
@@ -220,6 +257,10 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
 #pragma unroll
   for (int s = 0; s < kMrNW && s < NBM; ++s)
     if (s < nb) { issue_wq(s); issued += LW; tag[s] = issued; fence(); }
+  // A chunks whose buffer phase 1 never uses (all but the last of the first NA)
+#pragma unroll
+  for (int j = 0; j + 1 < kMrNA && j < NBM; ++j)
+    if (j < nb && fr[abuf[j]] < 0) { issue_a_tagged(j); fence(); }
   f32x4 u[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) u[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -251,21 +292,12 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
       fence();
       if (s + kMrNW < nb) { issue_wq(s + kMrNW); issued += LW; tag[s + kMrNW] = issued; }
       fence();
+      // A chunks whose buffer this step freed
+#pragma unroll
+      for (int j = 0; j + 1 < kMrNA && j < NBM; ++j)
+        if (j < nb && fr[abuf[j]] == s) { issue_a_tagged(j); fence(); }
     }
   }
-  // every operand buffer is free: the gains (one 1 KB block per wave,
-  // clamped into the row) and the first A chunks load while q is formed
-  {
-    const __amdgpu_buffer_rsrc_t g_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)a.gain + (int64_t)wl * d), 0, 2 * d, kRawBuffer);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rs, (__attribute__((address_space(3))) void*)(gsh + 1024 * w), 16,
-                                             min(1024 * w + 16 * lane, 2 * d - 16), 0, 0, 0);
-    issued += 1;
-  }
-  fence();
-#pragma unroll
-  for (int s = 0; s < kMrNA && s < NBM; ++s)
-    if (s < nb) { issue_a(s); issued += LA; tag[s] = issued; stag[s] = stores; fence(); }
   // lane (c16, g) of block jb holds u[row 4g + i of its group][key 16 jb + c16]
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
@@ -298,6 +330,12 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
   __builtin_amdgcn_s_waitcnt(kLgkmOnly);
   lds_barrier();   // dens visible
   const float rden = 1.f / dens[rl];   // one division per row
+  // the last of the first NA A chunks goes in after the LDS traffic above, so
+  // that traffic does not wait for it (the compiler orders every LDS access
+  // after all buffer->LDS loads in flight)
+  fence();
+  if (kMrNA - 1 < nb) issue_a_tagged(kMrNA - 1);
+  fence();
 
   // ---- h += r^T / den, chunk by chunk from buffer s % NA, each chunk stored
   // once updated; partial sum of squares of the new h.  After step s: A s+NA,
@@ -308,10 +346,10 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
   for (int s = 0; s < NBM; ++s) {
     if (s < nb) {
       // A chunk s (and the gains before it) in LDS
-      if (live) wait_vm_le(issued - tag[s] + stores - stag[s]);
-      else wait_vm_le(issued - tag[s]);
+      if (live) wait_vm_le(issued - atag[s] + stores - astag[s]);
+      else wait_vm_le(issued - atag[s]);
       lds_barrier();
-      const unsigned char* buf = ops + (s % kMrNA) * kMrA;
+      const unsigned char* buf = ops + abuf[s % kMrNA] * kMrA;
       // A rows ar(sb) = 32 cq + 8 (c16 / 4) + 4 sb + c16 % 4 (aswz(ar) does
       // not depend on sb); keys 32 ks + 8 g .. + 7 are 16-byte chunk 4 ks + g
       // of the row's hi half and 8 + 4 ks + g of its lo half
@@ -339,7 +377,7 @@ __device__ __forceinline__ void memread_norm_body(const MemArgs& a, unsigned cha
       }
       __builtin_amdgcn_s_waitcnt(kLgkmOnly);
       lds_barrier();
-      if (s + kMrNA < nb) { issue_a(s + kMrNA); issued += LA; tag[s + kMrNA] = issued; stag[s + kMrNA] = stores; }
+      if (s + kMrNA < nb) issue_a_tagged(s + kMrNA);
       fence();
       if (row < a.n) {
         const int c = 128 * s + colw;
