@@ -1,7 +1,9 @@
 """GPU parity at the edges of what the library accepts: the smallest node
 (one token, one memory token), the most memory tokens (64), the longest bf16
 node (T + M = 4096), the narrowest bf16 model (d = 128, 4:1 grouped-query
-heads of 32), and the largest fp32 node and width (T + M = 2048, d = 1024).
+heads of 32), the largest fp32 node and width (T + M = 2048, d = 1024), and
+bf16 widths whose column-chunk counts (3, 9, 23) the memory read handles with
+wait counts computed at run time.
 Each against the oracle (relative L2 1e-4 fp32, 2e-2 bf16, from a given
 non-zero state so the memory read is exercised), diagonal == sequential
 bitwise.
@@ -34,6 +36,14 @@ EDGES = [
                 seg_len=100, n_mem=3, n_segments=4),
     TINY.with_(name="f32_n2048_d1024", n_layers=1, d_model=1024, n_heads=8, n_kv_heads=4, head_dim=128,
                ffn_hidden=1024, seg_len=2000, n_mem=48, n_segments=2),
+    # bf16 widths outside the memory read's fixed-count instantiations (3, 9
+    # and 23 column chunks of 128: wait counts taken at run time)
+    SMALL.with_(name="d384_chunks3", n_layers=2, d_model=384, n_heads=6, n_kv_heads=2, head_dim=64, ffn_hidden=768,
+                seg_len=100, n_mem=8, n_segments=3),
+    SMALL.with_(name="d1152_chunks9", n_layers=2, d_model=1152, n_heads=18, n_kv_heads=6, head_dim=64,
+                ffn_hidden=1024, seg_len=64, n_mem=16, n_segments=3),
+    SMALL.with_(name="d2944_chunks23", n_layers=2, d_model=2944, n_heads=46, n_kv_heads=2, head_dim=64,
+                ffn_hidden=512, seg_len=32, n_mem=8, n_segments=2),
 ]
 
 
