@@ -375,33 +375,66 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       // two, a multiple of 16), so they share the partner offset and read 8
       // consecutive (cos, sin) pairs of the row's table.
       const int hd = g.head_dim, half = hd >> 1;
-      for (int pc = tid; pc < rows_here * PIECES_ROW; pc += 256) {
-        const int r = pc / PIECES_ROW, c8 = (pc % PIECES_ROW) * 8;
-        const int m = m0 + rc0 + r, n = n0 + c8;
-        if (m >= g.M || n >= g.v_col0) continue;
-        const float* src = Cs + r * EP_PITCH + c8;
-        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
-        bf16x8 o;
-        if (n < g.rope_cols) {
-          const int hb = n & (hd - 1);
-          const bool first = hb < half;
-          const int fi = first ? hb : hb - half;
-          const float* pp = src + (first ? half : -half);
-          const f32x4 p0 = *(const f32x4*)pp, p1 = *(const f32x4*)(pp + 4);
-          const f32x4* cs = (const f32x4*)(g.rope_cs + ((int64_t)m * half + fi) * 2);
-          const f32x4 t0 = cs[0], t1 = cs[1], t2 = cs[2], t3 = cs[3];   // (cos, sin) x 8
-          const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-          const float cv[8] = {t0[0], t0[2], t1[0], t1[2], t2[0], t2[2], t3[0], t3[2]};
-          const float sv[8] = {t0[1], t0[3], t1[1], t1[3], t2[1], t2[3], t3[1], t3[3]};
+      // Work unit = (row, head, 8-wide frequency chunk): the chunk's columns
+      // in both halves of the head, i and i + hd/2, rotated by the same 8
+      // (cos, sin) pairs.  A row has 256 / 16 = 16 units; thread t takes row
+      // t / 4 and units t % 4 + 4k, which share their frequency chunk (all of
+      // them when hd = 64 or 32, two chunks when hd = 128), so the table
+      // loads of a row are issued once and together.
+      static_assert(EPI != EPI_QKV || EP_RC % 64 == 0, "four threads per staged row");
+      const int nfc = half >> 3;                      // frequency chunks per head
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            o[e] = (bf16)(first ? xv[e] * cv[e] - pv[e] * sv[e] : xv[e] * cv[e] + pv[e] * sv[e]);
-        } else {
-          o = bf16x8{(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
-                     (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+      for (int rp = 0; rp < EP_RC / 64; ++rp) {
+        const int r = (tid >> 2) + 64 * rp;
+        const int m = m0 + rc0 + r;
+        if (r >= rows_here || m >= g.M) continue;
+        const float* srow = Cs + r * EP_PITCH;
+        bf16* crow = C + (int64_t)m * g.ldc;
+        f32x4 tcs[2][4];   // (cos, sin) x 8 for up to two frequency chunks
+        int tfc[2] = {-1, -1};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int u = (tid & 3) + 4 * k;
+          const int fc = u % nfc;
+          const int slot = (k == 0 || fc == tfc[0]) ? 0 : 1;
+          if (tfc[slot] != fc) {
+            tfc[slot] = fc;
+            const f32x4* cs = (const f32x4*)(g.rope_cs + ((int64_t)m * half + 8 * fc) * 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tcs[slot][q] = cs[q];
+          }
         }
-        *(bf16x8*)(C + (int64_t)m * g.ldc + n) = o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int u = (tid & 3) + 4 * k;
+          const int head = u / nfc, fc = u % nfc;
+          const int c1 = head * hd + 8 * fc, c2 = c1 + half;   // tile columns of the two pieces
+          const int n1 = n0 + c1, n2 = n0 + c2;
+          if (n1 >= g.v_col0) continue;                       // V heads: transposed below
+          const f32x4 a0 = *(const f32x4*)(srow + c1), a1 = *(const f32x4*)(srow + c1 + 4);
+          const f32x4 b0 = *(const f32x4*)(srow + c2), b1 = *(const f32x4*)(srow + c2 + 4);
+          const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          bf16x8 o1, o2;
+          if (n1 < g.rope_cols) {
+            const f32x4* t = tcs[fc == tfc[0] ? 0 : 1];
+            const float cv[8] = {t[0][0], t[0][2], t[1][0], t[1][2], t[2][0], t[2][2], t[3][0], t[3][2]};
+            const float sv[8] = {t[0][1], t[0][3], t[1][1], t[1][3], t[2][1], t[2][3], t[3][1], t[3][3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              o1[e] = (bf16)(av[e] * cv[e] - bv[e] * sv[e]);   // first half: x cos - partner sin
+              o2[e] = (bf16)(bv[e] * cv[e] + av[e] * sv[e]);   // second half: x cos + partner sin
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              o1[e] = (bf16)av[e];
+              o2[e] = (bf16)bv[e];
+            }
+          }
+          if (n1 < g.N) *(bf16x8*)(crow + n1) = o1;
+          if (n2 < g.N) *(bf16x8*)(crow + n2) = o2;
+        }
       }
       // V columns, transposed: one aligned group of 16 keys of one column per
       // item.  Within the group the stored order is 0-3, 8-11, 4-7, 12-15 (the
