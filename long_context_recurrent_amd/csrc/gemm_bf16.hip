@@ -80,6 +80,12 @@ constexpr int n_stages() {
 // reads are conflict-free whether the LDS serves 128 or 256 bytes per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// Word 3 of a raw buffer resource on gfx9 parts (no format conversion), and a
+// store offset past any bound used here (the store is dropped).
+constexpr int kRawBuffer = 0x00020000;
+constexpr int kDropOffset = 0x7fffff00;
+
 // s_waitcnt immediate (gfx9 layout): vmcnt <= n, lgkmcnt = 0, expcnt free.
 __host__ __device__ constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
@@ -287,16 +293,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       Y = (bf16*)g.desc->y + ((int64_t)seq * g.desc->seq_rows + (int64_t)(g.desc->c - layer) * g.T) * g.ldc;
       y_rows = seg_tokens(g.desc, g.desc->c - layer, g.T);
     }
+    // Stores go through buffer resources bounded to the tile's rows (and to
+    // y's rows), every lane issuing each one: a piece outside the node or the
+    // tile gets an offset past the bound and the hardware drops it.  Stores
+    // in conditional blocks would again leave the compiler unsure what is in
+    // flight (and it would wait for everything before the next piece).
+    const int c_rows = max(0, min(BM, g.M - m0));
+    const __amdgpu_buffer_rsrc_t c_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Cf + (int64_t)m0 * g.ldc), 0, c_rows * g.ldc * 4, kRawBuffer);
+    const int y_tile_rows = Y != nullptr ? max(0, min(BM, y_rows - m0)) : 0;
+    const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
+        Y != nullptr ? (void*)(Y + (int64_t)m0 * g.ldc) : (void*)Cf, 0, y_tile_rows * g.ldc * 2, kRawBuffer);
     f32x4 rb[2][PPT][2];
+    // Every lane loads (a piece past the tile or the node reads a row that
+    // exists and drops the value): loads in conditional blocks would leave
+    // the compiler unsure which are in flight, and it would then wait for
+    // all of them before every store, prefetched rows included.
     auto load_pass = [&](int rc0, f32x4 (&dstv)[PPT][2]) {
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
-        const int m = m0 + rc0 + r, n = n0 + c8;
-        if (r < BM - rc0 && m < g.M && n < g.N) {
-          dstv[k][0] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n);
-          dstv[k][1] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n + 4);
-        }
+        int m = m0 + rc0 + r, n = n0 + c8;
+        m = m < g.M ? m : g.M - 1;
+        n = n < g.N ? n : g.N - 8;
+        dstv[k][0] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n);
+        dstv[k][1] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n + 4);
       }
     };
     load_pass(0, rb[0]);
@@ -320,20 +341,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       for (int k = 0; k < PPT; ++k) {
         const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
         const int m = m0 + rc0 + r, n = n0 + c8;
-        if (r < BM - rc0 && m < g.M && n < g.N) {
-          const float* sv = Cs + r * CPITCH + c8;
-          const f32x4 x0 = rb[p & 1][k][0], x1 = rb[p & 1][k][1];
-          const f32x4 o0 = f32x4{x0[0] + sv[0], x0[1] + sv[1], x0[2] + sv[2], x0[3] + sv[3]};
-          const f32x4 o1 = f32x4{x1[0] + sv[4], x1[1] + sv[5], x1[2] + sv[6], x1[3] + sv[7]};
-          float* dstp = Cf + (int64_t)m * g.ldc + n;
-          *(f32x4*)dstp = o0;
-          *(f32x4*)(dstp + 4) = o1;
-          if (m < y_rows) {
-            const bf16x8 o = {(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3],
-                              (bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
-            *(bf16x8*)(Y + (int64_t)m * g.ldc + n) = o;
-          }
-        }
+        const bool ok = r < BM - rc0 && m < g.M && n < g.N;
+        const float* sv = Cs + r * CPITCH + c8;
+        const f32x4 x0 = rb[p & 1][k][0], x1 = rb[p & 1][k][1];
+        const f32x4 o0 = f32x4{x0[0] + sv[0], x0[1] + sv[1], x0[2] + sv[2], x0[3] + sv[3]};
+        const f32x4 o1 = f32x4{x1[0] + sv[4], x1[1] + sv[5], x1[2] + sv[6], x1[3] + sv[7]};
+        const bf16x8 o = {(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3],
+                          (bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
+        const int eo = (m - m0) * g.ldc + n;   // element offset from the tile's first row
+        const int cf_off = ok ? 4 * eo : kDropOffset;
+        const int y_off = ok && m < y_rows ? 2 * eo : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), c_rs, cf_off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), c_rs, cf_off + 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), y_rs, y_off, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
       lds_barrier();
