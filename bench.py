@@ -309,9 +309,10 @@ def oracle_threads():
 
 
 def cpu_baseline(inp, seconds):
-    """The oracle as it stands, on this host: nodes of segment 0, layer by
-    layer, until about `seconds` of CPU work; tokens/s = T / (L * mean node
-    time), i.e. one segment through every layer."""
+    """The oracle as it stands, on this host: nodes in sequential order
+    (segment 0 through every layer, then segment 1, ...), each layer carrying
+    its own memory state, until about `seconds` of CPU work; tokens/s =
+    T / (L * mean node time), i.e. one segment through every layer."""
     import numpy as np
     import oracle
     try:
@@ -321,21 +322,25 @@ def cpu_baseline(inp, seconds):
         cores = os.cpu_count()
     cfg = inp.cfg
     o = oracle.Oracle(inp)
-    A = np.zeros((cfg.d_model, cfg.d_key))
-    z = np.zeros(cfg.d_key)
-    h = o.node_input(0)
+    A = [np.zeros((cfg.d_model, cfg.d_key)) for _ in range(cfg.n_layers)]
+    z = [np.zeros(cfg.d_key) for _ in range(cfg.n_layers)]
     done, a = 0, time.perf_counter()
-    while done < cfg.n_layers:
-        h, _, _ = o.node(done, h, A, z)
-        done += 1
+    for s in range(cfg.n_segments):
+        h = o.node_input(s)
+        for l in range(cfg.n_layers):
+            h, A[l], z[l] = o.node(l, h, A[l], z[l])
+            done += 1
+            if time.perf_counter() - a > seconds:
+                break
         if time.perf_counter() - a > seconds:
             break
+    segs = (done + cfg.n_layers - 1) // cfg.n_layers
     el = time.perf_counter() - a
     per_node = el / done
     value = cfg.seg_len / (per_node * cfg.n_layers)
     log(f"cpu oracle: {done} nodes in {el:.1f}s -> {value:.1f} tokens/s")
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": host_cpu(),
-            "sample": f"{done} node(s) of segment 0 (layers 0..{done - 1}, {cfg.seg_len + cfg.n_mem} rows each, "
+            "sample": f"{done} node(s) of segments 0..{segs - 1} in sequential order ({cfg.seg_len + cfg.n_mem} rows each, "
                       f"float64 NumPy, BLAS threads = {cores}) in {el:.1f}s; "
                       f"tokens/s = T / (L * mean node time)"}
 
