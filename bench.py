@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--gemm-rows", type=int, default=0,
-                    help="rows per GEMM tile / 32 (0: the library's choice)")
+                    help="rows per GEMM tile / 16 (0: the library's choice)")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the diagonal forward (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -276,8 +276,8 @@ int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t *l_lo,
  * ARMT_OPT_TIME_KERNEL: k >= 0 brackets every launch of kernel k (an
  * armt_kernel_id) with HIP events on the handle's stream (forces direct
  * launches); -1 turns it off.  ARMT_OPT_GEMM_ROWS: rows per grouped-GEMM
- * tile as a multiple of 32 (2 .. 7; 0 = pick for the workload); results do
- * not depend on it.  Changing it drops the captured graphs. */
+ * tile as a multiple of 16 (4, 6, 8 .. 14; 0 = pick for the workload);
+ * results do not depend on it.  Changing it drops the captured graphs. */
 enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1, ARMT_OPT_GEMM_ROWS = 2 };
 int armt_set_option(armt_handle *h, int32_t option, int32_t value);
 

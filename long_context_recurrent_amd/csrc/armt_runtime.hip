@@ -244,10 +244,10 @@ void node_cost(const armt_handle* h, int k, double* flops, double* bytes) {
   *bytes = b;
 }
 
-int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus);
+int pick_row_blocks(int n, int n_cols, int cols_per_tile, int K, int P, int cus);
 
-int gemm_rows(const armt_handle* h, int n_cols, int cols_per_tile, int P) {
-  return h->mb ? h->mb : pick_row_blocks(h->n, n_cols, cols_per_tile, P * h->batch, h->cus);
+int gemm_rows(const armt_handle* h, int n_cols, int cols_per_tile, int K, int P) {
+  return h->mb ? h->mb : pick_row_blocks(h->n, n_cols, cols_per_tile, K, P * h->batch, h->cus);
 }
 
 struct StepCtx {
@@ -347,7 +347,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 2. QKV projection with RoPE
   {
-    GemmCall gc{h, g0, EPI_QKV, gemm_rows(h, h->qkv_dim, 256, P)};
+    GemmCall gc{h, g0, EPI_QKV, gemm_rows(h, h->qkv_dim, 256, d, P)};
     GemmArgs& g = gc.g;
     g.A = h->abuf; g.a_stride = nd; g.lda = d;
     g.B = h->w.w_qkv; g.b_stride = (int64_t)h->qkv_dim * d; g.N = h->qkv_dim; g.K = d;
@@ -370,7 +370,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 4. output projection + residual
   {
-    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, P)};
+    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, hhd, P)};
     GemmArgs& g = gc.g;
     g.A = h->attn; g.a_stride = (int64_t)n * hhd; g.lda = hhd;
     g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
@@ -385,7 +385,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 6. gate/up + SiLU product
   {
-    GemmCall gc{h, g0, EPI_SWIGLU, gemm_rows(h, F, 128, P)};
+    GemmCall gc{h, g0, EPI_SWIGLU, gemm_rows(h, F, 128, d, P)};
     GemmArgs& g = gc.g;
     g.A = h->abuf; g.a_stride = nd; g.lda = d;
     g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
@@ -394,7 +394,7 @@ hipError_t enqueue_step(StepCtx& cx, int l_lo, int l_hi, int par, int advance) {
   }
   // 7. down projection + residual (+ y rows of the last layer)
   {
-    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, P)};
+    GemmCall gc{h, g0, EPI_RESID, gemm_rows(h, d, 256, F, P)};
     GemmArgs& g = gc.g;
     g.A = h->ubuf; g.a_stride = (int64_t)n * F; g.lda = F;
     g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
@@ -426,8 +426,8 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
   // the descriptor points the last layer's down projection at y (segment 0)
   if ((e = launch_set_desc(h->desc, x, y, L - 1, 1, N, N, cx.st)) != hipSuccess) return e;
   if ((e = launch_widen(x, (float*)h->act[0], (int64_t)N * d, h->bf16, cx.st)) != hipSuccess) return e;
-  auto rows = [&](int n_cols, int cols_per_tile) {
-    return h->mb ? h->mb : pick_row_blocks(N, n_cols, cols_per_tile, 1, h->cus);
+  auto rows = [&](int n_cols, int cols_per_tile, int K) {
+    return h->mb ? h->mb : pick_row_blocks(N, n_cols, cols_per_tile, K, 1, h->cus);
   };
   for (int l = 0; l < L; ++l) {
     MemArgs m{};
@@ -446,7 +446,7 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
       g.C = h->qkv; g.c_stride = 0; g.ldc = h->qkv_dim;
       g.rope_cs = h->rope; g.rope_cols = (c.n_heads + c.n_kv_heads) * c.head_dim;
       g.v_col0 = g.rope_cols; g.vt = h->vt; g.vt_ld = h->n_pad; g.vt_stride = 0;
-      e = h->bf16 ? launch_gemm_bf16(g, EPI_QKV, rows(h->qkv_dim, 256), cx.st) : launch_gemm_f32(g, EPI_QKV, cx.st);
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_QKV, rows(h->qkv_dim, 256, d), cx.st) : launch_gemm_f32(g, EPI_QKV, cx.st);
       if (e != hipSuccess) return e;
     }
     {
@@ -463,7 +463,7 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
       g.A = h->attn; g.a_stride = 0; g.lda = hhd;
       g.B = h->w.w_o; g.b_stride = (int64_t)d * hhd; g.N = d; g.K = hhd;
       g.C = h->act[0]; g.c_stride = 0; g.ldc = d; g.desc = nullptr;
-      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256, hhd), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
       if (e != hipSuccess) return e;
     }
     // MLP block
@@ -474,7 +474,7 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
       g.A = h->abuf; g.a_stride = 0; g.lda = d;
       g.B = h->w.w_gate; g.B2 = h->w.w_up; g.b_stride = (int64_t)F * d; g.N = F; g.K = d;
       g.C = h->ubuf; g.c_stride = 0; g.ldc = F;
-      e = h->bf16 ? launch_gemm_bf16(g, EPI_SWIGLU, rows(F, 128), cx.st) : launch_gemm_f32(g, EPI_SWIGLU, cx.st);
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_SWIGLU, rows(F, 128, d), cx.st) : launch_gemm_f32(g, EPI_SWIGLU, cx.st);
       if (e != hipSuccess) return e;
     }
     {
@@ -482,7 +482,7 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
       g.A = h->ubuf; g.a_stride = 0; g.lda = F;
       g.B = h->w.w_down; g.b_stride = (int64_t)d * F; g.N = d; g.K = F;
       g.C = h->act[0]; g.c_stride = 0; g.ldc = d; g.desc = h->desc;
-      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
+      e = h->bf16 ? launch_gemm_bf16(g, EPI_RESID, rows(d, 256, F), cx.st) : launch_gemm_f32(g, EPI_RESID, cx.st);
       if (e != hipSuccess) return e;
     }
   }
@@ -568,18 +568,24 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, int32_t t_last,
 // one workgroup on every compute unit (the tiles hold one workgroup per CU).
 // Tiles shorter than 128 rows are not considered: their operand traffic per
 // FLOP is too high.
-int pick_row_blocks(int n, int n_cols, int cols_per_tile, int P, int cus) {
+int pick_row_blocks(int n, int n_cols, int cols_per_tile, int K, int P, int cus) {
+  // Tile heights are 16-row blocks.  Cost = rounds of workgroups over the
+  // CUs x (tile rows + a fixed per-tile overhead in rows: pipeline fill and
+  // epilogue).  Heights whose operand loads split unevenly over the four
+  // waves (16-row blocks per stage = 3 mod 4) slow every pipeline stage, so
+  // long-K products do not use them.
   constexpr int kTileOverheadRows = 48;
-  int best = 6;
+  int best = 12;
   long best_cost = -1;
   for (int i = 0; i < kGemmRowBlocksCount; ++i) {
-    const int mb = kGemmRowBlocks[i], bm = 32 * mb;
+    const int rb = kGemmRowBlocks[i], bm = 16 * rb;
     if (bm < 128) continue;
+    if (K >= 4096 && (rb + 16) % 4 == 3) continue;
     const long tiles = (long)((n + bm - 1) / bm) * ((n_cols + cols_per_tile - 1) / cols_per_tile) * P;
     const long rounds = (tiles + cus - 1) / cus;
     const long cost = rounds * (bm + kTileOverheadRows);
-    if (best_cost < 0 || cost < best_cost || (cost == best_cost && mb > best)) {
-      best = mb;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && rb > best)) {
+      best = rb;
       best_cost = cost;
     }
   }
@@ -804,7 +810,7 @@ int armt_logits(armt_handle* h, const void* y, int64_t rows, const void* g_final
     g.B = w_lm; g.b_stride = 0;
     g.M = m; g.N = vocab; g.K = d;
     g.C = logits + r0 * vocab; g.c_stride = 0; g.ldc = vocab;
-    e = h->bf16 ? launch_gemm_bf16(g, EPI_STORE, h->mb ? h->mb : pick_row_blocks(m, vocab, 256, 1, h->cus), h->stream)
+    e = h->bf16 ? launch_gemm_bf16(g, EPI_STORE, h->mb ? h->mb : pick_row_blocks(m, vocab, 256, d, 1, h->cus), h->stream)
                 : launch_gemm_f32(g, EPI_STORE, h->stream);
     if (e != hipSuccess) return hip_fail(e, "LM-head GEMM launch");
   }
@@ -1103,7 +1109,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     g.M = n; g.N = N; g.K = K;
     g.C = C; g.c_stride = c_ps; g.ldc = N;
     g.desc = nullptr; g.last_layer = L - 1; g.T = T;
-    return launch_gemm_bf16(g, epi, gemm_rows(h, N, 256, P), st);
+    return launch_gemm_bf16(g, epi, gemm_rows(h, N, 256, K, P), st);
   };
   const int64_t Lo = (int64_t)l0;   // slab offsets of layer l0
   // dX (fp32, layer-indexed slab) = dY W on the forward's grouped GEMM: dY as
@@ -1118,7 +1124,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     g.M = n; g.N = N; g.K = Kx;
     g.C = C; g.c_stride = c_ps; g.ldc = N;
     g.desc = nullptr; g.last_layer = L - 1; g.T = T;
-    return launch_gemm_bf16(g, EPI_STORE, gemm_rows(h, N, 256, P), st);
+    return launch_gemm_bf16(g, EPI_STORE, gemm_rows(h, N, 256, Kx, P), st);
   };
   // dW (fp32, [L][out][in], layer-indexed) += dY^T X on the forward's grouped
   // GEMM, in one pass over dW: K runs over the node's rows twice, first with
@@ -1147,7 +1153,7 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     g.M = out; g.N = in; g.K = k2;
     g.C = const_cast<void*>(dW); g.c_stride = (int64_t)out * in; g.ldc = in;   // caller's gradient buffer
     g.desc = nullptr; g.last_layer = L - 1; g.T = T;
-    return launch_gemm_bf16(g, EPI_RESID, h->mb ? h->mb : pick_row_blocks(out, in, 256, P, h->cus), st);
+    return launch_gemm_bf16(g, EPI_RESID, h->mb ? h->mb : pick_row_blocks(out, in, 256, k2, P, h->cus), st);
   };
 
   // ---- recompute the forward of each node

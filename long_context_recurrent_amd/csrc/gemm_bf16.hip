@@ -7,18 +7,20 @@
 // "Diagonal Batching for Recurrent Memory Transformers", Implementation).
 //
 // CDNA4 mapping.
-//  * Matrix core: v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  On MI355X it
-//    sustains the full dense bf16 rate, twice that of the 16x16x32 form.
-//  * Tile: a workgroup of 4 waves owns BM x 256 outputs, BM = 32 * MB rows,
-//    chosen per workload to pad the n = T + M node rows little.  Each wave owns
-//    all BM rows and 64 columns: MB x 2 accumulator blocks of 32 x 32
-//    (32 * MB accumulator registers per lane).
-//  * Operands: K advances 32 per pipeline stage.  Stages are filled straight
-//    from global memory into LDS by global_load_lds_dwordx4 (no staging
-//    registers), issued NS - 1 stages ahead; each 64-byte tile row keeps its
-//    four 16-byte chunks XOR-swizzled so the fragment reads of 16 consecutive
-//    rows hit 16 different bank groups.  The fragments of the next stage are
-//    read while the MFMAs of the current one run.
+//  * Matrix core: v_mfma_f32_16x16x32_bf16 (fp32 accumulation).  With enough
+//    independent accumulators in flight it sustains the same dense bf16 rate
+//    as the 32x32x16 form on MI355X, and its 16-row granularity lets a node's
+//    n = T + M rows split into tiles with little padding (1040 = 5 x 208).
+//  * Tile: a workgroup of 4 waves owns BM x 256 outputs, BM = 16 * RB rows,
+//    chosen per workload.  Each wave owns all BM rows and 64 columns: RB x 4
+//    accumulator blocks of 16 x 16 (16 * RB accumulator registers per lane).
+//  * Operands: K advances 32 per pipeline stage (one MFMA per block).
+//    Stages are filled straight from global memory into LDS by
+//    global_load_lds_dwordx4 (no staging registers), issued NS - 1 stages
+//    ahead; each 64-byte tile row keeps its four 16-byte chunks XOR-swizzled;
+//    a fragment read covers one 16-row block (1 KB) and its lanes hit 16
+//    different bank groups.  The fragments of the next stage are read while
+//    the MFMAs of the current one run.
 //  * Schedule: tiles are numbered so that each of the 8 XCDs works through a
 //    contiguous range (same layer, same weight columns, neighbouring rows of
 //    every sequence of the batch), keeping the shared operand tiles in that
@@ -34,9 +36,10 @@
 //                  last layer the segment-token rows (fewer in a short last
 //                  segment) are also written to the caller's y, rounded to bf16.
 //      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
-//                  rows; U = R(silu(gate) * up).
+//                  rows; a wave's gate and up blocks of the same output
+//                  columns sit in the same lanes; U = R(silu(gate) * up).
 //      EPI_STORE : fp32 store (LM-head logits; N a multiple of 8).
-//  Every output element accumulates over K in the same order whatever MB or
+//  Every output element accumulates over K in the same order whatever RB or
 //  the number of problems, so results do not depend on the wave width.
 #include <type_traits>
 #include <utility>
@@ -59,8 +62,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int BK = 32;          // k per pipeline stage
 constexpr int ROWB = BK * 2;    // bytes per tile row in a stage (64)
 constexpr int BNB = 256;        // B-tile rows per stage
@@ -69,15 +70,16 @@ constexpr int CPITCH = 256 + 4; // staged tile pitch (floats)
 constexpr int LDS_BYTES = 160 * 1024;
 
 // Stages that fit in LDS (at most 4); each holds BM + 256 rows of 64 bytes.
-template <int MB>
+template <int RB>
 constexpr int n_stages() {
-  return (LDS_BYTES / ((32 * MB + BNB) * ROWB)) > 4 ? 4 : (LDS_BYTES / ((32 * MB + BNB) * ROWB));
+  return (LDS_BYTES / ((16 * RB + BNB) * ROWB)) > 4 ? 4 : (LDS_BYTES / ((16 * RB + BNB) * ROWB));
 }
 
 // 16-byte chunk c (0..3) of tile row r sits at physical chunk
 // c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the same logical chunk of any 8 (or 16)
 // consecutive rows lands in 8 (16) different 16-byte bank groups, so fragment
-// reads are conflict-free whether the LDS serves 128 or 256 bytes per cycle.
+// reads (lane L: row 16i + L % 16, chunk L / 16) are conflict-free whether the
+// LDS serves 128 or 256 bytes per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -99,11 +101,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// First B-tile row (output column) of wave w's column block j (0, 1).
+// First B-tile row (output column) of wave w's 16-column block j (0..3).
+// SwiGLU: blocks 0, 1 are gate rows and blocks 2, 3 the up rows of the same
+// output columns.
 template <int EPI>
 __device__ __forceinline__ int col_block(int w, int j) {
-  if (EPI == EPI_SWIGLU) return j == 0 ? 32 * w : 128 + 32 * w;   // gate, matching up
-  return 64 * w + 32 * j;
+  if (EPI == EPI_SWIGLU) return (j < 2 ? 32 * w : 128 + 32 * w) + 16 * (j & 1);
+  return 64 * w + 16 * j;
 }
 
 // Stored position of key k in a V^T row: keys 4..7 and 8..11 of every
@@ -123,15 +127,14 @@ __device__ __forceinline__ int xcd_tile(int id, int total) {
 
 }  // namespace
 
-template <int MB, int EPI>
+template <int RB, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int BM = 32 * MB;
+  constexpr int BM = 16 * RB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
-  constexpr int NS = n_stages<MB>();
+  constexpr int NS = n_stages<RB>();
   constexpr int STAGE = (BM + BNB) * ROWB;             // bytes per stage
   constexpr int A_INSTR = BM / 16;                     // 1 KB wave loads per stage
   constexpr int INSTR = A_INSTR + BNB / 16;
-  constexpr int MAXQ = (INSTR + 3) / 4;                // loads per wave per stage
   static_assert(NS >= 3, "pipeline depth");
   static_assert(RC * CPITCH * 4 <= NS * STAGE, "epilogue staging fits");
 
@@ -161,17 +164,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       (EPI == EPI_SWIGLU) ? (const bf16*)g.B2 + (int64_t)layer * g.b_stride : B;
 
   // ---- direct global -> LDS loads.  A stage holds INSTR blocks of 16 tile
-  // rows (A rows, then B rows), each filled by one 1 KB wave load in which
+  // rows (A rows, then B rows), each filled by 1 KB of wave loads in which
   // lane L brings tile row 16q + L/4, physical chunk L%4 (= logical chunk
-  // swz(row, L%4)).  Wave w issues blocks q = w, w + 4, ...; every wave issues
-  // exactly MAXQ loads per stage (a wave with fewer blocks repeats its first
-  // one, rewriting identical bytes), so the vmcnt waits are constants.
-  const bf16* src[MAXQ];
-  int dst[MAXQ];
+  // swz(row, L%4)); the LDS address of a lane's 16 bytes follows from its
+  // lane number, so a load with some lanes off fills only their part.
+  // Wave w issues the whole blocks q = w, w + 4, ... below INSTR - EXTRA
+  // (EXTRA = INSTR % 4).  The last EXTRA blocks: one block -> each wave
+  // loads a quarter of it (lanes 16w .. 16w+15); two -> each wave half of
+  // one; three -> waves 0..2 one whole block each and wave 3 none (split
+  // three ways the extra instructions cost more than the imbalance).  The
+  // number of loads is fixed per wave, so its vmcnt waits are constants.
+  constexpr int EXTRA = INSTR % 4;
+  constexpr int NFULL = (INSTR - EXTRA) / 4;
+  constexpr int NLOAD = NFULL + (EXTRA ? 1 : 0);       // loads per wave per stage (at most)
+  const bf16* src[NLOAD];
+  int dst[NLOAD];
 #pragma unroll
-  for (int t = 0; t < MAXQ; ++t) {
+  for (int t = 0; t < NLOAD; ++t) {
     int q = w + 4 * t;
-    q = q < INSTR ? q : w;
+    if (t == NFULL) {
+      const int xb = EXTRA == 1 ? 0 : EXTRA == 2 ? (w >> 1) : (w < 3 ? w : 0);
+      q = INSTR - EXTRA + xb;
+    }
     const int rl = lane >> 2, pc = lane & 3;
     if (q < A_INSTR) {
       const int r = 16 * q + rl;
@@ -188,6 +202,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       dst[t] = (BM + 16 * (q - A_INSTR)) * ROWB;
     }
   }
+  // lanes of this wave that take part in its extra load (EXTRA = 1, 2), and
+  // whether this wave has one at all (EXTRA = 3; wave-uniform)
+  const bool my_part = EXTRA == 1 ? (lane >> 4) == w : EXTRA == 2 ? (lane >> 5) == (w & 1) : true;
+  const bool has_extra = EXTRA != 3 || w < 3;
   const int KT = g.K / BK;
   // Stage kt of the K loop; tiles past the end re-fetch the last tile into a
   // stage nobody reads any more.
@@ -195,51 +213,58 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int kc = kt < KT ? kt : KT - 1;
     unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int t = 0; t < MAXQ; ++t)
-      __builtin_amdgcn_global_load_lds((const void*)(src[t] + kc * BK),
-                                       (__attribute__((address_space(3))) void*)(st + dst[t]), 16, 0, 0);
-  };
-
-  f32x16 acc[MB][2];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  // Fragments of one stage: two 16-wide k-steps; lane (r32 = lane % 32,
-  // h = lane / 32) holds k = 8h..8h+7 of its row, i.e. logical chunk 2ks + h.
-  const int r32 = lane & 31, h = lane >> 5;
-  bf16x8 fa0[2][MB], fb0[2][2], fa1[2][MB], fb1[2][2];
-  auto read_frags = [&](int kt, bf16x8 (*fa)[MB], bf16x8 (*fb)[2]) {
-    const unsigned char* st = smem + (kt % NS) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = col_block<EPI>(w, j) + r32;
-        fb[ks][j] = *(const bf16x8*)(st + (BM + r) * ROWB + swz(r, 2 * ks + h) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int r = 32 * i + r32;
-        fa[ks][i] = *(const bf16x8*)(st + r * ROWB + swz(r, 2 * ks + h) * 16);
-      }
+    for (int t = 0; t < NLOAD; ++t) {
+      if (t < NFULL || (EXTRA == 3 ? has_extra : my_part))
+        __builtin_amdgcn_global_load_lds((const void*)(src[t] + kc * BK),
+                                         (__attribute__((address_space(3))) void*)(st + dst[t]), 16, 0, 0);
     }
   };
-  auto mfma_all = [&](bf16x8 (*fa)[MB], bf16x8 (*fb)[2]) {
+
+  f32x4 acc[RB][4];
+
+  // Fragments of one stage (k = 32): lane (r16 = lane % 16, c = lane / 16)
+  // holds k = 8c..8c+7 of row r16 of each 16-row A block and of each
+  // 16-column B block -- one 16-byte read per block.
+  const int r16 = lane & 15, kc = lane >> 4;
+  bf16x8 fa0[RB], fb0[4], fa1[RB], fb1[4];
+  auto read_frags = [&](int kt, bf16x8* fa, bf16x8* fb) {
+    const unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int j = 0; j < 4; ++j) {
+      const int r = col_block<EPI>(w, j) + r16;
+      fb[j] = *(const bf16x8*)(st + (BM + r) * ROWB + swz(r, kc) * 16);
+    }
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < RB; ++i) {
+      const int r = 16 * i + r16;
+      fa[i] = *(const bf16x8*)(st + r * ROWB + swz(r, kc) * 16);
+    }
+  };
+  // The first stage's products start from zero (an explicit zero-initialised
+  // accumulator makes the register allocator rotate the accumulators through
+  // copies on every trip of the K loop).
+  auto mfma_all = [&](const bf16x8* fa, const bf16x8* fb, auto first) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], decltype(first)::value ? f32x4{} : acc[i][j],
+                                                            0, 0, 0);
+  };
+
+  // Wait until this wave's loads of the oldest stage in flight landed (the
+  // NS - 2 younger stages may still be in flight).
+  auto wait_stage = [&]() {
+    if (has_extra)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * NLOAD));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * (NLOAD - 1)));
   };
 
   // prologue: stages 0 .. NS-2 in flight; stage 0 landed; its fragments read
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s);
-  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * MAXQ));
+  wait_stage();
   lds_barrier();
   read_frags(0, fa0, fb0);
   // One pipeline step: refill the stage freed two steps ago, wait until this
@@ -249,34 +274,38 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // fragments of stage kt already in registers.  After the last step the
   // fragments read belong to a re-fetched stage and are never used; KT is even
   // because K is a multiple of 64.
-  auto step = [&](int kt, bf16x8 (*fa_cur)[MB], bf16x8 (*fb_cur)[2], bf16x8 (*fa_nxt)[MB],
-                  bf16x8 (*fb_nxt)[2]) {
+  auto step = [&](int kt, const bf16x8* fa_cur, const bf16x8* fb_cur, bf16x8* fa_nxt, bf16x8* fb_nxt,
+                  auto first) {
     issue(kt + NS - 1);
-    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * MAXQ));
+    wait_stage();
     lds_barrier();
     read_frags(kt + 1, fa_nxt, fb_nxt);
-    mfma_all(fa_cur, fb_cur);
-    // Interleave the reads with the MFMAs (one read, then one MFMA) so the
-    // LDS and the matrix core work side by side; left alone, the scheduler
-    // sinks each read next to the MFMA of the following step that uses it.
-    constexpr int NREAD = 2 * (MB + 2), NMFMA = 4 * MB;
+    mfma_all(fa_cur, fb_cur, first);
+    // Interleave the reads with the MFMAs (one read, then a few MFMAs) so
+    // the LDS and the matrix core work side by side; left alone, the
+    // scheduler sinks each read next to the MFMA of the following step that
+    // uses it.
+    constexpr int NREAD = RB + 4, NMFMA = 4 * RB;
+    constexpr int PER = NMFMA / NREAD;
 #pragma unroll
     for (int i = 0; i < NREAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - PER * NREAD, 0);
   };
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, fa0, fb0, fa1, fb1);
-    step(kt + 1, fa1, fb1, fa0, fb0);
+  step(0, fa0, fb0, fa1, fb1, std::true_type{});
+  step(1, fa1, fb1, fa0, fb0, std::false_type{});
+  for (int kt = 2; kt < KT; kt += 2) {
+    step(kt, fa0, fb0, fa1, fb1, std::false_type{});
+    step(kt + 1, fa1, fb1, fa0, fb0, std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
   __syncthreads();
 
   // ---- epilogue: stage RC rows at a time as fp32 in LDS, then store.
-  // Accumulator element e of block (i, j) in lane (r32, h) is output row
-  // 32i + 8(e/4) + 4h + e%4, column col_block(w, j) + r32.
+  // Accumulator element e of block (i, j) in lane (r16, kc) is output row
+  // 16i + 4kc + e, column col_block(w, j) + r16.
   float* Cs = (float*)smem;
   if (EPI == EPI_RESID) {
     // Residual stream (fp32) += acc.  Each pass's residual rows are loaded
@@ -324,14 +353,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     static_for<NPASS>([&](auto PI) {
       constexpr int p = decltype(PI)::value, rc0 = RC * p;
       if (p + 1 < NPASS) load_pass(rc0 + RC, rb[(p + 1) & 1]);
-      static_for<MB>([&](auto II) {
+      static_for<RB>([&](auto II) {
         constexpr int i = decltype(II)::value;
-        if (32 * i >= rc0 && 32 * i < rc0 + RC) {
+        if (16 * i >= rc0 && 16 * i < rc0 + RC) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int rl = 32 * i - rc0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          for (int e = 0; e < 4; ++e) {
+            const int rl = 16 * i - rc0 + 4 * kc + e;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) Cs[rl * CPITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
+            for (int j = 0; j < 4; ++j) Cs[rl * CPITCH + col_block<EPI>(w, j) + r16] = acc[i][j][e];
           }
         }
       });
@@ -369,17 +398,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(EP_RC * EP_PITCH * 4 <= NS * STAGE, "epilogue staging fits");
   for (int rc0 = 0; rc0 < BM; rc0 += EP_RC) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      if (32 * i < rc0 || 32 * i >= rc0 + EP_RC) continue;
+    for (int i = 0; i < RB; ++i) {
+      if (16 * i < rc0 || 16 * i >= rc0 + EP_RC) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rl = 32 * i - rc0 + 8 * (e >> 2) + 4 * h + (e & 3);
+      for (int e = 0; e < 4; ++e) {
+        const int rl = 16 * i - rc0 + 4 * kc + e;
         if (EPI == EPI_SWIGLU) {
-          const float gt = acc[i][0][e], up = acc[i][1][e];
-          Cs[rl * EP_PITCH + 32 * w + r32] = gt * sigmoid_f(gt) * up;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float gt = acc[i][j][e], up = acc[i][j + 2][e];
+            Cs[rl * EP_PITCH + 32 * w + 16 * j + r16] = gt * sigmoid_f(gt) * up;
+          }
         } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) Cs[rl * EP_PITCH + col_block<EPI>(w, j) + r32] = acc[i][j][e];
+          for (int j = 0; j < 4; ++j) Cs[rl * EP_PITCH + col_block<EPI>(w, j) + r16] = acc[i][j][e];
         }
       }
     }
@@ -519,44 +551,48 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
 // host launchers
 // ---------------------------------------------------------------------------
 
-template <int MB, int EPI>
-static hipError_t launch_mb(const GemmArgs& g, hipStream_t st) {
-  constexpr int BM = 32 * MB;
+template <int RB, int EPI>
+static hipError_t launch_rb(const GemmArgs& g, hipStream_t st) {
+  constexpr int BM = 16 * RB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN_OUT - 1) / BN_OUT) * g.P * g.batch;
-  hipLaunchKernelGGL((gemm_bf16_kernel<MB, EPI>), dim3(tiles), dim3(256), 0, st, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<RB, EPI>), dim3(tiles), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
 template <int EPI>
-static hipError_t launch_epi(const GemmArgs& g, int mb, hipStream_t st) {
-  switch (mb) {
-    case 2: return launch_mb<2, EPI>(g, st);
-    case 3: return launch_mb<3, EPI>(g, st);
-    case 4: return launch_mb<4, EPI>(g, st);
-    case 5: return launch_mb<5, EPI>(g, st);
-    case 6: return launch_mb<6, EPI>(g, st);
-    case 7: return launch_mb<7, EPI>(g, st);
+static hipError_t launch_epi(const GemmArgs& g, int rb, hipStream_t st) {
+  switch (rb) {
+    case 4: return launch_rb<4, EPI>(g, st);
+    case 6: return launch_rb<6, EPI>(g, st);
+    case 8: return launch_rb<8, EPI>(g, st);
+    case 9: return launch_rb<9, EPI>(g, st);
+    case 10: return launch_rb<10, EPI>(g, st);
+    case 11: return launch_rb<11, EPI>(g, st);
+    case 12: return launch_rb<12, EPI>(g, st);
+    case 13: return launch_rb<13, EPI>(g, st);
+    case 14: return launch_rb<14, EPI>(g, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-const int kGemmRowBlocks[] = {2, 3, 4, 5, 6, 7};
-const int kGemmRowBlocksCount = 6;
+// Tile heights offered, in 16-row blocks.
+const int kGemmRowBlocks[] = {4, 6, 8, 9, 10, 11, 12, 13, 14};
+const int kGemmRowBlocksCount = 9;
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int mb, hipStream_t st) {
+hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int rb, hipStream_t st) {
   // K must be a multiple of 64 (two pipeline stages per loop trip)
   if (g.P <= 0 || g.batch <= 0 || g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % (2 * BK)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV:
       if (g.head_dim <= 0 || 256 % g.head_dim) return hipErrorInvalidValue;
-      return launch_epi<EPI_QKV>(g, mb, st);
-    case EPI_RESID: return launch_epi<EPI_RESID>(g, mb, st);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, mb, st);
+      return launch_epi<EPI_QKV>(g, rb, st);
+    case EPI_RESID: return launch_epi<EPI_RESID>(g, rb, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, rb, st);
     case EPI_STORE:
       // whole 8-column output pieces
       if (g.N % 8) return hipErrorInvalidValue;
-      return launch_epi<EPI_STORE>(g, mb, st);
+      return launch_epi<EPI_STORE>(g, rb, st);
     default: return hipErrorInvalidValue;
   }
 }

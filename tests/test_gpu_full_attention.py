@@ -87,9 +87,9 @@ def test_full_attention_prefix_and_lengths():
     for n in (1, 63, 64, 129, 777):
         part = model.forward(x[:n].contiguous())
         assert torch.equal(part, full[:n]), f"prefix of length {n} differs"
-    for mb in (2, 4, 7):
-        model.set_option(C.ARMT_OPT_GEMM_ROWS, mb)
-        assert torch.equal(model.forward(x), full), f"GEMM rows {32 * mb} changed the result"
+    for rb in (4, 9, 13, 14):
+        model.set_option(C.ARMT_OPT_GEMM_ROWS, rb)
+        assert torch.equal(model.forward(x), full), f"GEMM rows {16 * rb} changed the result"
 
 
 def test_full_attention_logits_and_errors():
