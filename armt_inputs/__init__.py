@@ -50,6 +50,10 @@ pages give no vocabulary size, so V is synthetic, ``HEAD_VOCAB``):
     index 3 + 9*L: W_lm [V, d] N(0, 0.02);  index 4 + 9*L: g_final [d] =
     1 + gain_std * N(0, 1) (gain_std 0 by default: gains of 1, like the layers').
 
+Sketch for sampled full-length checks (no part of the model): index 1,000,003:
+    R_sk [d, 2] N(0, 1) float32; a segment's output rows y_s [T, d] are
+    summarised as y_s R_sk [T, 2], so a check over every segment stays small.
+
 Matrices are stored row-major as [out_features, in_features].  Values are
 drawn in float32 and, for bf16 workloads, rounded once to bfloat16 so that the
 GPU path and the oracle consume the same numbers.
@@ -64,7 +68,7 @@ import os
 import numpy as np
 
 __all__ = ["ArmtConfig", "CONFIGS", "get_config", "ArmtInputs", "make_inputs",
-           "make_state", "make_head", "make_batch_x", "HEAD_VOCAB", "WEIGHT_NAMES"]
+           "make_state", "make_head", "make_batch_x", "make_sketch", "HEAD_VOCAB", "WEIGHT_NAMES"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -247,3 +251,12 @@ def make_batch_x(cfg: ArmtConfig, inputs: "ArmtInputs", batch: int, seed: int = 
         out[b] = _to_storage(_draw(seed, 5 + 9 * cfg.n_layers + b, (rows, d), 1.0), cfg.dtype)
     return out
 
+
+
+SKETCH_INDEX = 1_000_003
+
+
+def make_sketch(cfg: ArmtConfig, width: int = 2, seed: int = 0) -> np.ndarray:
+    """A fixed Gaussian matrix [d, width] (float32) used to summarise output
+    rows for the full-length checks; it is test data, not a model weight."""
+    return _draw(seed, SKETCH_INDEX, (cfg.d_model, width), 1.0)
