@@ -23,10 +23,13 @@ Extra fields:
                 summed durations, from HIP events recorded around every launch
                 on the library's stream during a timed pass, against the bf16
                 dense MFMA peak of 2.5 PFLOP/s; traffic = HBM bytes per launch
-                from the committed FETCH_SIZE / WRITE_SIZE record;
+                from the committed FETCH_SIZE / WRITE_SIZE counters
+                (profiles/pmc_<workload>.json);
   gemm_util     the same for all four grouped GEMMs together;
   kernels       every kernel: time per forward, FLOP/s and algorithmic GB/s,
-                each against its peak;
+                each against its peak; from the counter record, HBM bytes per
+                launch and their rate over the measured launch time, and the
+                matrix-core / vector-ALU busy fractions;
   launches      kernel and graph launches per forward, diagonal vs sequential;
   cpu_baseline  the CPU oracle timed on a bounded sample (first nodes of
                 segment 0) on this host.
@@ -89,10 +92,16 @@ def parse():
                     help="grouped backward (reversed diagonal waves) against the node-by-node backward on an "
                          "fp32 workload and on the 1B shape in bf16: time per forward + backward, one JSON line "
                          "per workload and schedule")
-    ap.add_argument("--traffic-record", metavar="DIR",
-                    help="write the FETCH_SIZE / WRITE_SIZE record of --roofline-kernel from the CSV "
-                         "output of four rocprofv3 --pmc passes under DIR (pmc_FETCH_SIZE, "
-                         "pmc_WRITE_SIZE, calib_FETCH_SIZE, calib_WRITE_SIZE); no GPU needed")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="print per-kernel tables of a rocprofv3 --kernel-trace database (rocpd SQLite) "
+                         "of --profile-only forwards (--forwards N in it); no GPU needed")
+    ap.add_argument("--forwards", type=int, default=5, help="forwards in the traced run (--trace-summary)")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="print the committed counter record of --workload as a table; no GPU needed")
+    ap.add_argument("--pmc-record", metavar="DIR",
+                    help="write profiles/pmc_<workload>.json, the per-kernel counter record, from the CSV "
+                         "output of rocprofv3 --pmc passes under DIR (pmc_* over bench.py --profile-only, "
+                         "calib_FETCH_SIZE / calib_WRITE_SIZE over --copy-calibration); no GPU needed")
     return ap.parse_args()
 
 
@@ -190,95 +199,213 @@ def timing_summary(mean, each, tokens):
             "tokens_per_s_median": tokens / statistics.median(each)}
 
 
-def kernel_summary(v, forwards):
+def kernel_summary(v, forwards, kernel=None, workload=None, rec=None):
     """Per-kernel figures from HIP-event timing: time per forward, algorithmic
-    FLOP/s against the bf16 MFMA peak and algorithmic bytes/s against HBM."""
+    FLOP/s against the bf16 MFMA peak and algorithmic bytes/s against HBM;
+    with a current counter record, the HBM bytes the counters measured per
+    launch over the same launch time, and the matrix-core busy fraction."""
     sec = v["ms"] * 1e-3
     tf = v["flops"] / sec / 1e12 if sec else 0.0
     gbs = v["bytes"] / sec / 1e9 if sec else 0.0
-    return {"us_per_forward": v["ms"] * 1e3 / forwards, "launches_per_forward": v["launches"] // forwards,
-            "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS, "gb_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    out = {"us_per_forward": v["ms"] * 1e3 / forwards, "launches_per_forward": v["launches"] // forwards,
+           "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS, "gb_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    if kernel is not None and rec is not None:
+        tb = measured_traffic(kernel, workload, rec)
+        if tb is not None and v["launches"]:
+            per_launch_s = sec / v["launches"]
+            out.update(traffic_bytes_per_launch=tb, traffic_gb_s=tb / per_launch_s / 1e9,
+                       traffic_frac_hbm=tb / per_launch_s / 1e9 / PEAK_HBM_GBS,
+                       traffic_over_algorithmic=tb * v["launches"] / v["bytes"] if v["bytes"] else None)
+        mu = counter_value(kernel, workload, "MfmaUtil", rec)
+        if mu is not None:
+            out["mfma_busy_counter"] = mu / 100.0
+        vb = counter_value(kernel, workload, "VALUBusy", rec)
+        if vb is not None:
+            out["valu_busy_counter"] = vb / 100.0
+    return out
 
 
-TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"gate_up": "gemm_bf16.hip", "down": "gemm_bf16.hip", "qkv": "gemm_bf16.hip",
-                  "o_proj": "gemm_bf16.hip", "attn": "attention.hip"}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"mem_read": "memory_mfma.hip", "qkv": "gemm_bf16.hip", "attn": "attention.hip",
+                  "o_proj": "gemm_bf16.hip", "mlp_norm": "memory.hip", "gate_up": "gemm_bf16.hip",
+                  "down": "gemm_bf16.hip", "mem_keys": "memory_mfma.hip", "mem_update": "memory_mfma.hip"}
+EPI_KERNEL = {1: "qkv", 3: "gate_up"}     # gemm_bf16_kernel<RB, EPI>; EPI 2 (residual) is O-proj or down
 
 
-def measured_traffic(kernel, workload):
-    """Average HBM bytes per launch of ``kernel`` from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE record of this workload, scaled by the copy-kernel
-    calibration factors stored with it; None when there is no record or the
-    kernel's source has changed since the counters were taken."""
+def _source_sha(kernel):
     import hashlib
-    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
-    src = KERNEL_SOURCES.get(kernel)
-    if not (src and os.path.exists(path)):
+    with open(os.path.join(ROOT, "long_context_recurrent_amd", "csrc", KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_record(workload):
+    """The committed per-kernel counter record of a workload (None if absent)."""
+    path = os.path.join(PROFILE_DIR, f"pmc_{workload}.json")
+    if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    with open(os.path.join(ROOT, "long_context_recurrent_amd", "csrc", src), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != digest:
-        log(f"traffic record for {kernel} is stale (kernel source changed); reporting null")
+        return json.load(f)
+
+
+def measured_traffic(kernel, workload, rec=None):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
+    WRITE_SIZE counters of this workload, scaled by the copy-kernel
+    calibration stored with them; None when there is no record or the
+    kernel's source changed since the counters were taken."""
+    rec = rec if rec is not None else pmc_record(workload)
+    k = (rec or {}).get("kernels", {}).get(kernel)
+    if not k or "FETCH_SIZE" not in k or "WRITE_SIZE" not in k:
         return None
-    return (rec["fetch_kib_per_dispatch"] * rec["fetch_factor"]
-            + rec["write_kib_per_dispatch"] * rec["write_factor"]) * 1024.0
+    if k.get("source_sha256") != _source_sha(kernel):
+        log(f"counter record for {kernel} is stale (kernel source changed); reporting null")
+        return None
+    cal = rec["calibration"]
+    return (k["FETCH_SIZE"] * cal["FETCH_SIZE_factor"] + k["WRITE_SIZE"] * cal["WRITE_SIZE_factor"]) * 1024.0
 
 
-TRAFFIC_KERNEL_NAMES = {"gate_up": ("gate_up (gemm_bf16_kernel<MB, EPI_SWIGLU>)", "gemm_bf16_kernel<", ", 3>")}
+def counter_value(kernel, workload, counter, rec=None):
+    """Average per-dispatch value of a collected counter (None if absent or stale)."""
+    rec = rec if rec is not None else pmc_record(workload)
+    k = (rec or {}).get("kernels", {}).get(kernel)
+    if not k or counter not in k or k.get("source_sha256") != _source_sha(kernel):
+        return None
+    return k[counter]
 
 
-def _pmc_rows(path, counter):
+def _pmc_label(name, resid_seen):
+    """Forward kernel of a dispatch from its kernel name; the residual GEMMs
+    alternate O-proj, down within every wave."""
+    if "gemm_bf16_kernel<" in name:
+        epi = int(name.split("gemm_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")[1])
+        if epi == 2:
+            return ("o_proj", "down")[resid_seen % 2]
+        return EPI_KERNEL.get(epi)
+    for key, k in (("memread_norm", "mem_read"), ("attn_bf16_kernel", "attn"), ("rmsnorm_kernel", "mlp_norm"),
+                   ("memkeys", "mem_keys"), ("memupdate", "mem_update")):
+        if key in name:
+            return k
+    return None
+
+
+def write_pmc_record(args):
+    """Per-kernel counter record of one profiled forward: every
+    DIR/pmc_*/run_counter_collection.csv (rocprofv3 --pmc passes over
+    ``bench.py --profile-only``) averaged per dispatch for each forward
+    kernel, and the factors that make FETCH_SIZE / WRITE_SIZE read the true
+    byte count of a plain 256 MiB copy (DIR/calib_*)."""
     import csv
-    with open(path, newline="") as f:
-        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
-
-
-def write_traffic_record(args):
-    """Average FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the roofline
-    kernel over one profiled forward, with the factors that make the same
-    counters read the true byte count of a plain 256 MiB copy."""
-    import hashlib
-    label, prefix, suffix = TRAFFIC_KERNEL_NAMES[args.roofline_kernel]
-    d = args.traffic_record
-    rec = {"kernel": label, "workload": args.workload}
-    copy_bytes = 64 * 1024 * 1024 * 4
-    calib = {"copy_bytes": copy_bytes}
-    for ctr, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
-        rows = [r for r in _pmc_rows(os.path.join(d, f"pmc_{ctr}", "run_counter_collection.csv"), ctr)
-                if prefix in r["Kernel_Name"] and r["Kernel_Name"].split("(")[0].endswith(suffix)]
-        if not rows:
-            sys.exit(f"no {ctr} rows for {label} under {d}")
-        rec["dispatches"] = len(rows)
-        rec[f"{key}_kib_per_dispatch"] = sum(float(r["Counter_Value"]) for r in rows) / len(rows)
-        crows = [r for r in _pmc_rows(os.path.join(d, f"calib_{ctr}", "run_counter_collection.csv"), ctr)
-                 if "copyBuffer" in r["Kernel_Name"]]
-        if not crows:
-            sys.exit(f"no copy-kernel {ctr} rows under {d}")
+    d = args.pmc_record
+    out = {"workload": args.workload, "kernels": {}, "calibration": {"copy_bytes": 64 * 1024 * 1024 * 4}}
+    sums = {}
+    passes = sorted(p for p in os.listdir(d) if p.startswith("pmc_"))
+    for p in passes:
+        with open(os.path.join(d, p, "run_counter_collection.csv"), newline="") as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+        by_dispatch = {}
+        for r in rows:
+            by_dispatch.setdefault(int(r["Dispatch_Id"]), []).append(r)
+        resid = 0
+        for did in sorted(by_dispatch):
+            rs = by_dispatch[did]
+            k = _pmc_label(rs[0]["Kernel_Name"], resid)
+            if "gemm_bf16_kernel<" in rs[0]["Kernel_Name"] and k in ("o_proj", "down"):
+                resid += 1
+            if k is None:
+                continue
+            for r in rs:
+                acc = sums.setdefault(k, {}).setdefault(r["Counter_Name"], [0.0, 0])
+                acc[0] += float(r["Counter_Value"])
+                acc[1] += 1
+    for k, ctrs in sums.items():
+        rec = {c: v[0] / v[1] for c, v in ctrs.items()}
+        rec["dispatches"] = max(v[1] for v in ctrs.values())
+        rec["source"] = KERNEL_SOURCES[k]
+        rec["source_sha256"] = _source_sha(k)
+        out["kernels"][k] = rec
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(d, f"calib_{ctr}", "run_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        with open(path, newline="") as f:
+            crows = [r for r in csv.DictReader(f) if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
         kib = sum(float(r["Counter_Value"]) for r in crows) / len(crows)
-        calib[f"{key}_kib"] = kib
-        rec[f"{key}_factor"] = round(copy_bytes / 1024.0 / kib, 4)
-    rec["calibration"] = calib
-    src = os.path.join(ROOT, "long_context_recurrent_amd", "csrc", KERNEL_SOURCES[args.roofline_kernel])
-    with open(src, "rb") as f:
-        rec["source_sha256"] = hashlib.sha256(f.read()).hexdigest()
-    rec["commands"] = [
-        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE "
-        "--kernel-include-regex \"gemm_bf16_kernel<[0-9], 3>\" --output-format csv -d DIR/pmc_FETCH_SIZE "
-        "-o run -- python3 /root/repo/bench.py --steps 1 --warmup 0 --profile-only",
-        "same with --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE",
-        "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/calib_FETCH_SIZE -o run "
-        "-- python3 /root/repo/bench.py --copy-calibration (and WRITE_SIZE into DIR/calib_WRITE_SIZE)",
-        "python3 bench.py --traffic-record DIR: per-dispatch Counter_Value averaged over the gate_up "
-        "dispatches of one forward; calibration = the __amd_rocclr_copyBuffer dispatches of 256 MiB",
+        out["calibration"][f"{ctr}_kib"] = kib
+        out["calibration"][f"{ctr}_factor"] = round(out["calibration"]["copy_bytes"] / 1024.0 / kib, 4)
+    out["commands"] = [
+        "cd /tmp && export TMPDIR=/tmp",
+        "timeout -s KILL 150 rocprofv3 --pmc <COUNTERS> --output-format csv -d DIR/pmc_<NAME> -o run -- "
+        "python3 /root/repo/bench.py --steps 1 --warmup 0 --profile-only   (one pass per counter set: "
+        + "; ".join(p[4:] for p in passes) + ")",
+        "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/calib_FETCH_SIZE -o run -- "
+        "python3 /root/repo/bench.py --copy-calibration   (and WRITE_SIZE into DIR/calib_WRITE_SIZE)",
+        f"python3 bench.py --workload {args.workload} --pmc-record DIR",
     ]
-    out = os.path.join(TRAFFIC_DIR, f"traffic_{args.roofline_kernel}_{args.workload}.json")
-    with open(out, "w") as f:
-        json.dump(rec, f, indent=1)
+    path = os.path.join(PROFILE_DIR, f"pmc_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
         f.write("\n")
-    log(f"wrote {out}: {rec['dispatches']} dispatches, "
-        f"{(rec['fetch_kib_per_dispatch'] * rec['fetch_factor'] + rec['write_kib_per_dispatch'] * rec['write_factor']) / 1024:.1f} MiB/launch")
+    log(f"wrote {path}: kernels {sorted(out['kernels'])}")
+
+
+def trace_summary(db_path, forwards):
+    """Markdown tables from a rocprofv3 --kernel-trace database: every forward
+    kernel's dispatches summed by logical kernel (the residual GEMMs split into
+    O-proj and down by their order in each wave) and by instantiation."""
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    rows = list(cur.execute("select dispatch_id, name, duration from kernels order by dispatch_id"))
+    per_kernel, per_name, resid = {}, {}, 0
+    for _, name, dur in rows:
+        short = name.replace("armt::", "").replace("void ", "")
+        a = per_name.setdefault(short, [0, 0.0, float("inf"), 0.0])
+        a[0] += 1
+        a[1] += dur
+        a[2] = min(a[2], dur)
+        a[3] = max(a[3], dur)
+        k = _pmc_label(name, resid)
+        if "gemm_bf16_kernel<" in name and k in ("o_proj", "down"):
+            resid += 1
+        if k is not None:
+            b = per_kernel.setdefault(k, [0, 0.0])
+            b[0] += 1
+            b[1] += dur
+    out = ["| kernel | calls | total ms | ms / forward | avg us / call |", "|:--|--:|--:|--:|--:|"]
+    total = 0.0
+    for k in KERNEL_SOURCES:
+        if k in per_kernel:
+            n, t = per_kernel[k]
+            total += t
+            out.append(f"| {k} | {n} | {t / 1e6:.1f} | {t / 1e6 / forwards:.2f} | {t / n / 1e3:.1f} |")
+    out.append(f"| sum | | {total / 1e6:.1f} | {total / 1e6 / forwards:.2f} | |")
+    out += ["", "| kernel (instantiation) | calls | total ms | avg us | min us | max us |",
+            "|:--|--:|--:|--:|--:|--:|"]
+    for short, (n, t, lo, hi) in sorted(per_name.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {short} | {n} | {t / 1e6:.1f} | {t / n / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} |")
+    return "\n".join(out)
+
+
+def pmc_markdown(workload):
+    """Markdown table of the committed counter record: per kernel the
+    matrix-core busy fraction (MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x SIMDs)), the vector-ALU busy fraction (VALUBusy =
+    SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x CUs)), the LDS bank-conflict
+    stall fraction, the counted bf16 MFMA FLOPs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+    512) and the calibrated HBM bytes per dispatch."""
+    rec = pmc_record(workload)
+    cal = rec["calibration"]
+    out = ["| kernel | dispatches | MFMA busy | VALU busy | LDS bank-conflict stall | MFMA GFLOP / dispatch "
+           "| HBM read MB / dispatch | HBM write MB / dispatch | HBM MB / dispatch |",
+           "|:--|--:|--:|--:|--:|--:|--:|--:|--:|"]
+    for k in KERNEL_SOURCES:
+        v = rec["kernels"].get(k)
+        if not v:
+            continue
+        rd = v.get("FETCH_SIZE", 0) * cal["FETCH_SIZE_factor"] * 1024 / 1e6
+        wr = v.get("WRITE_SIZE", 0) * cal["WRITE_SIZE_factor"] * 1024 / 1e6
+        fl = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512 / 1e9
+        out.append(f"| {k} | {v['dispatches']} | {v.get('MfmaUtil', 0):.1f}% | {v.get('VALUBusy', 0):.1f}% | "
+                   f"{v.get('LDSBankConflict', 0):.1f}% | {fl:.1f} | {rd:.1f} | {wr:.1f} | {rd + wr:.1f} |")
+    return "\n".join(out)
 
 
 def host_cpu():
@@ -376,7 +503,8 @@ def headline(args, dev):
     kstats = r.kernel_stats(nfwd)
     rk = kstats[args.roofline_kernel]
     achieved = rk["flops"] / (rk["ms"] * 1e-3) / 1e12
-    traffic = measured_traffic(args.roofline_kernel, args.workload)
+    prec = pmc_record(args.workload)
+    traffic = measured_traffic(args.roofline_kernel, args.workload, prec)
     gemm = [kstats[k] for k in ("qkv", "o_proj", "gate_up", "down")]
     g_flops = sum(k["flops"] for k in gemm)
     g_ms = sum(k["ms"] for k in gemm)
@@ -414,7 +542,7 @@ def headline(args, dev):
                      "avg_launch_us": rk["ms"] / max(rk["launches"], 1) * 1e3},
         "gemm_util": {"achieved": g_flops / (g_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
                       "frac": g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "kernels": {k: kernel_summary(v, nfwd) for k, v in kstats.items()},
+        "kernels": {k: kernel_summary(v, nfwd, k, args.workload, prec) for k, v in kstats.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -836,8 +964,14 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
-    if args.traffic_record:
-        write_traffic_record(args)
+    if args.pmc_record:
+        write_pmc_record(args)
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.forwards))
+        return
+    if args.pmc_summary:
+        print(pmc_markdown(args.workload))
         return
     import torch
 

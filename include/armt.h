@@ -277,8 +277,12 @@ int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t *l_lo,
  * armt_kernel_id) with HIP events on the handle's stream (forces direct
  * launches); -1 turns it off.  ARMT_OPT_GEMM_ROWS: rows per grouped-GEMM
  * tile as a multiple of 16 (4, 6, 8 .. 14; 0 = pick for the workload);
- * results do not depend on it.  Changing it drops the captured graphs. */
-enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1, ARMT_OPT_GEMM_ROWS = 2 };
+ * results do not depend on it.  Changing it drops the captured graphs.
+ * ARMT_OPT_DEBUG_SYNC: 1 = forwards launch their kernels directly and, after
+ * every kernel, synchronise the stream and check for a HIP error, so a
+ * failure returns ARMT_E_HIP naming the kernel and the wave's layers (slow;
+ * for debugging); 0 = off (default).  Results are unchanged. */
+enum { ARMT_OPT_GRAPHS = 0, ARMT_OPT_TIME_KERNEL = 1, ARMT_OPT_GEMM_ROWS = 2, ARMT_OPT_DEBUG_SYNC = 3 };
 int armt_set_option(armt_handle *h, int32_t option, int32_t value);
 
 /* Kernels of one wave, in launch order. */

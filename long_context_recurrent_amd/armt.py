@@ -20,12 +20,13 @@ __all__ = [
     "armt_llama_forward", "armt_backward_workspace_size", "armt_backward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
-    "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "KERNELS", "VIEWS",
+    "ARMT_F32", "ARMT_BF16", "ARMT_OPT_GRAPHS", "ARMT_OPT_TIME_KERNEL", "ARMT_OPT_GEMM_ROWS", "ARMT_OPT_DEBUG_SYNC",
+    "KERNELS", "VIEWS",
 ]
 
 ARMT_OK, ARMT_E_INVALID, ARMT_E_UNSUPPORTED, ARMT_E_WORKSPACE, ARMT_E_HIP = 0, -1, -2, -3, -4
 ARMT_F32, ARMT_BF16 = 0, 1
-ARMT_OPT_GRAPHS, ARMT_OPT_TIME_KERNEL, ARMT_OPT_GEMM_ROWS = 0, 1, 2
+ARMT_OPT_GRAPHS, ARMT_OPT_TIME_KERNEL, ARMT_OPT_GEMM_ROWS, ARMT_OPT_DEBUG_SYNC = 0, 1, 2, 3
 KERNELS = ["mem_read", "attn_norm", "qkv", "attn", "o_proj", "mlp_norm", "gate_up", "down", "mem_keys", "mem_update"]
 VIEWS = {"act0": 0, "act1": 1, "normed": 2, "qkv": 3, "vt": 4, "attn": 5, "swiglu": 6, "A": 7, "z": 8}
 
@@ -56,7 +57,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "libarmt.so")
+    """The in-tree libarmt.so, or the library named by ARMT_LIBRARY (a debug
+    build of the same sources, e.g. the host-sanitizer build)."""
+    return os.environ.get("ARMT_LIBRARY") or os.path.join(_PKG, "libarmt.so")
 
 
 def load_library():

@@ -1,6 +1,7 @@
 """Build libarmt.so (HIP, gfx950) in-tree.
 
     python -m long_context_recurrent_amd.build        # or build_library()
+    python -m long_context_recurrent_amd.build --host-sanitize   # ASan/UBSan host build
 
 Each .hip source under csrc/ is compiled with hipcc for gfx950 into an object
 under long_context_recurrent_amd/_build/, then linked into
@@ -75,6 +76,56 @@ def build_library(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+# Host sanitizers for the runtime (argument checks, layouts, the scheduler,
+# graph bookkeeping): AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host code of armt_runtime.hip only -- each flag behind -Xarch_host, so no
+# device code is built with them.  The other objects are the regular ones.
+SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer"] + [
+    f for opt in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined")
+    for f in ("-Xarch_host", opt)]
+SAN_LIB = os.path.join(BUILD, "sanitize", "libarmt.so")
+
+
+def asan_runtime() -> str:
+    """Shared AddressSanitizer runtime of the compiler (to preload into a
+    process that is not built with it, such as python)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or "clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libarmt.so with ASan + UBSan in the host code of the runtime, under
+    _build/sanitize/; load it with ARMT_LIBRARY=<path> and the runtime from
+    asan_runtime() preloaded."""
+    srcs = sources()
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build_library()
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    rt_src = os.path.join(CSRC, "armt_runtime.hip")
+    rt_obj = os.path.join(os.path.dirname(SAN_LIB), "armt_runtime.o")
+    flags = [f for f in COMMON if f != "-O3"]
+    cmd = [hipcc(), *flags, *DEVICE_FLAGS, *SANITIZE, "-c", rt_src, "-o", rt_obj]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{proc.stderr}")
+    objs = [rt_obj if o.endswith("armt_runtime.o") else o for o in objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-o", SAN_LIB, *objs]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{proc.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB} (host ASan + UBSan in the runtime)")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build_library(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "--host-sanitize":
+        build_host_sanitized(verbose=True)
+    else:
+        build_library(verbose=True)
     sys.exit(0)

@@ -41,7 +41,9 @@ using namespace armt;
 
 namespace {
 
-thread_local std::string g_last_error;
+// Message of the last non-OK status of this thread (a fixed buffer: setting
+// it never allocates).
+thread_local char g_last_error[512];
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -49,7 +51,7 @@ int fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
+  memcpy(g_last_error, buf, sizeof(buf));
   return code;
 }
 
@@ -206,6 +208,8 @@ struct armt_handle {
   int* moff = nullptr;
   std::map<std::tuple<int, int, int, int, int>, hipGraphExec_t> graphs;
   bool use_graphs = true;
+  bool debug_sync = false;    // sync + error check after every kernel of a forward
+  int last_kernel = -1;       // kernel id of the last launch (for error messages)
   int time_kernel = -1;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
   size_t events_used = 0;
@@ -254,6 +258,7 @@ struct StepCtx {
   armt_handle* h;
   hipStream_t st;
   bool timing;
+  bool check = false;   // synchronise and check for errors after every launch
 };
 
 hipError_t timed(StepCtx& cx, int kid, int P, hipError_t (*fn)(const void*, hipStream_t), const void* arg) {
@@ -271,8 +276,13 @@ hipError_t timed(StepCtx& cx, int kid, int P, hipError_t (*fn)(const void*, hipS
     hipError_t e = hipEventRecord(h->events[h->events_used].first, cx.st);
     if (e != hipSuccess) return e;
   }
+  h->last_kernel = kid;
   hipError_t e = fn(arg, cx.st);
   if (e != hipSuccess) return e;
+  if (cx.check) {
+    if ((e = hipStreamSynchronize(cx.st)) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (t) {
     e = hipEventRecord(h->events[h->events_used].second, cx.st);
     if (e != hipSuccess) return e;
@@ -491,10 +501,15 @@ hipError_t enqueue_llama(StepCtx& cx, const void* x, int N, void* y) {
 
 int run_step(armt_handle* h, int sched, int l_lo, int l_hi, int par, int advance) {
   const bool timing = h->time_kernel >= 0;
-  if (!h->use_graphs || timing) {
-    StepCtx cx{h, h->stream, timing};
+  if (!h->use_graphs || timing || h->debug_sync) {
+    StepCtx cx{h, h->stream, timing, h->debug_sync};
+    h->last_kernel = -1;
     hipError_t e = enqueue_step(cx, l_lo, l_hi, par, advance);
-    return e == hipSuccess ? ARMT_OK : hip_fail(e, "kernel launch");
+    if (e == hipSuccess) return ARMT_OK;
+    if (h->debug_sync && h->last_kernel >= 0)
+      return fail(ARMT_E_HIP, "HIP error in kernel %d of the wave of layers %d..%d: %s", h->last_kernel, l_lo,
+                  l_hi, hipGetErrorString(e));
+    return hip_fail(e, "kernel launch");
   }
   auto key = std::make_tuple(sched, l_lo, l_hi, par, advance);
   auto it = h->graphs.find(key);
@@ -561,7 +576,7 @@ int forward(armt_handle* h, int sched, const void* x, int32_t S, int32_t t_last,
   return ARMT_OK;
 }
 
-// 32-row blocks per GEMM tile for one grouped launch of P problems with
+// 16-row blocks per GEMM tile for one grouped launch of P problems with
 // n_cols output columns per problem (cols_per_tile per workgroup).  Every
 // tile height gives bitwise identical results, so the choice is free: it
 // minimises rounds x (tile rows + a fixed per-tile cost), where a round is
@@ -614,8 +629,10 @@ namespace {
 // Common part of the two create calls: carve the workspace, upload the RoPE
 // table for positions 0..n-1 and zero the V^T padding.  Takes ownership of h
 // (deleted on failure).
-int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, const Layout& lo,
-                void* workspace, void* hip_stream, int n, armt_handle** out) {
+// Handle fields for a workspace at `workspace` laid out as `lo` (no
+// allocation, no device work).
+void set_fields(armt_handle* h, const armt_config* cfg, const armt_weights* w, const Layout& lo,
+                void* workspace, void* hip_stream, int n) {
   h->cfg = *cfg;
   h->w = *w;
   h->stream = (hipStream_t)hip_stream;
@@ -645,7 +662,11 @@ int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, c
   h->pden = (float*)(base + lo.pden);
   h->beta = (float*)(base + lo.beta);
   h->moff = (int*)(base + lo.moff);
+}
 
+int init_handle(armt_handle* h, const armt_config* cfg, const armt_weights* w, const Layout& lo,
+                void* workspace, void* hip_stream, int n, armt_handle** out) {
+  set_fields(h, cfg, w, lo, workspace, hip_stream, n);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e, "hipGetDevice"); }
   e = hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -829,7 +850,7 @@ void armt_destroy(armt_handle* h) {
   delete h;
 }
 
-const char* armt_last_error(void) { return g_last_error.c_str(); }
+const char* armt_last_error(void) { return g_last_error; }
 
 int armt_wave_schedule(int32_t n_layers, int32_t n_segments, int32_t* l_lo, int32_t* l_hi, int32_t cap,
                        int32_t* n_waves) {
@@ -849,6 +870,10 @@ int armt_set_option(armt_handle* h, int32_t option, int32_t value) {
   if (!h) return fail(ARMT_E_INVALID, "handle is NULL");
   switch (option) {
     case ARMT_OPT_GRAPHS: h->use_graphs = value != 0; return ARMT_OK;
+    case ARMT_OPT_DEBUG_SYNC:
+      if (value != 0 && value != 1) return fail(ARMT_E_INVALID, "debug sync must be 0 or 1 (got %d)", value);
+      h->debug_sync = value != 0;
+      return ARMT_OK;
     case ARMT_OPT_TIME_KERNEL:
       if (value < -1 || value >= ARMT_K_COUNT) return fail(ARMT_E_INVALID, "kernel id %d out of range", value);
       h->time_kernel = value;

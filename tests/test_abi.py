@@ -140,3 +140,4 @@ def test_batched_workspace_validation():
     out = ctypes.c_void_p(0)
     assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 0, 4096, 1 << 30, None, ctypes.byref(out)) == -1
     assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 2, None, 1 << 30, None, ctypes.byref(out)) == -3
+

@@ -159,6 +159,28 @@ def test_graphs_replay_and_direct_launch_agree():
 
 
 @pytest.mark.parametrize("cfg", [TINY, MID64], ids=lambda c: c.name)
+def test_debug_sync_forward_is_unchanged(cfg):
+    """With the debug option every kernel is launched directly and followed
+    by a stream synchronisation and an error check; the results are bitwise
+    those of the graph-replayed forward, in both schedules."""
+    inp = make_inputs(cfg)
+    model = build_model(inp)
+    x = to_device(inp.x, cfg)
+    ref = [t.clone() for t in model.forward(x, "diagonal")]
+    model.set_option(C.ARMT_OPT_DEBUG_SYNC, 1)
+    for sched in ("diagonal", "sequential"):
+        got = model.forward(x, sched)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), sched
+    with pytest.raises(C.ArmtError):
+        model.set_option(C.ARMT_OPT_DEBUG_SYNC, 2)
+    model.set_option(C.ARMT_OPT_DEBUG_SYNC, 0)
+    got = model.forward(x, "diagonal")
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [TINY, MID64], ids=lambda c: c.name)
 def test_split_resume_bitwise(cfg):
     inp = make_inputs(cfg)
     model = build_model(inp)
