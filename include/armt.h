@@ -159,6 +159,24 @@ int armt_forward_diagonal(armt_handle *h, const void *x, int32_t n_segments,
                           const float *A0, const float *z0, void *y,
                           float *A_out, float *z_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * diagonal forward of one sequence with no handle and no caller workspace.
+ * Its workspace is a static device array of the library (64 MiB per GPU,
+ * held until the process ends); models whose armt_workspace_size exceeds it
+ * return ARMT_E_WORKSPACE.  Arguments as armt_forward_diagonal (batch 1) plus
+ * the config and the stacked device weights (borrowed for the call) and the
+ * HIP stream (NULL = default stream) the kernels are launched on; results
+ * equal those of a handle's armt_forward_diagonal up to the rounding of the
+ * RoPE table (computed on the device here).  Launches kernels only: no
+ * allocation, no host synchronisation, no graphs.  Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (other streams, other
+ * threads) race; calls queued on one stream are ordered. */
+int armt_forward_diagonal_noalloc(const armt_config *cfg, const armt_weights *w,
+                                  const void *x, int32_t n_segments,
+                                  const float *A0, const float *z0, void *y,
+                                  float *A_out, float *z_out, void *hip_stream);
+
 /* Any sequence length ("dynamic" segmenting): n_tokens >= 1 tokens run as
  * S = ceil(n_tokens / T) segments, the last one t = n_tokens - (S - 1) T
  * tokens long (1..T); x and y span n_tokens rows, everything else as above.

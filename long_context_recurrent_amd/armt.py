@@ -16,7 +16,7 @@ __all__ = [
     "ArmtError", "armt_config", "armt_weights", "load_library", "library_path",
     "armt_workspace_size", "armt_create", "armt_workspace_size_batched", "armt_create_batched",
     "armt_forward_sequential",
-    "armt_forward_diagonal", "armt_forward_sequential_tokens", "armt_forward_diagonal_tokens", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
+    "armt_forward_diagonal", "armt_forward_diagonal_noalloc", "armt_forward_sequential_tokens", "armt_forward_diagonal_tokens", "armt_logits", "armt_llama_workspace_size", "armt_llama_create",
     "armt_llama_forward", "armt_backward_workspace_size", "armt_backward", "armt_destroy", "armt_last_error",
     "armt_wave_schedule", "armt_set_option", "armt_kernel_stats",
     "armt_debug_view", "declared_functions",
@@ -82,6 +82,8 @@ def load_library():
                                       ctypes.POINTER(P)]),
         "armt_forward_sequential": (I32, [P, P, I32, P, P, P, P, P]),
         "armt_forward_diagonal": (I32, [P, P, I32, P, P, P, P, P]),
+        "armt_forward_diagonal_noalloc": (I32, [ctypes.POINTER(armt_config), ctypes.POINTER(armt_weights), P, I32,
+                                                P, P, P, P, P, P]),
         "armt_forward_sequential_tokens": (I32, [P, P, ctypes.c_int64, P, P, P, P, P]),
         "armt_forward_diagonal_tokens": (I32, [P, P, ctypes.c_int64, P, P, P, P, P]),
         "armt_logits": (I32, [P, P, ctypes.c_int64, P, P, I32, P]),
@@ -175,6 +177,13 @@ def armt_forward_sequential(h, x, n_segments: int, A0, z0, y, A_out, z_out):
 def armt_forward_diagonal(h, x, n_segments: int, A0, z0, y, A_out, z_out):
     _check(load_library().armt_forward_diagonal(h, _ptr(x), n_segments, _ptr(A0), _ptr(z0), _ptr(y),
                                                 _ptr(A_out), _ptr(z_out)))
+
+
+def armt_forward_diagonal_noalloc(cfg: armt_config, w: armt_weights, x, n_segments: int, A0, z0, y, A_out, z_out,
+                                  stream=None):
+    _check(load_library().armt_forward_diagonal_noalloc(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), n_segments,
+                                                        _ptr(A0), _ptr(z0), _ptr(y), _ptr(A_out), _ptr(z_out),
+                                                        _stream(stream)))
 
 
 def armt_forward_sequential_tokens(h, x, n_tokens: int, A0, z0, y, A_out, z_out):

@@ -28,6 +28,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <new>
 #include <string>
@@ -1469,6 +1470,109 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
   if ((e = hipMemcpyAsync(dz0, cx.f(cx.lo.dz), z_count * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess)
     return hip_fail(e, "copy dz0");
   return ARMT_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Diagonal forward for callers that cannot allocate (graph capture, tight
+// serving loops): the workspace is a file-scope device array instead of a
+// caller buffer.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Largest workspace the static scratch holds (the tiny and small workloads
+// and mid-sized models; the 1B / 3B shapes need a caller workspace).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+
+// Each GPU the library runs on holds its own copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the array's name is only a host-side stand-in).
+void* g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_lock{0};
+
+int scratch_address(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return fail(ARMT_E_UNSUPPORTED, "device %d: too many devices", device);
+  while (g_scratch_lock.exchange(1, std::memory_order_acquire)) {
+  }
+  hipError_t e = hipSuccess;
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) g_scratch[device] = p;
+  }
+  *ptr = g_scratch[device];
+  g_scratch_lock.store(0, std::memory_order_release);
+  return e == hipSuccess ? ARMT_OK : hip_fail(e, "hipGetSymbolAddress(scratch)");
+}
+
+// RoPE table [n][hd/2](cos, sin) of the angles pos * theta^(-2i/hd), in
+// double precision as the host table of the workspace path.
+__global__ void rope_table_kernel(float* tab, int n, int hd, double theta) {
+  const int half = hd / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * half) return;
+  const int p = idx / half, i = idx % half;
+  const double ang = p * pow(theta, -2.0 * i / hd);
+  tab[2 * idx] = (float)cos(ang);
+  tab[2 * idx + 1] = (float)sin(ang);
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int armt_forward_diagonal_noalloc(const armt_config* cfg, const armt_weights* w, const void* x, int32_t n_segments,
+                                  const float* A0, const float* z0, void* y, float* A_out, float* z_out,
+                                  void* hip_stream) {
+  int rc = validate_config(cfg);
+  if (rc != ARMT_OK) return rc;
+  if (!w) return fail(ARMT_E_INVALID, "weights must not be NULL");
+  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn,
+                        w->g_mlp, w->w_mq, w->w_mk, w->w_mv, w->w_beta, w->mem_emb};
+  for (const void* p : ptrs)
+    if (!p) return fail(ARMT_E_INVALID, "every weight pointer must be non-NULL");
+  const Layout lo = make_layout(cfg, 1);
+  if (lo.total > kScratchBytes)
+    return fail(ARMT_E_WORKSPACE,
+                "this model needs %zu bytes of workspace; the static scratch of "
+                "armt_forward_diagonal_noalloc holds %zu: create a handle with a workspace instead",
+                lo.total, kScratchBytes);
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  if ((rc = scratch_address(device, &ws)) != ARMT_OK) return rc;
+  // a handle on the stack over the scratch: direct launches (no graphs)
+  armt_handle h;
+  h.batch = 1;
+  h.norm_rows = (int64_t)cfg->n_layers * (cfg->seg_len + cfg->n_mem);
+  set_fields(&h, cfg, w, lo, ws, hip_stream, cfg->seg_len + cfg->n_mem);
+  h.device = device;
+  h.use_graphs = false;
+  e = hipDeviceGetAttribute(&h.cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess || h.cus <= 0) return hip_fail(e, "hipDeviceGetAttribute");
+  // what the forward reads before writing: the RoPE table and the zero V^T
+  // padding (another call may have left other values in the scratch)
+  const int half = cfg->head_dim / 2, items = h.n * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((items + 255) / 256), dim3(256), 0, h.stream, h.rope, h.n,
+                     cfg->head_dim, (double)cfg->rope_theta);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "RoPE table");
+  if (h.bf16) {
+    const int64_t words = (int64_t)(lo.attn - lo.vt) / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, h.stream, (uint32_t*)h.vt, words);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "V^T padding");
+  }
+  return forward(&h, SCHED_DIAG, x, n_segments, cfg->seg_len, A0, z0, y, A_out, z_out);
 }
 
 }  // extern "C"

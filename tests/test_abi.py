@@ -141,3 +141,21 @@ def test_batched_workspace_validation():
     assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 0, 4096, 1 << 30, None, ctypes.byref(out)) == -1
     assert lib.armt_create_batched(ctypes.byref(cfg), ctypes.byref(w), 2, None, 1 << 30, None, ctypes.byref(out)) == -3
 
+
+def test_noalloc_forward_rejects_before_any_gpu_work():
+    """armt_forward_diagonal_noalloc validates its config and weights and
+    rejects a model whose workspace exceeds the static scratch, with a
+    message, before it touches the device."""
+    lib = A.load_library()
+    w = A.armt_weights(*([1024] * 12))
+    assert lib.armt_forward_diagonal_noalloc(None, ctypes.byref(w), 1, 1, None, None, 1, 1, 1, None) == -1
+    cfg = _cfg()
+    assert lib.armt_forward_diagonal_noalloc(ctypes.byref(cfg), None, 1, 1, None, None, 1, 1, 1, None) == -1
+    w2 = A.armt_weights(*([1024] * 11 + [0]))
+    assert lib.armt_forward_diagonal_noalloc(ctypes.byref(cfg), ctypes.byref(w2), 1, 1, None, None, 1, 1, 1,
+                                             None) == -1
+    big = _cfg(n_layers=16, d_model=2048, n_heads=32, n_kv_heads=8, head_dim=64, ffn_hidden=8192,
+               seg_len=1024, n_mem=16, dtype=A.ARMT_BF16)
+    assert A.armt_workspace_size(big) > 64 << 20
+    rc = lib.armt_forward_diagonal_noalloc(ctypes.byref(big), ctypes.byref(w), 1, 1, None, None, 1, 1, 1, None)
+    assert rc == -3 and "scratch" in A.armt_last_error()
