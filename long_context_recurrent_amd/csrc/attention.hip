@@ -25,6 +25,8 @@
 // at depth), and O is rounded to bf16 once at the end.  Tile rows keep their 16-byte chunks XOR-swizzled so the
 // fragment reads are free of bank conflicts.  Query blocks are launched
 // heaviest first.
+#include <type_traits>
+
 #include "armt_common.h"
 #include "armt_kernels.h"
 
@@ -34,6 +36,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Physical 16-byte chunk of logical chunk c in row r of a tile whose rows
 // hold CH chunks: the same logical chunk of 8 (and of 16) consecutive rows
@@ -133,21 +136,51 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   for (int ks = 0; ks < ES; ++ks)
     qf[ks] = *(const bf16x8*)(qkv + (int64_t)qc * a.ld_qkv + head * HD + 16 * ks + 8 * hh);
 
+  // Per-lane LDS byte offsets of this lane's K and V^T fragments inside a
+  // tile buffer; the buffer's own offset is a compile-time constant below
+  // (the tile loop is unrolled by NBUF), so every fragment read is a single
+  // ds_read with an immediate offset.
+  int koff[2][ES], voff[2][2][DB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < ES; ++ks) {
+      const int r = kb * 32 + r32;
+      koff[kb][ks] = r * (HD * 2) + swzc<CH>(r, 2 * ks + hh) * 16;
+    }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int r = db * 32 + r32;
+        const int c = 2 * (2 * kb + ks) + hh;    // logical chunk of the V^T row
+        voff[kb][ks][db] = K_BYTES + r * 128 + swzc<8>(r, c) * 16;
+      }
+
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float mrun = -INFINITY, lsum = 0.f;
+  // Running row statistics, in scores scaled to log2 units (s * sl2).  The
+  // subtracted maximum mb is raised only when some lane's maximum exceeds it
+  // by more than RESCALE_LOG2 (then O and the row sum are rescaled); until
+  // then the exponentials stay below 2^RESCALE_LOG2, well inside fp32 and
+  // bf16 range, and the final O / l is unchanged.
+  constexpr float RESCALE_LOG2 = 8.f;
+  float mb = -INFINITY, lsum0 = 0.f, lsum1 = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;   // scores in log2 units
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  for (int t = 0; t < ntile; ++t) {
+  auto tile = [&](int t, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     // tile t landed (this wave's loads; the barrier covers the others'),
     // and every wave is done with tile t - 1, whose buffer is refilled next
     __builtin_amdgcn_s_waitcnt(att_wait((NBUF - 2) * LOADS));
     att_barrier();
     issue(t + NBUF - 1);
-    if (t >= wtiles) continue;
-    const unsigned char* kt = smem + (t % NBUF) * TILE;
-    const unsigned char* vtile = kt + K_BYTES;
+    if (t >= wtiles) return;
+    const unsigned char* tb = smem + buf * TILE;
 
     f32x16 s[2];
 #pragma unroll
@@ -155,8 +188,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < ES; ++ks) {
-        const int r = kb * 32 + r32;
-        const bf16x8 kf = *(const bf16x8*)(kt + r * (HD * 2) + swzc<CH>(r, 2 * ks + hh) * 16);
+        const bf16x8 kf = *(const bf16x8*)(tb + koff[kb][ks]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
       }
     }
@@ -178,40 +210,44 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
     }
-    // running max in raw score units; p = 2^(s * sl2 - m * sl2) (sl2 > 0)
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float mnew = fmaxf(mrun, mloc);
-    // rescale the running sums only when some lane's maximum grew
-    if (__any(mnew > mrun)) {
-      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);
-      lsum *= alpha;
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * sl2;
+    if (__any(mloc > mb + RESCALE_LOG2)) {
+      const float mnew = fmaxf(mb, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(mb - mnew);   // 0 on the first tile
+      lsum0 *= alpha;
+      lsum1 *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      mb = mnew;
     }
-    const float mb = mnew * sl2;
-    mrun = mnew;
     // P as the second operand of O^T = V^T P^T: 16-key group G = 2kb + ks,
-    // slot j = element 8ks + j of block kb
+    // slot j = element 8ks + j of block kb; the row sum adds the bf16 P that
+    // enters the product (two products against (1, 1) per dot instruction)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         f32x8 pv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + j], sl2, -mb));
-          lsum += pv[j];
-        }
+        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + j], sl2, -mb));
         const bf16x8 ph = __builtin_convertvector(pv, bf16x8);
-        const int c = 2 * (2 * kb + ks) + hh;    // logical chunk of the V^T row
+        float& ls = ks ? lsum1 : lsum0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{ph[2 * j], ph[2 * j + 1]}, ones, ls, false);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int r = db * 32 + r32;
-          const bf16x8 vf = *(const bf16x8*)(vtile + r * 128 + swzc<8>(r, c) * 16);
+          const bf16x8 vf = *(const bf16x8*)(tb + voff[kb][ks][db]);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, o[db], 0, 0, 0);
         }
       }
+  };
+  for (int t0 = 0; t0 < ntile; t0 += NBUF) {
+    tile(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < ntile) tile(t0 + 1, std::integral_constant<int, 1>{});
+    if (NBUF > 2 && t0 + 2 < ntile) tile(t0 + 2, std::integral_constant<int, 2 % NBUF>{});
   }
+  float lsum = lsum0 + lsum1;
   __builtin_amdgcn_s_waitcnt(att_wait(0));
   lsum += __shfl_xor(lsum, 32, kWave);
   if (q < n) {

@@ -23,7 +23,11 @@ be compared against:
 * ``A_norm``: the Frobenius norm of every A_l.
 
 A JSON sidecar records the command, the SHA-256 of the oracle and input
-sources it ran, the host and the wall time.  Progress is checkpointed (under
+sources it ran, the host and the wall time.  ``--spread N`` adds ``spread``:
+for each of the first N segments, the relative L2 between the stored sketch
+and that of the same oracle run with a 3e-6 relative jitter before every
+rounding (an equally valid accumulation order) -- how closely any
+implementation that is not bitwise the oracle can be expected to agree.  Progress is checkpointed (under
 ``--ckpt``, default /tmp/armt_fullsize_ckpt) so an interrupted run resumes.
 """
 
@@ -282,9 +286,73 @@ def write_golden(path, S, segs, col, A, z, sketch, meta):
         f.write("\n")
 
 
+def self_spread(inputs, n_segments, eps=3e-6, seed=123, log=print):
+    """The oracle's own sensitivity to rounding order: the same oracle with
+    every stored value multiplied by (1 + eps * N(0, 1)) just before it is
+    rounded -- an equally valid order of the fp32 accumulations, eps about
+    the relative error of a long fp32 sum -- run from the zero state through
+    the first ``n_segments`` segments.  Returns each segment's output rows
+    (R(h[:T]) of the last layer); a GPU result cannot be expected to agree
+    with the float64 oracle more closely than this run does."""
+    import numpy as np
+
+    import oracle
+
+    o = oracle.Oracle(inputs)
+    rng = np.random.default_rng(seed)
+    R, Rs = o.R, o.Rs
+
+    def jitter(f):
+        def g(x):
+            x = np.asarray(x, dtype=np.float64)
+            return f(x * (1.0 + eps * rng.standard_normal(x.shape)))
+        return g
+
+    o.R, o.Rs = jitter(R), jitter(Rs)
+    A, z = o.initial_state()
+    T, L = inputs.cfg.seg_len, inputs.weights["w_qkv"].shape[0]
+    out = []
+    for s in range(n_segments):
+        t0 = time.time()
+        h = o.node_input(s)
+        for l in range(L):
+            h, A[l], z[l] = o.node(l, h, A[l], z[l])
+        out.append(R(h[:T]))
+        log(f"spread: segment {s} in {time.time() - t0:.0f}s", flush=True)
+    return out
+
+
+def add_spread(name, n_segments, out_dir):
+    """Store, in an existing golden file, the relative L2 between the
+    jittered oracle's sketch and the stored sketch for its first segments."""
+    import numpy as np
+    from armt_inputs import get_config, make_inputs, make_sketch
+    path = os.path.join(out_dir, f"fullsize_{name}.npz")
+    g = dict(np.load(path, allow_pickle=False))
+    cfg = get_config(name)
+    inp = make_inputs(cfg, n_segments=n_segments)
+    sk = make_sketch(cfg).astype(np.float64)
+    ys = self_spread(inp, n_segments)
+    spread = np.array([np.linalg.norm(y @ sk - g["sketch"][s]) / np.linalg.norm(g["sketch"][s])
+                       for s, y in enumerate(ys)])
+    g["spread"] = spread
+    np.savez_compressed(path, **g)
+    with open(path[:-4] + ".json") as f:
+        meta = json.load(f)
+    meta["spread"] = {"segments": n_segments, "eps": 3e-6, "seed": 123, "sketch_rel_l2": [float(v) for v in spread],
+                      "command": f"python tests/golden/make_fullsize.py {name} --spread {n_segments}"}
+    with open(path[:-4] + ".json", "w") as f:
+        json.dump(meta, f, indent=1)
+        f.write("\n")
+    print(f"[{name}] spread of the first {n_segments} segments: {np.array2string(spread, precision=4)}", flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("run", choices=sorted(RUNS))
+    ap.add_argument("run", choices=sorted(RUNS) + ["1b_s32", "1b_s128"])
+    ap.add_argument("--spread", type=int, default=0,
+                    help="instead: add the jittered oracle's spread over the first N segments to an "
+                         "existing golden file of this workload")
     ap.add_argument("--workers", type=int, default=4, help="worker processes (nodes of a wave in parallel)")
     ap.add_argument("--blas-threads", type=int, default=2, help="BLAS threads per worker")
     ap.add_argument("--ckpt", default="/tmp/armt_fullsize_ckpt")
@@ -293,6 +361,9 @@ def main(argv=None):
     for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = str(args.blas_threads)
     sys.path.insert(0, ROOT)
+    if args.spread:
+        add_spread(args.run, args.spread, args.out)
+        return
     from armt_inputs import get_config, make_inputs, make_sketch
 
     drawn, outputs = RUNS[args.run]
