@@ -23,11 +23,14 @@ be compared against:
 * ``A_norm``: the Frobenius norm of every A_l.
 
 A JSON sidecar records the command, the SHA-256 of the oracle and input
-sources it ran, the host and the wall time.  ``--spread N`` adds ``spread``:
-for each of the first N segments, the relative L2 between the stored sketch
-and that of the same oracle run with a 3e-6 relative jitter before every
-rounding (an equally valid accumulation order) -- how closely any
-implementation that is not bitwise the oracle can be expected to agree.  Progress is checkpointed (under
+sources it ran, the host and the wall time.  ``--spread-full`` reruns the
+workload with the same oracle under a 3e-6 relative jitter before every
+rounding (an equally valid accumulation order, seeded per node) and adds how
+far that run lands from the stored one -- per segment (``spread``) and per
+layer of the final state (``spread_A_rows``, ``spread_A_sketch``,
+``spread_z``): how closely any implementation that is not bitwise the oracle
+can be expected to agree.  (``--spread N`` does the same for the first N
+segments only, in one process.)  Progress is checkpointed (under
 ``--ckpt``, default /tmp/armt_fullsize_ckpt) so an interrupted run resumes.
 """
 
@@ -68,8 +71,37 @@ def source_digests() -> dict:
             for rel in ("oracle/armt_oracle.py", "armt_inputs/__init__.py")}
 
 
+JITTER_EPS = 3e-6
+JITTER_SEED = 123
+_JIT = None         # (R, Rs) of the oracle object before jitter wrappers, when jittering
+_JRNG = None        # random stream of the node being run (jitter mode)
+
+
+def _set_jitter(o):
+    """Wrap the oracle's two rounding functions so that every value is
+    multiplied by (1 + JITTER_EPS * N(0, 1)) just before it is rounded -- an
+    equally valid order of the fp32 accumulations.  The random stream is
+    reset per node (seeded by the node's (segment, layer)), so results do not
+    depend on which worker runs which node."""
+    global _JIT
+    import numpy as np
+    _JIT = (o.R, o.Rs)
+
+    def jitter(f):
+        def g(x):
+            x = np.asarray(x, dtype=np.float64)
+            return f(x * (1.0 + JITTER_EPS * _JRNG.standard_normal(x.shape)))
+        return g
+
+    o.R, o.Rs = jitter(o.R), jitter(o.Rs)
+
+
 def _node(job):
-    s, l, h, A, z = job
+    global _JRNG
+    s, l, h, A, z = job[:5]
+    if _JIT is not None:
+        import numpy as np
+        _JRNG = np.random.default_rng([JITTER_SEED, s, l])
     if h is None:
         h = _O.node_input(s)
     return _O.node(l, h, A, z)
@@ -103,7 +135,7 @@ def _share(inputs, release):
     return keep, (inputs.cfg, desc)
 
 
-def _attach(shared):
+def _attach(shared, jitter=False):
     """Worker initializer: rebuild the inputs over the shared arrays."""
     from multiprocessing import shared_memory
 
@@ -122,10 +154,12 @@ def _attach(shared):
     weights = {k[2:]: v for k, v in arrays.items() if k.startswith("w:")}
     _O = oracle.Oracle(ArmtInputs(cfg, arrays["x"], arrays["mem_emb"], weights,
                                   arrays["g_attn"], arrays["g_mlp"]))
+    if jitter:
+        _set_jitter(_O)
 
 
 def run_waves(inputs, workers: int, on_output, ckpt_path: str | None = None, n_segments=None,
-              snap_after=(), log=print, release=False):
+              snap_after=(), log=print, release=False, jitter=False):
     """Run the oracle's nodes wave by wave from the zero state; call
     ``on_output(s, y_s)`` with each segment's output rows y_s = R(h[:T]) of
     the last layer.  Returns the final (A, z) lists and a dict
@@ -141,9 +175,12 @@ def run_waves(inputs, workers: int, on_output, ckpt_path: str | None = None, n_s
 
     import oracle
 
-    global _O
+    global _O, _JIT
     cfg = inputs.cfg
     _O = oracle.Oracle(inputs)
+    _JIT = None
+    if jitter:
+        _set_jitter(_O)
     T = cfg.seg_len
     L = inputs.weights["w_qkv"].shape[0]
     S = n_segments or inputs.x.shape[0] // cfg.seg_len
@@ -167,7 +204,7 @@ def run_waves(inputs, workers: int, on_output, ckpt_path: str | None = None, n_s
         # spawned workers (a forked child of a process that has run torch's
         # or OpenBLAS's thread pools can deadlock) over shared input arrays
         shm, shared = _share(inputs, release)
-        pool = mp.get_context("spawn").Pool(workers, initializer=_attach, initargs=(shared,))
+        pool = mp.get_context("spawn").Pool(workers, initializer=_attach, initargs=(shared, jitter))
     t0 = time.time()
     try:
         for i, wave in enumerate(oracle.waves(L, S)):
@@ -180,7 +217,7 @@ def run_waves(inputs, workers: int, on_output, ckpt_path: str | None = None, n_s
                 if s + 1 in snaps:
                     snaps[s + 1][0][l], snaps[s + 1][1][l] = An, zn
                 if l == L - 1:
-                    on_output(s, _O.R(h[:T]))
+                    on_output(s, (_JIT[0] if _JIT else _O.R)(h[:T]))
                 else:
                     pending[(s, l)] = h
             done = i + 1
@@ -347,9 +384,66 @@ def add_spread(name, n_segments, out_dir):
     print(f"[{name}] spread of the first {n_segments} segments: {np.array2string(spread, precision=4)}", flush=True)
 
 
+def add_spread_full(run, workers, out_dir, ckpt_dir):
+    """Run a whole workload (or the 1B pair) again with the jittered oracle
+    and store, in each of its golden files, how far that run lands from the
+    stored one: per segment (sketch relative L2, ``spread``), and per layer
+    for the final state (``spread_A_rows``, ``spread_A_sketch``,
+    ``spread_z``)."""
+    import numpy as np
+    from armt_inputs import get_config, make_inputs, make_sketch
+    drawn, outputs = RUNS[run]
+    cfg = get_config(drawn)
+    S = cfg.n_segments
+    inp = make_inputs(cfg)
+    sk64 = make_sketch(cfg).astype(np.float64)
+    sketches = np.zeros((S, cfg.seg_len, sk64.shape[1]))
+
+    def on_output(s, y):
+        sketches[s] = y @ sk64
+
+    t0 = time.time()
+    A, z, snaps = run_waves(inp, workers, on_output, os.path.join(ckpt_dir, f"{run}_jitter.npz"),
+                            snap_after=[s_out for _, s_out in outputs if s_out < S], release=True, jitter=True)
+    wall = time.time() - t0
+
+    def rel(a, b):
+        return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+    for name, s_out in outputs:
+        path = os.path.join(out_dir, f"fullsize_{name}.npz")
+        g = dict(np.load(path, allow_pickle=False))
+        A_out, z_out = (A, z) if s_out == S else snaps[s_out]
+        Aj = np.stack(A_out).astype(np.float32).astype(np.float64)
+        zj = np.stack(z_out).astype(np.float32).astype(np.float64)
+        L = Aj.shape[0]
+        g["spread"] = np.array([rel(sketches[s], g["sketch"][s]) for s in range(s_out)])
+        g["spread_A_rows"] = np.array([rel(Aj[l, ::A_STRIDE], g["A_rows"][l]) for l in range(L)])
+        g["spread_A_sketch"] = np.array([rel(Aj[l].T @ sk64, g["A_sketch"][l]) for l in range(L)])
+        g["spread_z"] = np.array([rel(zj[l], g["z"][l]) for l in range(L)])
+        np.savez_compressed(path, **g)
+        with open(path[:-4] + ".json") as f:
+            meta = json.load(f)
+        meta["spread"] = {"eps": JITTER_EPS, "seed": JITTER_SEED, "segments": s_out,
+                          "max_segment": float(g["spread"].max()),
+                          "max_layer_A_rows": float(g["spread_A_rows"].max()),
+                          "max_layer_A_sketch": float(g["spread_A_sketch"].max()),
+                          "max_layer_z": float(g["spread_z"].max()),
+                          "command": f"python tests/golden/make_fullsize.py {run} --spread-full",
+                          "wall_s": round(wall, 1)}
+        with open(path[:-4] + ".json", "w") as f:
+            json.dump(meta, f, indent=1)
+            f.write("\n")
+        print(f"[{name}] spread: segments max {g['spread'].max():.3e}, A rows max {g['spread_A_rows'].max():.3e}, "
+              f"A sketch max {g['spread_A_sketch'].max():.3e}, z max {g['spread_z'].max():.3e}", flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("run", choices=sorted(RUNS) + ["1b_s32", "1b_s128"])
+    ap.add_argument("--spread-full", action="store_true",
+                    help="instead: rerun the whole workload with the jittered oracle and add its distance "
+                         "from the stored run (per segment and per layer) to the golden files")
     ap.add_argument("--spread", type=int, default=0,
                     help="instead: add the jittered oracle's spread over the first N segments to an "
                          "existing golden file of this workload")
@@ -363,6 +457,10 @@ def main(argv=None):
     sys.path.insert(0, ROOT)
     if args.spread:
         add_spread(args.run, args.spread, args.out)
+        return
+    if args.spread_full:
+        os.makedirs(args.ckpt, exist_ok=True)
+        add_spread_full(args.run, args.workers, args.out, args.ckpt)
         return
     from armt_inputs import get_config, make_inputs, make_sketch
 

@@ -19,11 +19,12 @@ and the input generator):
   report on Table 2).
 
 The bar is the stated one for bf16 workloads: relative L2 <= 2e-2 on the
-whole output, on the sampled rows and on each layer's state; each segment's
-sketch is held to the same bar, except that for the first segments after
-the zero state it may reach twice the oracle's own spread under a rounding-
-order jitter when that spread exceeds the bar (stored with the samples by
-make_fullsize.py --spread).  The schedule is a reordering of the same
+whole output, on the sampled rows and on the state of all layers together;
+each segment's output and each layer's state are held to the same bar, or
+to twice the oracle's own spread there where that exceeds the bar -- the
+distance between the stored oracle run and the same oracle rerun with a
+3e-6 relative jitter before every rounding, an equally valid accumulation
+order (make_fullsize.py --spread-full).  The schedule is a reordering of the same
 recurrence (Pith review of arXiv 2506.05229, "What carries the argument"),
 so the last segments carry the full depth of the recurrence.
 """
@@ -122,12 +123,24 @@ def test_fullsize_against_oracle(name):
     stride = An.shape[1] // a_rows.shape[1]
     _check("A every 16th row (all layers)", An[:, ::stride], a_rows, bar, res)
     _check("z (all layers)", zn, g["z"].astype(np.float64), bar, res)
+    # every layer's state: within the bar, or within twice the oracle's own
+    # spread for that layer where that exceeds the bar (stored spread_*)
     a_sk = np.einsum("ldk,dw->lkw", An, make_sketch(cfg).astype(np.float64))
-    worst = max(range(L), key=lambda l: rel_l2(a_sk[l], g["A_sketch"][l]))
-    for l in sorted({0, L // 2, L - 1, worst}):
-        _check(f"A[{l}]^T R_sk", a_sk[l], g["A_sketch"][l].astype(np.float64), bar, res)
-        _check(f"A[{l}] rows", An[l, ::stride], a_rows[l], bar, res)
-        _check(f"z[{l}]", zn[l], g["z"][l].astype(np.float64), bar, res)
+    per_layer = {
+        "A_rows": [rel_l2(An[l, ::stride], a_rows[l]) for l in range(L)],
+        "A_sketch": [rel_l2(a_sk[l], g["A_sketch"][l]) for l in range(L)],
+        "z": [rel_l2(zn[l], g["z"][l]) for l in range(L)],
+    }
+    for key, errs in per_layer.items():
+        sp = g[f"spread_{key}"] if f"spread_{key}" in g else np.zeros(L)
+        worst = int(np.argmax(errs))
+        res[f"{key} worst layer"] = float(errs[worst])
+        say(f"  {key} per layer: worst layer {worst} rel L2 {errs[worst]:.2e} (oracle spread there "
+            f"{sp[worst]:.2e}), median {float(np.median(errs)):.2e}")
+        for l in range(L):
+            bound = max(bar, 2.0 * float(sp[l]))
+            assert np.isfinite(errs[l]) and errs[l] <= bound, \
+                f"layer {l} {key}: rel L2 {errs[l]:.3e} > {bound:.3e} (oracle spread {sp[l]:.3e})"
     norm_err = np.abs(np.linalg.norm(An.reshape(L, -1), axis=1) / g["A_norm"] - 1.0)
     res["A norm max rel diff"] = float(norm_err.max())
     say(f"  Frobenius norm of A_l: max rel diff {norm_err.max():.2e}")
