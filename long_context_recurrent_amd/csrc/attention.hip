@@ -24,7 +24,7 @@
 // per 64-key tile, which made this kernel 30% slower for a 5% smaller error
 // at depth), and O is rounded to bf16 once at the end.  Tile rows keep their 16-byte chunks XOR-swizzled so the
 // fragment reads are free of bank conflicts.  Query blocks are launched
-// heaviest first.
+// heaviest first over the whole grid.
 #include <type_traits>
 
 #include "armt_common.h"
@@ -60,7 +60,7 @@ __device__ __forceinline__ void att_barrier() {
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = HD / 8;                  // 16-byte chunks per K row
   constexpr int K_BYTES = 64 * HD * 2;        // K tile: 64 keys x HD
   constexpr int V_BYTES = HD * 64 * 2;        // V^T tile: HD rows x 64 keys
@@ -73,11 +73,26 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TILE];
 
   const int n = a.n;
+  // Query blocks of 128 end at n, n - 128, ...: the partial block is the
+  // first one, whose queries see the fewest keys.  Workgroup order: the
+  // blocks heaviest first across the whole grid (longest-processing-time
+  // order, so no long block starts late), and within one block index the
+  // R = H/G query heads that share a key/value head dispatched to one XCD
+  // back to back (workgroup i runs on XCD i % 8), so they share its L2.
   const int nqb = (n + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int head = blockIdx.y;
-  const int layer = a.l0 + blockIdx.z;
-  const int kvh = head / (a.H / a.G);
+  const int R = a.H / a.G;
+  const int per_level = a.H * a.P;
+  const int level = (int)blockIdx.x / per_level;
+  int li = (int)blockIdx.x - level * per_level;
+  if (((a.G * a.P) & 7) == 0) {
+    const int x = li & 7, j = li >> 3;
+    li = (x + 8 * (j / R)) * R + j % R;
+  }
+  const int qb = nqb - 1 - level;
+  const int grp = li / R;                       // (node, key/value head)
+  const int kvh = grp % a.G;
+  const int head = kvh * R + li % R;
+  const int layer = a.l0 + grp / a.G;
   const bf16* qkv = (const bf16*)a.qkv + (int64_t)layer * a.qkv_stride;
   const bf16* vt = (const bf16*)a.vt + (int64_t)layer * a.vt_stride + (int64_t)kvh * HD * a.vt_ld;
   const int kcol = (a.H + kvh) * HD;
@@ -85,13 +100,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r32 = lane & 31, hh = lane >> 5;
-  const int q0w = qb * 128 + 32 * w;
-  const int q = q0w + r32;
-  const int qc = q < n ? q : n - 1;
-  const int q_end = (qb + 1) * 128 < n ? (qb + 1) * 128 : n;
+  const int q0w = n - 128 * (nqb - qb) + 32 * w;   // may be negative in the first block
+  const int q = q0w + r32;                         // < n; rows q < 0 do not exist
+  const int qc = q < 0 ? 0 : q;
+  const int q_end = n - 128 * (nqb - 1 - qb);      // > 0
   const int ntile = (q_end + 63) / 64;
-  const int wq_end = q0w + 32 < n ? q0w + 32 : n;
-  const int wtiles = wq_end > q0w ? (wq_end + 63) / 64 : 0;
+  const int wtiles = q0w + 32 > 0 ? (q0w + 32 + 63) / 64 : 0;
 
   // DMA slots: 1 KB block b = w + 4t of a tile; K blocks first, then V^T
   int roff[LOADS], coff[LOADS], dst[LOADS];
@@ -163,12 +177,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   // Running row statistics, in scores scaled to log2 units (s * sl2).  The
-  // subtracted maximum mb is raised only when some lane's maximum exceeds it
-  // by more than RESCALE_LOG2 (then O and the row sum are rescaled); until
-  // then the exponentials stay below 2^RESCALE_LOG2, well inside fp32 and
-  // bf16 range, and the final O / l is unchanged.
-  constexpr float RESCALE_LOG2 = 8.f;
-  float mb = -INFINITY, lsum0 = 0.f, lsum1 = 0.f;
+  // subtracted offset mb is not the running maximum: it is raised (to the
+  // maximum, with O and the row sum rescaled) only when a tile's exponentials
+  // push some lane's row sum past 2^ROWSUM_LOG2 -- which the first tile
+  // always does (mb starts at -1e30, so its exponentials are infinite) and
+  // later tiles do only when a score exceeds mb by tens of binades.  Until
+  // then every exponential lies in [0, 2^ROWSUM_LOG2], far inside fp32 and
+  // bf16 range; bf16 keeps the same relative precision at any magnitude and
+  // every row holds a term >= 1 after its first rescale, so O / l is
+  // unchanged.  No tile needs its row maximum, which is the bulk of the
+  // softmax's vector work besides the exponentials.
+  constexpr float ROWSUM_LIMIT = 4294967296.f;   // 2^32
+  float mb = -1e30f, lsum0 = 0.f, lsum1 = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
@@ -182,65 +202,117 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     if (t >= wtiles) return;
     const unsigned char* tb = smem + buf * TILE;
 
-    f32x16 s[2];
+    // S^T of the tile: every K fragment is read before the first product
+    // (one LDS round trip per tile, not one per product pair).  Element e of
+    // block kb: key t*64 + 32kb + 8(e/4) + 4hh + e%4, query q.  Only the
+    // wave's last one or two tiles reach past its first query and need the
+    // causal mask: key > q <=> 32kb + 8(e/4) + e%4 > q - 64t - 4hh (rows
+    // q < 0 of the first block mask every key).
+    auto scores = [&](f32x16* s) {
+      if constexpr (HD <= 64) {
+        bf16x8 kf[2][ES];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < ES; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(tb + koff[kb][ks]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
-      }
-    }
-    // element e of block kb: key t*64 + 32kb + 8(e/4) + 4hh + e%4, query q.
-    // Only tiles that reach past the wave's first query need the causal mask.
-    float mloc = -INFINITY;
-    if (t * 64 + 63 > q0w) {
+          for (int ks = 0; ks < ES; ++ks) kf[kb][ks] = *(const bf16x8*)(tb + koff[kb][ks]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = t * 64 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key > q) s[kb][e] = -INFINITY;
-          mloc = fmaxf(mloc, s[kb][e]);
+          for (int ks = 0; ks < ES; ++ks)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qf[ks], s[kb], 0, 0, 0);
         }
-    } else {
+        // keep the reads ahead of the products (the scheduler would
+        // otherwise pair each read with its product to save registers)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * ES, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * ES, 0);
+      } else {
+        // HD = 128: 16 fragments would not fit beside the accumulators
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < ES; ++ks) {
+            const bf16x8 kf = *(const bf16x8*)(tb + koff[kb][ks]);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+          }
+        }
+      }
+      if (t * 64 + 63 > q0w) {
+        const int thr = q - t * 64 - 4 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * kb + 8 * (e >> 2) + (e & 3) > thr) s[kb][e] = -INFINITY;
+      }
+    };
+    f32x16 s[2];
+    scores(s);
+    // HD <= 64: the V^T fragments are read now and land while the
+    // exponentials run (at HD = 128 each is read next to its product)
+    bf16x8 vf[2][2][DB];
+    if constexpr (HD <= 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vf[kb][ks][db] = *(const bf16x8*)(tb + voff[kb][ks][db]);
+      asm volatile("" ::: "memory");
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * sl2;
-    if (__any(mloc > mb + RESCALE_LOG2)) {
+    // P = 2^(s sl2 - mb) in bf16, as the second operand of O^T = V^T P^T:
+    // 16-key group G = 2kb + ks, slot j = element 8ks + j of block kb.  The
+    // row sum adds the bf16 P that enters the product (two products against
+    // (1, 1) per dot instruction).
+    bf16x8 ph[2][2];
+    auto exps = [&](const f32x16* s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          f32x8 pv;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + j], sl2, -mb));
+          ph[kb][ks] = __builtin_convertvector(pv, bf16x8);
+          float& ls = ks ? lsum1 : lsum0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{ph[kb][ks][2 * j], ph[kb][ks][2 * j + 1]}, ones, ls, false);
+        }
+    };
+    const float l0 = lsum0, l1 = lsum1;
+    exps(s);
+    // the negated test also catches an infinite or NaN sum
+    // (rare: the scores are recomputed rather than kept live through the
+    // exponentials)
+    if (__any(!(lsum0 + lsum1 <= ROWSUM_LIMIT))) {
+      f32x16 s2[2];
+      scores(s2);
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s2[kb][e]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * sl2;
       const float mnew = fmaxf(mb, mloc);
       const float alpha = __builtin_amdgcn_exp2f(mb - mnew);   // 0 on the first tile
-      lsum0 *= alpha;
-      lsum1 *= alpha;
+      lsum0 = l0 * alpha;
+      lsum1 = l1 * alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       mb = mnew;
+      exps(s2);
     }
-    // P as the second operand of O^T = V^T P^T: 16-key group G = 2kb + ks,
-    // slot j = element 8ks + j of block kb; the row sum adds the bf16 P that
-    // enters the product (two products against (1, 1) per dot instruction)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f32x8 pv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + j], sl2, -mb));
-        const bf16x8 ph = __builtin_convertvector(pv, bf16x8);
-        float& ls = ks ? lsum1 : lsum0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{ph[2 * j], ph[2 * j + 1]}, ones, ls, false);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 vf = *(const bf16x8*)(tb + voff[kb][ks][db]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, o[db], 0, 0, 0);
+          if constexpr (HD > 64) vf[kb][ks][db] = *(const bf16x8*)(tb + voff[kb][ks][db]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][ks][db], ph[kb][ks], o[db], 0, 0, 0);
         }
-      }
   };
   for (int t0 = 0; t0 < ntile; t0 += NBUF) {
     tile(t0, std::integral_constant<int, 0>{});
@@ -250,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   float lsum = lsum0 + lsum1;
   __builtin_amdgcn_s_waitcnt(att_wait(0));
   lsum += __shfl_xor(lsum, 32, kWave);
-  if (q < n) {
+  if (q >= 0) {
     const float inv = 1.f / lsum;
     bf16* out = (bf16*)a.out + (int64_t)layer * a.out_stride + (int64_t)q * a.ld_out + head * HD;
 #pragma unroll
@@ -313,7 +385,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, bool use_bf16, hipStream_t st) {
   if (a.P <= 0 || a.n <= 0) return hipErrorInvalidValue;
   if (use_bf16) {
-    dim3 grid((a.n + 127) / 128, a.H, a.P);
+    dim3 grid(((a.n + 127) / 128) * a.H * a.P);
     switch (a.hd) {
       case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a); break;
       case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a); break;
