@@ -19,12 +19,13 @@ and the input generator):
   report on Table 2).
 
 The bar is the stated one for bf16 workloads: relative L2 <= 2e-2 on the
-whole output, on the sampled rows and on the state of all layers together;
-each segment's output and each layer's state are held to the same bar, or
-to twice the oracle's own spread there where that exceeds the bar -- the
-distance between the stored oracle run and the same oracle rerun with a
-3e-6 relative jitter before every rounding, an equally valid accumulation
-order (make_fullsize.py --spread-full).  The schedule is a reordering of the same
+sampled rows, on every segment's output sketch, on all segments together and
+on the state of every layer and of all layers together -- or twice the
+oracle's own spread there where that exceeds the bar: the distance between
+the stored oracle run and the same oracle rerun with a 3e-6 relative jitter
+before every rounding, an equally valid accumulation order
+(make_fullsize.py --spread-full; pooled over segments or layers for the
+aggregate checks).  The schedule is a reordering of the same
 recurrence (Pith review of arXiv 2506.05229, "What carries the argument"),
 so the last segments carry the full depth of the recurrence.
 """
@@ -62,9 +63,17 @@ def _bits_to_f64(b):
 def _check(name, got, ref, bar, results):
     e = rel_l2(got, ref)
     results[name] = e
-    say(f"  {name}: rel L2 {e:.2e}")
+    say(f"  {name}: rel L2 {e:.2e} (bound {bar:.2e})")
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert e <= bar, f"{name}: rel L2 {e:.3e} > {bar}"
+
+
+def _pooled_spread(spreads, refs):
+    """The oracle's spread over several parts together (relative L2 of the
+    concatenation), from each part's relative spread and its reference."""
+    num = sum((float(sp) * np.linalg.norm(r)) ** 2 for sp, r in zip(spreads, refs))
+    den = sum(np.linalg.norm(r) ** 2 for r in refs)
+    return float(np.sqrt(num / den))
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
@@ -114,15 +123,25 @@ def test_fullsize_against_oracle(name):
     for s_ in range(S):
         bound = max(bar, 2.0 * spread[s_]) if s_ < len(spread) else bar
         assert per_seg[s_] <= bound, f"segment {s_}: sketch rel L2 {per_seg[s_]:.3e} > {bound:.3e}"
-    _check("sketch of all segments", ysk, ref_sk, bar, res)
+    # all segments together: the bar, or twice the oracle's pooled spread
+    # where the spread of every segment is stored
+    agg = bar
+    if len(spread) == S:
+        agg = max(bar, 2.0 * _pooled_spread(spread, ref_sk))
+    _check("sketch of all segments", ysk, ref_sk, agg, res)
     del ysk
 
     # final memory state of every layer
     An, zn = to_np(A), to_np(z)
     a_rows = g["A_rows"].astype(np.float64)
     stride = An.shape[1] // a_rows.shape[1]
-    _check("A every 16th row (all layers)", An[:, ::stride], a_rows, bar, res)
-    _check("z (all layers)", zn, g["z"].astype(np.float64), bar, res)
+    z_ref = g["z"].astype(np.float64)
+    a_bound, z_bound = bar, bar
+    if "spread_A_rows" in g:
+        a_bound = max(bar, 2.0 * _pooled_spread(g["spread_A_rows"], a_rows))
+        z_bound = max(bar, 2.0 * _pooled_spread(g["spread_z"], z_ref))
+    _check("A every 16th row (all layers)", An[:, ::stride], a_rows, a_bound, res)
+    _check("z (all layers)", zn, z_ref, z_bound, res)
     # every layer's state: within the bar, or within twice the oracle's own
     # spread for that layer where that exceeds the bar (stored spread_*)
     a_sk = np.einsum("ldk,dw->lkw", An, make_sketch(cfg).astype(np.float64))
@@ -141,10 +160,15 @@ def test_fullsize_against_oracle(name):
             bound = max(bar, 2.0 * float(sp[l]))
             assert np.isfinite(errs[l]) and errs[l] <= bound, \
                 f"layer {l} {key}: rel L2 {errs[l]:.3e} > {bound:.3e} (oracle spread {sp[l]:.3e})"
+    # the Frobenius norm moves by at most the relative L2 of the whole state,
+    # whose oracle spread the sampled rows' spread stands for
     norm_err = np.abs(np.linalg.norm(An.reshape(L, -1), axis=1) / g["A_norm"] - 1.0)
     res["A norm max rel diff"] = float(norm_err.max())
-    say(f"  Frobenius norm of A_l: max rel diff {norm_err.max():.2e}")
-    assert norm_err.max() <= bar
+    say(f"  Frobenius norm of A_l: max rel diff {norm_err.max():.2e} (layer {int(norm_err.argmax())})")
+    sp_rows = g["spread_A_rows"] if "spread_A_rows" in g else np.zeros(L)
+    for l in range(L):
+        bound = max(bar, 2.0 * float(sp_rows[l]))
+        assert norm_err[l] <= bound, f"layer {l}: Frobenius norm rel diff {norm_err[l]:.3e} > {bound:.3e}"
 
     if name == "1b_s32":
         # logits of the last segment's sampled rows, end to end
