@@ -297,7 +297,7 @@ def write_pmc_record(args):
     d = args.pmc_record
     out = {"workload": args.workload, "kernels": {}, "calibration": {"copy_bytes": 64 * 1024 * 1024 * 4}}
     sums = {}
-    passes = sorted(p for p in os.listdir(d) if p.startswith("pmc_"))
+    passes = sorted(p for p in os.listdir(d) if p.startswith("pmc_") and os.path.isdir(os.path.join(d, p)))
     for p in passes:
         with open(os.path.join(d, p, "run_counter_collection.csv"), newline="") as f:
             rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
@@ -405,6 +405,20 @@ def pmc_markdown(workload):
         fl = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512 / 1e9
         out.append(f"| {k} | {v['dispatches']} | {v.get('MfmaUtil', 0):.1f}% | {v.get('VALUBusy', 0):.1f}% | "
                    f"{v.get('LDSBankConflict', 0):.1f}% | {fl:.1f} | {rd:.1f} | {wr:.1f} | {rd + wr:.1f} |")
+    # where the waves' resident cycles go (SQ_WAVE_CYCLES split into issuing,
+    # waiting on a counter or barrier, and ready but not issued) and the mean
+    # occupancy, when those passes are in the record
+    if any("SQ_WAIT_INST_ANY" in v for v in rec["kernels"].values()):
+        out += ["", "| kernel | waves / dispatch | mean occupancy (waves per CU) | issuing | waiting on a counter "
+                "or barrier | ready, not issued |", "|:--|--:|--:|--:|--:|--:|"]
+        for k in KERNEL_SOURCES:
+            v = rec["kernels"].get(k)
+            if not v or "SQ_WAIT_INST_ANY" not in v or not v.get("SQ_WAVE_CYCLES"):
+                continue
+            wc = v["SQ_WAVE_CYCLES"]
+            out.append(f"| {k} | {v.get('SQ_WAVES', 0):.0f} | {v.get('MeanOccupancyPerCU', 0):.1f} | "
+                       f"{100 * v['SQ_ACTIVE_INST_ANY'] / wc:.0f}% | {100 * v['SQ_WAIT_ANY'] / wc:.0f}% | "
+                       f"{100 * v['SQ_WAIT_INST_ANY'] / wc:.0f}% |")
     return "\n".join(out)
 
 
