@@ -48,6 +48,19 @@ __device__ __forceinline__ int swzc(int r, int c) {
   return c ^ (r & 15);
 }
 
+// buffer resource flags for raw (unswizzled, stride 0) buffer loads
+constexpr int kRawBuffer = 0x00020000;
+
+// One 16-byte-per-lane DMA of a wave into LDS (lane i's bytes at lds + 16 i)
+// through a raw buffer resource [base, base + bytes): reads past the end
+// return zero.  (Kept out of the kernels' lambdas: a buffer resource built
+// inside a lambda of a kernel template keeps the host compiler from emitting
+// the kernel's launch stub.)
+__device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, unsigned char* lds, int voffset) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRawBuffer);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 // s_waitcnt immediate: vmcnt <= n, lgkmcnt = 0, expcnt free
 __host__ __device__ constexpr int att_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
@@ -107,38 +120,35 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
   const int ntile = (q_end + 63) / 64;
   const int wtiles = q0w + 32 > 0 ? (q0w + 32 + 63) / 64 : 0;
 
-  // DMA slots: 1 KB block b = w + 4t of a tile; K blocks first, then V^T
-  int roff[LOADS], coff[LOADS], dst[LOADS];
+  // DMA slots: 1 KB block b = w + 4i of a tile (K blocks first, then V^T);
+  // byte offset of this lane's 16 bytes from the tile's first key row / V^T
+  // column.  The loads are buffer loads whose resource starts at the tile
+  // (key rows past n read as zero: they are masked anyway), so a tile's
+  // addresses cost scalar work only.
+  int voffs[LOADS], dst[LOADS];
 #pragma unroll
-  for (int t = 0; t < LOADS; ++t) {
-    const int b = w + 4 * t;
-    dst[t] = b * 1024;
+  for (int i = 0; i < LOADS; ++i) {
+    const int b = w + 4 * i;
+    dst[i] = b * 1024;
     if (b < K_BLOCKS) {
-      const int r = b * KROWS + lane / CH;           // key row in the tile
-      roff[t] = r;
-      coff[t] = kcol + swzc<CH>(r, lane % CH) * 8;
+      const int r = b * KROWS + lane / CH;             // key row in the tile
+      voffs[i] = 2 * (r * a.ld_qkv + kcol + swzc<CH>(r, lane % CH) * 8);
     } else {
       const int dim = (b - K_BLOCKS) * 8 + lane / 8;   // V^T row
-      roff[t] = dim;
-      coff[t] = swzc<8>(dim, lane % 8) * 8;
+      voffs[i] = 2 * (dim * a.vt_ld + swzc<8>(dim, lane % 8) * 8);
     }
   }
+  const int k_bytes = n * a.ld_qkv * 2;   // the node's key rows 0..n-1
+  const int v_bytes = HD * a.vt_ld * 2;
   auto issue = [&](int t) {
-    const int tt = t < ntile ? t : ntile - 1;
+    const int tt = t < ntile ? t : ntile - 1;   // past the end: a harmless re-fetch
     unsigned char* st = smem + (t % NBUF) * TILE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int b = w + 4 * i;
-      const bf16* src;
-      if (b < K_BLOCKS) {
-        int row = tt * 64 + roff[i];
-        row = row < n ? row : n - 1;
-        src = qkv + (int64_t)row * a.ld_qkv + coff[i];
-      } else {
-        src = vt + (int64_t)roff[i] * a.vt_ld + tt * 64 + coff[i];
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(st + dst[i]),
-                                       16, 0, 0);
+      if (w + 4 * i < K_BLOCKS)
+        buffer_to_lds(qkv + (int64_t)tt * 64 * a.ld_qkv, k_bytes - tt * 64 * a.ld_qkv * 2, st + dst[i], voffs[i]);
+      else
+        buffer_to_lds(vt + tt * 64, v_bytes - tt * 128, st + dst[i], voffs[i]);
     }
   };
 
@@ -385,6 +395,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, bool use_bf16, hipStream_t st) {
   if (a.P <= 0 || a.n <= 0) return hipErrorInvalidValue;
   if (use_bf16) {
+    // the tile loads address a node's keys and V^T with 32-bit buffer offsets
+    if ((int64_t)a.n * a.ld_qkv * 2 > INT32_MAX || (int64_t)a.hd * a.vt_ld * 2 > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid(((a.n + 127) / 128) * a.H * a.P);
     switch (a.hd) {
       case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a); break;
