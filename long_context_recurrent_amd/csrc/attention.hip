@@ -257,8 +257,12 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
             if (32 * kb + 8 * (e >> 2) + (e & 3) > thr) s[kb][e] = -INFINITY;
       }
     };
+    // The first tile always raises the softmax offset (it starts at -1e30):
+    // at hd <= 64 its scores are computed once, on the raising path below
+    // (at hd 128 the extra path costs more registers than it saves).
+    const bool first = HD <= 64 && t == 0;
     f32x16 s[2];
-    scores(s);
+    if (!first) scores(s);
     // HD <= 64: the V^T fragments are read now and land while the
     // exponentials run (at HD = 128 each is read next to its product)
     bf16x8 vf[2][2][DB];
@@ -292,11 +296,15 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
         }
     };
     const float l0 = lsum0, l1 = lsum1;
-    exps(s);
-    // the negated test also catches an infinite or NaN sum
-    // (rare: the scores are recomputed rather than kept live through the
-    // exponentials)
-    if (__any(!(lsum0 + lsum1 <= ROWSUM_LIMIT))) {
+    bool raise = first;
+    if (!first) {
+      exps(s);
+      // the negated test also catches an infinite or NaN sum
+      raise = __any(!(lsum0 + lsum1 <= ROWSUM_LIMIT));
+    }
+    // (rare after the first tile: the scores are recomputed rather than kept
+    // live through the exponentials)
+    if (raise) {
       f32x16 s2[2];
       scores(s2);
       float mloc = -INFINITY;
