@@ -111,6 +111,18 @@ def test_golden_file_matches_sources_and_shapes(name):
         assert np.all(np.isfinite(g[k])), k
     # z_l is a sum of phi-keys (phi > 0): every entry positive and growing with S
     assert np.all(g["z"] > 0)
+    # the oracle's own spread, where stored: one value per segment / layer,
+    # finite and non-negative, with the jitter that produced it recorded
+    if "spread" in g:
+        assert g["spread"].ndim == 1 and 1 <= len(g["spread"]) <= S
+        for k, n in (("spread", None), ("spread_A_rows", L), ("spread_A_sketch", L), ("spread_z", L)):
+            if k in g:
+                v = g[k]
+                assert n is None or v.shape == (n,), k
+                assert np.all(np.isfinite(v)) and np.all(v >= 0), k
+        assert meta["spread"]["eps"] == mf.JITTER_EPS and meta["spread"]["seed"] == mf.JITTER_SEED
+        if g["spread"].shape == (S,):
+            assert np.isclose(g["spread"].max(), meta["spread"]["max_segment"])
     # sampled rows agree with the sketch of the same segment
     sk = make_sketch(cfg).astype(np.float64)
     rows = (g["rows"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
