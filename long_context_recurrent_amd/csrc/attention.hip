@@ -8,7 +8,7 @@
 // bf16 path (flash-style, CDNA4 MFMA).  Workgroup = (128-query block, query
 // head, node); each of its 4 waves owns 32 queries.  Key tiles of 64 rows
 // and the matching V^T tiles (V is stored transposed by the QKV GEMM) stream
-// into LDS through global->LDS DMA loads, several tiles ahead, and are shared
+// into LDS through buffer->LDS DMA loads, two tiles ahead, and are shared
 // by the 4 waves.  Both products run on v_mfma_f32_32x32x16_bf16:
 //  * S^T = K Q^T, so lane (r32, h) holds 16 keys of query r32 per 32-key
 //    block and the online-softmax statistics are per lane (one exchange with
@@ -22,9 +22,10 @@
 // rounded to bf16 (the usual flash-attention practice; a bf16 hi + lo pair
 // would keep P exact at the cost of 8 more MFMAs and 64 more VALU operations
 // per 64-key tile, which made this kernel 30% slower for a 5% smaller error
-// at depth), and O is rounded to bf16 once at the end.  Tile rows keep their 16-byte chunks XOR-swizzled so the
-// fragment reads are free of bank conflicts.  Query blocks are launched
-// heaviest first over the whole grid.
+// at depth), and O is rounded to bf16 once at the end.  Tile rows keep their
+// 16-byte chunks XOR-swizzled so the fragment reads are free of bank
+// conflicts.  Query blocks end at n (the partial block is the first) and are
+// launched heaviest first over the whole grid.
 #include <type_traits>
 
 #include "armt_common.h"
