@@ -226,7 +226,9 @@ int armt_logits(armt_handle *h, const void *y, int64_t rows, const void *g_final
  * geometry, dtype, rms_eps and rope_theta; seg_len, n_mem, d_key and mem_eps
  * are ignored.  Constraints: head_dim in {32, 64, 128}; d_model and
  * ffn_hidden multiples of 64, d_model <= 4096; 1 <= max_tokens <= 262144
- * (ARMT_BF16) or 4096 (ARMT_F32).
+ * (ARMT_BF16, with max_tokens * (n_heads + 2 n_kv_heads) * head_dim * 2
+ * bytes of Q, K, V below 2^31) or 4096 (ARMT_F32); ARMT_E_UNSUPPORTED
+ * otherwise.
  * armt_llama_workspace_size: bytes of workspace for up to max_tokens
  * positions (host call).  armt_llama_create: as armt_create, but only
  * w_qkv, w_o, w_gate, w_up, w_down, g_attn and g_mlp are used (borrowed);

@@ -145,6 +145,10 @@ int validate_llama(const armt_config* c, int64_t max_tokens) {
   if (c->d_model % 64 || c->ffn_hidden % 64 || c->d_model > 4096)
     return fail(ARMT_E_UNSUPPORTED, "d_model and ffn_hidden must be multiples of 64, d_model <= 4096");
   if (c->dtype == ARMT_BF16 && max_tokens > (1 << 18)) return fail(ARMT_E_UNSUPPORTED, "bf16: max_tokens must be <= 262144");
+  // the bf16 attention addresses one sequence's keys with 32-bit offsets
+  const int64_t qkv_bytes = (int64_t)max_tokens * (c->n_heads + 2 * c->n_kv_heads) * c->head_dim * 2;
+  if (c->dtype == ARMT_BF16 && qkv_bytes > INT32_MAX)
+    return fail(ARMT_E_UNSUPPORTED, "bf16: max_tokens * (n_heads + 2 n_kv_heads) * head_dim * 2 must be < 2^31");
   if (c->dtype == ARMT_F32 && max_tokens > 4096) return fail(ARMT_E_UNSUPPORTED, "fp32: max_tokens must be <= 4096");
   return ARMT_OK;
 }

@@ -109,6 +109,8 @@ def test_full_attention_comparator_validation():
         (dict(), 0, -1), (dict(n_layers=0), 64, -1), (dict(d_model=96), 64, -1),
         (dict(head_dim=16, n_heads=4), 64, -2), (dict(), 4097, -2),
         (bf, (1 << 18) + 1, -2), (dict(d_model=8192, n_heads=64, head_dim=128), 64, -2),
+        # keys of one sequence beyond 32-bit offsets: 2^18 tokens x 96 heads x 64 x 2 B
+        (dict(bf, d_model=2048, n_heads=32, n_kv_heads=32), 1 << 18, -2),
     ]
     for kw, nt, code in cases:
         with pytest.raises(A.ArmtError) as e:
