@@ -240,18 +240,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       fa[i] = *(const bf16x8*)(st + r * ROWB + swz(r, kc) * 16);
     }
   };
-  // The first stage's products start from zero (an explicit zero-initialised
-  // accumulator makes the register allocator rotate the accumulators through
-  // copies on every trip of the K loop).
-  auto mfma_all = [&](const bf16x8* fa, const bf16x8* fb, auto first) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], decltype(first)::value ? f32x4{} : acc[i][j],
-                                                            0, 0, 0);
-  };
-
   // Wait until this wave's loads of the oldest stage in flight landed (the
   // NS - 2 younger stages may still be in flight).
   auto wait_stage = [&]() {
@@ -267,25 +255,41 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   wait_stage();
   lds_barrier();
   read_frags(0, fa0, fb0);
-  // One pipeline step: refill the stage freed two steps ago, wait until this
-  // wave's loads of stage kt+1 landed (the wait also drains this wave's LDS
-  // reads, so nobody refills a stage another wave still reads), barrier, read
-  // stage kt+1's fragments into the other register set, and multiply the
-  // fragments of stage kt already in registers.  After the last step the
-  // fragments read belong to a re-fetched stage and are never used; KT is even
-  // because K is a multiple of 64.
+  // One pipeline step: multiply part of the fragments of stage kt already in
+  // registers, refill the stage freed two steps ago, wait until this wave's
+  // loads of stage kt+1 landed (the wait also drains this wave's LDS reads,
+  // so nobody refills a stage another wave still reads), barrier, read stage
+  // kt+1's fragments into the other register set, and multiply the rest of
+  // stage kt.  After the last step the fragments read belong to a re-fetched
+  // stage and are never used; KT is even because K is a multiple of 64.
+  // The first H row blocks' products of a step go out before the refill,
+  // the wait and the barrier, so the matrix core has work while the waves
+  // meet; the rest interleave with the next stage's fragment reads.  (Best
+  // split measured per GEMM: a quarter of the rows for gate/up and QKV,
+  // half for the residual GEMMs, whose down projection runs the longest
+  // K loop.)
+  constexpr int H = (EPI == EPI_RESID) ? RB / 2 : RB / 4;
+  // Products of row blocks I0 .. I1-1.  The first stage's products start
+  // from zero (an explicit zero-initialised accumulator makes the register
+  // allocator rotate the accumulators through copies on every trip of the K
+  // loop).
+  auto mfma_rows = [&](const bf16x8* fa, const bf16x8* fb, auto first, auto I0, auto I1) {
+#pragma unroll
+    for (int i = decltype(I0)::value; i < decltype(I1)::value; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], decltype(first)::value ? f32x4{} : acc[i][j],
+                                                            0, 0, 0);
+  };
   auto step = [&](int kt, const bf16x8* fa_cur, const bf16x8* fb_cur, bf16x8* fa_nxt, bf16x8* fb_nxt,
                   auto first) {
+    mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
     issue(kt + NS - 1);
     wait_stage();
     lds_barrier();
     read_frags(kt + 1, fa_nxt, fb_nxt);
-    mfma_all(fa_cur, fb_cur, first);
-    // Interleave the reads with the MFMAs (one read, then a few MFMAs) so
-    // the LDS and the matrix core work side by side; left alone, the
-    // scheduler sinks each read next to the MFMA of the following step that
-    // uses it.
-    constexpr int NREAD = RB + 4, NMFMA = 4 * RB;
+    mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, H>{}, std::integral_constant<int, RB>{});
+    constexpr int NREAD = RB + 4, NMFMA = 4 * (RB - H);
     constexpr int PER = NMFMA / NREAD;
 #pragma unroll
     for (int i = 0; i < NREAD; ++i) {
