@@ -125,9 +125,21 @@ __device__ __forceinline__ int xcd_tile(int id, int total) {
   return x * q + (x < r ? x : r) + j;
 }
 
+// Raw buffer resource over [p, p + bytes) for wave-uniform p and bytes.  The
+// parts go through readfirstlane so the compiler keeps the resource in
+// scalar registers: a resource it cannot prove uniform wraps every buffer
+// access in a loop over the distinct values in the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kRawBuffer);
+}
+
 }  // namespace
 
-template <int RB, int EPI>
+template <int RB, int EPI, bool TAIL>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = 16 * RB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
@@ -164,57 +176,56 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
       (EPI == EPI_SWIGLU) ? (const bf16*)g.B2 + (int64_t)layer * g.b_stride : B;
 
   // ---- direct global -> LDS loads.  A stage holds INSTR blocks of 16 tile
-  // rows (A rows, then B rows), each filled by 1 KB of wave loads in which
-  // lane L brings tile row 16q + L/4, physical chunk L%4 (= logical chunk
-  // swz(row, L%4)); the LDS address of a lane's 16 bytes follows from its
-  // lane number, so a load with some lanes off fills only their part.
-  // Wave w issues the whole blocks q = w, w + 4, ... below INSTR - EXTRA
-  // (EXTRA = INSTR % 4).  The last EXTRA blocks: one block -> each wave
-  // loads a quarter of it (lanes 16w .. 16w+15); two -> each wave half of
-  // one; three -> waves 0..2 one whole block each and wave 3 none (split
-  // three ways the extra instructions cost more than the imbalance).  The
-  // number of loads is fixed per wave, so its vmcnt waits are constants.
+  // rows (A rows, then B rows; block q at byte 1024 q), each filled by 1 KB
+  // of wave loads in which lane L brings tile row 16q + L/4, physical chunk
+  // L%4 (= logical chunk swz(row, L%4)).  Wave w issues the whole blocks
+  // q = w, w + 4, ... below INSTR - EXTRA (EXTRA = INSTR % 4).  The last
+  // EXTRA blocks are 64 * EXTRA 16-byte slots, split evenly: wave w brings
+  // slots 16 EXTRA w + l with its lanes l < 16 EXTRA (a quarter, half or
+  // three quarters of a wave load), written from LDS byte
+  // 1024 (INSTR - EXTRA) + 256 EXTRA w on.  Every wave issues the same
+  // number of loads per stage, so its vmcnt waits are constants.
   constexpr int EXTRA = INSTR % 4;
   constexpr int NFULL = (INSTR - EXTRA) / 4;
-  constexpr int NLOAD = NFULL + (EXTRA ? 1 : 0);       // loads per wave per stage (at most)
+  constexpr int NLOAD = NFULL + (EXTRA ? 1 : 0);       // loads per wave per stage
   const bf16* src[NLOAD];
   int dst[NLOAD];
 #pragma unroll
   for (int t = 0; t < NLOAD; ++t) {
-    int q = w + 4 * t;
+    int q = w + 4 * t, ln = lane;
+    dst[t] = 1024 * q;
     if (t == NFULL) {
-      const int xb = EXTRA == 1 ? 0 : EXTRA == 2 ? (w >> 1) : (w < 3 ? w : 0);
-      q = INSTR - EXTRA + xb;
+      const int slot = 16 * EXTRA * w + lane;
+      q = INSTR - EXTRA + slot / 64;
+      ln = slot % 64;
+      dst[t] = 1024 * (INSTR - EXTRA) + 256 * EXTRA * w;
     }
-    const int rl = lane >> 2, pc = lane & 3;
+    const int rl = ln >> 2, pc = ln & 3;
     if (q < A_INSTR) {
       const int r = 16 * q + rl;
       int row = m0 + r;
       row = row < g.M ? row : g.M - 1;
       src[t] = A + (int64_t)row * g.lda + swz(r, pc) * 8;
-      dst[t] = 16 * q * ROWB;
     } else {
       const int r = 16 * (q - A_INSTR) + rl;          // B-tile row 0..255
       int nrow = n0 + ((EPI == EPI_SWIGLU) ? (r & 127) : r);
       nrow = nrow < g.N ? nrow : g.N - 1;
       const bf16* base = (EPI == EPI_SWIGLU && r >= 128) ? B2 : B;
       src[t] = base + (int64_t)nrow * g.K + swz(r, pc) * 8;
-      dst[t] = (BM + 16 * (q - A_INSTR)) * ROWB;
     }
   }
-  // lanes of this wave that take part in its extra load (EXTRA = 1, 2), and
-  // whether this wave has one at all (EXTRA = 3; wave-uniform)
-  const bool my_part = EXTRA == 1 ? (lane >> 4) == w : EXTRA == 2 ? (lane >> 5) == (w & 1) : true;
-  const bool has_extra = EXTRA != 3 || w < 3;
+  // lanes of this wave that take part in its extra load (lane 0 always does,
+  // so no wave skips the instruction)
+  const bool my_part = lane < 16 * EXTRA;
   const int KT = g.K / BK;
-  // Stage kt of the K loop; tiles past the end re-fetch the last tile into a
-  // stage nobody reads any more.
+  // Stage kt of the K loop; in short K loops, stages past the end re-fetch
+  // the last tile into a buffer nobody reads any more.
   auto issue = [&](int kt) {
     const int kc = kt < KT ? kt : KT - 1;
     unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int t = 0; t < NLOAD; ++t) {
-      if (t < NFULL || (EXTRA == 3 ? has_extra : my_part))
+      if (t < NFULL || my_part)
         __builtin_amdgcn_global_load_lds((const void*)(src[t] + kc * BK),
                                          (__attribute__((address_space(3))) void*)(st + dst[t]), 16, 0, 0);
     }
@@ -242,12 +253,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   };
   // Wait until this wave's loads of the oldest stage in flight landed (the
   // NS - 2 younger stages may still be in flight).
-  auto wait_stage = [&]() {
-    if (has_extra)
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * NLOAD));
-    else
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * (NLOAD - 1)));
-  };
+  auto wait_stage = [&]() { __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * NLOAD)); };
 
   // prologue: stages 0 .. NS-2 in flight; stage 0 landed; its fragments read
 #pragma unroll
@@ -260,8 +266,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // loads of stage kt+1 landed (the wait also drains this wave's LDS reads,
   // so nobody refills a stage another wave still reads), barrier, read stage
   // kt+1's fragments into the other register set, and multiply the rest of
-  // stage kt.  After the last step the fragments read belong to a re-fetched
-  // stage and are never used; KT is even because K is a multiple of 64.
+  // stage kt.  KT is even because K is a multiple of 64.
   // The first H row blocks' products of a step go out before the refill,
   // the wait and the barrier, so the matrix core has work while the waves
   // meet; the rest interleave with the next stage's fragment reads.  (Best
@@ -281,11 +286,58 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], decltype(first)::value ? f32x4{} : acc[i][j],
                                                             0, 0, 0);
   };
+  // Residual epilogue: each 64-row pass's fp32 residual rows are loaded into
+  // registers one pass ahead; the first pass's loads go out in the K loop's
+  // tail where registers allow (below), so they land while the last
+  // products run.
+  constexpr int PPT = RC * (BN_OUT / 8) / 256;     // pieces per thread per pass
+  float* const Cf = (float*)g.C + (int64_t)prob * g.c_stride;
+  f32x4 rb[2][PPT][2];
+  // Every lane loads (a piece past the tile or the node reads a row that
+  // exists and drops the value): loads in conditional blocks would leave
+  // the compiler unsure which are in flight, and it would then wait for
+  // all of them before every store, prefetched rows included.
+  auto load_pass = [&](int rc0, f32x4 (&dstv)[PPT][2]) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
+      int m = m0 + rc0 + r, n = n0 + c8;
+      m = m < g.M ? m : g.M - 1;
+      n = n < g.N ? n : g.N - 8;
+      dstv[k][0] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n);
+      dstv[k][1] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n + 4);
+    }
+  };
+  // Residual loads issued in the tail (up to 176-row tiles: taller ones have
+  // no registers to spare for them beside the two fragment sets).
+  constexpr bool PREFETCH = EPI == EPI_RESID && TAIL && RB <= 11;
+  constexpr int PF = PREFETCH ? 2 * PPT : 0;
+  static_assert(NS == 4, "tail steps assume four stages");
+  // Step kinds: 0 = steady state; for K >= 192 the last three steps refill
+  // nothing (the stages they would fill lie past K):
+  //   1 (kt = KT-3): the residual epilogue may issue its first pass's loads
+  //     instead; waits for stage kt+1 with stage KT-1 and those loads
+  //     younger;
+  //   2 (kt = KT-2): waits for stage KT-1, the last one, with only the
+  //     residual loads younger;
+  //   3 (kt = KT-1): products only.
   auto step = [&](int kt, const bf16x8* fa_cur, const bf16x8* fb_cur, bf16x8* fa_nxt, bf16x8* fb_nxt,
-                  auto first) {
+                  auto first, auto kind) {
+    constexpr int KIND = decltype(kind)::value;
+    if constexpr (KIND == 3) {
+      mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, 0>{}, std::integral_constant<int, RB>{});
+      return;
+    }
     mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
-    issue(kt + NS - 1);
-    wait_stage();
+    if constexpr (KIND == 0) {
+      issue(kt + NS - 1);
+      wait_stage();
+    } else if constexpr (KIND == 1) {
+      if constexpr (PREFETCH) load_pass(0, rb[0]);
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(NLOAD + PF));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PF));
+    }
     lds_barrier();
     read_frags(kt + 1, fa_nxt, fb_nxt);
     mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, H>{}, std::integral_constant<int, RB>{});
@@ -298,11 +350,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - PER * NREAD, 0);
   };
-  step(0, fa0, fb0, fa1, fb1, std::true_type{});
-  step(1, fa1, fb1, fa0, fb0, std::false_type{});
-  for (int kt = 2; kt < KT; kt += 2) {
-    step(kt, fa0, fb0, fa1, fb1, std::false_type{});
-    step(kt + 1, fa1, fb1, fa0, fb0, std::false_type{});
+  using K0 = std::integral_constant<int, 0>;
+  step(0, fa0, fb0, fa1, fb1, std::true_type{}, K0{});
+  step(1, fa1, fb1, fa0, fb0, std::false_type{}, K0{});
+  if constexpr (TAIL) {   // K >= 192 (KT is even)
+    for (int kt = 2; kt < KT - 4; kt += 2) {
+      step(kt, fa0, fb0, fa1, fb1, std::false_type{}, K0{});
+      step(kt + 1, fa1, fb1, fa0, fb0, std::false_type{}, K0{});
+    }
+    step(KT - 4, fa0, fb0, fa1, fb1, std::false_type{}, K0{});
+    step(KT - 3, fa1, fb1, fa0, fb0, std::false_type{}, std::integral_constant<int, 1>{});
+    step(KT - 2, fa0, fb0, fa1, fb1, std::false_type{}, std::integral_constant<int, 2>{});
+    step(KT - 1, fa1, fb1, fa0, fb0, std::false_type{}, std::integral_constant<int, 3>{});
+  } else {
+    // short K (64 or 128): every step refills (past the end: a re-fetch of
+    // the last stage into a buffer nobody reads)
+    for (int kt = 2; kt < KT; kt += 2) {
+      step(kt, fa0, fb0, fa1, fb1, std::false_type{}, K0{});
+      step(kt + 1, fa1, fb1, fa0, fb0, std::false_type{}, K0{});
+    }
   }
   __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
   __syncthreads();
@@ -318,8 +384,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     // stores.  The last layer's segment-token rows also go to the caller's y,
     // rounded once to bf16.
     constexpr int NPASS = (BM + RC - 1) / RC;
-    constexpr int PPT = RC * (BN_OUT / 8) / 256;     // pieces per thread per pass
-    float* Cf = (float*)g.C + (int64_t)prob * g.c_stride;
     bf16* Y = nullptr;
     int y_rows = 0;
     if (g.desc != nullptr && layer == g.last_layer) {
@@ -332,28 +396,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     // in conditional blocks would again leave the compiler unsure what is in
     // flight (and it would wait for everything before the next piece).
     const int c_rows = max(0, min(BM, g.M - m0));
-    const __amdgpu_buffer_rsrc_t c_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Cf + (int64_t)m0 * g.ldc), 0, c_rows * g.ldc * 4, kRawBuffer);
+    const __amdgpu_buffer_rsrc_t c_rs = uniform_rsrc(Cf + (int64_t)m0 * g.ldc, c_rows * g.ldc * 4);
     const int y_tile_rows = Y != nullptr ? max(0, min(BM, y_rows - m0)) : 0;
-    const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
-        Y != nullptr ? (void*)(Y + (int64_t)m0 * g.ldc) : (void*)Cf, 0, y_tile_rows * g.ldc * 2, kRawBuffer);
-    f32x4 rb[2][PPT][2];
-    // Every lane loads (a piece past the tile or the node reads a row that
-    // exists and drops the value): loads in conditional blocks would leave
-    // the compiler unsure which are in flight, and it would then wait for
-    // all of them before every store, prefetched rows included.
-    auto load_pass = [&](int rc0, f32x4 (&dstv)[PPT][2]) {
-#pragma unroll
-      for (int k = 0; k < PPT; ++k) {
-        const int pc = tid + 256 * k, r = pc >> 5, c8 = (pc & 31) * 8;
-        int m = m0 + rc0 + r, n = n0 + c8;
-        m = m < g.M ? m : g.M - 1;
-        n = n < g.N ? n : g.N - 8;
-        dstv[k][0] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n);
-        dstv[k][1] = *(const f32x4*)(Cf + (int64_t)m * g.ldc + n + 4);
-      }
-    };
-    load_pass(0, rb[0]);
+    const __amdgpu_buffer_rsrc_t y_rs =
+        uniform_rsrc(Y != nullptr ? (const void*)(Y + (int64_t)m0 * g.ldc) : (const void*)Cf, y_tile_rows * g.ldc * 2);
+    if constexpr (!PREFETCH) load_pass(0, rb[0]);   // (else issued in the K loop's tail)
     static_for<NPASS>([&](auto PI) {
       constexpr int p = decltype(PI)::value, rc0 = RC * p;
       if (p + 1 < NPASS) load_pass(rc0 + RC, rb[(p + 1) & 1]);
@@ -560,7 +607,11 @@ static hipError_t launch_rb(const GemmArgs& g, hipStream_t st) {
   constexpr int BM = 16 * RB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN_OUT - 1) / BN_OUT) * g.P * g.batch;
-  hipLaunchKernelGGL((gemm_bf16_kernel<RB, EPI>), dim3(tiles), dim3(256), 0, st, g);
+  // K loops of at least six stages end with three steps that refill nothing
+  if (g.K >= 6 * BK)
+    hipLaunchKernelGGL((gemm_bf16_kernel<RB, EPI, true>), dim3(tiles), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<RB, EPI, false>), dim3(tiles), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
