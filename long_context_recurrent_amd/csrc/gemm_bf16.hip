@@ -14,13 +14,16 @@
 //  * Tile: a workgroup of 4 waves owns BM x 256 outputs, BM = 16 * RB rows,
 //    chosen per workload.  Each wave owns all BM rows and 64 columns: RB x 4
 //    accumulator blocks of 16 x 16 (16 * RB accumulator registers per lane).
-//  * Operands: K advances 32 per pipeline stage (one MFMA per block).
-//    Stages are filled straight from global memory into LDS by
-//    global_load_lds_dwordx4 (no staging registers), issued NS - 1 stages
-//    ahead; each 64-byte tile row keeps its four 16-byte chunks XOR-swizzled;
-//    a fragment read covers one 16-row block (1 KB) and its lanes hit 16
-//    different bank groups.  The fragments of the next stage are read while
-//    the MFMAs of the current one run.
+//  * Operands: K advances 32 per pipeline step (one MFMA per block).
+//    Operand tiles are filled straight from global memory into LDS by
+//    global_load_lds_dwordx4 (no staging registers): the A tile in four
+//    stages of k = 32 (64-byte rows), issued three steps ahead; the weight
+//    tile in three double stages of k = 64 (128-byte rows), issued every
+//    other step at least three steps ahead, so its loads fetch whole cache
+//    lines.  Rows keep their 16-byte chunks XOR-swizzled; a fragment read
+//    covers one 16-row block and its lanes hit 16 different bank groups.
+//    The fragments of the next step are read while the MFMAs of the current
+//    one run.
 //  * Schedule: tiles are numbered so that each of the 8 XCDs works through a
 //    contiguous range (same layer, same weight columns, neighbouring rows of
 //    every sequence of the batch), keeping the shared operand tiles in that
@@ -69,11 +72,13 @@ constexpr int RC = 64;          // epilogue rows staged per pass
 constexpr int CPITCH = 256 + 4; // staged tile pitch (floats)
 constexpr int LDS_BYTES = 160 * 1024;
 
-// Stages that fit in LDS (at most 4); each holds BM + 256 rows of 64 bytes.
-template <int RB>
-constexpr int n_stages() {
-  return (LDS_BYTES / ((16 * RB + BNB) * ROWB)) > 4 ? 4 : (LDS_BYTES / ((16 * RB + BNB) * ROWB));
-}
+// Operand staging in LDS: NSA stages of the A tile (k = 32: BM rows of 64
+// bytes) and NSB double stages of the B tile (k = 64: 256 rows of 128
+// bytes, whole cache lines per row, so each B wave load covers 8 full lines
+// instead of 16 half lines).
+constexpr int NSA = 4;
+constexpr int NSB = 3;
+constexpr int B_STAGE = BNB * 2 * ROWB;   // 32 KB
 
 // 16-byte chunk c (0..3) of tile row r sits at physical chunk
 // c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the same logical chunk of any 8 (or 16)
@@ -81,6 +86,11 @@ constexpr int n_stages() {
 // reads (lane L: row 16i + L % 16, chunk L / 16) are conflict-free whether the
 // LDS serves 128 or 256 bytes per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// 16-byte chunk c (0..7) of a 128-byte B row r sits at physical chunk
+// c ^ ((r >> 1) & 7): the same logical chunk of 16 consecutive rows covers
+// all sixteen 16-byte bank groups of 256 bytes.
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // Word 3 of a raw buffer resource on gfx9 parts (no format conversion), and a
@@ -143,14 +153,13 @@ template <int RB, int EPI, bool TAIL>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = 16 * RB;
   constexpr int BN_OUT = (EPI == EPI_SWIGLU) ? 128 : 256;
-  constexpr int NS = n_stages<RB>();
-  constexpr int STAGE = (BM + BNB) * ROWB;             // bytes per stage
-  constexpr int A_INSTR = BM / 16;                     // 1 KB wave loads per stage
-  constexpr int INSTR = A_INSTR + BNB / 16;
-  static_assert(NS >= 3, "pipeline depth");
-  static_assert(RC * CPITCH * 4 <= NS * STAGE, "epilogue staging fits");
+  constexpr int A_STAGE = BM * ROWB;                   // bytes per A stage
+  constexpr int B_BASE = NSA * A_STAGE;                 // first B double stage
+  constexpr int LDS_USED = B_BASE + NSB * B_STAGE;
+  static_assert(LDS_USED <= LDS_BYTES, "operand stages fit");
+  static_assert(RC * CPITCH * 4 <= LDS_USED, "epilogue staging fits");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_USED];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -175,98 +184,130 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   const bf16* __restrict__ B2 =
       (EPI == EPI_SWIGLU) ? (const bf16*)g.B2 + (int64_t)layer * g.b_stride : B;
 
-  // ---- direct global -> LDS loads.  A stage holds INSTR blocks of 16 tile
-  // rows (A rows, then B rows; block q at byte 1024 q), each filled by 1 KB
-  // of wave loads in which lane L brings tile row 16q + L/4, physical chunk
-  // L%4 (= logical chunk swz(row, L%4)).  Wave w issues the whole blocks
-  // q = w, w + 4, ... below INSTR - EXTRA (EXTRA = INSTR % 4).  The last
-  // EXTRA blocks are 64 * EXTRA 16-byte slots, split evenly: wave w brings
-  // slots 16 EXTRA w + l with its lanes l < 16 EXTRA (a quarter, half or
-  // three quarters of a wave load), written from LDS byte
-  // 1024 (INSTR - EXTRA) + 256 EXTRA w on.  Every wave issues the same
-  // number of loads per stage, so its vmcnt waits are constants.
-  constexpr int EXTRA = INSTR % 4;
-  constexpr int NFULL = (INSTR - EXTRA) / 4;
-  constexpr int NLOAD = NFULL + (EXTRA ? 1 : 0);       // loads per wave per stage
-  const bf16* src[NLOAD];
-  int dst[NLOAD];
+  // ---- direct global -> LDS loads (wave loads of 1 KB, lane L's 16 bytes
+  // at byte 16 L of the block).
+  // A stage: RB blocks of 16 rows; in block q lane L brings row 16q + L/4,
+  // physical chunk L%4 (= logical chunk swz(row, L%4)).  Wave w issues the
+  // blocks q = w, w + 4, ... below 4 NFA (NFA = RB / 4), and waves
+  // w < EXA = RB % 4 one more whole block, 4 NFA + w.  (The choice is
+  // wave-uniform: a load under a lane mask lets the compiler merge it with
+  // the next load across the branch, and the LDS address of the merged load
+  // is then taken from the wrong lanes.)
+  // B double stage: 32 blocks of 8 rows; in block b lane L brings row
+  // 8b + L/8, physical chunk L%8 (= logical chunk swz8(row, L%8)); wave w
+  // issues blocks w, w + 4, ..., w + 28.
+  // The vmcnt waits count this wave's own loads: NB per B double stage and
+  // NFA or NFA + 1 per A stage.
+  constexpr int EXA = RB % 4;
+  constexpr int NFA = RB / 4;
+  constexpr int NA = NFA + (EXA ? 1 : 0);              // A loads per stage, at most
+  constexpr int NB = 8;                                // B loads per wave per double stage
+  const bool a_extra = EXA != 0 && w < EXA;            // wave-uniform
+  const bf16* srca[NA];
+  int dsta[NA];
 #pragma unroll
-  for (int t = 0; t < NLOAD; ++t) {
-    int q = w + 4 * t, ln = lane;
-    dst[t] = 1024 * q;
-    if (t == NFULL) {
-      const int slot = 16 * EXTRA * w + lane;
-      q = INSTR - EXTRA + slot / 64;
-      ln = slot % 64;
-      dst[t] = 1024 * (INSTR - EXTRA) + 256 * EXTRA * w;
-    }
-    const int rl = ln >> 2, pc = ln & 3;
-    if (q < A_INSTR) {
-      const int r = 16 * q + rl;
-      int row = m0 + r;
-      row = row < g.M ? row : g.M - 1;
-      src[t] = A + (int64_t)row * g.lda + swz(r, pc) * 8;
-    } else {
-      const int r = 16 * (q - A_INSTR) + rl;          // B-tile row 0..255
-      int nrow = n0 + ((EPI == EPI_SWIGLU) ? (r & 127) : r);
-      nrow = nrow < g.N ? nrow : g.N - 1;
-      const bf16* base = (EPI == EPI_SWIGLU && r >= 128) ? B2 : B;
-      src[t] = base + (int64_t)nrow * g.K + swz(r, pc) * 8;
-    }
+  for (int t = 0; t < NA; ++t) {
+    const int q = t < NFA ? w + 4 * t : (a_extra ? 4 * NFA + w : 0);
+    dsta[t] = 1024 * q;
+    const int r = 16 * q + (lane >> 2);
+    int row = m0 + r;
+    row = row < g.M ? row : g.M - 1;
+    srca[t] = A + (int64_t)row * g.lda + swz(r, lane & 3) * 8;
   }
-  // lanes of this wave that take part in its extra load (lane 0 always does,
-  // so no wave skips the instruction)
-  const bool my_part = lane < 16 * EXTRA;
-  const int KT = g.K / BK;
-  // Stage kt of the K loop; in short K loops, stages past the end re-fetch
-  // the last tile into a buffer nobody reads any more.
-  auto issue = [&](int kt) {
-    const int kc = kt < KT ? kt : KT - 1;
-    unsigned char* st = smem + (kt % NS) * STAGE;
+  const bf16* srcb[NB];
 #pragma unroll
-    for (int t = 0; t < NLOAD; ++t) {
-      if (t < NFULL || my_part)
-        __builtin_amdgcn_global_load_lds((const void*)(src[t] + kc * BK),
-                                         (__attribute__((address_space(3))) void*)(st + dst[t]), 16, 0, 0);
-    }
+  for (int t = 0; t < NB; ++t) {
+    const int r = 8 * (w + 4 * t) + (lane >> 3);        // B-tile row 0..255
+    int nrow = n0 + ((EPI == EPI_SWIGLU) ? (r & 127) : r);
+    nrow = nrow < g.N ? nrow : g.N - 1;
+    const bf16* base = (EPI == EPI_SWIGLU && r >= 128) ? B2 : B;
+    srcb[t] = base + (int64_t)nrow * g.K + swz8(r, lane & 7) * 8;
+  }
+  const int KT = g.K / BK;                              // even: K is a multiple of 64
+  // A stage kt / B double stage d (k = 64 d .. 64 d + 63); in short K loops,
+  // stages past the end re-fetch the last one into a buffer nobody reads.
+  auto issue_a = [&](int kt) {
+    const int kc = kt < KT ? kt : KT - 1;
+    unsigned char* st = smem + (kt % NSA) * A_STAGE;
+#pragma unroll
+    for (int t = 0; t < NFA; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(srca[t] + kc * BK),
+                                       (__attribute__((address_space(3))) void*)(st + dsta[t]), 16, 0, 0);
+    if (a_extra)
+      __builtin_amdgcn_global_load_lds((const void*)(srca[NA - 1] + kc * BK),
+                                       (__attribute__((address_space(3))) void*)(st + dsta[NA - 1]), 16, 0, 0);
+  };
+  auto issue_b = [&](int d) {
+    const int dc = d < KT / 2 ? d : KT / 2 - 1;
+    unsigned char* st = smem + B_BASE + (d % NSB) * B_STAGE;
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(srcb[t] + dc * 2 * BK),
+                                       (__attribute__((address_space(3))) void*)(st + 1024 * (w + 4 * t)), 16, 0,
+                                       0);
   };
 
   f32x4 acc[RB][4];
 
-  // Fragments of one stage (k = 32): lane (r16 = lane % 16, c = lane / 16)
+  // Fragments of one step (k = 32): lane (r16 = lane % 16, c = lane / 16)
   // holds k = 8c..8c+7 of row r16 of each 16-row A block and of each
-  // 16-column B block -- one 16-byte read per block.
+  // 16-column B block -- one 16-byte read per block (B: half kt % 2 of its
+  // double stage).
   const int r16 = lane & 15, kc = lane >> 4;
   bf16x8 fa0[RB], fb0[4], fa1[RB], fb1[4];
   auto read_frags = [&](int kt, bf16x8* fa, bf16x8* fb) {
-    const unsigned char* st = smem + (kt % NS) * STAGE;
+    const unsigned char* sa = smem + (kt % NSA) * A_STAGE;
+    const unsigned char* sb = smem + B_BASE + ((kt >> 1) % NSB) * B_STAGE;
+    const int h4 = 4 * (kt & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = col_block<EPI>(w, j) + r16;
-      fb[j] = *(const bf16x8*)(st + (BM + r) * ROWB + swz(r, kc) * 16);
+      fb[j] = *(const bf16x8*)(sb + r * (2 * ROWB) + swz8(r, h4 + kc) * 16);
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int r = 16 * i + r16;
-      fa[i] = *(const bf16x8*)(st + r * ROWB + swz(r, kc) * 16);
+      fa[i] = *(const bf16x8*)(sa + r * ROWB + swz(r, kc) * 16);
     }
   };
-  // Wait until this wave's loads of the oldest stage in flight landed (the
-  // NS - 2 younger stages may still be in flight).
-  auto wait_stage = [&]() { __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((NS - 2) * NLOAD)); };
+  // vmcnt waits (lgkmcnt 0 as well: this wave's LDS reads drained, so nobody
+  // refills a buffer another wave still reads once past the barrier).  A step
+  // kt waits for A stage kt+1 (issued two steps earlier); loads issued after
+  // it: even kt: the B double stage issued with it, one A stage, then this
+  // step's A stage and B double stage; odd kt: one A stage with its B double
+  // stage, then this step's A stage.  The B double stage holding k-step kt+1
+  // was issued before that A stage.
+  // wait_loads(S, E): at most S A stages and E other loads of this wave
+  // younger than what is waited for.
+  auto wait_loads = [&](auto nstages, auto nother) {
+    constexpr int S = decltype(nstages)::value, E = decltype(nother)::value;
+    if (a_extra)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(S * (NFA + 1) + E));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(S * NFA + E));
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using INB = std::integral_constant<int, NB>;
+  using I2NB = std::integral_constant<int, 2 * NB>;
 
-  // prologue: stages 0 .. NS-2 in flight; stage 0 landed; its fragments read
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
-  wait_stage();
+  // prologue, in the order the steady state would have issued it: B double
+  // stage 0, A stages 0 and 1, B double stage 1, A stage 2; then A stage 0
+  // and B double stage 0 landed and the first fragments read
+  issue_b(0);
+  issue_a(0);
+  issue_a(1);
+  issue_b(1);
+  issue_a(2);
+  wait_loads(I2{}, INB{});
   lds_barrier();
   read_frags(0, fa0, fb0);
-  // One pipeline step: multiply part of the fragments of stage kt already in
-  // registers, refill the stage freed two steps ago, wait until this wave's
-  // loads of stage kt+1 landed (the wait also drains this wave's LDS reads,
-  // so nobody refills a stage another wave still reads), barrier, read stage
-  // kt+1's fragments into the other register set, and multiply the rest of
-  // stage kt.  KT is even because K is a multiple of 64.
+  // One pipeline step kt: multiply part of the fragments already in
+  // registers, refill A stage kt+3 (the one read two steps ago) and, on even
+  // steps, B double stage kt/2 + 2 (the one read by steps kt-2 and kt-1),
+  // wait until this wave's loads of k-step kt+1 landed, barrier, read k-step
+  // kt+1's fragments into the other register set, and multiply the rest.
   // The first H row blocks' products of a step go out before the refill,
   // the wait and the barrier, so the matrix core has work while the waves
   // meet; the rest interleave with the next stage's fragment reads.  (Best
@@ -312,13 +353,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // no registers to spare for them beside the two fragment sets).
   constexpr bool PREFETCH = EPI == EPI_RESID && TAIL && RB <= 11;
   constexpr int PF = PREFETCH ? 2 * PPT : 0;
-  static_assert(NS == 4, "tail steps assume four stages");
-  // Step kinds: 0 = steady state; for K >= 192 the last three steps refill
-  // nothing (the stages they would fill lie past K):
+  static_assert(NSA == 4 && NSB == 3, "step kinds assume four A stages and three B double stages");
+  // Step kinds: 0 = steady state (even / odd k-step); for K >= 192 the last
+  // four steps stop refilling what lies past K:
+  //   4 (kt = KT-4): refills A stage KT-1 only; waits for A stage KT-3 with
+  //     B double stage KT/2 - 1 and two A stages younger;
   //   1 (kt = KT-3): the residual epilogue may issue its first pass's loads
-  //     instead; waits for stage kt+1 with stage KT-1 and those loads
+  //     instead; waits for A stage KT-2 with A stage KT-1 and those loads
   //     younger;
-  //   2 (kt = KT-2): waits for stage KT-1, the last one, with only the
+  //   2 (kt = KT-2): waits for A stage KT-1, the last one, with only the
   //     residual loads younger;
   //   3 (kt = KT-1): products only.
   auto step = [&](int kt, const bf16x8* fa_cur, const bf16x8* fb_cur, bf16x8* fa_nxt, bf16x8* fb_nxt,
@@ -330,13 +373,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
     mfma_rows(fa_cur, fb_cur, first, std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
     if constexpr (KIND == 0) {
-      issue(kt + NS - 1);
-      wait_stage();
+      issue_a(kt + 3);
+      if ((kt & 1) == 0) {
+        issue_b((kt >> 1) + 2);
+        wait_loads(I2{}, I2NB{});
+      } else {
+        wait_loads(I2{}, INB{});
+      }
+    } else if constexpr (KIND == 4) {
+      issue_a(kt + 3);
+      wait_loads(I2{}, INB{});
     } else if constexpr (KIND == 1) {
       if constexpr (PREFETCH) load_pass(0, rb[0]);
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(NLOAD + PF));
+      wait_loads(I1{}, std::integral_constant<int, PF>{});
     } else {
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PF));
+      wait_loads(I0{}, std::integral_constant<int, PF>{});
     }
     lds_barrier();
     read_frags(kt + 1, fa_nxt, fb_nxt);
@@ -353,12 +404,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   using K0 = std::integral_constant<int, 0>;
   step(0, fa0, fb0, fa1, fb1, std::true_type{}, K0{});
   step(1, fa1, fb1, fa0, fb0, std::false_type{}, K0{});
-  if constexpr (TAIL) {   // K >= 192 (KT is even)
+  if constexpr (TAIL) {   // K >= 192
     for (int kt = 2; kt < KT - 4; kt += 2) {
       step(kt, fa0, fb0, fa1, fb1, std::false_type{}, K0{});
       step(kt + 1, fa1, fb1, fa0, fb0, std::false_type{}, K0{});
     }
-    step(KT - 4, fa0, fb0, fa1, fb1, std::false_type{}, K0{});
+    step(KT - 4, fa0, fb0, fa1, fb1, std::false_type{}, std::integral_constant<int, 4>{});
     step(KT - 3, fa1, fb1, fa0, fb0, std::false_type{}, std::integral_constant<int, 1>{});
     step(KT - 2, fa0, fb0, fa1, fb1, std::false_type{}, std::integral_constant<int, 2>{});
     step(KT - 1, fa1, fb1, fa0, fb0, std::false_type{}, std::integral_constant<int, 3>{});
@@ -446,7 +497,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // of one pass drain while the next is staged.
   constexpr int EP_PITCH = (EPI == EPI_SWIGLU) ? 128 + 4 : CPITCH;
   constexpr int EP_RC = (EPI == EPI_SWIGLU) ? BM : RC;
-  static_assert(EP_RC * EP_PITCH * 4 <= NS * STAGE, "epilogue staging fits");
+  static_assert(EP_RC * EP_PITCH * 4 <= LDS_USED, "epilogue staging fits");
   for (int rc0 = 0; rc0 < BM; rc0 += EP_RC) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
