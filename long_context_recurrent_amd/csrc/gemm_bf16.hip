@@ -28,9 +28,9 @@
 //    contiguous range (same layer, same weight columns, neighbouring rows of
 //    every sequence of the batch), keeping the shared operand tiles in that
 //    XCD's L2.
-//  * Epilogue: fp32 results are staged through LDS, so every global store is a
-//    coalesced 16-byte write and every bf16 rounding happens once, on the fp32
-//    value:
+//  * Epilogue: every bf16 rounding happens once, on the fp32 value; except
+//    for SwiGLU, fp32 results are staged through LDS, so every global store
+//    is a coalesced 16-byte write:
 //      EPI_QKV   : RoPE on the Q and K heads (partner column i + hd/2 read from
 //                  the staged tile), bf16 store; V heads are stored transposed
 //                  ([G * hd][n_pad], keys reordered within groups of 16) for
@@ -40,7 +40,10 @@
 //                  segment) are also written to the caller's y, rounded to bf16.
 //      EPI_SWIGLU: the B tile holds 128 gate rows then the 128 matching up
 //                  rows; a wave's gate and up blocks of the same output
-//                  columns sit in the same lanes; U = R(silu(gate) * up).
+//                  columns sit in the same lanes; U = R(silu(gate) * up),
+//                  computed and stored straight from the registers (the
+//                  products run with the operands swapped, so a lane holds
+//                  four consecutive columns of one row).
 //      EPI_STORE : fp32 store (LM-head logits; N a multiple of 8).
 //  Every output element accumulates over K in the same order whatever RB or
 //  the number of problems, so results do not depend on the wave width.
@@ -93,6 +96,7 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ (
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // Word 3 of a raw buffer resource on gfx9 parts (no format conversion), and a
 // store offset past any bound used here (the store is dropped).
 constexpr int kRawBuffer = 0x00020000;
@@ -319,13 +323,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // from zero (an explicit zero-initialised accumulator makes the register
   // allocator rotate the accumulators through copies on every trip of the K
   // loop).
+  // SwiGLU multiplies with the operands swapped (weights as the first), so
+  // its accumulator blocks hold C^T: the epilogue then finds one output row
+  // and four consecutive columns per lane (see there).
   auto mfma_rows = [&](const bf16x8* fa, const bf16x8* fb, auto first, auto I0, auto I1) {
 #pragma unroll
     for (int i = decltype(I0)::value; i < decltype(I1)::value; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], decltype(first)::value ? f32x4{} : acc[i][j],
-                                                            0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 c = decltype(first)::value ? f32x4{} : acc[i][j];
+        acc[i][j] = (EPI == EPI_SWIGLU) ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], c, 0, 0, 0)
+                                        : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], c, 0, 0, 0);
+      }
   };
   // Residual epilogue: each 64-row pass's fp32 residual rows are loaded into
   // registers one pass ahead; the first pass's loads go out in the K loop's
@@ -491,12 +500,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     });
     return;
   }
-  // The SwiGLU tile has 128 output columns: with a 132-float pitch all BM rows
-  // fit the stage buffers at once, so it takes a single pass.  Passes are
-  // separated by barriers that wait for LDS traffic only; the global stores
-  // of one pass drain while the next is staged.
-  constexpr int EP_PITCH = (EPI == EPI_SWIGLU) ? 128 + 4 : CPITCH;
-  constexpr int EP_RC = (EPI == EPI_SWIGLU) ? BM : RC;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // U = R(silu(gate) * up) straight from the registers: with the operands
+    // swapped, element e of block (i, j) in lane (r16, kc) is output row
+    // 16i + r16, column col_block(w, j) + 4kc + e, and the up block j + 2
+    // holds the same positions as the gate block j.  Each lane stores four
+    // consecutive bf16 outputs (8 bytes) per block pair through a buffer
+    // resource bounded to the tile's rows (rows past the node are dropped by
+    // the bound; N is a multiple of 4).
+    bf16* C = (bf16*)g.C + (int64_t)prob * g.c_stride;
+    const int c_rows = max(0, min(BM, g.M - m0));
+    const __amdgpu_buffer_rsrc_t u_rs = uniform_rsrc(C + (int64_t)m0 * g.ldc, c_rows * g.ldc * 2);
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gt = acc[i][j][e], up = acc[i][j + 2][e];
+          o[e] = (bf16)(gt * sigmoid_f(gt) * up);
+        }
+        const int n = n0 + 32 * w + 16 * j + 4 * kc;
+        const int off = n < g.N ? 2 * ((16 * i + r16) * g.ldc + n) : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), u_rs, off, 0, 0);
+      }
+    return;
+  }
+  // Passes are separated by barriers that wait for LDS traffic only; the
+  // global stores of one pass drain while the next is staged.
+  constexpr int EP_PITCH = CPITCH;
+  constexpr int EP_RC = RC;
   static_assert(EP_RC * EP_PITCH * 4 <= LDS_USED, "epilogue staging fits");
   for (int rc0 = 0; rc0 < BM; rc0 += EP_RC) {
 #pragma unroll
@@ -505,16 +539,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rl = 16 * i - rc0 + 4 * kc + e;
-        if (EPI == EPI_SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float gt = acc[i][j][e], up = acc[i][j + 2][e];
-            Cs[rl * EP_PITCH + 32 * w + 16 * j + r16] = gt * sigmoid_f(gt) * up;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Cs[rl * EP_PITCH + col_block<EPI>(w, j) + r16] = acc[i][j][e];
-        }
+        for (int j = 0; j < 4; ++j) Cs[rl * EP_PITCH + col_block<EPI>(w, j) + r16] = acc[i][j][e];
       }
     }
     __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
@@ -694,7 +720,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, int epi, int rb, hipStream_t st) 
       if (g.head_dim <= 0 || 256 % g.head_dim) return hipErrorInvalidValue;
       return launch_epi<EPI_QKV>(g, rb, st);
     case EPI_RESID: return launch_epi<EPI_RESID>(g, rb, st);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, rb, st);
+    case EPI_SWIGLU:
+      // four-column output pieces
+      if (g.N % 4) return hipErrorInvalidValue;
+      return launch_epi<EPI_SWIGLU>(g, rb, st);
     case EPI_STORE:
       // whole 8-column output pieces
       if (g.N % 8) return hipErrorInvalidValue;
