@@ -6,7 +6,9 @@
 // treated as batches).
 //
 // bf16 path (flash-style, CDNA4 MFMA).  Workgroup = (128-query block, query
-// head, node); each of its 4 waves owns 32 queries.  Key tiles of 64 rows
+// head, node), each of its 4 waves owning 32 queries; with four query heads
+// per key/value head, (32-query block, key/value head, node), wave w owning
+// the block's queries of query head 4 kvh + w.  Key tiles of 64 rows
 // and the matching V^T tiles (V is stored transposed by the QKV GEMM) stream
 // into LDS through buffer->LDS DMA loads, two tiles ahead, and are shared
 // by the 4 waves.  Both products run on v_mfma_f32_32x32x16_bf16:
@@ -87,37 +89,54 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TILE];
 
   const int n = a.n;
-  // Query blocks of 128 end at n, n - 128, ...: the partial block is the
-  // first one, whose queries see the fewest keys.  Workgroup order: the
-  // blocks heaviest first across the whole grid (longest-processing-time
-  // order, so no long block starts late), and within one block index the
-  // R = H/G query heads that share a key/value head dispatched to one XCD
-  // back to back (workgroup i runs on XCD i % 8), so they share its L2.
-  const int nqb = (n + 127) / 128;
   const int R = a.H / a.G;
-  const int per_level = a.H * a.P;
-  const int level = (int)blockIdx.x / per_level;
-  int li = (int)blockIdx.x - level * per_level;
-  if (((a.G * a.P) & 7) == 0) {
-    const int x = li & 7, j = li >> 3;
-    li = (x + 8 * (j / R)) * R + j % R;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hh = lane >> 5;
+  int layer, kvh, head, q0w, q_end;
+  if (R == 4) {
+    // Four query heads per K/V head: a workgroup takes 32 queries of all
+    // four (wave w: query head 4 kvh + w), so every wave needs the same key
+    // tiles and none idles at the tile barriers near the diagonal.  Query
+    // blocks of 32 end at n, n - 32, ... (the partial block is the first);
+    // workgroups run heaviest block first.
+    const int per_level = a.G * a.P;
+    const int level = (int)blockIdx.x / per_level;
+    const int grp = (int)blockIdx.x - level * per_level;   // (node, key/value head)
+    kvh = grp % a.G;
+    layer = a.l0 + grp / a.G;
+    head = kvh * R + w;
+    q_end = n - 32 * level;                                 // > 0
+    q0w = q_end - 32;                                       // may be negative in the first block
+  } else {
+    // Query blocks of 128 end at n, n - 128, ...: the partial block is the
+    // first one, whose queries see the fewest keys.  Workgroup order: the
+    // blocks heaviest first across the whole grid (longest-processing-time
+    // order, so no long block starts late), and within one block index the
+    // R = H/G query heads that share a key/value head dispatched to one XCD
+    // back to back (workgroup i runs on XCD i % 8), so they share its L2.
+    const int nqb = (n + 127) / 128;
+    const int per_level = a.H * a.P;
+    const int level = (int)blockIdx.x / per_level;
+    int li = (int)blockIdx.x - level * per_level;
+    if (((a.G * a.P) & 7) == 0) {
+      const int x = li & 7, j = li >> 3;
+      li = (x + 8 * (j / R)) * R + j % R;
+    }
+    const int qb = nqb - 1 - level;
+    const int grp = li / R;                       // (node, key/value head)
+    kvh = grp % a.G;
+    head = kvh * R + li % R;
+    layer = a.l0 + grp / a.G;
+    q0w = n - 128 * (nqb - qb) + 32 * w;          // may be negative in the first block
+    q_end = n - 128 * (nqb - 1 - qb);             // > 0
   }
-  const int qb = nqb - 1 - level;
-  const int grp = li / R;                       // (node, key/value head)
-  const int kvh = grp % a.G;
-  const int head = kvh * R + li % R;
-  const int layer = a.l0 + grp / a.G;
   const bf16* qkv = (const bf16*)a.qkv + (int64_t)layer * a.qkv_stride;
   const bf16* vt = (const bf16*)a.vt + (int64_t)layer * a.vt_stride + (int64_t)kvh * HD * a.vt_ld;
   const int kcol = (a.H + kvh) * HD;
 
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, r32 = lane & 31, hh = lane >> 5;
-  const int q0w = n - 128 * (nqb - qb) + 32 * w;   // may be negative in the first block
   const int q = q0w + r32;                         // < n; rows q < 0 do not exist
   const int qc = q < 0 ? 0 : q;
-  const int q_end = n - 128 * (nqb - 1 - qb);      // > 0
   const int ntile = (q_end + 63) / 64;
   const int wtiles = q0w + 32 > 0 ? (q0w + 32 + 63) / 64 : 0;
 
@@ -406,7 +425,9 @@ hipError_t launch_attention(const AttnArgs& a, bool use_bf16, hipStream_t st) {
   if (use_bf16) {
     // the tile loads address a node's keys and V^T with 32-bit buffer offsets
     if ((int64_t)a.n * a.ld_qkv * 2 > INT32_MAX || (int64_t)a.hd * a.vt_ld * 2 > INT32_MAX) return hipErrorInvalidValue;
-    dim3 grid(((a.n + 127) / 128) * a.H * a.P);
+    // four query heads per K/V head: one workgroup per 32 queries of the four;
+    // otherwise one per 128 queries of one head
+    dim3 grid(a.H == 4 * a.G ? ((a.n + 31) / 32) * a.G * a.P : ((a.n + 127) / 128) * a.H * a.P);
     switch (a.hd) {
       case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, st, a); break;
       case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, st, a); break;
