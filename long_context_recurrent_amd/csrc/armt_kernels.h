@@ -44,6 +44,7 @@ struct GemmArgs {
   const CallDesc* desc;      // y pointer and wave counter (nullptr: no y)
   int last_layer;            // layer whose segment rows also go to y
   int T;                     // segment rows
+  int ldb;                   // row stride of B in elements (0: K)
 };
 
 struct AttnArgs {

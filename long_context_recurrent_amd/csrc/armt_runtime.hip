@@ -1144,25 +1144,25 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     return launch_gemm_bf16(g, epi, gemm_rows(h, N, 256, K, P), st);
   };
   const int64_t Lo = (int64_t)l0;   // slab offsets of layer l0
-  // dX (fp32, layer-indexed slab) = dY W on the forward's grouped GEMM: dY as
-  // a bf16 pair along k ([n][hi | lo], from the per-layer scratch ysp)
-  // against the doubled transposed weights wt ([in][W^T | W^T])
+  // dX (fp32, layer-indexed slab) = dY W on the forward's grouped GEMM: the
+  // bf16 value of dY (the hi half of the per-layer scratch ysp, [n][hi | lo])
+  // against the transposed weights (the first half of wt, [in][W^T | W^T]);
+  // the gradient enters the product rounded once to bf16
   bf16* const ysp = (bf16*)(cx.ws + cx.lo.ysp);
   auto dx_gemm = [&](int Kx, const bf16* wt, float* C, int64_t c_ps, int N) -> hipError_t {
     GemmArgs g{};
     g.P = P; g.l0 = l0; g.batch = 1;
     g.A = ysp; g.a_stride = (int64_t)n * Kx; g.lda = Kx;
-    g.B = wt; g.b_stride = (int64_t)N * Kx;
-    g.M = n; g.N = N; g.K = Kx;
+    g.B = wt; g.b_stride = (int64_t)N * Kx; g.ldb = Kx;
+    g.M = n; g.N = N; g.K = Kx / 2;
     g.C = C; g.c_stride = c_ps; g.ldc = N;
     g.desc = nullptr; g.last_layer = L - 1; g.T = T;
     return launch_gemm_bf16(g, EPI_STORE, gemm_rows(h, N, 256, Kx, P), st);
   };
   // dW (fp32, [L][out][in], layer-indexed) += dY^T X on the forward's grouped
-  // GEMM, in one pass over dW: K runs over the node's rows twice, first with
-  // the bf16 hi parts of dY, then with its lo parts, against X both times
-  // (dY^T -> [out][hi | lo], X^T -> [in][X | X], each half n_pad rows with
-  // zeros past the node)
+  // GEMM, in one pass over dW: K runs over the node's rows with the bf16 value
+  // of dY against X (dY^T -> the first half of [out][2 n_pad], X^T -> the
+  // first half of [in][2 n_pad], n_pad rows with zeros past the node)
   const int n_pad = (n + 63) / 64 * 64;
   bf16* const ta = (bf16*)(cx.ws + cx.lo.ta);
   bf16* const tb = (bf16*)(cx.ws + cx.lo.tb);
@@ -1172,20 +1172,18 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
     const int64_t sa = (int64_t)out * k2, sb = (int64_t)in * k2;
     bf16* a0 = ta + Lo * sa;
     bf16* b0 = tb + Lo * sb;
-    hipError_t e = bw_transpose_bf16(dY, false, out, y_ps, n, n_pad, out, a0, a0 + n_pad, k2, sa, P, st);
+    hipError_t e = bw_transpose_bf16(dY, false, out, y_ps, n, n_pad, out, a0, nullptr, k2, sa, P, st);
     if (e != hipSuccess) return e;
     if ((e = bw_transpose_bf16(X16, true, in, x_ps, n, n_pad, in, b0, nullptr, k2, sb, P, st)) != hipSuccess)
-      return e;
-    if ((e = bw_transpose_bf16(X16, true, in, x_ps, n, n_pad, in, b0 + n_pad, nullptr, k2, sb, P, st)) != hipSuccess)
       return e;
     GemmArgs g{};
     g.P = P; g.l0 = l0; g.batch = 1;
     g.A = ta; g.a_stride = sa; g.lda = k2;
-    g.B = tb; g.b_stride = sb;
-    g.M = out; g.N = in; g.K = k2;
+    g.B = tb; g.b_stride = sb; g.ldb = k2;
+    g.M = out; g.N = in; g.K = n_pad;
     g.C = const_cast<void*>(dW); g.c_stride = (int64_t)out * in; g.ldc = in;   // caller's gradient buffer
     g.desc = nullptr; g.last_layer = L - 1; g.T = T;
-    return launch_gemm_bf16(g, EPI_RESID, h->mb ? h->mb : pick_row_blocks(out, in, 256, k2, P, h->cus), st);
+    return launch_gemm_bf16(g, EPI_RESID, h->mb ? h->mb : pick_row_blocks(out, in, 256, n_pad, P, h->cus), st);
   };
 
   // ---- recompute the forward of each node
@@ -1266,10 +1264,11 @@ hipError_t backward_wave(BwCtx& cx, int c, int l0, int P, const void* dy, float*
   else BW_TRY(gg(dh, nd, 1, d, Uo, nF, F, 1, dW_d, (int64_t)d * F, F, 1, d, F, n, 1, P, st));
   BW_TRY(bw_swiglu_bwd(Gt, Up, dUo, dG, dUp, nF, nF, P, st));
   if (wb) {
-    // db = dG W_g + dUp W_u as one product: [dG | dUp] pairs against [W_g^T | W_u^T] doubled
+    // db = dG W_g + dUp W_u as one product: [dG | dUp] (bf16 values, the hi
+    // halves of [dG_hi | dUp_hi | dG_lo | dUp_lo]) against [W_g^T | W_u^T]
     bf16* y0 = ysp + Lo * n * 4 * F;
-    BW_TRY(bw_split_bf16(dG, F, nF, n, F, y0, 4 * F, (int64_t)n * 4 * F, F, P, st));
-    BW_TRY(bw_split_bf16(dUp, F, nF, n, F, y0 + 2 * F, 4 * F, (int64_t)n * 4 * F, F, P, st));
+    BW_TRY(bw_split_bf16(dG, F, nF, n, F, y0, 4 * F, (int64_t)n * 4 * F, 2 * F, P, st));
+    BW_TRY(bw_split_bf16(dUp, F, nF, n, F, y0 + F, 4 * F, (int64_t)n * 4 * F, 2 * F, P, st));
     BW_TRY(dx_gemm(4 * F, (const bf16*)(cx.ws + cx.lo.wtgu), cx.f(cx.lo.db), nd, d));
   } else {
     BW_TRY(gg(dG, nF, F, 1, W_g, (int64_t)F * d, d, 1, db, nd, d, 1, n, d, F, 0, P, st));
@@ -1408,21 +1407,21 @@ int armt_backward(armt_handle* h, int32_t schedule, const void* x, int32_t n_seg
     cx.g_attn = g32;
     cx.g_mlp = g32 + Ld;
     cx.w_beta = g32 + 2 * Ld;
-    // transposed weights, each twice along k, for the input-gradient products
+    // transposed weights for the input-gradient products ([in][out] rows of
+    // ld elements; W_g^T and W_u^T side by side for the one gate/up product)
     const int hd = c.n_heads * c.head_dim;
-    struct { const void* w; int out, in; size_t at; int ld, off0, off1; } tw[] = {
-        {h->w.w_down, d, F, cx.lo.wtd, 2 * d, 0, d},
-        {h->w.w_gate, F, d, cx.lo.wtgu, 4 * F, 0, F},
-        {h->w.w_up, F, d, cx.lo.wtgu, 4 * F, 2 * F, 3 * F},
-        {h->w.w_o, d, hd, cx.lo.wto, 2 * d, 0, d},
-        {h->w.w_qkv, qd, d, cx.lo.wtq, 2 * qd, 0, qd}};
+    struct { const void* w; int out, in; size_t at; int ld, off; } tw[] = {
+        {h->w.w_down, d, F, cx.lo.wtd, 2 * d, 0},
+        {h->w.w_gate, F, d, cx.lo.wtgu, 4 * F, 0},
+        {h->w.w_up, F, d, cx.lo.wtgu, 4 * F, F},
+        {h->w.w_o, d, hd, cx.lo.wto, 2 * d, 0},
+        {h->w.w_qkv, qd, d, cx.lo.wtq, 2 * qd, 0}};
     for (const auto& t : tw) {
       bf16* dst = (bf16*)((char*)workspace + t.at);
       const int64_t dps = (int64_t)t.in * t.ld;
-      for (int off : {t.off0, t.off1})
-        if ((e = bw_transpose_bf16(t.w, true, t.in, (int64_t)t.out * t.in, t.out, t.out, t.in, dst + off, nullptr,
-                                   t.ld, dps, L, st)) != hipSuccess)
-          return hip_fail(e, "transposed weights");
+      if ((e = bw_transpose_bf16(t.w, true, t.in, (int64_t)t.out * t.in, t.out, t.out, t.in, dst + t.off, nullptr,
+                                 t.ld, dps, L, st)) != hipSuccess)
+        return hip_fail(e, "transposed weights");
     }
   } else {
     cx.g_attn = (const float*)h->w.g_attn;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     int nrow = n0 + ((EPI == EPI_SWIGLU) ? (r & 127) : r);
     nrow = nrow < g.N ? nrow : g.N - 1;
     const bf16* base = (EPI == EPI_SWIGLU && r >= 128) ? B2 : B;
-    srcb[t] = base + (int64_t)nrow * g.K + swz8(r, lane & 7) * 8;
+    srcb[t] = base + (int64_t)nrow * (g.ldb ? g.ldb : g.K) + swz8(r, lane & 7) * 8;
   }
   const int KT = g.K / BK;                              // even: K is a multiple of 64
   // A stage kt / B double stage d (k = 64 d .. 64 d + 63); in short K loops,
