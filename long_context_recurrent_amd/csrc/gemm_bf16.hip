@@ -315,10 +315,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
   // The first H row blocks' products of a step go out before the refill,
   // the wait and the barrier, so the matrix core has work while the waves
   // meet; the rest interleave with the next stage's fragment reads.  (Best
-  // split measured per GEMM: a quarter of the rows for gate/up and QKV,
-  // half for the residual GEMMs, whose down projection runs the longest
-  // K loop.)
-  constexpr int H = (EPI == EPI_RESID) ? RB / 2 : RB / 4;
+  // split measured per GEMM: a quarter of the rows for gate/up and QKV, a
+  // third for the residual GEMMs; a third or half for gate/up, half or a
+  // quarter for the residual GEMMs measured slower.)
+  constexpr int H = (EPI == EPI_RESID) ? RB / 3 : RB / 4;
   // Products of row blocks I0 .. I1-1.  The first stage's products start
   // from zero (an explicit zero-initialised accumulator makes the register
   // allocator rotate the accumulators through copies on every trip of the K
