@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
   constexpr int TILE = K_BYTES + V_BYTES;
   constexpr int NBUF = HD >= 128 ? 2 : 3;
   constexpr int K_BLOCKS = K_BYTES / 1024;    // 1 KB wave loads per tile
+  static_assert(K_BLOCKS % 4 == 0, "a wave's K and V^T blocks follow from the load index alone");
   constexpr int LOADS = (TILE / 1024) / 4;    // per wave per tile
   constexpr int KROWS = 1024 / (HD * 2);      // K rows per 1 KB load
   constexpr int ES = HD / 16, DB = HD / 32;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
   for (int i = 0; i < LOADS; ++i) {
     const int b = w + 4 * i;
     dst[i] = b * 1024;
-    if (b < K_BLOCKS) {
+    if (4 * i < K_BLOCKS) {   // == (b < K_BLOCKS): K_BLOCKS is a multiple of 4 and w < 4
       const int r = b * KROWS + lane / CH;             // key row in the tile
       voffs[i] = 2 * (r * a.ld_qkv + kcol + swzc<CH>(r, lane % CH) * 8);
     } else {
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256, HD <= 64 ? 3 : 2) void attn_bf16_kernel(AttnAr
     unsigned char* st = smem + (t % NBUF) * TILE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      if (w + 4 * i < K_BLOCKS)
+      if (4 * i < K_BLOCKS)   // compile-time: no branch per load and tile
         buffer_to_lds(qkv + (int64_t)tt * 64 * a.ld_qkv, k_bytes - tt * 64 * a.ld_qkv * 2, st + dst[i], voffs[i]);
       else
         buffer_to_lds(vt + tt * 64, v_bytes - tt * 128, st + dst[i], voffs[i]);
